@@ -1,0 +1,357 @@
+"""Stage-count, LDS-footprint and occupancy model, and a ring-schedule simulator.
+
+TEST INFRASTRUCTURE ONLY (see oracle/__init__.py).
+
+Sources:
+  * "Lesson 6: Shared Memory layout and async pipeline" (learn.payai.win,
+    CUTLASS course), section 4 (performance trade-offs): the number of loads
+    that must be in flight is the ceiling of T_copy / T_compute, plus one stage
+    being computed on; the staging buffer grows linearly in the stage count,
+    S * (tile_A + tile_B) * sizeof(T); the resident-block count is the buffer
+    capacity divided by the per-block footprint, rounded down.  The exercise
+    at the end of that page fixes three values of the stage formula and says
+    both arguments must be positive integers.
+  * "cute(9) multistage_gemm", sections 4-6 and 8: the ring state (next global
+    K tile to load, slot being read, slot being written), the prologue that
+    fills S-1 slots, the steady state that waits until at most S-2 batches are
+    in flight, synchronises, prefetches and computes, and the worked trace for
+    K=256, BK=32, S=3.
+  * The same lesson, sections 2 and 3: the three-phase order (wait, barrier,
+    issue load k+S-1 into the free slot, compute slot k; then drain) and the
+    read-after-write / write-after-read hazards that it must avoid.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+
+# --------------------------------------------------------------------------
+# Stage-count and footprint model
+
+def minimum_stages(copy_cycles: int, compute_cycles: int) -> int:
+    """Smallest stage count that hides a copy latency behind compute.
+
+    In-flight loads >= ceil(copy / compute), plus the one stage being computed
+    on.  Both arguments must be positive integers (anything else raises).
+    Written with integer arithmetic only: ceil(c / t) = -((-c) // t)."""
+    for v in (copy_cycles, compute_cycles):
+        if isinstance(v, bool) or not isinstance(v, int) or v <= 0:
+            raise ValueError("copy and compute cycle counts must be positive integers")
+    in_flight = -((-copy_cycles) // compute_cycles)
+    return in_flight + 1
+
+
+def lds_bytes(tile_m: int, tile_n: int, tile_k: int, stages: int,
+              elem_bytes: int = 2) -> int:
+    """Staging-buffer footprint S * (tile_m*tile_k + tile_k*tile_n) * sizeof(T)."""
+    if min(tile_m, tile_n, tile_k, stages, elem_bytes) <= 0:
+        raise ValueError("all sizes must be positive")
+    return stages * (tile_m * tile_k + tile_k * tile_n) * elem_bytes
+
+
+def blocks_per_unit(footprint_bytes: int, capacity_bytes: int,
+                    other_limit: int | None = None) -> int:
+    """Resident blocks per compute unit: floor(capacity / footprint), further
+    capped by any other per-unit limit (waves, registers, hardware slots)."""
+    if footprint_bytes <= 0 or capacity_bytes <= 0:
+        raise ValueError("footprint and capacity must be positive")
+    n = capacity_bytes // footprint_bytes
+    if other_limit is not None:
+        n = min(n, other_limit)
+    return n
+
+
+# --------------------------------------------------------------------------
+# Ring-schedule simulator
+#
+# A schedule is a list of operations executed identically by every thread of
+# the block.  The simulator replays it against a worst-case memory system in
+# which an outstanding load completes only when a wait forces it, and checks
+# the invariants the pages state:
+#   RAW   a slot is read only after the load that filled it was retired by a
+#         wait that precedes a block-wide barrier that precedes the read;
+#   WAR   a slot is refilled only after a barrier that follows every read of
+#         its previous occupant;
+#   every K tile is loaded exactly once and computed on in order, fragment by
+#   fragment, from the slot it was loaded into;
+#   never more than S-1 tiles are loaded but not yet retired.
+
+@dataclass
+class Op:
+    kind: str            # "issue", "fence", "wait", "sync", "read", "compute"
+    tile: int = -1
+    slot: int = -1
+    frag: int = -1
+    n: int = -1          # wait: how many units may remain outstanding
+
+
+@dataclass
+class SimResult:
+    ok: bool
+    errors: list = field(default_factory=list)
+    issued: list = field(default_factory=list)      # (tile, slot) in issue order
+    reads: list = field(default_factory=list)       # (slot, tile, frag)
+    computed: list = field(default_factory=list)    # (tile, frag)
+    max_in_flight: int = 0
+
+
+def simulate(ops: list[Op], ntile: int, stages: int, nfrag: int,
+             units: str = "groups") -> SimResult:
+    """Replay `ops`.  `units` says what a wait counts: "groups" (a fence
+    closes a batch; waits count batches, empty batches included) or "loads"
+    (every issue is one counted unit, no fences)."""
+    res = SimResult(ok=True)
+    slot_tile = [None] * stages         # tile currently held by each slot
+    slot_ready = [False] * stages       # retired by a wait and published by a barrier
+    slot_retired = [False] * stages     # retired by a wait, not yet published
+    slot_last_read_epoch = [-1] * stages
+    epoch = 0                           # barrier count
+    outstanding = []                    # list of units; each unit = list of (tile, slot)
+    open_group = []
+    loaded = set()
+    frag_regs = {}                      # frag -> (tile, slot) of the last read of that fragment
+
+    def err(msg):
+        res.ok = False
+        res.errors.append(msg)
+
+    def in_flight_tiles():
+        tiles = {t for u in outstanding for (t, _) in u}
+        tiles |= {t for (t, _) in open_group}
+        return len(tiles)
+
+    for op in ops:
+        if op.kind == "issue":
+            t, s = op.tile, op.slot
+            if not (0 <= t < ntile):
+                err(f"issue of tile {t} outside 0..{ntile - 1}")
+            if t in loaded:
+                err(f"tile {t} loaded twice")
+            loaded.add(t)
+            if slot_tile[s] is not None and slot_last_read_epoch[s] >= epoch:
+                err(f"WAR: slot {s} refilled with tile {t} before a barrier after its last read")
+            slot_tile[s] = t
+            slot_ready[s] = False
+            slot_retired[s] = False
+            res.issued.append((t, s))
+            if units == "groups":
+                open_group.append((t, s))
+            else:
+                outstanding.append([(t, s)])
+            res.max_in_flight = max(res.max_in_flight, in_flight_tiles())
+        elif op.kind == "fence":
+            outstanding.append(open_group)
+            open_group = []
+        elif op.kind == "wait":
+            keep = max(op.n, 0)
+            while len(outstanding) > keep:
+                unit = outstanding.pop(0)
+                for (t, s) in unit:
+                    if slot_tile[s] == t:
+                        slot_retired[s] = True
+        elif op.kind == "sync":
+            epoch += 1
+            for s in range(stages):
+                if slot_retired[s]:
+                    slot_ready[s] = True
+        elif op.kind == "read":
+            s = op.slot
+            t = slot_tile[s]
+            res.reads.append((s, t, op.frag))
+            frag_regs[op.frag] = (t, s, slot_ready[s])
+            slot_last_read_epoch[s] = epoch
+        elif op.kind == "compute":
+            got = frag_regs.get(op.frag)
+            if got is None:
+                err(f"compute of tile {op.tile} fragment {op.frag} with no fragment read")
+                continue
+            t, s, ready = got
+            if t != op.tile:
+                err(f"compute of tile {op.tile} fragment {op.frag} used tile {t} from slot {s}")
+            elif not ready:
+                err(f"RAW: tile {t} read from slot {s} before it was retired and published")
+            res.computed.append((op.tile, op.frag))
+        else:
+            raise ValueError(op.kind)
+
+    expect = [(t, f) for t in range(ntile) for f in range(nfrag)]
+    if res.computed != expect:
+        err("tiles/fragments were not computed exactly once, in order")
+    if sorted(loaded) != list(range(ntile)):
+        err("not every tile was loaded")
+    if res.max_in_flight > stages - 1:
+        err(f"{res.max_in_flight} tiles in flight with {stages} stages")
+    return res
+
+
+def schedule_cute_multistage(ntile: int, stages: int, nfrag: int) -> list[Op]:
+    """The ring schedule of the multistage kernel walked through in
+    "cute(9) multistage_gemm" sections 5 and 6: prologue of S-1 batches, one
+    fence per batch; then per K tile and per K fragment: at the last fragment
+    wait until at most S-2 batches are in flight, barrier, advance the read
+    slot; prefetch the next fragment; at the first fragment issue the next
+    global tile (if any remain) and fence unconditionally; compute.  The
+    prologue only issues tiles that exist (the page assumes ntile >= S-1).
+    The page has two K fragments per tile; with one the prefetch would
+    overwrite the fragment about to be used, so nfrag >= 2 is required."""
+    if nfrag < 2:
+        raise ValueError("the walked-through schedule needs at least two fragments per tile")
+    ops: list[Op] = []
+    itile_to_read = 0
+    ismem_read = 0
+    ismem_write = 0
+    for _ in range(stages - 1):
+        if itile_to_read < ntile:
+            ops.append(Op("issue", tile=itile_to_read, slot=ismem_write))
+        ops.append(Op("fence"))
+        itile_to_read += 1
+        ismem_write += 1
+    itile_to_read = min(itile_to_read, ntile)
+    ismem_write %= stages
+    ops.append(Op("wait", n=stages - 2))
+    ops.append(Op("sync"))
+    # Fragment registers are named by the fragment index; which tile's data a
+    # fragment holds is what the compute check verifies.
+    ops.append(Op("read", slot=ismem_read, frag=0))
+    for itile in range(ntile):
+        for ik in range(nfrag):
+            ik_next = (ik + 1) % nfrag
+            if ik == nfrag - 1:
+                ops.append(Op("wait", n=stages - 2))
+                ops.append(Op("sync"))
+                ismem_read = (ismem_read + 1) % stages
+            ops.append(Op("read", slot=ismem_read, frag=ik_next))
+            if ik == 0:
+                if itile_to_read < ntile:
+                    ops.append(Op("issue", tile=itile_to_read, slot=ismem_write))
+                    itile_to_read += 1
+                    ismem_write = (ismem_write + 1) % stages
+                ops.append(Op("fence"))
+            ops.append(Op("compute", tile=itile, frag=ik))
+    return ops
+
+
+def schedule_three_phase(ntile: int, stages: int, nfrag: int,
+                         wait_counts: list[int] | None = None,
+                         loads_per_tile: int = 1) -> list[Op]:
+    """The three-phase order of the CUTLASS lesson, section 2, counted in
+    individual loads (no fences): prologue issues tiles 0..S-2; then for each
+    tile k: wait, barrier, issue tile k+S-1 into slot (k+S-1) mod S if it
+    exists, read and compute every fragment of slot k mod S.  `wait_counts[k]`
+    is the number of loads allowed to remain outstanding at tile k; by default
+    the loosest safe value is derived here."""
+    ops: list[Op] = []
+    for t in range(min(stages - 1, ntile)):
+        for _ in range(loads_per_tile):
+            ops.append(Op("issue_part", tile=t, slot=t % stages))
+    for k in range(ntile):
+        if wait_counts is None:
+            # loads issued after tile k's loads, so far: tiles k+1 .. min(k+S-2, ntile-1)
+            n = loads_per_tile * max(0, min(k + stages - 2, ntile - 1) - k)
+        else:
+            n = wait_counts[k]
+        ops.append(Op("wait", n=n))
+        ops.append(Op("sync"))
+        nxt = k + stages - 1
+        if nxt < ntile:
+            for _ in range(loads_per_tile):
+                ops.append(Op("issue_part", tile=nxt, slot=nxt % stages))
+        for f in range(nfrag):
+            ops.append(Op("read", slot=k % stages, frag=f))
+            ops.append(Op("compute", tile=k, frag=f))
+    return ops
+
+
+def simulate_loads(ops: list[Op], ntile: int, stages: int, nfrag: int,
+                   loads_per_tile: int) -> SimResult:
+    """Replay a schedule whose issues are split into `loads_per_tile` counted
+    loads per tile ("issue_part" ops); a tile is retired once all its parts
+    are.  Waits count loads."""
+    res = SimResult(ok=True)
+    slot_tile = [None] * stages
+    slot_parts_done = [0] * stages
+    slot_published = [False] * stages
+    slot_last_read_epoch = [-1] * stages
+    epoch = 0
+    outstanding = []            # (tile, slot) per load, in issue order
+    issued_parts = {}
+    frag_regs = {}
+
+    def err(msg):
+        res.ok = False
+        res.errors.append(msg)
+
+    for op in ops:
+        if op.kind == "issue_part":
+            t, s = op.tile, op.slot
+            if not (0 <= t < ntile):
+                err(f"issue of tile {t} outside 0..{ntile - 1}")
+            parts = issued_parts.get(t, 0)
+            if parts == 0:
+                if slot_tile[s] is not None and slot_last_read_epoch[s] >= epoch:
+                    err(f"WAR: slot {s} refilled with tile {t} before a barrier after its last read")
+                slot_tile[s] = t
+                slot_parts_done[s] = 0
+                slot_published[s] = False
+                res.issued.append((t, s))
+            elif parts >= loads_per_tile:
+                err(f"tile {t} loaded twice")
+            issued_parts[t] = parts + 1
+            outstanding.append((t, s))
+            in_flight = len({tt for (tt, _) in outstanding})
+            res.max_in_flight = max(res.max_in_flight, in_flight)
+        elif op.kind == "wait":
+            keep = max(op.n, 0)
+            while len(outstanding) > keep:
+                t, s = outstanding.pop(0)
+                if slot_tile[s] == t:
+                    slot_parts_done[s] += 1
+        elif op.kind == "sync":
+            epoch += 1
+            for s in range(stages):
+                if slot_tile[s] is not None and slot_parts_done[s] == loads_per_tile:
+                    slot_published[s] = True
+        elif op.kind == "read":
+            s = op.slot
+            frag_regs[op.frag] = (slot_tile[s], s, slot_published[s])
+            res.reads.append((s, slot_tile[s], op.frag))
+            slot_last_read_epoch[s] = epoch
+        elif op.kind == "compute":
+            t, s, ready = frag_regs[op.frag]
+            if t != op.tile:
+                err(f"compute of tile {op.tile} used tile {t} from slot {s}")
+            elif not ready:
+                err(f"RAW: tile {t} read from slot {s} before all its loads were retired and published")
+            res.computed.append((op.tile, op.frag))
+        else:
+            raise ValueError(op.kind)
+    expect = [(t, f) for t in range(ntile) for f in range(nfrag)]
+    if res.computed != expect:
+        err("tiles/fragments were not computed exactly once, in order")
+    if sorted(issued_parts) != list(range(ntile)) or any(
+            v != loads_per_tile for v in issued_parts.values()):
+        err("not every tile was loaded completely")
+    if res.max_in_flight > stages - 1:
+        err(f"{res.max_in_flight} tiles in flight with {stages} stages")
+    return res
+
+
+def loosest_wait_counts(ntile: int, stages: int, loads_per_tile: int) -> list[int]:
+    """For the three-phase order: the largest number of loads that may remain
+    outstanding when tile k is about to be consumed, found by search against
+    the simulator (largest n whose schedule still passes, tile by tile)."""
+    counts: list[int] = []
+    for k in range(ntile):
+        best = 0
+        for n in range(0, loads_per_tile * stages + 1):
+            trial = counts + [n] + [0] * (ntile - k - 1)
+            ops = schedule_three_phase(ntile, stages, 1, trial, loads_per_tile)
+            r = simulate_loads(ops, ntile, stages, 1, loads_per_tile)
+            # only the RAW check of tile k matters for this n
+            raw_k = [e for e in r.errors if e.startswith(f"RAW: tile {k} ")]
+            if not raw_k:
+                best = n
+            else:
+                break
+        counts.append(best)
+    return counts
