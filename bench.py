@@ -1,0 +1,278 @@
+"""Benchmark of the stage-pipelined fp16 TN GEMM on one MI355X.
+
+One step = one D = A @ B^T call (the whole hot path: prologue, pipelined
+mainloop and epilogue in one kernel) on inputs already resident in HBM.
+
+Prints ONE JSON line (rank 0):
+  value        whole-job TFLOP/s = 2 M N K * steps / timed wall time
+  roofline     the GEMM kernel against the dense fp16 MFMA peak: achieved =
+               2 M N K per launch / mean launch duration (HIP events around
+               each launch on the stream it is launched on); traffic = HBM
+               bytes per launch from the committed rocprofv3 counter summary,
+               or null if the kernel source changed since it was taken
+  cpu_baseline the CPU oracle timed on a bounded row sample of the same
+               workload, on this host's cores
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fp16 GEMM TFLOP/s at M=N=K=4096/8192 and % of MI355X fp16 MFMA peak"
+PEAK_TFLOPS = 2516.6          # MI355X dense fp16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "stage_pipelined_mainloop_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch from profiles/traffic_<workload>.json when it was
+    measured on the current kernel source; otherwise None."""
+    p = os.path.join(PROFILES, f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(A, B, target_s: float):
+    import oracle
+    M, K = A.shape
+    N = B.shape[0]
+    # calibrate on a few rows, then size the sample to about target_s
+    t0 = time.perf_counter()
+    oracle.gemm_tn_f64_rows(A, B, 0, 2)
+    dt = max(time.perf_counter() - t0, 1e-6)
+    rows = int(max(2, min(M, 2 * target_s / dt)))
+    t0 = time.perf_counter()
+    oracle.gemm_tn_f64_rows(A, B, 0, rows)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * N * K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of D ({rows} x {N} outputs, K={K}), fp64 accumulation, "
+                      f"{dt:.1f} s wall"}
+
+
+def time_launches(fn, steps: int, warmup: int):
+    """Mean and min milliseconds of `fn` (one launch on the current stream),
+    measured with HIP events around each launch."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for s, e in ev:
+        s.record(stream)
+        fn()
+        e.record(stream)
+    torch.cuda.synchronize()
+    ms = [s.elapsed_time(e) for s, e in ev]
+    return sum(ms) / len(ms), min(ms)
+
+
+def variant_info(cfg):
+    import stage_pipelined_mainloop_amd as sg
+    st, info = sg.sg_query_config(cfg)
+    d = info.as_dict()
+    d["query_status"] = st
+    return d
+
+
+def mode_variants(args) -> int:
+    """Time every compiled variant on one workload; one JSON line each."""
+    import numpy as np
+    import torch
+
+    import stage_pipelined_mainloop_amd as sg
+    from stage_pipelined_mainloop_amd import inputs
+    M, N, K, dist, seed = inputs.WORKLOADS[args.workload]
+    A, B = inputs.workload(args.workload)
+    alpha = float(np.float32(1.0 / math.sqrt(K))) if args.workload == "attn_scores" else None
+    a = torch.from_numpy(A).cuda()
+    b = torch.from_numpy(B).cuda()
+    d = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    for c in sg.configs():
+        mean, mn = time_launches(lambda: sg.gemm(a, b, out=d, alpha=alpha, config=c),
+                                 args.steps, args.warmup)
+        t = 2.0 * M * N * K / (mean / 1e3) / 1e12
+        print(json.dumps({"mode": "variants", "workload": args.workload,
+                          "variant": c.as_tuple(), "ms_mean": round(mean, 4),
+                          "ms_min": round(mn, 4), "tflops": round(t, 1),
+                          "pct_peak": round(100 * t / PEAK_TFLOPS, 2),
+                          "info": variant_info(c)}), flush=True)
+    return 0
+
+
+def mode_ksweep(args) -> int:
+    """M = N = 2048, K in the sweep list, every compiled stage count of the
+    128x128x32 and 256x256x32 (8-wave) tiles; LDS bytes and occupancy from
+    the library's query."""
+    import torch
+
+    import stage_pipelined_mainloop_amd as sg
+    from stage_pipelined_mainloop_amd import inputs
+    for K in inputs.KSWEEP_K:
+        A, B = inputs.ksweep(K)
+        a = torch.from_numpy(A).cuda()
+        b = torch.from_numpy(B).cuda()
+        M = N = inputs.KSWEEP_MN
+        d = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        for c in sg.configs():
+            if c.tile_k != 32 or (c.tile_m, c.tile_n, c.waves) not in ((128, 128, 4), (256, 256, 8)):
+                continue
+            mean, mn = time_launches(lambda: sg.gemm(a, b, out=d, config=c), args.steps, args.warmup)
+            t = 2.0 * M * N * K / (mean / 1e3) / 1e12
+            gbs = 2.0 * (M * K + N * K + M * N) / (mean / 1e3) / 1e9
+            print(json.dumps({"mode": "ksweep", "M": M, "N": N, "K": K,
+                              "variant": c.as_tuple(), "ms_mean": round(mean, 4),
+                              "tflops": round(t, 1), "pct_peak": round(100 * t / PEAK_TFLOPS, 2),
+                              "hbm_gbs_compulsory": round(gbs, 1),
+                              "info": variant_info(c)}), flush=True)
+    return 0
+
+
+def mode_calibrate_copy(args) -> int:
+    """A plain device copy of known size, for scaling the FETCH_SIZE and
+    WRITE_SIZE counters: each launch reads and writes exactly 512 MiB."""
+    import torch
+    n = 512 * 1024 * 1024
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    mean, _ = time_launches(lambda: dst.copy_(src), args.steps, args.warmup)
+    print(json.dumps({"mode": "calibrate_copy", "bytes_read": n, "bytes_written": n,
+                      "ms_mean": round(mean, 4), "gbs": round(2 * n / (mean / 1e3) / 1e9, 1)}),
+          flush=True)
+    return 0
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--mode", default="bench",
+                    choices=["bench", "variants", "ksweep", "calibrate_copy"])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="square8192")
+    ap.add_argument("--config", default=None,
+                    help="explicit variant tile_m,tile_n,tile_k,stages,waves")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); "
+              "the path shards into independent output tiles, see the design notes",
+              file=sys.stderr)
+        return 2
+    if args.mode == "variants":
+        return mode_variants(args)
+    if args.mode == "ksweep":
+        return mode_ksweep(args)
+    if args.mode == "calibrate_copy":
+        return mode_calibrate_copy(args)
+
+    import numpy as np
+    import torch
+
+    import stage_pipelined_mainloop_amd as sg
+    from stage_pipelined_mainloop_amd import inputs
+
+    M, N, K, dist, seed = inputs.WORKLOADS[args.workload]
+    A, B = inputs.workload(args.workload)
+    alpha = float(np.float32(1.0 / math.sqrt(K))) if args.workload == "attn_scores" else None
+    dev = torch.device("cuda:0")
+    a = torch.from_numpy(A).to(dev)
+    b = torch.from_numpy(B).to(dev)
+    d = torch.empty((M, N), dtype=torch.float16, device=dev)
+    cfg = tuple(int(x) for x in args.config.split(",")) if args.config else None
+    chosen = sg.SgConfig(*cfg) if cfg else sg.sg_select_config(M, N, K)
+
+    def step():
+        sg.gemm(a, b, out=d, alpha=alpha, config=cfg)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    mean_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+
+    flops = 2.0 * M * N * K
+    value = flops * args.steps / wall / 1e12
+    achieved = flops / mean_launch_s / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
+                "traffic": load_traffic(args.workload)}
+    if args.workload == "attn_scores":
+        # the score GEMM is bound by writing S to HBM
+        algo_bytes = 2.0 * (M * K + N * K + M * N)
+        gbs = algo_bytes / mean_launch_s / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                    "traffic": load_traffic(args.workload)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "M": M, "N": N, "K": K, "dist": dist,
+                   "alpha": alpha if alpha is not None else 1.0,
+                   "variant": "x".join(str(v) for v in chosen.as_tuple()[:3])
+                              + f" S{chosen.stages} w{chosen.waves}",
+                   "pct_of_fp16_peak": round(100.0 * value / PEAK_TFLOPS, 2),
+                   "kernel_ms_mean": round(mean_launch_s * 1e3, 4),
+                   "kernel_ms_min": round(min(launch_ms), 4)},
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(A, B, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,128 @@
+/*
+ * stagegemm: stage-pipelined half-precision TN GEMM for MI355X (gfx950).
+ *
+ *     D = alpha * A * B^T
+ *
+ * A is M x K, B is N x K and D is M x N, all row-major and contiguous
+ * (leading dimensions K, K and N), all IEEE binary16.  Products are
+ * accumulated in fp32 and each output is rounded once to fp16
+ * (round-to-nearest-even).
+ *
+ * Sources of the operation:
+ *   - "cute(9) multistage_gemm", section 11.1: A(M,K), B(N,K) and D(M,N) are
+ *     row-major and D = A @ B^T (the "TN" GEMM); sections 4-8 describe the
+ *     kStage-deep shared-memory ring that the kernels behind this interface
+ *     implement in LDS (prologue of S-1 tiles, a steady state that overlaps the
+ *     load of tile k+S-1 with the math on tile k, a drain and an epilogue).
+ *   - "CUDA operator notes 2", section "GEMM": fp16 matrices with an fp32
+ *     scale factor alpha applied to the product before the cast to half.
+ *   - "Lesson 6: Shared Memory layout and async pipeline", section 4: the
+ *     stage-count model S_min = ceil(T_copy / T_compute) + 1 and the LDS
+ *     footprint S * (tile_A + tile_B) * sizeof(T) behind sg_minimum_stages
+ *     and sg_query_config.
+ *
+ * Ownership and threading.  Every matrix pointer is a caller-owned DEVICE
+ * pointer.  The library allocates nothing, copies nothing and never
+ * synchronises: a GEMM call validates its arguments on the host, enqueues one
+ * kernel on `stream` (a hipStream_t; NULL = the default stream) and returns.
+ * The result is ready when the stream reaches that point.  Calls may be made
+ * from several host threads at once.
+ *
+ * Errors.  No function throws or aborts.  All argument checks happen before
+ * any HIP call, so a rejected call has no effect on the device.
+ *
+ * Limits and layout rules (a reading: the pages assume tile multiples or pad):
+ *   - M, N, K >= 0.  M == 0 or N == 0 is a no-op returning SG_OK; K == 0
+ *     writes +0 to all of D (the empty sum).
+ *   - K % 8 == 0 and N % 8 == 0 (rows are whole 16-byte chunks), and A, B, D
+ *     16-byte aligned; otherwise SG_ERR_ALIGN.  M is unrestricted.  Tails in
+ *     M, N and K that are not tile multiples are handled inside the kernel.
+ *   - K <= 2^21, N <= 2^21, every matrix below 2^40 elements and the launch
+ *     below 2^32 threads; otherwise SG_ERR_SHAPE.
+ *   - D must not overlap A or B (SG_ERR_ALIAS).
+ */
+#ifndef STAGEGEMM_H
+#define STAGEGEMM_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sg_status {
+    SG_OK = 0,
+    SG_ERR_NULL = 1,        /* a required pointer is NULL */
+    SG_ERR_SHAPE = 2,       /* negative or too large dimension */
+    SG_ERR_ALIGN = 3,       /* K % 8, N % 8 or 16-byte pointer alignment */
+    SG_ERR_UNSUPPORTED = 4, /* no compiled kernel for the requested config */
+    SG_ERR_ALIAS = 5,       /* D overlaps A or B */
+    SG_ERR_HIP = 6          /* the HIP runtime reported an error at launch */
+} sg_status;
+
+/* A compiled kernel variant: output tile tile_m x tile_n, K step tile_k,
+ * `stages` LDS ring slots, `waves` 64-lane wavefronts per workgroup. */
+typedef struct sg_config {
+    int tile_m;
+    int tile_n;
+    int tile_k;
+    int stages;
+    int waves;
+} sg_config;
+
+/* Static facts about a compiled variant. */
+typedef struct sg_config_info {
+    int threads;            /* workgroup size */
+    int lds_bytes;          /* LDS ring: stages * (tile_m + tile_n) * tile_k * 2 */
+    int loads_per_stage;    /* 16-byte global->LDS loads per lane per stage */
+    int wg_per_cu_lds;      /* floor(160 KiB / lds_bytes) */
+    int regs;               /* VGPRs + AGPRs per lane (code object), -1 if unknown */
+    int wg_per_cu_regs;     /* workgroups per CU allowed by the register file, -1 if unknown */
+    int wg_per_cu;          /* resident workgroups per CU reported by the runtime, -1 if unknown */
+} sg_config_info;
+
+/* D = A * B^T.  See the rules above.  `stream` is a hipStream_t. */
+sg_status gemm_fp16_tn(int M, int N, int K, const void *A, const void *B, void *D,
+                       void *stream);
+
+/* D = alpha * A * B^T: the fp32 accumulator is multiplied by the fp32 alpha
+ * before the single rounding to fp16 ("CUDA operator notes 2", "GEMM"). */
+sg_status gemm_fp16_tn_alpha(int M, int N, int K, float alpha, const void *A,
+                             const void *B, void *D, void *stream);
+
+/* As gemm_fp16_tn_alpha, but runs the named compiled variant instead of the
+ * one the library would choose (used by the stage-count sweep).
+ * SG_ERR_UNSUPPORTED if no such variant is compiled; SG_ERR_NULL if cfg is
+ * NULL. */
+sg_status gemm_fp16_tn_cfg(int M, int N, int K, float alpha, const void *A,
+                           const void *B, void *D, const sg_config *cfg,
+                           void *stream);
+
+/* The variant gemm_fp16_tn would run for this shape (no pointers needed). */
+sg_status sg_select_config(int M, int N, int K, sg_config *out);
+
+/* Enumerate the compiled variants: index 0 .. sg_num_configs()-1. */
+int sg_num_configs(void);
+sg_status sg_get_config(int index, sg_config *out);
+
+/* Footprint, register use and occupancy of a compiled variant.  Reads the
+ * kernel's attributes through the HIP runtime (the only query that touches
+ * HIP; SG_ERR_HIP without a device, with every LDS-derived field still
+ * filled in). */
+sg_status sg_query_config(const sg_config *cfg, sg_config_info *info);
+
+/* S_min = ceil(copy_cycles / compute_cycles) + 1 ("Lesson 6", section 4, and
+ * its exercise); -1 unless both arguments are positive. */
+int sg_minimum_stages(long long copy_cycles, long long compute_cycles);
+
+/* Number of this lane's 16-byte loads the kernel lets remain in flight when
+ * it is about to consume K tile `k` of `ntile` (its s_waitcnt vmcnt value):
+ * loads_per_stage * min(stages - 2, ntile - 1 - k).  -1 for bad arguments. */
+int sg_pipeline_wait_count(int stages, int loads_per_stage, int ntile, int k);
+
+/* Human-readable name of a status code (static storage). */
+const char *sg_status_string(sg_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STAGEGEMM_H */

@@ -1,1 +1,58 @@
-"""Stage-pipelined half-precision TN GEMM for MI355X (gfx950)."""
+"""Stage-pipelined half-precision TN GEMM for MI355X (gfx950).
+
+    D = alpha * A @ B.T     A: (M, K) fp16, B: (N, K) fp16, D: (M, N) fp16
+
+The work is done by hand-written HIP kernels in libstagegemm.so behind the
+C-ABI declared in include/stagegemm.h.  `_lib` mirrors that ABI name for name
+(pointers and sizes); `gemm` is a thin torch convenience that passes tensor
+pointers and the current HIP stream.  PyTorch only provides device memory and
+streams.  Importing this package loads nothing; the library is loaded on the
+first call and a missing build raises.
+"""
+from __future__ import annotations
+
+from ._lib import (SgConfig, SgConfigInfo, SgError, configs, gemm_fp16_tn, gemm_fp16_tn_alpha,
+                   gemm_fp16_tn_cfg, sg_get_config, sg_minimum_stages, sg_num_configs,
+                   sg_pipeline_wait_count, sg_query_config, sg_select_config, sg_status_string)
+
+
+def gemm(A, B, out=None, alpha: float | None = None, config=None, stream=None):
+    """D = alpha * A @ B.T on the GPU for fp16 CUDA (HIP) tensors.
+
+    A: (M, K), B: (N, K), out: (M, N) or None (allocated).  `config` picks a
+    compiled variant (SgConfig or a 5-tuple) instead of the library's choice.
+    `stream` is a torch.cuda.Stream (default: the current stream)."""
+    import torch
+
+    if A.dtype != torch.float16 or B.dtype != torch.float16:
+        raise TypeError("A and B must be float16")
+    if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[1]:
+        raise ValueError(f"shapes {tuple(A.shape)} and {tuple(B.shape)} do not form A @ B.T")
+    if not (A.is_cuda and B.is_cuda):
+        raise ValueError("A and B must be device tensors")
+    if not (A.is_contiguous() and B.is_contiguous()):
+        raise ValueError("A and B must be contiguous (row-major)")
+    M, K = A.shape
+    N = B.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=A.device)
+    elif (out.dtype != torch.float16 or tuple(out.shape) != (M, N) or not out.is_contiguous()
+          or out.device != A.device):
+        raise ValueError("out must be a contiguous (M, N) float16 tensor on A's device")
+    s = (stream if stream is not None else torch.cuda.current_stream(A.device)).cuda_stream
+    a, b, d = A.data_ptr(), B.data_ptr(), out.data_ptr()
+    if config is not None:
+        gemm_fp16_tn_cfg(M, N, K, 1.0 if alpha is None else float(alpha), a, b, d, config, s)
+    elif alpha is None:
+        gemm_fp16_tn(M, N, K, a, b, d, s)
+    else:
+        gemm_fp16_tn_alpha(M, N, K, float(alpha), a, b, d, s)
+    return out
+
+
+__all__ = [
+    "gemm", "gemm_fp16_tn", "gemm_fp16_tn_alpha", "gemm_fp16_tn_cfg", "sg_select_config",
+    "sg_num_configs", "sg_get_config", "sg_query_config", "sg_minimum_stages",
+    "sg_pipeline_wait_count", "sg_status_string", "configs", "SgConfig", "SgConfigInfo",
+    "SgError",
+]

@@ -1,0 +1,169 @@
+"""ctypes binding of libstagegemm.so: the C-ABI functions under the same names.
+
+Argument marshalling only.  Every step of the GEMM runs in the HIP kernels of
+the shared library; nothing here computes, and there is no fallback: if the
+library is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libstagegemm.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "stagegemm.h")
+
+SG_OK = 0
+SG_ERR_NULL = 1
+SG_ERR_SHAPE = 2
+SG_ERR_ALIGN = 3
+SG_ERR_UNSUPPORTED = 4
+SG_ERR_ALIAS = 5
+SG_ERR_HIP = 6
+
+
+class SgConfig(ctypes.Structure):
+    _fields_ = [("tile_m", ctypes.c_int), ("tile_n", ctypes.c_int), ("tile_k", ctypes.c_int),
+                ("stages", ctypes.c_int), ("waves", ctypes.c_int)]
+
+    def as_tuple(self):
+        return (self.tile_m, self.tile_n, self.tile_k, self.stages, self.waves)
+
+    def __repr__(self):
+        return "SgConfig(%d, %d, %d, stages=%d, waves=%d)" % self.as_tuple()
+
+
+class SgConfigInfo(ctypes.Structure):
+    _fields_ = [("threads", ctypes.c_int), ("lds_bytes", ctypes.c_int),
+                ("loads_per_stage", ctypes.c_int), ("wg_per_cu_lds", ctypes.c_int),
+                ("regs", ctypes.c_int), ("wg_per_cu_regs", ctypes.c_int),
+                ("wg_per_cu", ctypes.c_int)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class SgError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {sg_status_string(status)}")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libstagegemm.so (built in-tree); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+        # PyTorch-ROCm ships its own libamdhip64 (same soname).  Loading torch
+        # first makes this library bind to that already-loaded runtime, so
+        # torch's device memory and stream handles belong to the runtime our
+        # launches go through.  Loading ours first would bring in a second HIP
+        # runtime that rejects torch's streams.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        L.gemm_fp16_tn.argtypes = [i, i, i, vp, vp, vp, vp]
+        L.gemm_fp16_tn.restype = i
+        L.gemm_fp16_tn_alpha.argtypes = [i, i, i, f, vp, vp, vp, vp]
+        L.gemm_fp16_tn_alpha.restype = i
+        L.gemm_fp16_tn_cfg.argtypes = [i, i, i, f, vp, vp, vp, ctypes.POINTER(SgConfig), vp]
+        L.gemm_fp16_tn_cfg.restype = i
+        L.sg_select_config.argtypes = [i, i, i, ctypes.POINTER(SgConfig)]
+        L.sg_select_config.restype = i
+        L.sg_num_configs.argtypes = []
+        L.sg_num_configs.restype = i
+        L.sg_get_config.argtypes = [i, ctypes.POINTER(SgConfig)]
+        L.sg_get_config.restype = i
+        L.sg_query_config.argtypes = [ctypes.POINTER(SgConfig), ctypes.POINTER(SgConfigInfo)]
+        L.sg_query_config.restype = i
+        L.sg_minimum_stages.argtypes = [ctypes.c_longlong, ctypes.c_longlong]
+        L.sg_minimum_stages.restype = i
+        L.sg_pipeline_wait_count.argtypes = [i, i, i, i]
+        L.sg_pipeline_wait_count.restype = i
+        L.sg_status_string.argtypes = [i]
+        L.sg_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/stagegemm.h declares."""
+    with open(HEADER) as fh:
+        text = fh.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)
+
+
+# --- the C-ABI under the same names ----------------------------------------
+
+def _check(st: int, what: str) -> int:
+    if st != SG_OK:
+        raise SgError(st, what)
+    return st
+
+
+def gemm_fp16_tn(M: int, N: int, K: int, A: int, B: int, D: int, stream: int = 0) -> int:
+    return _check(lib().gemm_fp16_tn(M, N, K, A, B, D, stream), "gemm_fp16_tn")
+
+
+def gemm_fp16_tn_alpha(M: int, N: int, K: int, alpha: float, A: int, B: int, D: int,
+                       stream: int = 0) -> int:
+    return _check(lib().gemm_fp16_tn_alpha(M, N, K, alpha, A, B, D, stream),
+                  "gemm_fp16_tn_alpha")
+
+
+def gemm_fp16_tn_cfg(M: int, N: int, K: int, alpha: float, A: int, B: int, D: int,
+                     cfg, stream: int = 0) -> int:
+    c = cfg if isinstance(cfg, SgConfig) else SgConfig(*cfg)
+    return _check(lib().gemm_fp16_tn_cfg(M, N, K, alpha, A, B, D, ctypes.byref(c), stream),
+                  "gemm_fp16_tn_cfg")
+
+
+def sg_select_config(M: int, N: int, K: int) -> SgConfig:
+    c = SgConfig()
+    _check(lib().sg_select_config(M, N, K, ctypes.byref(c)), "sg_select_config")
+    return c
+
+
+def sg_num_configs() -> int:
+    return int(lib().sg_num_configs())
+
+
+def sg_get_config(index: int) -> SgConfig:
+    c = SgConfig()
+    _check(lib().sg_get_config(index, ctypes.byref(c)), "sg_get_config")
+    return c
+
+
+def sg_query_config(cfg) -> tuple[int, SgConfigInfo]:
+    """Returns (status, info); info's LDS fields are filled even when the
+    register / occupancy query needs a device that is not there."""
+    c = cfg if isinstance(cfg, SgConfig) else SgConfig(*cfg)
+    info = SgConfigInfo()
+    st = lib().sg_query_config(ctypes.byref(c), ctypes.byref(info))
+    return st, info
+
+
+def sg_minimum_stages(copy_cycles: int, compute_cycles: int) -> int:
+    return int(lib().sg_minimum_stages(copy_cycles, compute_cycles))
+
+
+def sg_pipeline_wait_count(stages: int, loads_per_stage: int, ntile: int, k: int) -> int:
+    return int(lib().sg_pipeline_wait_count(stages, loads_per_stage, ntile, k))
+
+
+def sg_status_string(status: int) -> str:
+    return lib().sg_status_string(status).decode()
+
+
+def configs() -> list[SgConfig]:
+    return [sg_get_config(i) for i in range(sg_num_configs())]

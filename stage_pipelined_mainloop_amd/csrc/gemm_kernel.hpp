@@ -1,0 +1,321 @@
+// Stage-pipelined fp16 TN GEMM kernel for gfx950 (CDNA4).
+//
+//   D[m][n] = RNE16( alpha * sum_k A[m][k] * B[n][k] ),   fp32 accumulation.
+//
+// Structure (the method of "cute(9) multistage_gemm", sections 4-7, and the
+// three-phase order of "Lesson 6: Shared Memory layout and async pipeline",
+// sections 2-3), redesigned for CDNA4:
+//
+//   * One workgroup per BM x BN output tile; NW = WM x WN wavefronts of 64
+//     lanes, each owning a (BM/WM) x (BN/WN) sub-tile built from 32x32 MFMA
+//     blocks (v_mfma_f32_32x32x16_f16, fp32 accumulators).
+//   * An S-slot ring in LDS.  Each slot holds one K step: A rows [BM x BK] and
+//     B rows [BN x BK], both K-contiguous (the TN layout needs no transpose).
+//   * Global -> LDS copies are LDS-DMA buffer loads (buffer_load_dwordx4 ...
+//     lds): 16 bytes per lane, written by the memory pipeline straight into
+//     LDS without passing through VGPRs -- the CDNA counterpart of the async
+//     copy the pages build on.  Each wave issues L of them per K step.  There
+//     are no commit groups on this hardware, so a "batch" is those L loads and
+//     the wait for tile k is `s_waitcnt vmcnt(L * min(S-2, ntile-1-k))`: the
+//     loads issued after tile k's may stay in flight, tile k's may not.
+//   * Per K step k (one barrier per step):
+//        wait(own loads of tile k)  + lgkmcnt(0)      RAW on own part, and own
+//                                                     LDS reads of step k-1 done
+//        s_barrier                                    every wave: tile k landed,
+//                                                     slot (k-1)%S no longer read
+//        issue tile k+S-1 into slot (k+S-1)%S = (k-1)%S   (if it exists)  WAR-safe
+//        ds_read_b128 fragments of slot k%S, MFMA      overlaps the loads in flight
+//     The prologue issues tiles 0..S-2; the last S-2 steps issue nothing and
+//     their waits shrink to 0 (drain).  Filling S-1 slots, not S, leaves the
+//     slot the first refill needs ("cute(9) multistage_gemm", section 5.1).
+//   * Bank conflicts: 16-byte chunk c of LDS row r is stored at chunk position
+//     c ^ swz(r).  LDS-DMA writes 64 consecutive 16-byte chunks per wave load,
+//     so the swizzle is applied by choosing which global chunk each lane
+//     fetches; the fragment reads then hit distinct banks.
+//   * Bounds: buffer resources per workgroup cover only the valid rows, so
+//     rows past M (A) or N (B) read as zero and stores past M are dropped;
+//     K-tail chunks and N-tail columns are sent to an offset past the
+//     resource's range (reads 0 / store dropped).  Zero fill gives exactly the
+//     plain sum (the padding reading of "CUDA operator notes 2", "GEMM").
+//   * Epilogue: operands are fed to the MFMA swapped (B rows as the first
+//     operand), so each lane's accumulators are four consecutive columns of
+//     one row of D: alpha * acc, convert to fp16 (RNE), one 8-byte store.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sg {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// gfx9 buffer resource word 3 (raw 32-bit data format, no swizzle).
+constexpr int kRsrcWord3 = 0x00020000;
+// An offset no per-workgroup resource reaches (num_records < 2^31).
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+// s_waitcnt immediate for gfx9: vmcnt bits [3:0] and [15:14], expcnt [6:4],
+// lgkmcnt [11:8].  expcnt is never waited on here.
+constexpr int waitcnt_imm(int vm, int lgkm)
+{
+    return (vm & 15) | (7 << 4) | ((lgkm & 15) << 8) | (((vm >> 4) & 3) << 14);
+}
+
+// Loads of this lane allowed in flight when consuming K tile k.
+__host__ __device__ constexpr int pipeline_wait_count(int stages, int loads, int ntile, int k)
+{
+    int after = ntile - 1 - k;
+    if (after > stages - 2) after = stages - 2;
+    if (after < 0) after = 0;
+    return loads * after;
+}
+
+// XOR swizzle of 16-byte chunk positions within an LDS row, by row index.
+// Rows of 4 chunks (BK = 32): bit0 = r2, bit1 = r1 ^ r3.
+// Rows of 8 chunks (BK = 64): bit0 = r1, bit1 = r2, bit2 = r0 ^ r3.
+// Both keep the 32-row ds_read_b128 fragment pattern on distinct banks for
+// 8-lane / 128-byte and 16-lane / 256-byte bank groups, and depend only on
+// r mod 16, so every 32-row MFMA block sees the same pattern.
+template <int CPR>
+__device__ __forceinline__ int swz(int r)
+{
+    if constexpr (CPR == 4) {
+        return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1);
+    } else {
+        static_assert(CPR == 8, "rows of 4 or 8 chunks");
+        return ((r >> 1) & 1) | (((r >> 2) & 1) << 1) | ((((r) ^ (r >> 3)) & 1) << 2);
+    }
+}
+
+template <int BM_, int BN_, int BK_, int S_, int WM_, int WN_>
+struct Cfg {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_, WM = WM_, WN = WN_;
+    static constexpr int NW = WM * WN;              // wavefronts
+    static constexpr int T = 64 * NW;               // threads
+    static constexpr int WTM = BM / WM;             // wave sub-tile
+    static constexpr int WTN = BN / WN;
+    static constexpr int FM = WTM / 32;             // 32x32 MFMA blocks per wave
+    static constexpr int FN = WTN / 32;
+    static constexpr int RB = BK * 2;               // LDS row bytes
+    static constexpr int CPR = BK / 8;              // 16-byte chunks per row
+    static constexpr int NKS = BK / 16;             // MFMA K steps per tile
+    static constexpr int A_BYTES = BM * RB;
+    static constexpr int B_BYTES = BN * RB;
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    static constexpr int LDS_BYTES = S * STAGE_BYTES;
+    static constexpr int NA = BM * CPR / (64 * NW); // LDS-DMA loads per wave per stage
+    static constexpr int NB = BN * CPR / (64 * NW);
+    static constexpr int L = NA + NB;
+    static_assert(S >= 2, "a ring needs at least two slots");
+    static_assert(BK == 32 || BK == 64, "BK");
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile is whole 32x32 blocks");
+    static_assert(NA * 64 * NW == BM * CPR && NB * 64 * NW == BN * CPR, "even load split");
+    static_assert(NA >= 1 && NB >= 1, "every wave loads both operands");
+    static_assert(L * (S - 2) <= 63, "vmcnt is a 6-bit counter");
+    static_assert(LDS_BYTES <= 163840, "160 KiB of LDS per workgroup");
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             kRsrcWord3);
+}
+
+// Compiler-level fence: no memory access moves across it (emits nothing).
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0()
+{
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(N, 0));
+}
+
+// Wait until at most `n` (runtime, n = L * j for j in 0..S-2) of this lane's
+// loads are outstanding and all its LDS reads have returned.
+template <class C>
+__device__ __forceinline__ void wait_tile(int j)
+{
+    if constexpr (C::S - 2 >= 3) { if (j == 3) { wait_vm_lgkm0<3 * C::L>(); return; } }
+    if constexpr (C::S - 2 >= 2) { if (j == 2) { wait_vm_lgkm0<2 * C::L>(); return; } }
+    if constexpr (C::S - 2 >= 1) { if (j == 1) { wait_vm_lgkm0<1 * C::L>(); return; } }
+    wait_vm_lgkm0<0>();
+}
+
+// Grid position -> output tile.  Workgroups are dealt round-robin to the 8
+// XCDs; renumber so each XCD receives a contiguous run of tiles, then walk
+// the run in groups of GM tile-rows so concurrently resident workgroups of
+// one XCD share A and B panels in that XCD's L2.
+__device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, int &tm, int &tn)
+{
+    const int total = tiles_m * tiles_n;
+    if ((total & 7) == 0) pid = (pid & 7) * (total >> 3) + (pid >> 3);
+    constexpr int GM = 4;
+    const int per_group = GM * tiles_n;
+    const int group = pid / per_group;
+    const int first_m = group * GM;
+    int gm = tiles_m - first_m;
+    if (gm > GM) gm = GM;
+    const int in_group = pid - group * per_group;
+    tm = first_m + in_group % gm;
+    tn = in_group / gm;
+}
+
+template <class C>
+__global__ void __launch_bounds__(C::T)
+gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
+               _Float16 *__restrict__ D, int M, int N, int K, float alpha)
+{
+    __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / C::WN;
+    const int wn = wave % C::WN;
+
+    const int tiles_m = (M + C::BM - 1) / C::BM;
+    const int tiles_n = (N + C::BN - 1) / C::BN;
+    int tm, tn;
+    tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * C::BM;
+    const int n0 = tn * C::BN;
+    const int rows_a = (M - m0 < C::BM) ? (M - m0) : C::BM;
+    const int rows_b = (N - n0 < C::BN) ? (N - n0) : C::BN;
+
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (size_t)m0 * K, (uint32_t)rows_a * K * 2u);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + (size_t)n0 * K, (uint32_t)rows_b * K * 2u);
+
+    const int ntile = (K + C::BK - 1) / C::BK;
+
+    // ---- per-lane LDS-DMA source offsets (bytes) and K columns, fixed over K
+    uint32_t a_off[C::NA], b_off[C::NB];
+    int a_col[C::NA], b_col[C::NB];
+#pragma unroll
+    for (int i = 0; i < C::NA; ++i) {
+        const int q = (i * C::NW + wave) * 64 + lane;     // LDS chunk index in the A slot
+        const int r = q / C::CPR;
+        const int c = (q % C::CPR) ^ swz<C::CPR>(r);
+        a_off[i] = (uint32_t)(r * K + c * 8) * 2u;
+        a_col[i] = c * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < C::NB; ++i) {
+        const int q = (i * C::NW + wave) * 64 + lane;
+        const int r = q / C::CPR;
+        const int c = (q % C::CPR) ^ swz<C::CPR>(r);
+        b_off[i] = (uint32_t)(r * K + c * 8) * 2u;
+        b_col[i] = c * 8;
+    }
+
+    // Issue the L loads of K tile `t` into ring slot `slot`.
+    auto issue = [&](int t, int slot) {
+        const int kbase = t * C::BK;
+        const int krem = K - kbase;                  // valid K columns in this tile
+        const uint32_t kb = (uint32_t)kbase * 2u;
+        char *sa = smem + slot * C::STAGE_BYTES;
+        char *sb = sa + C::A_BYTES;
+#pragma unroll
+        for (int i = 0; i < C::NA; ++i) {
+            const uint32_t v = (a_col[i] < krem) ? a_off[i] + kb : kOutOfRange;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ra, (__attribute__((address_space(3))) void *)(sa + (i * C::NW + wave) * 1024),
+                16, v, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < C::NB; ++i) {
+            const uint32_t v = (b_col[i] < krem) ? b_off[i] + kb : kOutOfRange;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rb, (__attribute__((address_space(3))) void *)(sb + (i * C::NW + wave) * 1024),
+                16, v, 0, 0, 0);
+        }
+    };
+
+    // ---- per-lane fragment read offsets within a slot (bytes), per MFMA K step
+    const int half = lane >> 5;                      // which 8-wide K group of the step
+    const int ra_row = wm * C::WTM + (lane & 31);
+    const int rb_row = wn * C::WTN + (lane & 31);
+    int fa[C::NKS], fb[C::NKS];
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) {
+        const int c = 2 * ks + half;
+        fa[ks] = ra_row * C::RB + ((c ^ swz<C::CPR>(ra_row)) << 4);
+        fb[ks] = C::A_BYTES + rb_row * C::RB + ((c ^ swz<C::CPR>(rb_row)) << 4);
+    }
+
+    f32x16 acc[C::FM][C::FN];
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    // ---- prologue: tiles 0 .. S-2
+#pragma unroll
+    for (int t = 0; t < C::S - 1; ++t)
+        if (t < ntile) issue(t, t);
+
+    // ---- steady state and drain
+    int slot = 0;                                    // slot of tile k
+    int wslot = C::S - 1;                            // slot of tile k+S-1
+#pragma unroll 1
+    for (int k = 0; k < ntile; ++k) {
+        int after = ntile - 1 - k;
+        if (after > C::S - 2) after = C::S - 2;
+        compiler_fence();
+        wait_tile<C>(after);
+        __builtin_amdgcn_s_barrier();
+        compiler_fence();
+        if (k + C::S - 1 < ntile) issue(k + C::S - 1, wslot);
+
+        const char *sbase = smem + slot * C::STAGE_BYTES;
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks) {
+            f16x8 fragA[C::FM], fragB[C::FN];
+#pragma unroll
+            for (int i = 0; i < C::FM; ++i)
+                fragA[i] = *(const f16x8 *)(sbase + fa[ks] + i * 32 * C::RB);
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+                fragB[j] = *(const f16x8 *)(sbase + fb[ks] + j * 32 * C::RB);
+#pragma unroll
+            for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fragB[j], fragA[i],
+                                                                       acc[i][j], 0, 0, 0);
+        }
+        slot = (slot + 1 == C::S) ? 0 : slot + 1;
+        wslot = (wslot + 1 == C::S) ? 0 : wslot + 1;
+    }
+
+    // ---- epilogue: lane holds D[m][n .. n+3] for m = row of (lane & 31),
+    // n = 8 * (e / 4) + 4 * half within each 32x32 block.
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(D + (size_t)m0 * N, (uint32_t)rows_a * N * 2u);
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+        const int ml = wm * C::WTM + i * 32 + (lane & 31);          // row within the tile
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + wn * C::WTN + j * 32 + 8 * g + 4 * half;
+                const f32x16 &a = acc[i][j];
+                const _Float16 h0 = (_Float16)(alpha * a[4 * g + 0]);
+                const _Float16 h1 = (_Float16)(alpha * a[4 * g + 1]);
+                const _Float16 h2 = (_Float16)(alpha * a[4 * g + 2]);
+                const _Float16 h3 = (_Float16)(alpha * a[4 * g + 3]);
+                u32x2 packed;
+                packed[0] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+                packed[1] = (uint32_t)__builtin_bit_cast(uint16_t, h2) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
+                const uint32_t off = (n < N) ? (uint32_t)(ml * N + n) * 2u : kOutOfRange;
+                __builtin_amdgcn_raw_buffer_store_b64(packed, rd, off, 0, 0);
+            }
+        }
+    }
+}
+
+}  // namespace sg

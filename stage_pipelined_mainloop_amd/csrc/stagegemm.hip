@@ -1,0 +1,233 @@
+// C-ABI of the stage-pipelined fp16 TN GEMM: argument validation, the table
+// of compiled variants, variant selection and the launch on the caller's
+// stream.  The interface is documented in include/stagegemm.h.
+#include "stagegemm.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm_kernel.hpp"
+
+namespace {
+
+typedef hipError_t (*launch_fn)(int M, int N, int K, float alpha, const void *A, const void *B,
+                                void *D, hipStream_t stream);
+
+struct Variant {
+    sg_config cfg;
+    int threads;
+    int lds_bytes;
+    int loads;
+    const void *kernel;
+    launch_fn launch;
+};
+
+template <class C>
+hipError_t launch(int M, int N, int K, float alpha, const void *A, const void *B, void *D,
+                  hipStream_t stream)
+{
+    const long long tiles = (long long)((M + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
+    const _Float16 *a = static_cast<const _Float16 *>(A);
+    const _Float16 *b = static_cast<const _Float16 *>(B);
+    _Float16 *d = static_cast<_Float16 *>(D);
+    void *args[] = {&a, &b, &d, &M, &N, &K, &alpha};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&sg::gemm_tn_kernel<C>),
+                           dim3((unsigned)tiles), dim3(C::T), args, 0, stream);
+}
+
+template <class C>
+constexpr Variant variant()
+{
+    return Variant{{C::BM, C::BN, C::BK, C::S, C::NW}, C::T, C::LDS_BYTES, C::L,
+                   reinterpret_cast<const void *>(&sg::gemm_tn_kernel<C>), &launch<C>};
+}
+
+// Compiled variants.  256x256 tiles carry the large square shapes (half the
+// global->LDS traffic of 128x128 per flop); 128x128 tiles fill the chip for
+// M = N = 2048 (one workgroup per CU).  Stage counts 2..5 for the sweep.
+const Variant kVariants[] = {
+    variant<sg::Cfg<256, 256, 32, 2, 2, 4>>(),
+    variant<sg::Cfg<256, 256, 32, 3, 2, 4>>(),
+    variant<sg::Cfg<256, 256, 32, 4, 2, 4>>(),
+    variant<sg::Cfg<256, 256, 32, 5, 2, 4>>(),
+    variant<sg::Cfg<256, 256, 32, 3, 2, 2>>(),
+    variant<sg::Cfg<256, 256, 32, 4, 2, 2>>(),
+    variant<sg::Cfg<256, 256, 64, 2, 2, 4>>(),
+    variant<sg::Cfg<128, 128, 32, 2, 2, 2>>(),
+    variant<sg::Cfg<128, 128, 32, 3, 2, 2>>(),
+    variant<sg::Cfg<128, 128, 32, 4, 2, 2>>(),
+    variant<sg::Cfg<128, 128, 32, 5, 2, 2>>(),
+};
+constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
+
+const Variant *find_variant(const sg_config *c)
+{
+    for (int i = 0; i < kNumVariants; ++i) {
+        const sg_config &v = kVariants[i].cfg;
+        if (v.tile_m == c->tile_m && v.tile_n == c->tile_n && v.tile_k == c->tile_k &&
+            v.stages == c->stages && v.waves == c->waves)
+            return &kVariants[i];
+    }
+    return nullptr;
+}
+
+const Variant *select_variant(int M, int N, int K)
+{
+    (void)K;
+    const long long big_tiles = (long long)((M + 255) / 256) * ((N + 255) / 256);
+    sg_config c;
+    if (big_tiles >= 128)
+        c = sg_config{256, 256, 32, 4, 8};
+    else
+        c = sg_config{128, 128, 32, 4, 4};
+    return find_variant(&c);
+}
+
+bool overlaps(const void *p, size_t pbytes, const void *q, size_t qbytes)
+{
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    const uintptr_t b = reinterpret_cast<uintptr_t>(q);
+    return pbytes && qbytes && a < b + qbytes && b < a + pbytes;
+}
+
+// Every check that does not need the runtime.  SG_OK means "launch".
+sg_status validate(int M, int N, int K, const void *A, const void *B, const void *D)
+{
+    if (M < 0 || N < 0 || K < 0) return SG_ERR_SHAPE;
+    if (M == 0 || N == 0) return SG_OK;
+    if (!D) return SG_ERR_NULL;
+    if (K > 0 && (!A || !B)) return SG_ERR_NULL;
+    if (K > (1 << 21) || N > (1 << 21)) return SG_ERR_SHAPE;
+    const long long lim = 1LL << 40;
+    if ((long long)M * K >= lim || (long long)M * N >= lim) return SG_ERR_SHAPE;
+    if ((K & 7) || (N & 7)) return SG_ERR_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(D) & 15) ||
+        (K > 0 && ((reinterpret_cast<uintptr_t>(A) & 15) || (reinterpret_cast<uintptr_t>(B) & 15))))
+        return SG_ERR_ALIGN;
+    const size_t dbytes = (size_t)M * N * 2;
+    if (K > 0 && (overlaps(D, dbytes, A, (size_t)M * K * 2) ||
+                  overlaps(D, dbytes, B, (size_t)N * K * 2)))
+        return SG_ERR_ALIAS;
+    return SG_OK;
+}
+
+sg_status run(const Variant *v, int M, int N, int K, float alpha, const void *A, const void *B,
+              void *D, void *stream)
+{
+    const long long tiles = (long long)((M + v->cfg.tile_m - 1) / v->cfg.tile_m) *
+                            ((N + v->cfg.tile_n - 1) / v->cfg.tile_n);
+    if (tiles * v->threads >= (1LL << 32)) return SG_ERR_SHAPE;
+    const hipError_t e = v->launch(M, N, K, alpha, A, B, D, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SG_OK : SG_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+sg_status gemm_fp16_tn_alpha(int M, int N, int K, float alpha, const void *A, const void *B,
+                             void *D, void *stream)
+{
+    const sg_status st = validate(M, N, K, A, B, D);
+    if (st != SG_OK || M == 0 || N == 0) return st;
+    const Variant *v = select_variant(M, N, K);
+    if (!v) return SG_ERR_UNSUPPORTED;
+    return run(v, M, N, K, alpha, A, B, D, stream);
+}
+
+sg_status gemm_fp16_tn(int M, int N, int K, const void *A, const void *B, void *D, void *stream)
+{
+    return gemm_fp16_tn_alpha(M, N, K, 1.0f, A, B, D, stream);
+}
+
+sg_status gemm_fp16_tn_cfg(int M, int N, int K, float alpha, const void *A, const void *B,
+                           void *D, const sg_config *cfg, void *stream)
+{
+    if (!cfg) return SG_ERR_NULL;
+    const sg_status st = validate(M, N, K, A, B, D);
+    if (st != SG_OK) return st;
+    const Variant *v = find_variant(cfg);
+    if (!v) return SG_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return SG_OK;
+    return run(v, M, N, K, alpha, A, B, D, stream);
+}
+
+sg_status sg_select_config(int M, int N, int K, sg_config *out)
+{
+    if (!out) return SG_ERR_NULL;
+    if (M < 0 || N < 0 || K < 0) return SG_ERR_SHAPE;
+    const Variant *v = select_variant(M, N, K);
+    if (!v) return SG_ERR_UNSUPPORTED;
+    *out = v->cfg;
+    return SG_OK;
+}
+
+int sg_num_configs(void) { return kNumVariants; }
+
+sg_status sg_get_config(int index, sg_config *out)
+{
+    if (!out) return SG_ERR_NULL;
+    if (index < 0 || index >= kNumVariants) return SG_ERR_UNSUPPORTED;
+    *out = kVariants[index].cfg;
+    return SG_OK;
+}
+
+sg_status sg_query_config(const sg_config *cfg, sg_config_info *info)
+{
+    if (!cfg || !info) return SG_ERR_NULL;
+    const Variant *v = find_variant(cfg);
+    if (!v) return SG_ERR_UNSUPPORTED;
+    info->threads = v->threads;
+    info->lds_bytes = v->lds_bytes;
+    info->loads_per_stage = v->loads;
+    info->wg_per_cu_lds = 163840 / v->lds_bytes;
+    info->regs = -1;
+    info->wg_per_cu_regs = -1;
+    info->wg_per_cu = -1;
+    hipFuncAttributes attr;
+    if (hipFuncGetAttributes(&attr, v->kernel) != hipSuccess) return SG_ERR_HIP;
+    info->regs = attr.numRegs;
+    if (attr.numRegs > 0) {
+        // 512 registers per lane per SIMD, allocated in granules of 8; four
+        // SIMDs per CU, waves of a workgroup spread over them.
+        const int alloc = (attr.numRegs + 7) / 8 * 8;
+        int waves_per_simd = 512 / alloc;
+        if (waves_per_simd > 8) waves_per_simd = 8;
+        info->wg_per_cu_regs = (4 * waves_per_simd) / cfg->waves;
+    }
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, v->kernel, v->threads, 0) ==
+        hipSuccess)
+        info->wg_per_cu = blocks;
+    return SG_OK;
+}
+
+int sg_minimum_stages(long long copy_cycles, long long compute_cycles)
+{
+    if (copy_cycles <= 0 || compute_cycles <= 0) return -1;
+    const long long in_flight = (copy_cycles + compute_cycles - 1) / compute_cycles;
+    if (in_flight + 1 > 0x7fffffffLL) return -1;
+    return (int)(in_flight + 1);
+}
+
+int sg_pipeline_wait_count(int stages, int loads_per_stage, int ntile, int k)
+{
+    if (stages < 2 || loads_per_stage < 1 || ntile < 1 || k < 0 || k >= ntile) return -1;
+    return sg::pipeline_wait_count(stages, loads_per_stage, ntile, k);
+}
+
+const char *sg_status_string(sg_status status)
+{
+    switch (status) {
+    case SG_OK: return "SG_OK";
+    case SG_ERR_NULL: return "SG_ERR_NULL: a required pointer is NULL";
+    case SG_ERR_SHAPE: return "SG_ERR_SHAPE: dimension negative or beyond the supported range";
+    case SG_ERR_ALIGN: return "SG_ERR_ALIGN: K and N must be multiples of 8 and pointers 16-byte aligned";
+    case SG_ERR_UNSUPPORTED: return "SG_ERR_UNSUPPORTED: no compiled kernel for this configuration";
+    case SG_ERR_ALIAS: return "SG_ERR_ALIAS: D overlaps A or B";
+    case SG_ERR_HIP: return "SG_ERR_HIP: the HIP runtime reported an error";
+    }
+    return "unknown sg_status";
+}
+
+}  // extern "C"

@@ -1,0 +1,143 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, rejects bad arguments with the documented status before any
+HIP call, and its host-side model functions agree with the oracle's model and
+ring-schedule simulator."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from stage_pipelined_mainloop_amd import _lib
+
+L = _lib.lib()
+S = _lib
+
+
+def test_every_declared_symbol_is_exported():
+    declared = _lib.header_functions()
+    assert len(declared) == 10
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    for name in declared:
+        assert name in exported, name
+        assert hasattr(L, name)
+
+
+# Fake, never-dereferenced device addresses: every call below fails validation
+# before the library touches the HIP runtime.
+P = 0x7f0000000000
+
+
+@pytest.mark.parametrize("args,status", [
+    ((-1, 8, 8, P, P + 0x100000, P + 0x200000), S.SG_ERR_SHAPE),
+    ((8, -8, 8, P, P + 0x100000, P + 0x200000), S.SG_ERR_SHAPE),
+    ((8, 8, -8, P, P + 0x100000, P + 0x200000), S.SG_ERR_SHAPE),
+    ((8, 8, 8, 0, P + 0x100000, P + 0x200000), S.SG_ERR_NULL),
+    ((8, 8, 8, P, 0, P + 0x200000), S.SG_ERR_NULL),
+    ((8, 8, 8, P, P + 0x100000, 0), S.SG_ERR_NULL),
+    ((8, 8, 12, P, P + 0x100000, P + 0x200000), S.SG_ERR_ALIGN),     # K % 8
+    ((8, 12, 8, P, P + 0x100000, P + 0x200000), S.SG_ERR_ALIGN),     # N % 8
+    ((8, 8, 8, P + 8, P + 0x100000, P + 0x200000), S.SG_ERR_ALIGN),  # 16-byte alignment
+    ((8, 8, 8, P, P + 0x100002, P + 0x200000), S.SG_ERR_ALIGN),
+    ((8, 8, 8, P, P + 0x100000, P + 0x200004), S.SG_ERR_ALIGN),
+    ((8, 8, 8, P, P + 0x100000, P + 0x40), S.SG_ERR_ALIAS),           # D overlaps A
+    ((8, 8, 8, P, P + 0x100000, P + 0x100000), S.SG_ERR_ALIAS),       # D == B
+    ((8, 8, (1 << 21) + 8, P, P + 0x10000000, P + 0x20000000), S.SG_ERR_SHAPE),
+    ((8, (1 << 21) + 8, 8, P, P + 0x10000000, P + 0x20000000), S.SG_ERR_SHAPE),
+    ((1 << 30, 8, 1 << 11, P, P + (1 << 44), P + (1 << 45)), S.SG_ERR_SHAPE),  # M*K >= 2^40
+])
+def test_argument_errors(args, status):
+    M, N, K, a, b, d = args
+    assert L.gemm_fp16_tn(M, N, K, a, b, d, None) == status
+    assert L.gemm_fp16_tn_alpha(M, N, K, 0.5, a, b, d, None) == status
+    cfg = _lib.SgConfig(128, 128, 32, 3, 4)
+    assert L.gemm_fp16_tn_cfg(M, N, K, 1.0, a, b, d, ctypes.byref(cfg), None) == status
+
+
+def test_empty_outputs_are_no_ops():
+    # M == 0 or N == 0: nothing to compute, any pointers accepted, no launch
+    assert L.gemm_fp16_tn(0, 8, 8, 0, 0, 0, None) == S.SG_OK
+    assert L.gemm_fp16_tn(8, 0, 8, 0, 0, 0, None) == S.SG_OK
+    assert L.gemm_fp16_tn_alpha(0, 0, 0, 2.0, 0, 0, 0, None) == S.SG_OK
+
+
+def test_cfg_errors():
+    assert L.gemm_fp16_tn_cfg(8, 8, 8, 1.0, P, P + 0x100000, P + 0x200000, None, None) == S.SG_ERR_NULL
+    bad = _lib.SgConfig(96, 128, 32, 3, 4)
+    assert L.gemm_fp16_tn_cfg(8, 8, 8, 1.0, P, P + 0x100000, P + 0x200000,
+                              ctypes.byref(bad), None) == S.SG_ERR_UNSUPPORTED
+    st, _ = _lib.sg_query_config(bad)
+    assert st == S.SG_ERR_UNSUPPORTED
+
+
+def test_status_strings_are_stable():
+    names = {0: "SG_OK", 1: "SG_ERR_NULL", 2: "SG_ERR_SHAPE", 3: "SG_ERR_ALIGN",
+             4: "SG_ERR_UNSUPPORTED", 5: "SG_ERR_ALIAS", 6: "SG_ERR_HIP"}
+    for code, name in names.items():
+        assert _lib.sg_status_string(code).startswith(name)
+    assert _lib.sg_status_string(99) == "unknown sg_status"
+
+
+def test_minimum_stages_matches_the_worked_values():
+    for c in [(300, 120, 4), (120, 120, 2), (1, 120, 2), (241, 120, 4), (240, 120, 3)]:
+        assert _lib.sg_minimum_stages(c[0], c[1]) == c[2] == oracle.minimum_stages(c[0], c[1])
+    assert _lib.sg_minimum_stages(0, 5) == -1
+    assert _lib.sg_minimum_stages(5, -1) == -1
+
+
+def test_wait_counts_match_the_ring_simulator():
+    for stages in (2, 3, 4, 5):
+        for loads in (4, 8):
+            for ntile in range(1, 21):
+                want = oracle.loosest_wait_counts(ntile, stages, loads)
+                got = [_lib.sg_pipeline_wait_count(stages, loads, ntile, k) for k in range(ntile)]
+                assert got == want, (stages, loads, ntile)
+                # and the schedule with those waits passes every invariant
+                ops = oracle.schedule_three_phase(ntile, stages, 2, got, loads)
+                assert oracle.simulate_loads(ops, ntile, stages, 2, loads).ok
+    assert _lib.sg_pipeline_wait_count(1, 4, 4, 0) == -1
+    assert _lib.sg_pipeline_wait_count(3, 4, 4, 4) == -1
+
+
+def test_config_table_and_lds_model():
+    cfgs = _lib.configs()
+    assert len(cfgs) == _lib.sg_num_configs() >= 8
+    assert len({c.as_tuple() for c in cfgs}) == len(cfgs)
+    stages_256 = {c.stages for c in cfgs if (c.tile_m, c.tile_n, c.tile_k, c.waves) == (256, 256, 32, 8)}
+    stages_128 = {c.stages for c in cfgs if (c.tile_m, c.tile_n, c.tile_k) == (128, 128, 32)}
+    assert stages_256 == {2, 3, 4, 5} and stages_128 == {2, 3, 4, 5}
+    for c in cfgs:
+        st, info = _lib.sg_query_config(c)
+        assert st in (S.SG_OK, S.SG_ERR_HIP)
+        lds = oracle.lds_bytes(c.tile_m, c.tile_n, c.tile_k, c.stages)
+        assert info.lds_bytes == lds <= 160 * 1024
+        assert info.wg_per_cu_lds == oracle.blocks_per_unit(lds, 160 * 1024)
+        assert info.threads == 64 * c.waves
+        # 16-byte loads per lane per stage: (tile_m + tile_n) * tile_k * 2 bytes over the workgroup
+        assert info.loads_per_stage * 16 * info.threads == (c.tile_m + c.tile_n) * c.tile_k * 2
+    with pytest.raises(_lib.SgError):
+        _lib.sg_get_config(len(cfgs))
+
+
+def test_selection_returns_compiled_variants():
+    for shape in [(256, 256, 256), (4096, 4096, 4096), (2048, 2048, 128), (4096, 4096, 128),
+                  (8192, 8192, 8192), (8000, 7936, 8200), (1, 8, 8)]:
+        c = _lib.sg_select_config(*shape)
+        assert c.as_tuple() in {x.as_tuple() for x in _lib.configs()}
+
+
+def _gpu_visible() -> bool:
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="maps a launch failure; only meaningful with no GPU")
+def test_launch_without_device_reports_hip_error():
+    # all validation passes, so the library tries to launch and HIP refuses
+    assert L.gemm_fp16_tn(8, 8, 8, P, P + 0x100000, P + 0x200000, None) == S.SG_ERR_HIP

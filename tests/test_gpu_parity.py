@@ -1,0 +1,246 @@
+"""GPU parity of the HIP path against the CPU oracle.
+
+Every call goes through the C-ABI (libstagegemm.so) via the thin binding.
+Inputs are the seeded generators of stage_pipelined_mainloop_amd.inputs; the
+expected values come only from oracle/.  Bound per element:
+|D - D_ref| <= 2 ulp16(|D_ref|) + 1e-4 sqrt(K), every element finite.
+
+Small shapes are compared element by element in full.  The full-size
+workloads (run with the variant the benchmark times) are compared on whole
+sampled rows and columns, chosen to cross every tile boundary and the ragged
+tails, plus a check that every element is finite.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import stage_pipelined_mainloop_amd as sg
+from stage_pipelined_mainloop_amd import inputs
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(x: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def run_gemm(A, B, alpha=None, config=None):
+    a, b = to_dev(A), to_dev(B)
+    d = torch.full((A.shape[0], B.shape[0]), float("nan"), dtype=torch.float16, device=DEV)
+    sg.gemm(a, b, out=d, alpha=alpha, config=config)
+    torch.cuda.synchronize()
+    return d
+
+
+def full_check(A, B, alpha=None, config=None, label=""):
+    K = A.shape[1]
+    say(f"[case] full {label} M={A.shape[0]} N={B.shape[0]} K={K} alpha={alpha} cfg={config}")
+    d = run_gemm(A, B, alpha, config).cpu().numpy()
+    ref = oracle.gemm_tn_f64(A, B, 1.0 if alpha is None else alpha)
+    rep = oracle.check(d, ref, K)
+    assert rep.ok, f"{label}: {rep}"
+    return d
+
+
+def sample_lines(n, extra_seed, count=6):
+    base = [0, 1, 31, 32, 63, 64, 127, 128, 129, 255, 256, 257, 511, 512, n // 2,
+            n - 257, n - 256, n - 129, n - 128, n - 33, n - 32, n - 2, n - 1]
+    g = np.random.Generator(np.random.PCG64(extra_seed))
+    base += list(g.integers(0, n, count))
+    return sorted({int(v) for v in base if 0 <= v < n})
+
+
+def sampled_check(A, B, d_dev, alpha, label, seed=0):
+    M, K = A.shape
+    N = B.shape[0]
+    say(f"[case] sampled {label} M={M} N={N} K={K} alpha={alpha}")
+    assert bool(torch.isfinite(d_dev).all()), f"{label}: non-finite output"
+    rows = sample_lines(M, 1000 + seed)
+    cols = sample_lines(N, 2000 + seed)
+    d = d_dev.cpu().numpy()
+    rr = np.repeat(rows, N)
+    rc = np.tile(np.arange(N), len(rows))
+    cr = np.repeat(np.arange(M), len(cols))
+    cc = np.tile(cols, M)
+    r = np.concatenate([rr, cr])
+    c = np.concatenate([rc, cc])
+    ref = oracle.gemm_tn_f64_at(A, B, r, c, 1.0 if alpha is None else alpha)
+    rep = oracle.check(d[r, c], ref, K)
+    assert rep.ok, f"{label}: {rep} at (row {r[rep.argmax]}, col {c[rep.argmax]})"
+
+
+VARIANTS = [c.as_tuple() for c in sg.configs()] if True else []
+
+
+# ---------------------------------------------------------------------------
+# small shapes, full comparison
+
+def test_square256_default_and_every_variant():
+    A, B = inputs.workload("square256")
+    full_check(A, B, label="square256 default")
+    for cfg in VARIANTS:
+        full_check(A, B, config=cfg, label=f"square256 {cfg}")
+
+
+@pytest.mark.parametrize("shape", [(300, 264, 200), (257, 136, 40), (1, 8, 8), (129, 520, 1000),
+                                   (512, 512, 8)])
+def test_every_variant_on_ragged_shapes(shape):
+    M, N, K = shape
+    A, B = inputs.operands(M, N, K, 300 + M)
+    for cfg in VARIANTS:
+        full_check(A, B, config=cfg, label=f"ragged {shape} {cfg}")
+
+
+@pytest.mark.parametrize("cfg", [None, (128, 128, 32, 3, 4), (256, 256, 32, 5, 8),
+                                 (256, 256, 64, 2, 8)])
+def test_tiny_shape_grid(cfg):
+    # every M, N and K tail against every tile boundary of the variant
+    say(f"[case] tiny grid cfg={cfg}")
+    g = np.random.Generator(np.random.PCG64(17))
+    for M in (1, 2, 33, 127, 129, 255, 257, 300):
+        for N in (8, 16, 136, 248, 264):
+            for K in (8, 24, 40, 72, 136):
+                A = g.uniform(-1, 1, (M, K)).astype(np.float16)
+                B = g.uniform(-1, 1, (N, K)).astype(np.float16)
+                d = run_gemm(A, B, config=cfg).cpu().numpy()
+                rep = oracle.check(d, oracle.gemm_tn_f64(A, B), K)
+                assert rep.ok, (M, N, K, cfg, str(rep))
+
+
+def test_k_zero_writes_zeros():
+    say("[case] K=0")
+    A = np.zeros((70, 0), np.float16)
+    B = np.zeros((24, 0), np.float16)
+    d = run_gemm(A, B).cpu().numpy()
+    assert np.all(d.view(np.uint16) == 0)
+
+
+def test_empty_m_or_n_leaves_output_untouched():
+    say("[case] M=0 / N=0")
+    a = torch.zeros((0, 16), dtype=torch.float16, device=DEV)
+    b = torch.zeros((8, 16), dtype=torch.float16, device=DEV)
+    out = sg.gemm(a, b)
+    torch.cuda.synchronize()
+    assert tuple(out.shape) == (0, 8)
+
+
+@pytest.mark.parametrize("cfg", [None, (128, 128, 32, 4, 4), (256, 256, 32, 4, 8)])
+def test_canary_guard_bands(cfg):
+    # D sits inside a larger buffer filled with a NaN pattern; nothing outside
+    # D may change and every element of D must be written
+    M, N, K = 300, 264, 136
+    say(f"[case] canary cfg={cfg}")
+    A, B = inputs.operands(M, N, K, 77)
+    guard = 4096
+    buf = torch.full((M * N + 2 * guard,), float("nan"), dtype=torch.float16, device=DEV)
+    d = buf[guard:guard + M * N].view(M, N)
+    sg.gemm(to_dev(A), to_dev(B), out=d, config=cfg)
+    torch.cuda.synchronize()
+    host = buf.cpu().numpy()
+    pattern = np.float16(np.nan).view(np.uint16)
+    assert np.all(host[:guard].view(np.uint16) == pattern)
+    assert np.all(host[guard + M * N:].view(np.uint16) == pattern)
+    rep = oracle.check(host[guard:guard + M * N].reshape(M, N), oracle.gemm_tn_f64(A, B), K)
+    assert rep.ok, str(rep)
+
+
+@pytest.mark.parametrize("alpha", [1.0, 0.5, -2.0, 1.0 / 3.0, 1e-3])
+def test_alpha_values(alpha):
+    A, B = inputs.operands(384, 392, 520, 91)
+    a32 = float(np.float32(alpha))
+    full_check(A, B, alpha=a32, label=f"alpha {alpha}")
+
+
+def test_alpha_one_is_bitwise_plain():
+    A, B = inputs.operands(256, 256, 264, 93)
+    d1 = run_gemm(A, B).cpu().numpy()
+    d2 = run_gemm(A, B, alpha=1.0).cpu().numpy()
+    assert np.array_equal(d1.view(np.uint16), d2.view(np.uint16))
+
+
+def test_identity_and_permutation_exact():
+    say("[case] identity / permutation")
+    K = 512
+    A, _ = inputs.operands(300, K, K, 95)
+    eye = np.eye(K, dtype=np.float16)
+    d = run_gemm(A, eye).cpu().numpy()
+    assert np.array_equal(d.view(np.uint16), A.view(np.uint16))
+    perm = np.random.Generator(np.random.PCG64(3)).permutation(K)
+    P = np.zeros((K, K), np.float16)
+    P[np.arange(K), perm] = 1.0
+    d = run_gemm(A, P).cpu().numpy()
+    assert np.array_equal(d.view(np.uint16), A[:, perm].view(np.uint16))
+
+
+def test_all_ones_k8200():
+    say("[case] all ones K=8200")
+    A = np.ones((260, 8200), np.float16)
+    B = np.ones((136, 8200), np.float16)
+    d = run_gemm(A, B).cpu().numpy()
+    assert np.all(d == np.float16(8200))
+
+
+def test_deterministic_and_stream():
+    A, B = inputs.operands(1024, 1024, 1024, 97)
+    a, b = to_dev(A), to_dev(B)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        d1 = sg.gemm(a, b)
+        d2 = sg.gemm(a, b)
+    s.synchronize()
+    assert torch.equal(d1.view(torch.int16), d2.view(torch.int16))
+    rep = oracle.check(d1.cpu().numpy(), oracle.gemm_tn_f64(A, B), 1024)
+    assert rep.ok, str(rep)
+
+
+# ---------------------------------------------------------------------------
+# the workloads at full size, sampled comparison
+
+def test_attention_scores_full():
+    # Q, K 4096 x 128 N(0,1), S = Q K^T / sqrt(128)
+    A, B = inputs.workload("attn_scores")
+    alpha = float(np.float32(1.0 / math.sqrt(128.0)))
+    full_check(A, B, alpha=alpha, label="attn_scores")
+
+
+def test_square4096():
+    A, B = inputs.workload("square4096")
+    d = run_gemm(A, B)
+    sampled_check(A, B, d, None, "square4096", seed=2)
+
+
+@pytest.mark.parametrize("K", inputs.KSWEEP_K)
+def test_ksweep_every_stage_count(K):
+    A, B = inputs.ksweep(K)
+    a, b = to_dev(A), to_dev(B)
+    for cfg in VARIANTS:
+        if cfg[2] != 32 or cfg[:2] not in ((128, 128), (256, 256)):
+            continue
+        d = torch.full((2048, 2048), float("nan"), dtype=torch.float16, device=DEV)
+        sg.gemm(a, b, out=d, config=cfg)
+        torch.cuda.synchronize()
+        sampled_check(A, B, d, None, f"ksweep K={K} {cfg}", seed=K)
+
+
+def test_square8192():
+    A, B = inputs.workload("square8192")
+    d = run_gemm(A, B)
+    sampled_check(A, B, d, None, "square8192", seed=5)
+
+
+def test_ragged8000():
+    A, B = inputs.workload("ragged8000")
+    d = run_gemm(A, B)
+    sampled_check(A, B, d, None, "ragged8000", seed=6)
