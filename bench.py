@@ -141,7 +141,7 @@ def mode_ksweep(args) -> int:
         M = N = inputs.KSWEEP_MN
         d = torch.empty((M, N), dtype=torch.float16, device="cuda")
         for c in sg.configs():
-            if c.tile_k != 32 or (c.tile_m, c.tile_n, c.waves) not in ((128, 128, 4), (256, 256, 8)):
+            if (c.tile_m, c.tile_n, c.waves) not in ((128, 128, 4), (256, 256, 8)):
                 continue
             mean, mn = time_launches(lambda: sg.gemm(a, b, out=d, config=c), args.steps, args.warmup)
             t = 2.0 * M * N * K / (mean / 1e3) / 1e12
@@ -177,7 +177,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="square8192")
     ap.add_argument("--config", default=None,
-                    help="explicit variant tile_m,tile_n,tile_k,stages,waves")
+                    help="explicit variant tile_m,tile_n,tile_k,stages,waves,schedule")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -261,7 +261,7 @@ def main() -> int:
         "config": {"workload": args.workload, "M": M, "N": N, "K": K, "dist": dist,
                    "alpha": alpha if alpha is not None else 1.0,
                    "variant": "x".join(str(v) for v in chosen.as_tuple()[:3])
-                              + f" S{chosen.stages} w{chosen.waves}",
+                              + f" S{chosen.stages} w{chosen.waves} sched{chosen.schedule}",
                    "pct_of_fp16_peak": round(100.0 * value / PEAK_TFLOPS, 2),
                    "kernel_ms_mean": round(mean_launch_s * 1e3, 4),
                    "kernel_ms_min": round(min(launch_ms), 4)},

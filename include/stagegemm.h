@@ -59,13 +59,20 @@ typedef enum sg_status {
 } sg_status;
 
 /* A compiled kernel variant: output tile tile_m x tile_n, K step tile_k,
- * `stages` LDS ring slots, `waves` 64-lane wavefronts per workgroup. */
+ * `stages` LDS ring slots, `waves` 64-lane wavefronts per workgroup, and the
+ * mainloop order `schedule`:
+ *   0  "Lesson 6", section 2: per K step wait, barrier, refill the free slot,
+ *      then read fragments and compute;
+ *   1  "cute(9) multistage_gemm", sections 6 and 9: fragments double-buffered
+ *      in registers, the next tile's first fragments read right after the
+ *      barrier and before the current tile's last MFMAs. */
 typedef struct sg_config {
     int tile_m;
     int tile_n;
     int tile_k;
     int stages;
     int waves;
+    int schedule;
 } sg_config;
 
 /* Static facts about a compiled variant. */

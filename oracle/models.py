@@ -355,3 +355,52 @@ def loosest_wait_counts(ntile: int, stages: int, loads_per_tile: int) -> list[in
                 break
         counts.append(best)
     return counts
+
+
+def schedule_cute_loads(ntile: int, stages: int, nfrag: int, loads_per_tile: int,
+                        wait_counts: list[int] | None = None) -> list[Op]:
+    """The order of "cute(9) multistage_gemm" sections 5-6 with each tile's
+    copy split into `loads_per_tile` counted loads and no fences (waits count
+    loads).  Prologue: tiles 0..S-2, wait for tile 0, barrier, read fragment 0
+    of tile 0.  Then for tile k and fragment ik: at the last fragment (and
+    only if tile k+1 exists) wait for tile k+1, barrier, read fragment 0 of
+    tile k+1; otherwise read fragment ik+1 of tile k; at the first fragment
+    issue tile k+S-1 if it exists; compute fragment ik of tile k.
+    `wait_counts[t]` is the wait used before tile t is first read (default:
+    the loads issued after tile t's, i.e. the loosest safe value)."""
+    if nfrag < 2:
+        raise ValueError("the walked-through schedule needs at least two fragments per tile")
+    ops: list[Op] = []
+    issued = []
+
+    def issue(t):
+        for _ in range(loads_per_tile):
+            ops.append(Op("issue_part", tile=t, slot=t % stages))
+        issued.append(t)
+
+    def wait_for(t):
+        if wait_counts is None:
+            n = loads_per_tile * (max(issued) - t)
+        else:
+            n = wait_counts[t]
+        ops.append(Op("wait", n=n))
+        ops.append(Op("sync"))
+
+    for t in range(min(stages - 1, ntile)):
+        issue(t)
+    if ntile == 0:
+        return ops
+    wait_for(0)
+    ops.append(Op("read", slot=0, frag=0))
+    for k in range(ntile):
+        for ik in range(nfrag):
+            if ik == nfrag - 1:
+                if k + 1 < ntile:
+                    wait_for(k + 1)
+                    ops.append(Op("read", slot=(k + 1) % stages, frag=0))
+            else:
+                ops.append(Op("read", slot=k % stages, frag=ik + 1))
+            if ik == 0 and k + stages - 1 < ntile:
+                issue(k + stages - 1)
+            ops.append(Op("compute", tile=k, frag=ik))
+    return ops

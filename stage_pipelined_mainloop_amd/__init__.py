@@ -20,7 +20,7 @@ def gemm(A, B, out=None, alpha: float | None = None, config=None, stream=None):
     """D = alpha * A @ B.T on the GPU for fp16 CUDA (HIP) tensors.
 
     A: (M, K), B: (N, K), out: (M, N) or None (allocated).  `config` picks a
-    compiled variant (SgConfig or a 5-tuple) instead of the library's choice.
+    compiled variant (SgConfig or a 6-tuple) instead of the library's choice.
     `stream` is a torch.cuda.Stream (default: the current stream)."""
     import torch
 

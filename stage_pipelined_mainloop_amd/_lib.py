@@ -25,13 +25,13 @@ SG_ERR_HIP = 6
 
 class SgConfig(ctypes.Structure):
     _fields_ = [("tile_m", ctypes.c_int), ("tile_n", ctypes.c_int), ("tile_k", ctypes.c_int),
-                ("stages", ctypes.c_int), ("waves", ctypes.c_int)]
+                ("stages", ctypes.c_int), ("waves", ctypes.c_int), ("schedule", ctypes.c_int)]
 
     def as_tuple(self):
-        return (self.tile_m, self.tile_n, self.tile_k, self.stages, self.waves)
+        return (self.tile_m, self.tile_n, self.tile_k, self.stages, self.waves, self.schedule)
 
     def __repr__(self):
-        return "SgConfig(%d, %d, %d, stages=%d, waves=%d)" % self.as_tuple()
+        return "SgConfig(%d, %d, %d, stages=%d, waves=%d, schedule=%d)" % self.as_tuple()
 
 
 class SgConfigInfo(ctypes.Structure):

@@ -37,6 +37,9 @@
 //     K-tail chunks and N-tail columns are sent to an offset past the
 //     resource's range (reads 0 / store dropped).  Zero fill gives exactly the
 //     plain sum (the padding reading of "CUDA operator notes 2", "GEMM").
+//   * K order: each workgroup may start its K loop at a rotated tile (see
+//     kt_rot below) so that lockstep workgroups do not all fetch the same
+//     column band of power-of-two-strided rows at once.
 //   * Epilogue: operands are fed to the MFMA swapped (B rows as the first
 //     operand), so each lane's accumulators are four consecutive columns of
 //     one row of D: alpha * acc, convert to fp16 (RNE), one 8-byte store.
@@ -44,6 +47,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 namespace sg {
 
@@ -89,9 +94,13 @@ __device__ __forceinline__ int swz(int r)
     }
 }
 
-template <int BM_, int BN_, int BK_, int S_, int WM_, int WN_>
+// SCHED selects the mainloop order: 0 = the three-phase order of "Lesson 6"
+// (wait, barrier, refill, compute), 1 = the cute page's order with the next
+// tile's first fragments prefetched across the barrier.
+template <int BM_, int BN_, int BK_, int S_, int WM_, int WN_, int SCHED_ = 1>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_, WM = WM_, WN = WN_;
+    static constexpr int SCHED = SCHED_;
     static constexpr int NW = WM * WN;              // wavefronts
     static constexpr int T = 64 * NW;               // threads
     static constexpr int WTM = BM / WM;             // wave sub-tile
@@ -109,6 +118,8 @@ struct Cfg {
     static constexpr int NB = BN * CPR / (64 * NW);
     static constexpr int L = NA + NB;
     static_assert(S >= 2, "a ring needs at least two slots");
+    static_assert(SCHED == 0 || SCHED == 1, "mainloop order");
+    static_assert(NKS % 2 == 0, "fragment double buffer alternates per K step");
     static_assert(BK == 32 || BK == 64, "BK");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile is whole 32x32 blocks");
     static_assert(NA * 64 * NW == BM * CPR && NB * 64 * NW == BN * CPR, "even load split");
@@ -165,7 +176,7 @@ __device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, i
 template <class C>
 __global__ void __launch_bounds__(C::T)
 gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
-               _Float16 *__restrict__ D, int M, int N, int K, float alpha)
+               _Float16 *__restrict__ D, int M, int N, int K, float alpha, int kt_rot)
 {
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
@@ -187,6 +198,14 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + (size_t)n0 * K, (uint32_t)rows_b * K * 2u);
 
     const int ntile = (K + C::BK - 1) / C::BK;
+    // K-loop rotation.  With a power-of-two row stride every row of a K tile
+    // sits at the same offset modulo the memory-channel interleave, so tiles
+    // fetched in lockstep by all workgroups of an XCD queue on one channel.
+    // Workgroup row tm starts its K loop at tile (tm mod kt_rot): workgroups
+    // sharing an A panel stay in lockstep, the others spread over kt_rot
+    // channels.  The sum is the same set of products in a different order.
+    int kt0 = 0;
+    if (kt_rot > 1 && ntile > 0) kt0 = (tm % kt_rot) % ntile;
 
     // ---- per-lane LDS-DMA source offsets (bytes) and K columns, fixed over K
     uint32_t a_off[C::NA], b_off[C::NB];
@@ -210,7 +229,9 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
 
     // Issue the L loads of K tile `t` into ring slot `slot`.
     auto issue = [&](int t, int slot) {
-        const int kbase = t * C::BK;
+        int kt = t + kt0;
+        if (kt >= ntile) kt -= ntile;
+        const int kbase = kt * C::BK;
         const int krem = K - kbase;                  // valid K columns in this tile
         const uint32_t kb = (uint32_t)kbase * 2u;
         char *sa = smem + slot * C::STAGE_BYTES;
@@ -251,43 +272,143 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
+    // LDS -> VGPR fragments of one MFMA K step, and the MFMAs of one K step.
+    // Read order follows first use by mfma_step: A0, all of B, then A1...
+    auto read_frags = [&](f16x8 (&ra)[C::FM], f16x8 (&rb)[C::FN], const char *sbase, int ks) {
+        ra[0] = *(const f16x8 *)(sbase + fa[ks]);
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+            rb[j] = *(const f16x8 *)(sbase + fb[ks] + j * 32 * C::RB);
+#pragma unroll
+        for (int i = 1; i < C::FM; ++i)
+            ra[i] = *(const f16x8 *)(sbase + fa[ks] + i * 32 * C::RB);
+    };
+    auto mfma_step = [&](const f16x8 (&ra)[C::FM], const f16x8 (&rb)[C::FN]) {
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(rb[j], ra[i], acc[i][j], 0, 0, 0);
+    };
+    // Wait for this lane's loads of tile `t` (and its own LDS reads), then a
+    // workgroup barrier: tile t is visible to every wave and every read
+    // issued before the barrier has completed.
+    auto sync_tile = [&](int t) {
+        int after = ntile - 1 - t;
+        if (after > C::S - 2) after = C::S - 2;
+        compiler_fence();
+        __builtin_amdgcn_sched_barrier(0);
+        wait_tile<C>(after);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        compiler_fence();
+    };
+
+    // The same with a compile-time count of later tiles in flight (steady
+    // state: always S-2), so no branch splits the scheduling region.
+    auto sync_tile_steady = [&]() {
+        compiler_fence();
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm_lgkm0<(C::S - 2) * C::L>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        compiler_fence();
+    };
+
     // ---- prologue: tiles 0 .. S-2
 #pragma unroll
     for (int t = 0; t < C::S - 1; ++t)
         if (t < ntile) issue(t, t);
 
-    // ---- steady state and drain
     int slot = 0;                                    // slot of tile k
     int wslot = C::S - 1;                            // slot of tile k+S-1
+    if constexpr (C::SCHED == 0) {
+        // ---- "Lesson 6" three-phase order: wait, barrier, refill, compute.
 #pragma unroll 1
-    for (int k = 0; k < ntile; ++k) {
-        int after = ntile - 1 - k;
-        if (after > C::S - 2) after = C::S - 2;
-        compiler_fence();
-        wait_tile<C>(after);
-        __builtin_amdgcn_s_barrier();
-        compiler_fence();
-        if (k + C::S - 1 < ntile) issue(k + C::S - 1, wslot);
-
-        const char *sbase = smem + slot * C::STAGE_BYTES;
+        for (int k = 0; k < ntile; ++k) {
+            sync_tile(k);
+            if (k + C::S - 1 < ntile) issue(k + C::S - 1, wslot);
+            const char *sbase = smem + slot * C::STAGE_BYTES;
 #pragma unroll
-        for (int ks = 0; ks < C::NKS; ++ks) {
-            f16x8 fragA[C::FM], fragB[C::FN];
-#pragma unroll
-            for (int i = 0; i < C::FM; ++i)
-                fragA[i] = *(const f16x8 *)(sbase + fa[ks] + i * 32 * C::RB);
-#pragma unroll
-            for (int j = 0; j < C::FN; ++j)
-                fragB[j] = *(const f16x8 *)(sbase + fb[ks] + j * 32 * C::RB);
-#pragma unroll
-            for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-                for (int j = 0; j < C::FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fragB[j], fragA[i],
-                                                                       acc[i][j], 0, 0, 0);
+            for (int ks = 0; ks < C::NKS; ++ks) {
+                f16x8 ra[C::FM], rb[C::FN];
+                read_frags(ra, rb, sbase, ks);
+                mfma_step(ra, rb);
+            }
+            slot = (slot + 1 == C::S) ? 0 : slot + 1;
+            wslot = (wslot + 1 == C::S) ? 0 : wslot + 1;
         }
-        slot = (slot + 1 == C::S) ? 0 : slot + 1;
-        wslot = (wslot + 1 == C::S) ? 0 : wslot + 1;
+    } else {
+        // ---- "cute(9) multistage_gemm" order (sections 6.2, 9): fragments are
+        // double-buffered in VGPRs; step ks reads step ks+1 while its MFMAs
+        // run.  At the last K step of tile k the wave waits for tile k+1,
+        // barriers, and prefetches tile k+1's first step before issuing the
+        // last MFMAs of tile k, so LDS latency hides under them.  The refill
+        // of slot (k-1) mod S is issued at the first step of tile k: every
+        // read of that slot was issued before the previous barrier.
+        f16x8 ra0[C::FM], rb0[C::FN], ra1[C::FM], rb1[C::FN];
+        // One K tile.  MODE: 2 = steady state (a next tile exists and tile
+        // k+S-1 is issued), 1 = drain (a next tile exists, nothing issued),
+        // 0 = the last tile.  The modes are separate loops so that every K
+        // step is one branch-free scheduling region: a branch joining the
+        // barrier path would make the compiler wait for the prefetched reads
+        // before the remaining MFMAs.  Within a step the MFMAs are interleaved
+        // one by one with the LDS reads and LDS-DMA issues.
+        auto tile = [&](int k, auto mode) {
+            constexpr int MODE = decltype(mode)::value;
+            const char *sbase = smem + slot * C::STAGE_BYTES;
+            const int nslot = (slot + 1 == C::S) ? 0 : slot + 1;
+#pragma unroll
+            for (int ks = 0; ks < C::NKS; ++ks) {
+                // NKS is even, so step ks uses buffer ks & 1 in every tile
+                f16x8(&cra)[C::FM] = (ks & 1) ? ra1 : ra0;
+                f16x8(&crb)[C::FN] = (ks & 1) ? rb1 : rb0;
+                f16x8(&nra)[C::FM] = (ks & 1) ? ra0 : ra1;
+                f16x8(&nrb)[C::FN] = (ks & 1) ? rb0 : rb1;
+                int nreads = C::FM + C::FN;
+                if (ks == C::NKS - 1) {
+                    if constexpr (MODE == 2) {
+                        sync_tile_steady();
+                    } else if constexpr (MODE == 1) {
+                        sync_tile(k + 1);
+                    } else {
+                        nreads = 0;
+                    }
+                    if constexpr (MODE != 0)
+                        read_frags(nra, nrb, smem + nslot * C::STAGE_BYTES, 0);
+                } else {
+                    read_frags(nra, nrb, sbase, ks + 1);
+                }
+                int nissue = 0;
+                if constexpr (MODE == 2) {
+                    if (ks == 0) {
+                        issue(k + C::S - 1, wslot);
+                        nissue = C::L;
+                    }
+                }
+                mfma_step(cra, crb);
+                // order: LDS read, MFMA, [LDS-DMA], LDS read, MFMA, ...
+#pragma unroll
+                for (int m = 0; m < C::FM * C::FN; ++m) {
+                    if (m < nreads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (m < nissue) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            slot = nslot;
+            wslot = (wslot + 1 == C::S) ? 0 : wslot + 1;
+        };
+        if (ntile > 0) {
+            sync_tile(0);
+            read_frags(ra0, rb0, smem, 0);
+            int k = 0;
+#pragma unroll 1
+            for (; k < ntile - (C::S - 1); ++k) tile(k, std::integral_constant<int, 2>{});
+#pragma unroll 1
+            for (; k < ntile - 1; ++k) tile(k, std::integral_constant<int, 1>{});
+            tile(ntile - 1, std::integral_constant<int, 0>{});
+        }
     }
 
     // ---- epilogue: lane holds D[m][n .. n+3] for m = row of (lane & 31),

@@ -53,7 +53,7 @@ def test_argument_errors(args, status):
     M, N, K, a, b, d = args
     assert L.gemm_fp16_tn(M, N, K, a, b, d, None) == status
     assert L.gemm_fp16_tn_alpha(M, N, K, 0.5, a, b, d, None) == status
-    cfg = _lib.SgConfig(128, 128, 32, 3, 4)
+    cfg = _lib.SgConfig(128, 128, 32, 3, 4, 1)
     assert L.gemm_fp16_tn_cfg(M, N, K, 1.0, a, b, d, ctypes.byref(cfg), None) == status
 
 
@@ -66,7 +66,7 @@ def test_empty_outputs_are_no_ops():
 
 def test_cfg_errors():
     assert L.gemm_fp16_tn_cfg(8, 8, 8, 1.0, P, P + 0x100000, P + 0x200000, None, None) == S.SG_ERR_NULL
-    bad = _lib.SgConfig(96, 128, 32, 3, 4)
+    bad = _lib.SgConfig(96, 128, 32, 3, 4, 1)
     assert L.gemm_fp16_tn_cfg(8, 8, 8, 1.0, P, P + 0x100000, P + 0x200000,
                               ctypes.byref(bad), None) == S.SG_ERR_UNSUPPORTED
     st, _ = _lib.sg_query_config(bad)
@@ -95,9 +95,12 @@ def test_wait_counts_match_the_ring_simulator():
                 want = oracle.loosest_wait_counts(ntile, stages, loads)
                 got = [_lib.sg_pipeline_wait_count(stages, loads, ntile, k) for k in range(ntile)]
                 assert got == want, (stages, loads, ntile)
-                # and the schedule with those waits passes every invariant
+                # and both mainloop orders pass every invariant with those waits
                 ops = oracle.schedule_three_phase(ntile, stages, 2, got, loads)
                 assert oracle.simulate_loads(ops, ntile, stages, 2, loads).ok
+                for nfrag in (2, 4):
+                    ops = oracle.schedule_cute_loads(ntile, stages, nfrag, loads, got)
+                    assert oracle.simulate_loads(ops, ntile, stages, nfrag, loads).ok
     assert _lib.sg_pipeline_wait_count(1, 4, 4, 0) == -1
     assert _lib.sg_pipeline_wait_count(3, 4, 4, 4) == -1
 
@@ -106,9 +109,12 @@ def test_config_table_and_lds_model():
     cfgs = _lib.configs()
     assert len(cfgs) == _lib.sg_num_configs() >= 8
     assert len({c.as_tuple() for c in cfgs}) == len(cfgs)
-    stages_256 = {c.stages for c in cfgs if (c.tile_m, c.tile_n, c.tile_k, c.waves) == (256, 256, 32, 8)}
-    stages_128 = {c.stages for c in cfgs if (c.tile_m, c.tile_n, c.tile_k) == (128, 128, 32)}
-    assert stages_256 == {2, 3, 4, 5} and stages_128 == {2, 3, 4, 5}
+    for sched in (0, 1):
+        stages_256 = {c.stages for c in cfgs
+                      if (c.tile_m, c.tile_n, c.tile_k, c.waves, c.schedule) == (256, 256, 32, 8, sched)}
+        stages_128 = {c.stages for c in cfgs
+                      if (c.tile_m, c.tile_n, c.tile_k, c.waves, c.schedule) == (128, 128, 32, 4, sched)}
+        assert stages_256 == {2, 3, 4, 5} and stages_128 == {2, 3, 4, 5}, sched
     for c in cfgs:
         st, info = _lib.sg_query_config(c)
         assert st in (S.SG_OK, S.SG_ERR_HIP)

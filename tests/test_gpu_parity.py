@@ -81,7 +81,7 @@ def sampled_check(A, B, d_dev, alpha, label, seed=0):
     assert rep.ok, f"{label}: {rep} at (row {r[rep.argmax]}, col {c[rep.argmax]})"
 
 
-VARIANTS = [c.as_tuple() for c in sg.configs()] if True else []
+VARIANTS = [c.as_tuple() for c in sg.configs()]
 
 
 # ---------------------------------------------------------------------------
@@ -103,8 +103,9 @@ def test_every_variant_on_ragged_shapes(shape):
         full_check(A, B, config=cfg, label=f"ragged {shape} {cfg}")
 
 
-@pytest.mark.parametrize("cfg", [None, (128, 128, 32, 3, 4), (256, 256, 32, 5, 8),
-                                 (256, 256, 64, 2, 8)])
+@pytest.mark.parametrize("cfg", [None, (128, 128, 32, 3, 4, 1), (256, 256, 32, 5, 8, 1),
+                                 (256, 256, 64, 2, 8, 1), (256, 256, 32, 3, 8, 0),
+                                 (128, 128, 64, 3, 4, 1)])
 def test_tiny_shape_grid(cfg):
     # every M, N and K tail against every tile boundary of the variant
     say(f"[case] tiny grid cfg={cfg}")
@@ -117,6 +118,18 @@ def test_tiny_shape_grid(cfg):
                 d = run_gemm(A, B, config=cfg).cpu().numpy()
                 rep = oracle.check(d, oracle.gemm_tn_f64(A, B), K)
                 assert rep.ok, (M, N, K, cfg, str(rep))
+
+
+@pytest.mark.parametrize("shape,cfg", [((4352, 4352, 264), None),
+                                       ((4352, 4104, 200), (256, 256, 64, 2, 8, 1)),
+                                       ((2304, 2304, 520), (128, 128, 32, 4, 4, 1)),
+                                       ((2304, 2312, 1000), (256, 256, 32, 3, 8, 0))])
+def test_rotated_k_loop_with_k_tail(shape, cfg):
+    # more than 256 workgroups, so each tile row starts its K loop at a
+    # rotated tile and the K-tail tile lands mid-sequence
+    M, N, K = shape
+    A, B = inputs.operands(M, N, K, 500 + K)
+    full_check(A, B, config=cfg, label=f"rotated {shape}")
 
 
 def test_k_zero_writes_zeros():
@@ -136,7 +149,8 @@ def test_empty_m_or_n_leaves_output_untouched():
     assert tuple(out.shape) == (0, 8)
 
 
-@pytest.mark.parametrize("cfg", [None, (128, 128, 32, 4, 4), (256, 256, 32, 4, 8)])
+@pytest.mark.parametrize("cfg", [None, (128, 128, 32, 4, 4, 1), (256, 256, 32, 4, 8, 1),
+                                 (256, 256, 32, 4, 8, 0)])
 def test_canary_guard_bands(cfg):
     # D sits inside a larger buffer filled with a NaN pattern; nothing outside
     # D may change and every element of D must be written
@@ -226,7 +240,7 @@ def test_ksweep_every_stage_count(K):
     A, B = inputs.ksweep(K)
     a, b = to_dev(A), to_dev(B)
     for cfg in VARIANTS:
-        if cfg[2] != 32 or cfg[:2] not in ((128, 128), (256, 256)):
+        if cfg[:2] not in ((128, 128), (256, 256)):
             continue
         d = torch.full((2048, 2048), float("nan"), dtype=torch.float16, device=DEV)
         sg.gemm(a, b, out=d, config=cfg)

@@ -7,7 +7,8 @@ import os
 import pytest
 
 import oracle
-from oracle.models import Op, schedule_cute_multistage, schedule_three_phase, simulate, simulate_loads
+from oracle.models import (Op, schedule_cute_loads, schedule_cute_multistage, schedule_three_phase,
+                           simulate, simulate_loads)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -148,3 +149,23 @@ def test_planted_fill_of_all_slots_is_caught():
         ops += [Op("read", slot=k % stages, frag=0), Op("compute", tile=k, frag=0)]
     r = simulate_loads(ops, ntile, stages, 1, L)
     assert not r.ok
+
+
+@pytest.mark.parametrize("stages", [2, 3, 4, 5, 6])
+@pytest.mark.parametrize("L", [1, 4, 8])
+def test_cute_order_with_counted_loads_invariants(stages, L):
+    for ntile in range(1, 41):
+        for nfrag in (2, 4):
+            ops = schedule_cute_loads(ntile, stages, nfrag, L)
+            r = simulate_loads(ops, ntile, stages, nfrag, L)
+            assert r.ok, (ntile, stages, nfrag, L, r.errors[:3])
+
+
+def test_cute_order_with_counted_loads_catches_a_loose_wait():
+    ntile, stages, L = 12, 4, 4
+    base = [L * max(0, min(stages - 2, ntile - 1 - t)) for t in range(ntile)]
+    for t in range(ntile):
+        loose = list(base)
+        loose[t] += 1
+        r = simulate_loads(schedule_cute_loads(ntile, stages, 2, L, loose), ntile, stages, 2, L)
+        assert not r.ok and any(e.startswith("RAW") for e in r.errors), t
