@@ -96,7 +96,8 @@ __device__ __forceinline__ int swz(int r)
 
 // SCHED selects the mainloop order: 0 = the three-phase order of "Lesson 6"
 // (wait, barrier, refill, compute), 1 = the cute page's order with the next
-// tile's first fragments prefetched across the barrier.
+// tile's first fragments prefetched across the barrier, 2 = ping-pong of two
+// wave groups (one computes while the other reads and refills).
 template <int BM_, int BN_, int BK_, int S_, int WM_, int WN_, int SCHED_ = 1>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_, WM = WM_, WN = WN_;
@@ -118,7 +119,9 @@ struct Cfg {
     static constexpr int NB = BN * CPR / (64 * NW);
     static constexpr int L = NA + NB;
     static_assert(S >= 2, "a ring needs at least two slots");
-    static_assert(SCHED == 0 || SCHED == 1, "mainloop order");
+    static_assert(SCHED == 0 || SCHED == 1 || SCHED == 2, "mainloop order");
+    static_assert(SCHED != 2 || (S == 2 && NW % 4 == 0 && (NW / 2) % 2 == 0 && BK == 64),
+                  "ping-pong: two slots, two even wave groups, 128-byte rows");
     static_assert(NKS % 2 == 0, "fragment double buffer alternates per K step");
     static_assert(BK == 32 || BK == 64, "BK");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile is whole 32x32 blocks");
@@ -207,49 +210,41 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
     int kt0 = 0;
     if (kt_rot > 1 && ntile > 0) kt0 = (tm % kt_rot) % ntile;
 
-    // ---- per-lane LDS-DMA source offsets (bytes) and K columns, fixed over K
-    uint32_t a_off[C::NA], b_off[C::NB];
-    int a_col[C::NA], b_col[C::NB];
-#pragma unroll
-    for (int i = 0; i < C::NA; ++i) {
-        const int q = (i * C::NW + wave) * 64 + lane;     // LDS chunk index in the A slot
-        const int r = q / C::CPR;
-        const int c = (q % C::CPR) ^ swz<C::CPR>(r);
-        a_off[i] = (uint32_t)(r * K + c * 8) * 2u;
-        a_col[i] = c * 8;
-    }
-#pragma unroll
-    for (int i = 0; i < C::NB; ++i) {
-        const int q = (i * C::NW + wave) * 64 + lane;
-        const int r = q / C::CPR;
-        const int c = (q % C::CPR) ^ swz<C::CPR>(r);
-        b_off[i] = (uint32_t)(r * K + c * 8) * 2u;
-        b_col[i] = c * 8;
-    }
+    // ---- per-lane LDS-DMA source offsets.  Wave load i of an operand fills
+    // LDS chunks q = (i*NW + wave)*64 + lane: row r = q / CPR, position
+    // q % CPR, holding logical chunk c = position ^ swz(r).  64/CPR rows per
+    // load; r mod 16 (all swz depends on) is the same for every i when
+    // 64/CPR >= 16 or NW is even, so c is fixed per lane and the source
+    // offset of load i is base + i * (NW * 64/CPR) rows.
+    constexpr int ROWS_PER_LOAD = 64 / C::CPR;
+    static_assert(ROWS_PER_LOAD >= 16 || C::NW % 2 == 0, "swizzle fixed across a wave's loads");
+    const int l_row0 = wave * ROWS_PER_LOAD + lane / C::CPR;
+    const int l_chunk = (lane % C::CPR) ^ swz<C::CPR>(l_row0);
+    const uint32_t l_base = (uint32_t)(l_row0 * K + l_chunk * 8) * 2u;
+    const uint32_t l_step = (uint32_t)(C::NW * ROWS_PER_LOAD) * (uint32_t)K * 2u;
 
     // Issue the L loads of K tile `t` into ring slot `slot`.
     auto issue = [&](int t, int slot) {
         int kt = t + kt0;
         if (kt >= ntile) kt -= ntile;
         const int kbase = kt * C::BK;
-        const int krem = K - kbase;                  // valid K columns in this tile
-        const uint32_t kb = (uint32_t)kbase * 2u;
+        // K-tail: this lane's chunk lies past K -> an offset past the range
+        // (reads 0); its later loads keep that offset (step 0).
+        const bool valid = l_chunk * 8 < K - kbase;
+        const uint32_t v = valid ? l_base + (uint32_t)kbase * 2u : kOutOfRange;
+        const uint32_t step = valid ? l_step : 0u;
         char *sa = smem + slot * C::STAGE_BYTES;
         char *sb = sa + C::A_BYTES;
 #pragma unroll
-        for (int i = 0; i < C::NA; ++i) {
-            const uint32_t v = (a_col[i] < krem) ? a_off[i] + kb : kOutOfRange;
+        for (int i = 0; i < C::NA; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 ra, (__attribute__((address_space(3))) void *)(sa + (i * C::NW + wave) * 1024),
-                16, v, 0, 0, 0);
-        }
+                16, v + (uint32_t)i * step, 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < C::NB; ++i) {
-            const uint32_t v = (b_col[i] < krem) ? b_off[i] + kb : kOutOfRange;
+        for (int i = 0; i < C::NB; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rb, (__attribute__((address_space(3))) void *)(sb + (i * C::NW + wave) * 1024),
-                16, v, 0, 0, 0);
-        }
+                16, v + (uint32_t)i * step, 0, 0, 0);
     };
 
     // ---- per-lane fragment read offsets within a slot (bytes), per MFMA K step
@@ -338,6 +333,96 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
             slot = (slot + 1 == C::S) ? 0 : slot + 1;
             wslot = (wslot + 1 == C::S) ? 0 : wslot + 1;
         }
+    } else if constexpr (C::SCHED == 2) {
+        // ---- Ping-pong.  The two waves sharing a SIMD belong to different
+        // groups (waves are dealt to SIMDs round-robin): G0 = waves 0..NG-1,
+        // G1 = waves NG..NW-1.  Time is cut into phases, each ending in one
+        // workgroup barrier.  In every phase one group issues all MFMAs of a
+        // K tile from registers (C) while the other reads all fragments of
+        // its next K tile from LDS (M), so each SIMD's matrix pipe is fed by
+        // one wave while the other wave's LDS traffic is in flight:
+        //     phase:  0      1      2      3    ...  2n-1    2n
+        //     G0:    M(0)   C(0)   M(1)   C(1)  ...  C(n-1)  idle
+        //     G1:    idle   M(0)   C(0)   M(1)  ...  M(n-1)  C(n-1)
+        // Ring (two slots): tile j lives in slot j%2.  G0 refills at the start
+        // of M(j) (phase 2j): tile j+1 into slot (j+1)%2, whose previous tile
+        // j-1 was last read in phases 2j-2 (G0) and 2j-1 (G1), each closed by
+        // lgkmcnt(0) + barrier (WAR).  G0 waits vmcnt(0) at the end of C(j),
+        // so tile j+1 is complete before the barrier that opens phase 2j+2,
+        // where it is first read (RAW).  Tile 0 is loaded by all waves before
+        // the loop.  Every wave executes 2n+2 barriers.
+        constexpr int NG = C::NW / 2;
+        const int grp = wave / NG;                 // wave-uniform
+        const int gw = wave - grp * NG;
+        constexpr int NAG = C::BM * C::CPR / (64 * NG);
+        constexpr int NBG = C::BN * C::CPR / (64 * NG);
+        static_assert(NAG * 64 * NG == C::BM * C::CPR && NBG * 64 * NG == C::BN * C::CPR, "split");
+        // Loader lane -> LDS chunk q = (i*NG + gw)*64 + lane: row
+        // r = (i*NG + gw)*8 + lane/8, position lane%8.  NG is even, so r mod 16
+        // and hence the swizzle do not depend on i: one base offset per
+        // operand, advanced by NG*8 rows per load.
+        const int pr0 = gw * 8 + (lane >> 3);
+        const int pc = (lane & 7) ^ swz<C::CPR>(pr0);
+        const uint32_t p_base = (uint32_t)(pr0 * K + pc * 8) * 2u;
+        const uint32_t p_step = (uint32_t)(NG * 8) * (uint32_t)K * 2u;
+        auto issue_g0 = [&](int t, int slot) {
+            int kt = t + kt0;
+            if (kt >= ntile) kt -= ntile;
+            const int kbase = kt * C::BK;
+            const bool valid = pc * 8 < K - kbase;
+            uint32_t v = valid ? p_base + (uint32_t)kbase * 2u : kOutOfRange;
+            const uint32_t step = valid ? p_step : 0u;
+            char *sa = smem + slot * C::STAGE_BYTES;
+            char *sb = sa + C::A_BYTES;
+#pragma unroll
+            for (int i = 0; i < NAG; ++i) {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    ra, (__attribute__((address_space(3))) void *)(sa + (i * NG + gw) * 1024),
+                    16, v + (uint32_t)i * step, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < NBG; ++i) {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rb, (__attribute__((address_space(3))) void *)(sb + (i * NG + gw) * 1024),
+                    16, v + (uint32_t)i * step, 0, 0, 0);
+            }
+        };
+        auto barrier = [&]() {
+            compiler_fence();
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            compiler_fence();
+        };
+        f16x8 fra[C::NKS][C::FM], frb[C::NKS][C::FN];
+        // tile 0 (already issued by the prologue) complete and visible
+        compiler_fence();
+        wait_vm_lgkm0<0>();
+        barrier();
+        if (grp == 1) barrier();                   // G1 idles in phase 0
+#pragma unroll 1
+        for (int j = 0; j < ntile; ++j) {
+            // M(j)
+            if (grp == 0 && j + 1 < ntile) issue_g0(j + 1, (j + 1) & 1);
+            const char *sbase = smem + (j & 1) * C::STAGE_BYTES;
+#pragma unroll
+            for (int ks = 0; ks < C::NKS; ++ks) read_frags(fra[ks], frb[ks], sbase, ks);
+            compiler_fence();
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+            barrier();
+            // C(j).  The computing wave runs at raised priority so that the
+            // SIMD's issue arbiter prefers its MFMAs over the other wave's
+            // LDS/VMEM traffic (measured: +15% at 8192^3).
+            __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int ks = 0; ks < C::NKS; ++ks) mfma_step(fra[ks], frb[ks]);
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(0);
+            if (grp == 0) __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+            barrier();
+        }
+        if (grp == 0) barrier();                   // G0 idles in the last phase
     } else {
         // ---- "cute(9) multistage_gemm" order (sections 6.2, 9): fragments are
         // double-buffered in VGPRs; step ks reads step ks+1 while its MFMAs

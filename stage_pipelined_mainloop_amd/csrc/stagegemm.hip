@@ -46,6 +46,8 @@ constexpr Variant variant()
 // global->LDS traffic of 128x128 per flop); 128x128 tiles fill the chip for
 // M = N = 2048 (one workgroup per CU).  Stage counts 2..5 for the sweep.
 const Variant kVariants[] = {
+    // ping-pong wave groups (schedule 2)
+    variant<sg::Cfg<256, 256, 64, 2, 2, 4, 2>>(),
     // cute-page order (schedule 1)
     variant<sg::Cfg<256, 256, 32, 2, 2, 4, 1>>(),
     variant<sg::Cfg<256, 256, 32, 3, 2, 4, 1>>(),

@@ -105,7 +105,7 @@ def test_every_variant_on_ragged_shapes(shape):
 
 @pytest.mark.parametrize("cfg", [None, (128, 128, 32, 3, 4, 1), (256, 256, 32, 5, 8, 1),
                                  (256, 256, 64, 2, 8, 1), (256, 256, 32, 3, 8, 0),
-                                 (128, 128, 64, 3, 4, 1)])
+                                 (128, 128, 64, 3, 4, 1), (256, 256, 64, 2, 8, 2)])
 def test_tiny_shape_grid(cfg):
     # every M, N and K tail against every tile boundary of the variant
     say(f"[case] tiny grid cfg={cfg}")
@@ -123,7 +123,8 @@ def test_tiny_shape_grid(cfg):
 @pytest.mark.parametrize("shape,cfg", [((4352, 4352, 264), None),
                                        ((4352, 4104, 200), (256, 256, 64, 2, 8, 1)),
                                        ((2304, 2304, 520), (128, 128, 32, 4, 4, 1)),
-                                       ((2304, 2312, 1000), (256, 256, 32, 3, 8, 0))])
+                                       ((2304, 2312, 1000), (256, 256, 32, 3, 8, 0)),
+                                       ((4352, 4360, 336), (256, 256, 64, 2, 8, 2))])
 def test_rotated_k_loop_with_k_tail(shape, cfg):
     # more than 256 workgroups, so each tile row starts its K loop at a
     # rotated tile and the K-tail tile lands mid-sequence
@@ -150,7 +151,7 @@ def test_empty_m_or_n_leaves_output_untouched():
 
 
 @pytest.mark.parametrize("cfg", [None, (128, 128, 32, 4, 4, 1), (256, 256, 32, 4, 8, 1),
-                                 (256, 256, 32, 4, 8, 0)])
+                                 (256, 256, 32, 4, 8, 0), (256, 256, 64, 2, 8, 2)])
 def test_canary_guard_bands(cfg):
     # D sits inside a larger buffer filled with a NaN pattern; nothing outside
     # D may change and every element of D must be written
