@@ -79,8 +79,9 @@ typedef struct sg_config {
 typedef struct sg_config_info {
     int threads;            /* workgroup size */
     int lds_bytes;          /* LDS ring: stages * (tile_m + tile_n) * tile_k * 2 */
+    int lds_total_bytes;    /* LDS allocated: the ring or the epilogue staging, if larger */
     int loads_per_stage;    /* 16-byte global->LDS loads per lane per stage */
-    int wg_per_cu_lds;      /* floor(160 KiB / lds_bytes) */
+    int wg_per_cu_lds;      /* floor(160 KiB / lds_total_bytes) */
     int regs;               /* VGPRs + AGPRs per lane (code object), -1 if unknown */
     int wg_per_cu_regs;     /* workgroups per CU allowed by the register file, -1 if unknown */
     int wg_per_cu;          /* resident workgroups per CU reported by the runtime, -1 if unknown */

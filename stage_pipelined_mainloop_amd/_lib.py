@@ -36,7 +36,7 @@ class SgConfig(ctypes.Structure):
 
 class SgConfigInfo(ctypes.Structure):
     _fields_ = [("threads", ctypes.c_int), ("lds_bytes", ctypes.c_int),
-                ("loads_per_stage", ctypes.c_int), ("wg_per_cu_lds", ctypes.c_int),
+                ("lds_total_bytes", ctypes.c_int), ("loads_per_stage", ctypes.c_int), ("wg_per_cu_lds", ctypes.c_int),
                 ("regs", ctypes.c_int), ("wg_per_cu_regs", ctypes.c_int),
                 ("wg_per_cu", ctypes.c_int)]
 

@@ -42,7 +42,9 @@
 //     column band of power-of-two-strided rows at once.
 //   * Epilogue: operands are fed to the MFMA swapped (B rows as the first
 //     operand), so each lane's accumulators are four consecutive columns of
-//     one row of D: alpha * acc, convert to fp16 (RNE), one 8-byte store.
+//     one row of D.  alpha * acc is converted to fp16 (one rounding), staged
+//     through a per-wave LDS region and written back row-contiguously with
+//     16-byte stores.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -114,7 +116,13 @@ struct Cfg {
     static constexpr int A_BYTES = BM * RB;
     static constexpr int B_BYTES = BN * RB;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-    static constexpr int LDS_BYTES = S * STAGE_BYTES;
+    static constexpr int RING_BYTES = S * STAGE_BYTES;
+    // Epilogue staging: each wave's WTM x WTN fp16 sub-tile, rows padded by
+    // 16 bytes (row stride 9 x 16 B for 128-byte rows) against bank conflicts.
+    static constexpr int EPI_ROW = WTN * 2 + 16;
+    static constexpr int EPI_WAVE_BYTES = WTM * EPI_ROW;
+    static constexpr int EPI_BYTES = NW * EPI_WAVE_BYTES;
+    static constexpr int LDS_BYTES = RING_BYTES > EPI_BYTES ? RING_BYTES : EPI_BYTES;
     static constexpr int NA = BM * CPR / (64 * NW); // LDS-DMA loads per wave per stage
     static constexpr int NB = BN * CPR / (64 * NW);
     static constexpr int L = NA + NB;
@@ -129,6 +137,7 @@ struct Cfg {
     static_assert(NA >= 1 && NB >= 1, "every wave loads both operands");
     static_assert(L * (S - 2) <= 63, "vmcnt is a 6-bit counter");
     static_assert(LDS_BYTES <= 163840, "160 KiB of LDS per workgroup");
+    static_assert((WTN * 2) % 16 == 0 && 64 % ((WTN * 2) / 16) == 0, "epilogue row chunks");
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
@@ -496,17 +505,27 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
         }
     }
 
-    // ---- epilogue: lane holds D[m][n .. n+3] for m = row of (lane & 31),
-    // n = 8 * (e / 4) + 4 * half within each 32x32 block.
-    const __amdgpu_buffer_rsrc_t rd = make_rsrc(D + (size_t)m0 * N, (uint32_t)rows_a * N * 2u);
+    // ---- epilogue ("cute(9) multistage_gemm", section 7.2: registers ->
+    // shared memory -> global, so the global writes are row-contiguous).
+    // Lane holds D[m][n .. n+3] for m = row (lane & 31) of each 32x32 block
+    // and n = 8 * g + 4 * half.  Each wave converts alpha * acc to fp16
+    // (one rounding), writes its sub-tile into a private LDS region, then
+    // reads it back row by row and stores 16 bytes per lane: every store
+    // instruction covers whole row segments of WTN * 2 bytes.
+    compiler_fence();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    __builtin_amdgcn_s_barrier();                 // every wave is done with the ring
+    __builtin_amdgcn_sched_barrier(0);
+    compiler_fence();
+    char *epi = smem + wave * C::EPI_WAVE_BYTES;
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) {
-        const int ml = wm * C::WTM + i * 32 + (lane & 31);          // row within the tile
+        const int r = i * 32 + (lane & 31);
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * C::WTN + j * 32 + 8 * g + 4 * half;
                 const f32x16 &a = acc[i][j];
                 const _Float16 h0 = (_Float16)(alpha * a[4 * g + 0]);
                 const _Float16 h1 = (_Float16)(alpha * a[4 * g + 1]);
@@ -517,10 +536,28 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
                             ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
                 packed[1] = (uint32_t)__builtin_bit_cast(uint16_t, h2) |
                             ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
-                const uint32_t off = (n < N) ? (uint32_t)(ml * N + n) * 2u : kOutOfRange;
-                __builtin_amdgcn_raw_buffer_store_b64(packed, rd, off, 0, 0);
+                const int c = j * 32 + 8 * g + 4 * half;          // column within the sub-tile
+                *(u32x2 *)(epi + r * C::EPI_ROW + c * 2) = packed;
             }
         }
+    }
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));   // this wave's LDS writes landed
+    compiler_fence();
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    constexpr int CPRW = C::WTN * 2 / 16;              // 16-byte chunks per sub-tile row
+    constexpr int RPI = 64 / CPRW;                     // rows per wave instruction
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(D + (size_t)m0 * N, (uint32_t)rows_a * N * 2u);
+    const int ec = lane % CPRW;
+    const int n = n0 + wn * C::WTN + ec * 8;
+    const bool n_ok = n < N;                           // N % 8 == 0: a chunk is all in or out
+#pragma unroll
+    for (int it = 0; it < C::WTM / RPI; ++it) {
+        const int r = it * RPI + lane / CPRW;
+        const u32x4 v = *(const u32x4 *)(epi + r * C::EPI_ROW + ec * 16);
+        const int ml = wm * C::WTM + r;                // row within the workgroup tile
+        const uint32_t off = n_ok ? (uint32_t)(ml * N + n) * 2u : kOutOfRange;
+        __builtin_amdgcn_raw_buffer_store_b128(v, rd, off, 0, 0);
     }
 }
 

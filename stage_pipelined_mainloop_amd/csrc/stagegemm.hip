@@ -16,6 +16,7 @@ typedef hipError_t (*launch_fn)(int M, int N, int K, float alpha, const void *A,
 struct Variant {
     sg_config cfg;
     int threads;
+    int ring_bytes;
     int lds_bytes;
     int loads;
     const void *kernel;
@@ -38,7 +39,8 @@ hipError_t launch(int M, int N, int K, float alpha, const void *A, const void *B
 template <class C>
 constexpr Variant variant()
 {
-    return Variant{{C::BM, C::BN, C::BK, C::S, C::NW, C::SCHED}, C::T, C::LDS_BYTES, C::L,
+    return Variant{{C::BM, C::BN, C::BK, C::S, C::NW, C::SCHED}, C::T, C::RING_BYTES, C::LDS_BYTES,
+                   C::L,
                    reinterpret_cast<const void *>(&sg::gemm_tn_kernel<C>), &launch<C>};
 }
 
@@ -199,7 +201,8 @@ sg_status sg_query_config(const sg_config *cfg, sg_config_info *info)
     const Variant *v = find_variant(cfg);
     if (!v) return SG_ERR_UNSUPPORTED;
     info->threads = v->threads;
-    info->lds_bytes = v->lds_bytes;
+    info->lds_bytes = v->ring_bytes;
+    info->lds_total_bytes = v->lds_bytes;
     info->loads_per_stage = v->loads;
     info->wg_per_cu_lds = 163840 / v->lds_bytes;
     info->regs = -1;

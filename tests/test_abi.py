@@ -120,7 +120,8 @@ def test_config_table_and_lds_model():
         assert st in (S.SG_OK, S.SG_ERR_HIP)
         lds = oracle.lds_bytes(c.tile_m, c.tile_n, c.tile_k, c.stages)
         assert info.lds_bytes == lds <= 160 * 1024
-        assert info.wg_per_cu_lds == oracle.blocks_per_unit(lds, 160 * 1024)
+        assert lds <= info.lds_total_bytes <= 160 * 1024
+        assert info.wg_per_cu_lds == oracle.blocks_per_unit(info.lds_total_bytes, 160 * 1024)
         assert info.threads == 64 * c.waves
         # 16-byte loads per lane per stage: (tile_m + tile_n) * tile_k * 2 bytes over the workgroup
         assert info.loads_per_stage * 16 * info.threads == (c.tile_m + c.tile_n) * c.tile_k * 2
