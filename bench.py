@@ -55,6 +55,45 @@ def load_traffic(workload: str):
     return t.get("hbm_bytes_per_launch")
 
 
+def mfma_ceiling(a, b, target_ms: float = 20.0):
+    """TFLOP/s of pure fp16 MFMAs on fragments of the workload's own inputs
+    (libsgprobe.so): the power-limited ceiling for this operand data."""
+    import ctypes
+
+    import torch
+    so = os.path.join(ROOT, "stage_pipelined_mainloop_amd", "libsgprobe.so")
+    L = ctypes.CDLL(so)
+    L.sg_probe_mfma_ceiling.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p,
+                                        ctypes.c_longlong, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_void_p, ctypes.c_void_p]
+    L.sg_probe_mfma_ceiling.restype = ctypes.c_int
+    L.sg_probe_mfma_ceiling_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    L.sg_probe_mfma_ceiling_flops.restype = ctypes.c_double
+    blocks = 1024
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=a.device)
+    stream = torch.cuda.current_stream(a.device)
+
+    def run(iters):
+        rc = L.sg_probe_mfma_ceiling(a.data_ptr(), a.numel(), b.data_ptr(), b.numel(), blocks,
+                                     iters, sink.data_ptr(), stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"mfma ceiling probe failed to launch ({rc})")
+
+    run(50)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    run(50)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    iters = max(50, int(50 * target_ms / max(e0.elapsed_time(e1), 1e-3)))
+    e0.record(stream)
+    run(iters)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return L.sg_probe_mfma_ceiling_flops(blocks, iters) / (e0.elapsed_time(e1) / 1e3) / 1e12
+
+
 def cpu_baseline(A, B, target_s: float):
     import oracle
     M, K = A.shape
@@ -268,6 +307,11 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    if args.workload != "attn_scores":
+        # measured after the timed region so it does not heat the GPU first
+        ceil = mfma_ceiling(a, b)
+        out["config"]["mfma_ceiling_tflops"] = round(ceil, 1)
+        out["config"]["frac_of_mfma_ceiling"] = round(achieved / ceil, 4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(A, B, args.cpu_seconds)
     print(json.dumps(out), flush=True)

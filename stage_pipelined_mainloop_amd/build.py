@@ -11,6 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libstagegemm.so")
+PROBE_LIB = os.path.join(PKG, "libsgprobe.so")
 RESOURCES = os.path.join(PKG, "kernel_resources.txt")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -32,6 +33,11 @@ def sources() -> list[str]:
     return [os.path.join(CSRC, "stagegemm.hip")]
 
 
+def probe_sources() -> list[str]:
+    """Measurement probe (MFMA ceiling on given operands), a separate library."""
+    return [os.path.join(CSRC, "mfma_ceiling.hip")]
+
+
 def build(verbose: bool = False) -> str:
     """Compile every HIP source into libstagegemm.so next to this file and
     record per-kernel register / LDS / occupancy remarks in
@@ -47,6 +53,12 @@ def build(verbose: bool = False) -> str:
     remarks = [ln for ln in p.stderr.splitlines() if "remark:" in ln]
     with open(RESOURCES, "w") as f:
         f.write("\n".join(_clean(r) for r in remarks) + "\n")
+    tmp = PROBE_LIB + ".tmp"
+    p2 = subprocess.run([HIPCC, *FLAGS, *probe_sources(), "-o", tmp], capture_output=True, text=True)
+    if p2.returncode != 0:
+        sys.stderr.write(p2.stdout + p2.stderr)
+        raise RuntimeError("hipcc failed building libsgprobe.so")
+    os.replace(tmp, PROBE_LIB)
     if verbose:
         sys.stdout.write(p.stderr)
     return LIB
