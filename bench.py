@@ -276,9 +276,10 @@ def main() -> int:
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
                 "traffic": load_traffic(args.workload)}
-    if args.workload == "attn_scores":
-        # the score GEMM is bound by writing S to HBM
-        algo_bytes = 2.0 * (M * K + N * K + M * N)
+    algo_bytes = 2.0 * (M * K + N * K + M * N)
+    ridge = PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)          # ~315 flop/B
+    if flops / algo_bytes < ridge:
+        # below the ridge (attention scores, tall-skinny): bound by HBM traffic
         gbs = algo_bytes / mean_launch_s / 1e9
         roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
@@ -307,7 +308,7 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": None,
     }
-    if args.workload != "attn_scores":
+    if roofline["bound"] == "mfma":
         # measured after the timed region so it does not heat the GPU first
         ceil = mfma_ceiling(a, b)
         out["config"]["mfma_ceiling_tflops"] = round(ceil, 1)

@@ -96,6 +96,19 @@ sg_status gemm_fp16_tn(int M, int N, int K, const void *A, const void *B, void *
 sg_status gemm_fp16_tn_alpha(int M, int N, int K, float alpha, const void *A,
                              const void *B, void *D, void *stream);
 
+/* D = alpha * A * B^T + beta * C, the full GEMM of "CUDA operator notes 2",
+ * section "GEMM" (C = alpha A B + beta C with fp16 matrices and fp32 alpha,
+ * beta).  C is M x N row-major fp16 (ldc = N), read only.  The fp32
+ * accumulator is combined as fma(beta, c, alpha * acc) in fp32 and rounded
+ * once to fp16.  beta == 0: C is not read (it may be NULL, and NaNs in it do
+ * not propagate).  Otherwise C must be non-NULL (SG_ERR_NULL), 16-byte
+ * aligned (SG_ERR_ALIGN), and either be D itself -- an in-place update, as
+ * on the page -- or not overlap D at all (SG_ERR_ALIAS).  C may overlap A or
+ * B.  Other rules as gemm_fp16_tn. */
+sg_status gemm_fp16_tn_alpha_beta(int M, int N, int K, float alpha, float beta,
+                                  const void *A, const void *B, const void *C, void *D,
+                                  void *stream);
+
 /* As gemm_fp16_tn_alpha, but runs the named compiled variant instead of the
  * one the library would choose (used by the stage-count sweep).
  * SG_ERR_UNSUPPORTED if no such variant is compiled; SG_ERR_NULL if cfg is

@@ -19,15 +19,17 @@ docstring or source comment.  Parity is pinned by tests that check these
 functions against values the pages print, closed forms, brute force and an
 independent library routine, not against themselves.
 """
-from ._native import (build, f16_to_f64, f64_to_f16, gemm_tn_exact, gemm_tn_f64,
-                      gemm_tn_f64_at, gemm_tn_f64_rows, num_threads)
+from ._native import (build, f16_to_f64, f64_to_f16, gemm_tn_exact, gemm_tn_exact_beta,
+                      gemm_tn_f64, gemm_tn_f64_at, gemm_tn_f64_beta, gemm_tn_f64_rows,
+                      num_threads)
 from .check import CheckReport, check, ulp16
 from .models import (blocks_per_unit, lds_bytes, loosest_wait_counts, minimum_stages,
                      schedule_cute_loads, schedule_cute_multistage, schedule_three_phase, simulate,
                      simulate_loads)
 
 __all__ = [
-    "build", "f16_to_f64", "f64_to_f16", "gemm_tn_exact", "gemm_tn_f64",
+    "build", "f16_to_f64", "f64_to_f16", "gemm_tn_exact", "gemm_tn_exact_beta",
+    "gemm_tn_f64", "gemm_tn_f64_beta",
     "gemm_tn_f64_at", "gemm_tn_f64_rows", "num_threads", "CheckReport", "check",
     "ulp16", "blocks_per_unit", "lds_bytes", "loosest_wait_counts", "minimum_stages",
     "schedule_cute_loads", "schedule_cute_multistage", "schedule_three_phase", "simulate",

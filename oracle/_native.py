@@ -65,6 +65,14 @@ def lib() -> ctypes.CDLL:
         L.sgo_gemm_tn_exact.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_float, u16p, u16p, u16p]
         L.sgo_gemm_tn_exact.restype = ctypes.c_int
+        L.sgo_gemm_tn_f64_beta.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_float, ctypes.c_float, u16p, u16p,
+                                           ctypes.c_void_p, u16p]
+        L.sgo_gemm_tn_f64_beta.restype = None
+        L.sgo_gemm_tn_exact_beta.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_float, ctypes.c_float, u16p, u16p,
+                                             ctypes.c_void_p, u16p]
+        L.sgo_gemm_tn_exact_beta.restype = ctypes.c_int
         L.sgo_num_threads.argtypes = []
         L.sgo_num_threads.restype = ctypes.c_int
         _lib = L
@@ -150,6 +158,44 @@ def gemm_tn_exact(A, B, alpha: float = 1.0) -> np.ndarray:
         rc = lib().sgo_gemm_tn_exact(M, N, K, float(alpha), a, b, d)
         if rc != 0:
             raise ValueError(f"exact oracle refused the input (code {rc})")
+    return d.view(np.float16)
+
+
+def _c_arg(C, M, N, beta):
+    if beta == 0.0:
+        return None, None
+    c = _bits(C)
+    assert c.shape == (M, N)
+    return c, c.ctypes.data
+
+
+def gemm_tn_f64_beta(A, B, C, alpha: float = 1.0, beta: float = 0.0) -> np.ndarray:
+    """D = RNE16(alpha * A @ B.T + beta * C); C is not read when beta == 0."""
+    a, b = _bits(A), _bits(B)
+    M, K = a.shape
+    N, K2 = b.shape
+    assert K == K2
+    keep, cptr = _c_arg(C, M, N, float(np.float32(beta)))
+    d = np.empty((M, N), np.uint16)
+    if M and N:
+        lib().sgo_gemm_tn_f64_beta(M, N, K, float(alpha), float(beta), a, b, cptr, d)
+    del keep
+    return d.view(np.float16)
+
+
+def gemm_tn_exact_beta(A, B, C, alpha: float = 1.0, beta: float = 0.0) -> np.ndarray:
+    """Exact (128-bit integer) RNE16(alpha * A @ B.T + beta * C)."""
+    a, b = _bits(A), _bits(B)
+    M, K = a.shape
+    N, K2 = b.shape
+    assert K == K2
+    keep, cptr = _c_arg(C, M, N, float(np.float32(beta)))
+    d = np.empty((M, N), np.uint16)
+    if M and N:
+        rc = lib().sgo_gemm_tn_exact_beta(M, N, K, float(alpha), float(beta), a, b, cptr, d)
+        if rc != 0:
+            raise ValueError(f"exact oracle refused the input (code {rc})")
+    del keep
     return d.view(np.float16)
 
 

@@ -143,6 +143,24 @@ void sgo_gemm_tn_f64(int M, int N, int K, float alpha,
         }
 }
 
+/* D[i][j] = RNE16( alpha * sum_k A[i][k] * B[j][k] + beta * C[i][j] ): the
+ * GEMM of "CUDA operator notes 2", section "GEMM" (C = alpha A B + beta C),
+ * one rounding.  beta == 0 does not read C (C may be NULL). */
+void sgo_gemm_tn_f64_beta(int M, int N, int K, float alpha, float beta,
+                          const uint16_t *A, const uint16_t *B, const uint16_t *C,
+                          uint16_t *D)
+{
+    ensure_decode_table();
+    const double a64 = (double)alpha, b64 = (double)beta;
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int i = 0; i < M; ++i)
+        for (int j = 0; j < N; ++j) {
+            double s = a64 * dot_f64(A + (size_t)i * K, B + (size_t)j * K, K);
+            if (beta != 0.0f) s += b64 * g_dec[C[(size_t)i * N + j]];   /* beta*c exact */
+            D[(size_t)i * N + j] = sgo_f64_to_f16(s);
+        }
+}
+
 /* The same definition evaluated only at the listed (row, col) pairs. */
 void sgo_gemm_tn_f64_at(int K, float alpha, const uint16_t *A, const uint16_t *B,
                         long count, const int *rows, const int *cols, uint16_t *out)
@@ -268,4 +286,47 @@ int sgo_gemm_tn_exact(int M, int N, int K, float alpha,
         }
     }
     return 0;
+}
+
+/* Exact D = RNE16(alpha * sum A[i][k] B[j][k] + beta * C[i][j]).  alpha*sum is
+ * an integer times 2^(ae-48), beta*c an integer times 2^(be-24); both are
+ * brought to the smaller exponent.  Returns -1 for non-finite input, -2 when
+ * the alignment shift would not fit the 128-bit sum (refused, not rounded). */
+int sgo_gemm_tn_exact_beta(int M, int N, int K, float alpha, float beta,
+                           const uint16_t *A, const uint16_t *B, const uint16_t *C,
+                           uint16_t *D)
+{
+    int64_t am, bm; int ae, be;
+    if (split_f32(alpha, &am, &ae) || split_f32(beta, &bm, &be)) return -1;
+    if (K >= (1 << 20)) return -2;
+    int bad = 0;
+    for (size_t t = 0; t < (size_t)M * K; ++t) (void)f16_to_units24(A[t], &bad);
+    for (size_t t = 0; t < (size_t)N * K; ++t) (void)f16_to_units24(B[t], &bad);
+    if (beta != 0.0f)
+        for (size_t t = 0; t < (size_t)M * N; ++t) (void)f16_to_units24(C[t], &bad);
+    if (bad) return -1;
+    const int ea = ae - 48, eb = be - 24;
+    const int e = ea < eb ? ea : eb;
+    const int sa = ea - e, sb = eb - e;          /* left shifts onto the common exponent */
+    /* |am*sum| < 2^24 * 2^80 * 2^20 = 2^124; |bm*c| < 2^24 * 2^40 = 2^64 */
+    if ((am != 0 && sa > 2) || (bm != 0 && sb > 60)) return -2;
+    int fail = 0;
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int i = 0; i < M; ++i) {
+        int dummy = 0;
+        for (int j = 0; j < N; ++j) {
+            i128 sum = 0;
+            for (int k = 0; k < K; ++k)
+                sum += (i128)f16_to_units24(A[(size_t)i * K + k], &dummy) *
+                       (i128)f16_to_units24(B[(size_t)j * K + k], &dummy);
+            i128 total = (sum * (i128)am) * ((i128)1 << sa);
+            if (beta != 0.0f)
+                total += ((i128)bm * (i128)f16_to_units24(C[(size_t)i * N + j], &dummy)) *
+                         ((i128)1 << sb);
+            int sign = total < 0;
+            u128 mag = (u128)(sign ? -total : total);
+            D[(size_t)i * N + j] = round_units_to_f16(sign, mag, e);
+        }
+    }
+    return fail;
 }

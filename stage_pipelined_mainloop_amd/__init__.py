@@ -12,16 +12,19 @@ first call and a missing build raises.
 from __future__ import annotations
 
 from ._lib import (SgConfig, SgConfigInfo, SgError, configs, gemm_fp16_tn, gemm_fp16_tn_alpha,
-                   gemm_fp16_tn_cfg, sg_get_config, sg_minimum_stages, sg_num_configs,
+                   gemm_fp16_tn_alpha_beta, gemm_fp16_tn_cfg, sg_get_config, sg_minimum_stages, sg_num_configs,
                    sg_pipeline_wait_count, sg_query_config, sg_select_config, sg_status_string)
 
 
-def gemm(A, B, out=None, alpha: float | None = None, config=None, stream=None):
-    """D = alpha * A @ B.T on the GPU for fp16 CUDA (HIP) tensors.
+def gemm(A, B, out=None, alpha: float | None = None, config=None, stream=None,
+         beta: float | None = None, C=None):
+    """D = alpha * A @ B.T (+ beta * C) on the GPU for fp16 CUDA (HIP) tensors.
 
     A: (M, K), B: (N, K), out: (M, N) or None (allocated).  `config` picks a
     compiled variant (SgConfig or a 6-tuple) instead of the library's choice.
-    `stream` is a torch.cuda.Stream (default: the current stream)."""
+    With a non-zero `beta`, C is an (M, N) fp16 tensor (it may be `out`
+    itself for an in-place update).  `stream` is a torch.cuda.Stream
+    (default: the current stream)."""
     import torch
 
     if A.dtype != torch.float16 or B.dtype != torch.float16:
@@ -41,7 +44,15 @@ def gemm(A, B, out=None, alpha: float | None = None, config=None, stream=None):
         raise ValueError("out must be a contiguous (M, N) float16 tensor on A's device")
     s = (stream if stream is not None else torch.cuda.current_stream(A.device)).cuda_stream
     a, b, d = A.data_ptr(), B.data_ptr(), out.data_ptr()
-    if config is not None:
+    if beta is not None and beta != 0.0:
+        if config is not None:
+            raise ValueError("beta is not available with an explicit config")
+        if C is None or C.dtype != torch.float16 or tuple(C.shape) != (M, N) \
+                or not C.is_contiguous() or C.device != A.device:
+            raise ValueError("beta needs C: a contiguous (M, N) float16 tensor on A's device")
+        gemm_fp16_tn_alpha_beta(M, N, K, 1.0 if alpha is None else float(alpha), float(beta),
+                                a, b, C.data_ptr(), d, s)
+    elif config is not None:
         gemm_fp16_tn_cfg(M, N, K, 1.0 if alpha is None else float(alpha), a, b, d, config, s)
     elif alpha is None:
         gemm_fp16_tn(M, N, K, a, b, d, s)
@@ -51,7 +62,8 @@ def gemm(A, B, out=None, alpha: float | None = None, config=None, stream=None):
 
 
 __all__ = [
-    "gemm", "gemm_fp16_tn", "gemm_fp16_tn_alpha", "gemm_fp16_tn_cfg", "sg_select_config",
+    "gemm", "gemm_fp16_tn", "gemm_fp16_tn_alpha", "gemm_fp16_tn_alpha_beta", "gemm_fp16_tn_cfg",
+    "sg_select_config",
     "sg_num_configs", "sg_get_config", "sg_query_config", "sg_minimum_stages",
     "sg_pipeline_wait_count", "sg_status_string", "configs", "SgConfig", "SgConfigInfo",
     "SgError",

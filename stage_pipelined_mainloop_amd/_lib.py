@@ -75,6 +75,8 @@ def lib() -> ctypes.CDLL:
         L.gemm_fp16_tn.restype = i
         L.gemm_fp16_tn_alpha.argtypes = [i, i, i, f, vp, vp, vp, vp]
         L.gemm_fp16_tn_alpha.restype = i
+        L.gemm_fp16_tn_alpha_beta.argtypes = [i, i, i, f, f, vp, vp, vp, vp, vp]
+        L.gemm_fp16_tn_alpha_beta.restype = i
         L.gemm_fp16_tn_cfg.argtypes = [i, i, i, f, vp, vp, vp, ctypes.POINTER(SgConfig), vp]
         L.gemm_fp16_tn_cfg.restype = i
         L.sg_select_config.argtypes = [i, i, i, ctypes.POINTER(SgConfig)]
@@ -119,6 +121,12 @@ def gemm_fp16_tn_alpha(M: int, N: int, K: int, alpha: float, A: int, B: int, D: 
                        stream: int = 0) -> int:
     return _check(lib().gemm_fp16_tn_alpha(M, N, K, alpha, A, B, D, stream),
                   "gemm_fp16_tn_alpha")
+
+
+def gemm_fp16_tn_alpha_beta(M: int, N: int, K: int, alpha: float, beta: float, A: int, B: int,
+                            C: int, D: int, stream: int = 0) -> int:
+    return _check(lib().gemm_fp16_tn_alpha_beta(M, N, K, alpha, beta, A, B, C, D, stream),
+                  "gemm_fp16_tn_alpha_beta")
 
 
 def gemm_fp16_tn_cfg(M: int, N: int, K: int, alpha: float, A: int, B: int, D: int,

@@ -188,8 +188,12 @@ __device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, i
 template <class C>
 __global__ void __launch_bounds__(C::T)
 gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
-               _Float16 *__restrict__ D, int M, int N, int K, float alpha, int kt_rot)
+               const _Float16 *Cm, _Float16 *D, int M, int N, int K, float alpha, float beta,
+               int kt_rot)
 {
+    // Cm and D may be the same buffer (in-place D = alpha A B^T + beta D): each
+    // wave reads C only inside its own sub-tile and finishes those reads
+    // before it stores, so they are not declared __restrict__.
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
     const int lane = threadIdx.x & 63;
@@ -519,25 +523,60 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
     __builtin_amdgcn_sched_barrier(0);
     compiler_fence();
     char *epi = smem + wave * C::EPI_WAVE_BYTES;
+    auto stage4 = [&](int r, int c, float v0, float v1, float v2, float v3) {
+        u32x2 packed;
+        packed[0] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v0) |
+                    ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v1) << 16);
+        packed[1] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v2) |
+                    ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v3) << 16);
+        *(u32x2 *)(epi + r * C::EPI_ROW + c * 2) = packed;
+    };
+    if (beta == 0.0f) {
+        // D = RNE16(alpha * acc): one rounding of the exact product (the
+        // compiler emits v_fma_mixlo_f16); C is not read.
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i) {
-        const int r = i * 32 + (lane & 31);
+        for (int i = 0; i < C::FM; ++i) {
+            const int r = i * 32 + (lane & 31);
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j) {
+            for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const f32x16 &a = acc[i][j];
-                const _Float16 h0 = (_Float16)(alpha * a[4 * g + 0]);
-                const _Float16 h1 = (_Float16)(alpha * a[4 * g + 1]);
-                const _Float16 h2 = (_Float16)(alpha * a[4 * g + 2]);
-                const _Float16 h3 = (_Float16)(alpha * a[4 * g + 3]);
-                u32x2 packed;
-                packed[0] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
-                            ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-                packed[1] = (uint32_t)__builtin_bit_cast(uint16_t, h2) |
-                            ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
-                const int c = j * 32 + 8 * g + 4 * half;          // column within the sub-tile
-                *(u32x2 *)(epi + r * C::EPI_ROW + c * 2) = packed;
+                for (int g = 0; g < 4; ++g) {
+                    const f32x16 &a = acc[i][j];
+                    stage4(r, j * 32 + 8 * g + 4 * half, alpha * a[4 * g + 0],
+                           alpha * a[4 * g + 1], alpha * a[4 * g + 2], alpha * a[4 * g + 3]);
+                }
+        }
+    } else {
+        // D = RNE16(alpha * acc + beta * C) ("CUDA operator notes 2", "GEMM"):
+        // C is read in the accumulator layout (4 halves per lane and group),
+        // combined in fp32 and rounded once to fp16.
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cm + (size_t)m0 * N, (uint32_t)rows_a * N * 2u);
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) {
+            const int r = i * 32 + (lane & 31);
+            const int ml = wm * C::WTM + r;
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j) {
+                u32x2 cv[4];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int n = n0 + wn * C::WTN + j * 32 + 8 * g + 4 * half;
+                    const uint32_t off = (n < N) ? (uint32_t)(ml * N + n) * 2u : kOutOfRange;
+                    cv[g] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rc, off, 0, 0));
+                }
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x16 &a = acc[i][j];
+                    const float c0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(cv[g][0] & 0xffffu));
+                    const float c1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(cv[g][0] >> 16));
+                    const float c2 = (float)__builtin_bit_cast(_Float16, (uint16_t)(cv[g][1] & 0xffffu));
+                    const float c3 = (float)__builtin_bit_cast(_Float16, (uint16_t)(cv[g][1] >> 16));
+                    stage4(r, j * 32 + 8 * g + 4 * half,
+                           __builtin_fmaf(beta, c0, alpha * a[4 * g + 0]),
+                           __builtin_fmaf(beta, c1, alpha * a[4 * g + 1]),
+                           __builtin_fmaf(beta, c2, alpha * a[4 * g + 2]),
+                           __builtin_fmaf(beta, c3, alpha * a[4 * g + 3]));
+                }
             }
         }
     }

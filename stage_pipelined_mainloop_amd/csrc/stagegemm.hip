@@ -10,8 +10,9 @@
 
 namespace {
 
-typedef hipError_t (*launch_fn)(int M, int N, int K, float alpha, const void *A, const void *B,
-                                void *D, int kt_rot, hipStream_t stream);
+typedef hipError_t (*launch_fn)(int M, int N, int K, float alpha, float beta, const void *A,
+                                const void *B, const void *Cm, void *D, int kt_rot,
+                                hipStream_t stream);
 
 struct Variant {
     sg_config cfg;
@@ -24,14 +25,15 @@ struct Variant {
 };
 
 template <class C>
-hipError_t launch(int M, int N, int K, float alpha, const void *A, const void *B, void *D,
-                  int kt_rot, hipStream_t stream)
+hipError_t launch(int M, int N, int K, float alpha, float beta, const void *A, const void *B,
+                  const void *Cm, void *D, int kt_rot, hipStream_t stream)
 {
     const long long tiles = (long long)((M + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
     const _Float16 *a = static_cast<const _Float16 *>(A);
     const _Float16 *b = static_cast<const _Float16 *>(B);
+    const _Float16 *c = static_cast<const _Float16 *>(Cm);
     _Float16 *d = static_cast<_Float16 *>(D);
-    void *args[] = {&a, &b, &d, &M, &N, &K, &alpha, &kt_rot};
+    void *args[] = {&a, &b, &c, &d, &M, &N, &K, &alpha, &beta, &kt_rot};
     return hipLaunchKernel(reinterpret_cast<const void *>(&sg::gemm_tn_kernel<C>),
                            dim3((unsigned)tiles), dim3(C::T), args, 0, stream);
 }
@@ -88,21 +90,30 @@ const Variant *find_variant(const sg_config *c)
     return nullptr;
 }
 
-// Choice from the measured sweeps (MI355X, fp16 uniform[-1,1] inputs):
-//   * at least 128 tiles of 256x256: 256x256x64, two stages, 8 waves, cute
-//     order (best at 8192^3, 8000x7936x8200 and 4096^3);
-//   * smaller grids (e.g. M = N = 2048, 64 such tiles): 128x128x64, three
-//     stages, 4 waves, cute order (one workgroup per CU at 2048^2; best for
-//     every K of the 2048^2 sweep).
+// Choice from the measured sweeps (MI355X, fp16 uniform[-1,1] inputs).
+// Tile family by a wave-quantisation estimate: 256x256 workgroups run one per
+// CU, 128x128 ones do a quarter of the work at about 1.3x the cost per flop;
+// cost = rounds of 256 workgroups x per-workgroup work.  Large grids
+// (8192^3, 8000x7936x8200, 4096^3, 4096^2 x 128) pick 256x256x64, two
+// stages, 8 waves, cute order.  Small or skinny grids (2048^2 sweep,
+// 81920 x 256 x 256) pick 128x128x64, cute order, with the stage count of
+// the lesson's occupancy trade-off: three stages (96 KiB, one workgroup per
+// CU) when the grid is at most one workgroup per CU, else two stages
+// (64 KiB, two resident per CU) so a second workgroup hides latency.
 const Variant *select_variant(int M, int N, int K)
 {
     (void)K;
-    const long long big_tiles = (long long)((M + 255) / 256) * ((N + 255) / 256);
+    const long long t256 = (long long)((M + 255) / 256) * ((N + 255) / 256);
+    const long long t128 = (long long)((M + 127) / 128) * ((N + 127) / 128);
+    const double cost256 = (double)((t256 + 255) / 256) * 4.0;
+    const double cost128 = (double)((t128 + 255) / 256) * 1.3;
     sg_config c;
-    if (big_tiles >= 128)
+    if (cost256 <= cost128)
         c = sg_config{256, 256, 64, 2, 8, 1};
-    else
+    else if (t128 <= 256)
         c = sg_config{128, 128, 64, 3, 4, 1};
+    else
+        c = sg_config{128, 128, 64, 2, 4, 1};
     return find_variant(&c);
 }
 
@@ -134,8 +145,20 @@ sg_status validate(int M, int N, int K, const void *A, const void *B, const void
     return SG_OK;
 }
 
-sg_status run(const Variant *v, int M, int N, int K, float alpha, const void *A, const void *B,
-              void *D, void *stream)
+// C operand of the beta variant: beta == 0 reads nothing; otherwise C must be
+// 16-byte aligned and either be D itself (in place) or not overlap D.
+sg_status validate_c(int M, int N, float beta, const void *Cm, const void *D)
+{
+    if (beta == 0.0f || M == 0 || N == 0) return SG_OK;
+    if (!Cm) return SG_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(Cm) & 15) return SG_ERR_ALIGN;
+    const size_t bytes = (size_t)M * N * 2;
+    if (Cm != D && overlaps(Cm, bytes, D, bytes)) return SG_ERR_ALIAS;
+    return SG_OK;
+}
+
+sg_status run(const Variant *v, int M, int N, int K, float alpha, float beta, const void *A,
+              const void *B, const void *Cm, void *D, void *stream)
 {
     const long long tiles = (long long)((M + v->cfg.tile_m - 1) / v->cfg.tile_m) *
                             ((N + v->cfg.tile_n - 1) / v->cfg.tile_n);
@@ -145,8 +168,8 @@ sg_status run(const Variant *v, int M, int N, int K, float alpha, const void *A,
     // where all workgroups are resident and the operands fit in the 256 MB
     // last-level cache).
     const int kt_rot = (tiles > 256) ? 4 : 1;
-    const hipError_t e =
-        v->launch(M, N, K, alpha, A, B, D, kt_rot, static_cast<hipStream_t>(stream));
+    const hipError_t e = v->launch(M, N, K, alpha, beta, A, B, beta == 0.0f ? nullptr : Cm, D,
+                                   kt_rot, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SG_OK : SG_ERR_HIP;
 }
 
@@ -161,7 +184,19 @@ sg_status gemm_fp16_tn_alpha(int M, int N, int K, float alpha, const void *A, co
     if (st != SG_OK || M == 0 || N == 0) return st;
     const Variant *v = select_variant(M, N, K);
     if (!v) return SG_ERR_UNSUPPORTED;
-    return run(v, M, N, K, alpha, A, B, D, stream);
+    return run(v, M, N, K, alpha, 0.0f, A, B, nullptr, D, stream);
+}
+
+sg_status gemm_fp16_tn_alpha_beta(int M, int N, int K, float alpha, float beta, const void *A,
+                                  const void *B, const void *Cm, void *D, void *stream)
+{
+    sg_status st = validate(M, N, K, A, B, D);
+    if (st != SG_OK) return st;
+    st = validate_c(M, N, beta, Cm, D);
+    if (st != SG_OK || M == 0 || N == 0) return st;
+    const Variant *v = select_variant(M, N, K);
+    if (!v) return SG_ERR_UNSUPPORTED;
+    return run(v, M, N, K, alpha, beta, A, B, Cm, D, stream);
 }
 
 sg_status gemm_fp16_tn(int M, int N, int K, const void *A, const void *B, void *D, void *stream)
@@ -178,7 +213,7 @@ sg_status gemm_fp16_tn_cfg(int M, int N, int K, float alpha, const void *A, cons
     const Variant *v = find_variant(cfg);
     if (!v) return SG_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return SG_OK;
-    return run(v, M, N, K, alpha, A, B, D, stream);
+    return run(v, M, N, K, alpha, 0.0f, A, B, nullptr, D, stream);
 }
 
 sg_status sg_select_config(int M, int N, int K, sg_config *out)

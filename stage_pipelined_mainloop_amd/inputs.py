@@ -20,6 +20,8 @@ WORKLOADS = {
     "attn_scores": (4096, 4096, 128, "normal", 7),
     "square8192": (8192, 8192, 8192, "uniform", 9),
     "ragged8000": (8000, 7936, 8200, "uniform", 11),
+    # the tall-skinny shape of the multistage page's own test run
+    "tall81920": (81920, 256, 256, "uniform", 13),
 }
 KSWEEP_K = (128, 512, 2048, 8192, 16384)
 KSWEEP_MN = 2048

@@ -17,7 +17,7 @@ S = _lib
 
 def test_every_declared_symbol_is_exported():
     declared = _lib.header_functions()
-    assert len(declared) == 10
+    assert len(declared) == 11
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
@@ -29,6 +29,12 @@ def test_every_declared_symbol_is_exported():
 # Fake, never-dereferenced device addresses: every call below fails validation
 # before the library touches the HIP runtime.
 P = 0x7f0000000000
+
+
+def _must_be_rejected(status):
+    # a fake-pointer case that passed validation would launch a kernel on
+    # addresses that do not exist; only rejections are allowed here
+    assert status not in (S.SG_OK, S.SG_ERR_HIP), "fake-pointer case must fail validation"
 
 
 @pytest.mark.parametrize("args,status", [
@@ -50,11 +56,39 @@ P = 0x7f0000000000
     ((1 << 30, 8, 1 << 11, P, P + (1 << 44), P + (1 << 45)), S.SG_ERR_SHAPE),  # M*K >= 2^40
 ])
 def test_argument_errors(args, status):
+    _must_be_rejected(status)
     M, N, K, a, b, d = args
     assert L.gemm_fp16_tn(M, N, K, a, b, d, None) == status
     assert L.gemm_fp16_tn_alpha(M, N, K, 0.5, a, b, d, None) == status
     cfg = _lib.SgConfig(128, 128, 32, 3, 4, 1)
     assert L.gemm_fp16_tn_cfg(M, N, K, 1.0, a, b, d, ctypes.byref(cfg), None) == status
+
+
+@pytest.mark.parametrize("c_off,beta,status", [
+    (None, 0.5, S.SG_ERR_NULL),              # C required when beta != 0
+    (0x300008, 0.5, S.SG_ERR_ALIGN),          # C not 16-byte aligned
+    (0x200040, 0.5, S.SG_ERR_ALIAS),          # C overlaps D without being D
+    (0x1fffc0, 0.5, S.SG_ERR_ALIAS),          # C = [..., D + 64): overlaps D's start
+])
+def test_beta_c_argument_errors(c_off, beta, status):
+    _must_be_rejected(status)
+    c = None if c_off is None else P + c_off
+    assert L.gemm_fp16_tn_alpha_beta(8, 8, 8, 1.0, beta, P, P + 0x100000, c, P + 0x200000,
+                                     None) == status
+
+
+def test_beta_c_argument_errors_follow_the_plain_checks():
+    # the A/B/D checks come first, with the same codes as the plain call
+    assert L.gemm_fp16_tn_alpha_beta(8, 8, 12, 1.0, 0.5, P, P + 0x100000, P + 0x300000,
+                                     P + 0x200000, None) == S.SG_ERR_ALIGN
+    assert L.gemm_fp16_tn_alpha_beta(-1, 8, 8, 1.0, 0.5, P, P + 0x100000, P + 0x300000,
+                                     P + 0x200000, None) == S.SG_ERR_SHAPE
+    # beta == 0: C is never looked at, so a NULL or misaligned C is accepted;
+    # M == 0 is a no-op
+    assert L.gemm_fp16_tn_alpha_beta(0, 8, 8, 1.0, 0.0, P, P + 0x100000, None,
+                                     P + 0x200000, None) == S.SG_OK
+    assert L.gemm_fp16_tn_alpha_beta(0, 8, 8, 1.0, 0.0, P, P + 0x100000, P + 3,
+                                     P + 0x200000, None) == S.SG_OK
 
 
 def test_empty_outputs_are_no_ops():

@@ -178,6 +178,41 @@ def test_alpha_values(alpha):
     full_check(A, B, alpha=a32, label=f"alpha {alpha}")
 
 
+@pytest.mark.parametrize("shape", [(300, 264, 200), (4352, 520, 264), (256, 256, 0)])
+@pytest.mark.parametrize("alpha,beta", [(1.0, 1.0), (0.5, -0.75), (-1.0, 0.3), (0.0, 2.0)])
+def test_beta_c(shape, alpha, beta):
+    M, N, K = shape
+    say(f"[case] beta {shape} alpha={alpha} beta={beta}")
+    A, B = inputs.operands(M, N, K, 600 + M + K)
+    Cm = inputs.matrix(M, N, 700 + N, "normal")
+    a32, b32 = float(np.float32(alpha)), float(np.float32(beta))
+    c_dev = to_dev(Cm)
+    d = torch.full((M, N), float("nan"), dtype=torch.float16, device=DEV)
+    sg.gemm(to_dev(A), to_dev(B), out=d, alpha=a32, beta=b32, C=c_dev)
+    torch.cuda.synchronize()
+    rep = oracle.check(d.cpu().numpy(), oracle.gemm_tn_f64_beta(A, B, Cm, a32, b32), K)
+    assert rep.ok, str(rep)
+    # in place: C is D
+    d2 = to_dev(Cm)
+    sg.gemm(to_dev(A), to_dev(B), out=d2, alpha=a32, beta=b32, C=d2)
+    torch.cuda.synchronize()
+    assert torch.equal(d2.view(torch.int16), d.view(torch.int16))
+
+
+def test_beta_zero_does_not_read_c():
+    say("[case] beta zero with NaN C")
+    A, B = inputs.operands(300, 264, 200, 801)
+    nanc = torch.full((300, 264), float("nan"), dtype=torch.float16, device=DEV)
+    d = torch.empty((300, 264), dtype=torch.float16, device=DEV)
+    a, b = to_dev(A), to_dev(B)          # keep the tensors alive across the launch
+    sg._lib.gemm_fp16_tn_alpha_beta(300, 264, 200, 0.5, 0.0, a.data_ptr(), b.data_ptr(),
+                                    nanc.data_ptr(), d.data_ptr(),
+                                    torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    rep = oracle.check(d.cpu().numpy(), oracle.gemm_tn_f64(A, B, 0.5), 200)
+    assert rep.ok, str(rep)
+
+
 def test_alpha_one_is_bitwise_plain():
     A, B = inputs.operands(256, 256, 264, 93)
     d1 = run_gemm(A, B).cpu().numpy()
@@ -253,6 +288,12 @@ def test_square8192():
     A, B = inputs.workload("square8192")
     d = run_gemm(A, B)
     sampled_check(A, B, d, None, "square8192", seed=5)
+
+
+def test_tall_skinny_81920():
+    A, B = inputs.workload("tall81920")
+    d = run_gemm(A, B)
+    sampled_check(A, B, d, None, "tall81920", seed=7)
 
 
 def test_ragged8000():
