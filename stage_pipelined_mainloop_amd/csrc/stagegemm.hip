@@ -24,18 +24,24 @@ struct Variant {
     launch_fn launch;
 };
 
+// The kernel's parameter list; the argument array below must match it.
+typedef void (*gemm_kernel_fn)(const _Float16 *, const _Float16 *, const _Float16 *, _Float16 *,
+                               int, int, int, float, float, int);
+
 template <class C>
 hipError_t launch(int M, int N, int K, float alpha, float beta, const void *A, const void *B,
                   const void *Cm, void *D, int kt_rot, hipStream_t stream)
 {
+    const gemm_kernel_fn kernel = &sg::gemm_tn_kernel<C>;   // fails to compile on drift
     const long long tiles = (long long)((M + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
     const _Float16 *a = static_cast<const _Float16 *>(A);
     const _Float16 *b = static_cast<const _Float16 *>(B);
     const _Float16 *c = static_cast<const _Float16 *>(Cm);
     _Float16 *d = static_cast<_Float16 *>(D);
     void *args[] = {&a, &b, &c, &d, &M, &N, &K, &alpha, &beta, &kt_rot};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&sg::gemm_tn_kernel<C>),
-                           dim3((unsigned)tiles), dim3(C::T), args, 0, stream);
+    static_assert(sizeof(args) / sizeof(args[0]) == 10, "one entry per kernel parameter");
+    return hipLaunchKernel(reinterpret_cast<const void *>(kernel), dim3((unsigned)tiles),
+                           dim3(C::T), args, 0, stream);
 }
 
 template <class C>

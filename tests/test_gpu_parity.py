@@ -133,6 +133,17 @@ def test_rotated_k_loop_with_k_tail(shape, cfg):
     full_check(A, B, config=cfg, label=f"rotated {shape}")
 
 
+@pytest.mark.parametrize("shape", [(40, 16, 1 << 21), (8, 1 << 21, 8), (264, 24, (1 << 21) - 8)])
+def test_maximum_k_and_n(shape):
+    # K and N at the documented limit 2^21: per-workgroup buffer ranges and
+    # offsets come closest to 2^31 here
+    M, N, K = shape
+    g = np.random.Generator(np.random.PCG64(901))
+    A = g.uniform(-1, 1, (M, K)).astype(np.float16)
+    B = g.uniform(-1, 1, (N, K)).astype(np.float16)
+    full_check(A, B, label=f"limit {shape}")
+
+
 def test_k_zero_writes_zeros():
     say("[case] K=0")
     A = np.zeros((70, 0), np.float16)
