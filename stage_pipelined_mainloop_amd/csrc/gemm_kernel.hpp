@@ -62,6 +62,13 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kRsrcWord3 = 0x00020000;
 // An offset no per-workgroup resource reaches (num_records < 2^31).
 constexpr uint32_t kOutOfRange = 0x80000000u;
+// Cache-policy bits of the D stores (gfx950 buffer instruction aux field):
+// nt (2) marks the lines as streaming and sc1 (16) writes them through the
+// XCD's L2 at device scope.  D is written once and never re-read by the
+// kernel, so keeping it out of L2 leaves the capacity to the A and B panels
+// that neighbouring workgroups re-read; measured +9 % at 8192^3 and -10 %
+// time on the 4096x4096x128 shape against the default policy.
+constexpr int kStoreStreaming = 2 | 16;
 
 // s_waitcnt immediate for gfx9: vmcnt bits [3:0] and [15:14], expcnt [6:4],
 // lgkmcnt [11:8].  expcnt is never waited on here.
@@ -596,7 +603,7 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
         const u32x4 v = *(const u32x4 *)(epi + r * C::EPI_ROW + ec * 16);
         const int ml = wm * C::WTM + r;                // row within the workgroup tile
         const uint32_t off = n_ok ? (uint32_t)(ml * N + n) * 2u : kOutOfRange;
-        __builtin_amdgcn_raw_buffer_store_b128(v, rd, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(v, rd, off, 0, kStoreStreaming);
     }
 }
 
