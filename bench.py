@@ -6,8 +6,9 @@ mainloop and epilogue in one kernel) on inputs already resident in HBM.
 Prints ONE JSON line (rank 0):
   value        whole-job TFLOP/s = 2 M N K * steps / timed wall time
   roofline     the GEMM kernel against the dense fp16 MFMA peak: achieved =
-               2 M N K per launch / mean launch duration (HIP events around
-               each launch on the stream it is launched on); traffic = HBM
+               2 M N K per launch / mean launch duration (one pair of HIP
+               events around the back-to-back timed launches, on the stream
+               they are launched on); traffic = HBM
                bytes per launch from the committed rocprofv3 counter summary,
                or null if the kernel source changed since it was taken
   cpu_baseline the CPU oracle timed on a bounded row sample of the same
@@ -114,22 +115,43 @@ def cpu_baseline(A, B, target_s: float):
 
 
 def time_launches(fn, steps: int, warmup: int):
-    """Mean and min milliseconds of `fn` (one launch on the current stream),
-    measured with HIP events around each launch."""
+    """Launch `fn` (one launch on the current stream) `warmup` times, then
+    `steps` times back to back between one pair of HIP events; returns the
+    mean milliseconds per launch.  No events sit between the launches: an
+    event pair around every launch adds about 2.5 us to each reading, which
+    is a fifth of a 12 us kernel."""
     import torch
     for _ in range(warmup):
         fn()
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    for s, e in ev:
-        s.record(stream)
+    e0.record(stream)
+    for _ in range(steps):
         fn()
-        e.record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
-    ms = [s.elapsed_time(e) for s, e in ev]
-    return sum(ms) / len(ms), min(ms)
+    return e0.elapsed_time(e1) / steps
+
+
+def launch_spread(fn, steps: int, flush=None):
+    """Median and minimum of per-launch event timings (each includes the
+    event overhead); with `flush`, it runs before every launch, outside the
+    events, to measure with cold caches."""
+    import torch
+    stream = torch.cuda.current_stream()
+    ms = []
+    for _ in range(steps):
+        if flush is not None:
+            flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        e1.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    ms.sort()
+    return ms[len(ms) // 2], ms[0]
 
 
 def variant_info(cfg):
@@ -154,12 +176,12 @@ def mode_variants(args) -> int:
     b = torch.from_numpy(B).cuda()
     d = torch.empty((M, N), dtype=torch.float16, device="cuda")
     for c in sg.configs():
-        mean, mn = time_launches(lambda: sg.gemm(a, b, out=d, alpha=alpha, config=c),
-                                 args.steps, args.warmup)
+        mean = time_launches(lambda: sg.gemm(a, b, out=d, alpha=alpha, config=c),
+                             args.steps, args.warmup)
         t = 2.0 * M * N * K / (mean / 1e3) / 1e12
         print(json.dumps({"mode": "variants", "workload": args.workload,
                           "variant": c.as_tuple(), "ms_mean": round(mean, 4),
-                          "ms_min": round(mn, 4), "tflops": round(t, 1),
+                          "tflops": round(t, 1),
                           "pct_peak": round(100 * t / PEAK_TFLOPS, 2),
                           "info": variant_info(c)}), flush=True)
     return 0
@@ -182,7 +204,7 @@ def mode_ksweep(args) -> int:
         for c in sg.configs():
             if (c.tile_m, c.tile_n, c.waves) not in ((128, 128, 4), (256, 256, 8)):
                 continue
-            mean, mn = time_launches(lambda: sg.gemm(a, b, out=d, config=c), args.steps, args.warmup)
+            mean = time_launches(lambda: sg.gemm(a, b, out=d, config=c), args.steps, args.warmup)
             t = 2.0 * M * N * K / (mean / 1e3) / 1e12
             gbs = 2.0 * (M * K + N * K + M * N) / (mean / 1e3) / 1e9
             print(json.dumps({"mode": "ksweep", "M": M, "N": N, "K": K,
@@ -200,7 +222,7 @@ def mode_calibrate_copy(args) -> int:
     n = 512 * 1024 * 1024
     src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
-    mean, _ = time_launches(lambda: dst.copy_(src), args.steps, args.warmup)
+    mean = time_launches(lambda: dst.copy_(src), args.steps, args.warmup)
     print(json.dumps({"mode": "calibrate_copy", "bytes_read": n, "bytes_written": n,
                       "ms_mean": round(mean, 4), "gbs": round(2 * n / (mean / 1e3) / 1e9, 1)}),
           flush=True)
@@ -212,13 +234,15 @@ def main() -> int:
     ap.add_argument("--mode", default="bench",
                     choices=["bench", "variants", "ksweep", "calibrate_copy"])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="square8192")
     ap.add_argument("--config", default=None,
                     help="explicit variant tile_m,tile_n,tile_k,stages,waves,schedule")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time single launches after a 512 MiB cache flush")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -256,19 +280,29 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
 
+    # Timed region: the K steps back to back between one pair of HIP events
+    # on the stream the kernels are launched on, plus the host wall clock.
     stream = torch.cuda.current_stream(dev)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
+    e0.record(stream)
+    for _ in range(args.steps):
         step()
-        ends[i].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    mean_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+    mean_launch_s = e0.elapsed_time(e1) / args.steps / 1e3
+    # after the timed region: spread of single launches (each reading holds
+    # the ~2.5 us event overhead), and optionally with cold caches
+    med_ms, min_ms = launch_spread(step, min(args.steps, 30))
+    cold = None
+    if args.cold:
+        flush_buf = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev)
+        cmed, cmin = launch_spread(step, min(args.steps, 30), flush=lambda: flush_buf.fill_(1))
+        cold = {"flush": "512 MiB fill before each launch", "kernel_ms_median": round(cmed, 4),
+                "kernel_ms_min": round(cmin, 4)}
+        del flush_buf
 
     flops = 2.0 * M * N * K
     value = flops * args.steps / wall / 1e12
@@ -304,10 +338,13 @@ def main() -> int:
                               + f" S{chosen.stages} w{chosen.waves} sched{chosen.schedule}",
                    "pct_of_fp16_peak": round(100.0 * value / PEAK_TFLOPS, 2),
                    "kernel_ms_mean": round(mean_launch_s * 1e3, 4),
-                   "kernel_ms_min": round(min(launch_ms), 4)},
+                   "kernel_ms_median_single": round(med_ms, 4),
+                   "kernel_ms_min_single": round(min_ms, 4)},
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    if cold is not None:
+        out["config"]["cold_cache"] = cold
     if roofline["bound"] == "mfma":
         # measured after the timed region so it does not heat the GPU first
         ceil = mfma_ceiling(a, b)

@@ -65,7 +65,14 @@ typedef enum sg_status {
  *      then read fragments and compute;
  *   1  "cute(9) multistage_gemm", sections 6 and 9: fragments double-buffered
  *      in registers, the next tile's first fragments read right after the
- *      barrier and before the current tile's last MFMAs. */
+ *      barrier and before the current tile's last MFMAs;
+ *   2  the same ring split over two wave groups that alternate between
+ *      reading fragments and issuing MFMAs (two stages only);
+ *   3  persistent: one workgroup per resident slot computes a sequence of
+ *      output tiles whose K tiles stream through one ring (order 1 within
+ *      each), so the next tile's loads overlap this tile's last MFMAs and
+ *      epilogue; two or three stages, D = alpha * A * B^T only (the C
+ *      operand of gemm_fp16_tn_alpha_beta selects another variant). */
 typedef struct sg_config {
     int tile_m;
     int tile_n;
@@ -117,7 +124,10 @@ sg_status gemm_fp16_tn_cfg(int M, int N, int K, float alpha, const void *A,
                            const void *B, void *D, const sg_config *cfg,
                            void *stream);
 
-/* The variant gemm_fp16_tn would run for this shape (no pointers needed). */
+/* The variant gemm_fp16_tn (and gemm_fp16_tn_alpha) would run for this
+ * shape (no pointers needed).  gemm_fp16_tn_alpha_beta with beta != 0 runs
+ * the same variant unless it is persistent (schedule 3): then the tiled
+ * variant of the same tile and stage count. */
 sg_status sg_select_config(int M, int N, int K, sg_config *out);
 
 /* Enumerate the compiled variants: index 0 .. sg_num_configs()-1. */
@@ -138,6 +148,20 @@ int sg_minimum_stages(long long copy_cycles, long long compute_cycles);
  * it is about to consume K tile `k` of `ntile` (its s_waitcnt vmcnt value):
  * loads_per_stage * min(stages - 2, ntile - 1 - k).  -1 for bad arguments. */
 int sg_pipeline_wait_count(int stages, int loads_per_stage, int ntile, int k);
+
+/* The same for the persistent schedule (3): one workgroup streams the K tiles
+ * of its output tiles (`total` = ntile x its output-tile count) through one
+ * ring, and after each output tile issues the next load group early and then
+ * `stores_per_tile` 16-byte stores per lane.  Count of this lane's loads and
+ * stores the kernel lets remain in flight when it is about to consume stream
+ * tile `q`: the later load group (three stages) and the stores issued after
+ * tile q's loads.  Exact except with three stages and one K tile per output
+ * tile, where the stores of the output tile two back are not counted (the
+ * kernel then waits longer than it must).  -1 for bad arguments (stages
+ * outside 2..3, non-positive sizes, q outside 0..total-1, total not a
+ * multiple of ntile). */
+int sg_persistent_wait_count(int stages, int loads_per_stage, int stores_per_tile, int ntile,
+                             int total, int q);
 
 /* Human-readable name of a status code (static storage). */
 const char *sg_status_string(sg_status status);

@@ -23,9 +23,10 @@ from ._native import (build, f16_to_f64, f64_to_f16, gemm_tn_exact, gemm_tn_exac
                       gemm_tn_f64, gemm_tn_f64_at, gemm_tn_f64_beta, gemm_tn_f64_rows,
                       num_threads)
 from .check import CheckReport, check, ulp16
-from .models import (blocks_per_unit, lds_bytes, loosest_wait_counts, minimum_stages,
-                     schedule_cute_loads, schedule_cute_multistage, schedule_three_phase, simulate,
-                     simulate_loads)
+from .models import (blocks_per_unit, lds_bytes, loosest_persistent_wait_counts,
+                     loosest_wait_counts, minimum_stages, schedule_cute_loads,
+                     schedule_cute_multistage, schedule_persistent_loads, schedule_three_phase,
+                     simulate, simulate_loads)
 
 __all__ = [
     "build", "f16_to_f64", "f64_to_f16", "gemm_tn_exact", "gemm_tn_exact_beta",
@@ -33,5 +34,5 @@ __all__ = [
     "gemm_tn_f64_at", "gemm_tn_f64_rows", "num_threads", "CheckReport", "check",
     "ulp16", "blocks_per_unit", "lds_bytes", "loosest_wait_counts", "minimum_stages",
     "schedule_cute_loads", "schedule_cute_multistage", "schedule_three_phase", "simulate",
-    "simulate_loads",
+    "simulate_loads", "loosest_persistent_wait_counts", "schedule_persistent_loads",
 ]

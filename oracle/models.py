@@ -298,13 +298,17 @@ def simulate_loads(ops: list[Op], ntile: int, stages: int, nfrag: int,
                 err(f"tile {t} loaded twice")
             issued_parts[t] = parts + 1
             outstanding.append((t, s))
-            in_flight = len({tt for (tt, _) in outstanding})
+            in_flight = len({tt for (tt, _) in outstanding if tt is not None})
             res.max_in_flight = max(res.max_in_flight, in_flight)
+        elif op.kind in ("store", "dummy"):
+            # a global store, or a load aimed out of range into scratch LDS:
+            # counted by the same in-order counter, touches no ring slot
+            outstanding.append((None, None))
         elif op.kind == "wait":
             keep = max(op.n, 0)
             while len(outstanding) > keep:
                 t, s = outstanding.pop(0)
-                if slot_tile[s] == t:
+                if t is not None and slot_tile[s] == t:
                     slot_parts_done[s] += 1
         elif op.kind == "sync":
             epoch += 1
@@ -404,3 +408,86 @@ def schedule_cute_loads(ntile: int, stages: int, nfrag: int, loads_per_tile: int
                 issue(k + stages - 1)
             ops.append(Op("compute", tile=k, frag=ik))
     return ops
+
+
+def schedule_persistent_loads(ntile: int, ntiles_out: int, stages: int, nfrag: int,
+                              loads_per_tile: int, stores_per_tile: int,
+                              wait_counts: list[int]) -> list[Op]:
+    """One workgroup that computes `ntiles_out` output tiles of `ntile` K
+    tiles each as ONE stream of K tiles through the ring (stream tile
+    g = u * ntile + k lives in slot g mod S).  The order of
+    schedule_cute_loads over the whole stream ("cute(9) multistage_gemm"
+    section 9: the wait for the next tile and its first fragment read sit at
+    the last fragment of the current one; "Lesson 6": S - 1 tiles in flight),
+    with two changes.  At each output-tile boundary, after the last compute
+    of the output tile's last K tile g, the group of tile g + S is issued at
+    once (if it exists), then the epilogue's `stores_per_tile` counted global
+    stores.  And every K tile but the stream's last issues `loads_per_tile`
+    counted operations at its first fragment: its group g + S - 1 if that
+    exists and was not issued early, otherwise the same number of loads aimed
+    out of range (they fill no slot).  Loads and stores share one in-order
+    counter.  `wait_counts[g]` is the count used before stream tile g is
+    first read."""
+    if nfrag < 2:
+        raise ValueError("the walked-through schedule needs at least two fragments per tile")
+    total = ntile * ntiles_out
+    ops: list[Op] = []
+    issued: set[int] = set()
+
+    def issue(t):
+        for _ in range(loads_per_tile):
+            ops.append(Op("issue_part", tile=t, slot=t % stages))
+        issued.add(t)
+
+    def wait_for(t):
+        ops.append(Op("wait", n=wait_counts[t]))
+        ops.append(Op("sync"))
+
+    for t in range(min(stages - 1, total)):
+        issue(t)
+    if total == 0:
+        return ops
+    wait_for(0)
+    ops.append(Op("read", slot=0, frag=0))
+    for g in range(total):
+        for f in range(nfrag):
+            if f == nfrag - 1:
+                if g + 1 < total:
+                    wait_for(g + 1)
+                    ops.append(Op("read", slot=(g + 1) % stages, frag=0))
+            else:
+                ops.append(Op("read", slot=g % stages, frag=f + 1))
+            if f == 0 and g + 1 < total:
+                nxt = g + stages - 1
+                if nxt < total and nxt not in issued:
+                    issue(nxt)
+                else:
+                    ops.extend(Op("dummy") for _ in range(loads_per_tile))
+            ops.append(Op("compute", tile=g, frag=f))
+        if (g + 1) % ntile == 0:
+            if g + stages < total and g + stages not in issued:
+                issue(g + stages)
+            ops.extend(Op("store") for _ in range(stores_per_tile))
+    return ops
+
+
+def loosest_persistent_wait_counts(ntile: int, ntiles_out: int, stages: int,
+                                   loads_per_tile: int, stores_per_tile: int,
+                                   nfrag: int = 2) -> list[int]:
+    """The largest count of outstanding counted operations (loads and
+    stores) that still lets K tile g of the persistent stream be read safely,
+    found tile by tile by search against the simulator."""
+    total = ntile * ntiles_out
+    counts: list[int] = []
+    for g in range(total):
+        best = 0
+        for n in range(0, (loads_per_tile + stores_per_tile) * (stages + 1) + 1):
+            trial = counts + [n] + [0] * (total - g - 1)
+            ops = schedule_persistent_loads(ntile, ntiles_out, stages, nfrag, loads_per_tile,
+                                            stores_per_tile, trial)
+            r = simulate_loads(ops, total, stages, nfrag, loads_per_tile)
+            if any(e.startswith(f"RAW: tile {g} ") for e in r.errors):
+                break
+            best = n
+        counts.append(best)
+    return counts

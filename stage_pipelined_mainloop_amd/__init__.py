@@ -13,7 +13,8 @@ from __future__ import annotations
 
 from ._lib import (SgConfig, SgConfigInfo, SgError, configs, gemm_fp16_tn, gemm_fp16_tn_alpha,
                    gemm_fp16_tn_alpha_beta, gemm_fp16_tn_cfg, sg_get_config, sg_minimum_stages, sg_num_configs,
-                   sg_pipeline_wait_count, sg_query_config, sg_select_config, sg_status_string)
+                   sg_persistent_wait_count, sg_pipeline_wait_count, sg_query_config, sg_select_config,
+                   sg_status_string)
 
 
 def gemm(A, B, out=None, alpha: float | None = None, config=None, stream=None,
@@ -65,6 +66,6 @@ __all__ = [
     "gemm", "gemm_fp16_tn", "gemm_fp16_tn_alpha", "gemm_fp16_tn_alpha_beta", "gemm_fp16_tn_cfg",
     "sg_select_config",
     "sg_num_configs", "sg_get_config", "sg_query_config", "sg_minimum_stages",
-    "sg_pipeline_wait_count", "sg_status_string", "configs", "SgConfig", "SgConfigInfo",
+    "sg_pipeline_wait_count", "sg_persistent_wait_count", "sg_status_string", "configs", "SgConfig", "SgConfigInfo",
     "SgError",
 ]

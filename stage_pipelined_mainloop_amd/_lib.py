@@ -91,6 +91,8 @@ def lib() -> ctypes.CDLL:
         L.sg_minimum_stages.restype = i
         L.sg_pipeline_wait_count.argtypes = [i, i, i, i]
         L.sg_pipeline_wait_count.restype = i
+        L.sg_persistent_wait_count.argtypes = [i, i, i, i, i, i]
+        L.sg_persistent_wait_count.restype = i
         L.sg_status_string.argtypes = [i]
         L.sg_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -167,6 +169,12 @@ def sg_minimum_stages(copy_cycles: int, compute_cycles: int) -> int:
 
 def sg_pipeline_wait_count(stages: int, loads_per_stage: int, ntile: int, k: int) -> int:
     return int(lib().sg_pipeline_wait_count(stages, loads_per_stage, ntile, k))
+
+
+def sg_persistent_wait_count(stages: int, loads_per_stage: int, stores_per_tile: int, ntile: int,
+                             total: int, q: int) -> int:
+    return int(lib().sg_persistent_wait_count(stages, loads_per_stage, stores_per_tile, ntile,
+                                              total, q))
 
 
 def sg_status_string(status: int) -> str:

@@ -86,6 +86,44 @@ __host__ __device__ constexpr int pipeline_wait_count(int stages, int loads, int
     return loads * after;
 }
 
+// Persistent schedule: one workgroup's K tiles of all its output tiles form
+// one stream (stream tile g = u * ntile + k for output tile u, K step k; its
+// loads, "group g", go to ring slot g mod S).  Every stream tile but the last
+// issues L loads per lane at its first K step -- group g + S - 1, or, when
+// that group does not exist or was issued early, L loads aimed out of range
+// into the wave's epilogue staging area (they move no data and fill no ring
+// slot, so every tile runs the same code) -- and waits for group g + 1 at its
+// last K step.  When g ends an output tile, group g + S is issued at once
+// (into the slot g's reads released) before the epilogue's stores, so that
+// the stores stay out of the next wait.
+__host__ __device__ constexpr bool persistent_real_issue(int stages, int ntile, int total, int u,
+                                                         int k)
+{
+    return u * ntile + k + stages - 1 < total && !(k == 0 && u > 0);
+}
+
+// Counted operations (loads and stores, which leave vmcnt in issue order)
+// allowed outstanding at the wait for group g + 1 inside stream tile
+// g = u * ntile + k (g + 1 < total): the operations issued after that group.
+// With two slots: none, except after an output-tile boundary (k == 0, u > 0)
+// where group g + 1 was issued early and is followed by the stores and by
+// this tile's out-of-range loads.  With three slots: this tile's loads, plus
+// after a boundary the early group (if any) and the stores, or one tile later
+// (k == 1) the stores and the previous tile's loads.  With three slots and one
+// K tile per output tile the stores of the tile two back are left out (a
+// smaller count only waits longer).
+__host__ __device__ constexpr int persistent_wait_count(int stages, int loads, int stores,
+                                                        int ntile, int total, int u, int k)
+{
+    const int g = u * ntile + k;
+    const bool first = k == 0 && u > 0;
+    if (stages == 2) return first ? loads + stores : 0;
+    if (g == 0) return loads;
+    if (first) return (g + 2 < total ? loads : 0) + stores + loads;
+    if (k == 1 && u > 0) return stores + 2 * loads;
+    return loads;
+}
+
 // XOR swizzle of 16-byte chunk positions within an LDS row, by row index.
 // Rows of 4 chunks (BK = 32): bit0 = r2, bit1 = r1 ^ r3.
 // Rows of 8 chunks (BK = 64): bit0 = r1, bit1 = r2, bit2 = r0 ^ r3.
@@ -127,14 +165,28 @@ struct Cfg {
     // Epilogue staging: each wave's WTM x WTN fp16 sub-tile, rows padded by
     // 16 bytes (row stride 9 x 16 B for 128-byte rows) against bank conflicts.
     static constexpr int EPI_ROW = WTN * 2 + 16;
-    static constexpr int EPI_WAVE_BYTES = WTM * EPI_ROW;
+    static constexpr int EPI_WAVE_BYTES = 32 * EPI_ROW;    // one 32-row block at a time
     static constexpr int EPI_BYTES = NW * EPI_WAVE_BYTES;
-    static constexpr int LDS_BYTES = RING_BYTES > EPI_BYTES ? RING_BYTES : EPI_BYTES;
+    // Persistent schedule: the ring stays live during each output tile's
+    // epilogue, so the staging area is separate and holds one 32-row block
+    // of every wave's sub-tile at a time, rows unpadded (an 8-byte XOR
+    // swizzle keeps the accesses conflict-free).
+    static constexpr int EPI_BLOCK_WAVE_BYTES = 32 * WTN * 2;
+    static constexpr int EPI_BLOCK_BYTES = NW * EPI_BLOCK_WAVE_BYTES;
+    static constexpr int LDS_BYTES = SCHED == 3 ? RING_BYTES + EPI_BLOCK_BYTES
+                                   : (RING_BYTES > EPI_BYTES ? RING_BYTES : EPI_BYTES);
+    // Epilogue stores per lane per output tile: 16 bytes each, WTN * 2 / 16
+    // lanes per sub-tile row.
+    static constexpr int EPI_CHUNKS_PER_ROW = WTN * 2 / 16;
+    static constexpr int EPI_ROWS_PER_STORE = 64 / EPI_CHUNKS_PER_ROW;
+    static constexpr int STORES = FM * (32 / EPI_ROWS_PER_STORE);
     static constexpr int NA = BM * CPR / (64 * NW); // LDS-DMA loads per wave per stage
     static constexpr int NB = BN * CPR / (64 * NW);
     static constexpr int L = NA + NB;
     static_assert(S >= 2, "a ring needs at least two slots");
-    static_assert(SCHED == 0 || SCHED == 1 || SCHED == 2, "mainloop order");
+    static_assert(SCHED >= 0 && SCHED <= 3, "mainloop order");
+    static_assert(SCHED != 3 || S == 2 || S == 3, "persistent ring: two or three slots");
+    static_assert(SCHED != 3 || WTN == 64, "persistent staging rows are 128 bytes");
     static_assert(SCHED != 2 || (S == 2 && NW % 4 == 0 && (NW / 2) % 2 == 0 && BK == 64),
                   "ping-pong: two slots, two even wave groups, 128-byte rows");
     static_assert(NKS % 2 == 0, "fragment double buffer alternates per K step");
@@ -142,7 +194,8 @@ struct Cfg {
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile is whole 32x32 blocks");
     static_assert(NA * 64 * NW == BM * CPR && NB * 64 * NW == BN * CPR, "even load split");
     static_assert(NA >= 1 && NB >= 1, "every wave loads both operands");
-    static_assert(L * (S - 2) <= 63, "vmcnt is a 6-bit counter");
+    static_assert(L * (S - 2) + (SCHED == 3 ? STORES + 2 * L : 0) <= 63, "vmcnt is a 6-bit counter");
+    static_assert(32 % EPI_ROWS_PER_STORE == 0, "a 32-row block is whole store instructions");
     static_assert(LDS_BYTES <= 163840, "160 KiB of LDS per workgroup");
     static_assert((WTN * 2) % 16 == 0 && 64 % ((WTN * 2) / 16) == 0, "epilogue row chunks");
 };
@@ -198,6 +251,7 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
                const _Float16 *Cm, _Float16 *D, int M, int N, int K, float alpha, float beta,
                int kt_rot)
 {
+    static_assert(C::SCHED <= 2, "schedule 3 is gemm_tn_persistent_kernel");
     // Cm and D may be the same buffer (in-place D = alpha A B^T + beta D): each
     // wave reads C only inside its own sub-tile and finishes those reads
     // before it stores, so they are not declared __restrict__.
@@ -519,10 +573,15 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
     // ---- epilogue ("cute(9) multistage_gemm", section 7.2: registers ->
     // shared memory -> global, so the global writes are row-contiguous).
     // Lane holds D[m][n .. n+3] for m = row (lane & 31) of each 32x32 block
-    // and n = 8 * g + 4 * half.  Each wave converts alpha * acc to fp16
-    // (one rounding), writes its sub-tile into a private LDS region, then
-    // reads it back row by row and stores 16 bytes per lane: every store
-    // instruction covers whole row segments of WTN * 2 bytes.
+    // and n = 8 * g + 4 * half.  Per 32-row block i of its sub-tile, each
+    // wave converts alpha * acc (+ beta * C) to fp16 (one rounding), writes
+    // the block into a private LDS region, waits for those writes, reads it
+    // back row by row and stores 16 bytes per lane: every store instruction
+    // covers whole row segments of WTN * 2 bytes, and block i's stores drain
+    // while block i + 1 is converted (measured -8 % time on 4096x4096x128
+    // against staging the whole sub-tile first).  LDS executes one wave's
+    // accesses in order, so block i + 1's writes cannot overtake block i's
+    // reads.
     compiler_fence();
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
@@ -538,12 +597,22 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
                     ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v3) << 16);
         *(u32x2 *)(epi + r * C::EPI_ROW + c * 2) = packed;
     };
-    if (beta == 0.0f) {
-        // D = RNE16(alpha * acc): one rounding of the exact product (the
-        // compiler emits v_fma_mixlo_f16); C is not read.
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    constexpr int CPRW = C::EPI_CHUNKS_PER_ROW;        // 16-byte chunks per sub-tile row
+    constexpr int RPI = C::EPI_ROWS_PER_STORE;         // rows per wave instruction
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(D + (size_t)m0 * N, (uint32_t)rows_a * N * 2u);
+    const int ec = lane % CPRW;
+    const int n_st = n0 + wn * C::WTN + ec * 8;
+    const bool n_ok = n_st < N;                        // N % 8 == 0: a chunk is all in or out
+    const bool with_c = beta != 0.0f;
+    const __amdgpu_buffer_rsrc_t rc =
+        make_rsrc(with_c ? Cm + (size_t)m0 * N : D, with_c ? (uint32_t)rows_a * N * 2u : 0u);
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i) {
-            const int r = i * 32 + (lane & 31);
+    for (int i = 0; i < C::FM; ++i) {
+        const int r = lane & 31;                       // row within block i (and staging row)
+        if (!with_c) {
+            // D = RNE16(alpha * acc): one rounding of the exact product (the
+            // compiler emits v_fma_mixlo_f16); C is not read.
 #pragma unroll
             for (int j = 0; j < C::FN; ++j)
 #pragma unroll
@@ -552,16 +621,13 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
                     stage4(r, j * 32 + 8 * g + 4 * half, alpha * a[4 * g + 0],
                            alpha * a[4 * g + 1], alpha * a[4 * g + 2], alpha * a[4 * g + 3]);
                 }
-        }
-    } else {
-        // D = RNE16(alpha * acc + beta * C) ("CUDA operator notes 2", "GEMM"):
-        // C is read in the accumulator layout (4 halves per lane and group),
-        // combined in fp32 and rounded once to fp16.
-        const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cm + (size_t)m0 * N, (uint32_t)rows_a * N * 2u);
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i) {
-            const int r = i * 32 + (lane & 31);
-            const int ml = wm * C::WTM + r;
+        } else {
+            // D = RNE16(alpha * acc + beta * C) ("CUDA operator notes 2",
+            // "GEMM"): C is read in the accumulator layout (4 halves per lane
+            // and group), combined in fp32 and rounded once to fp16.  Each
+            // wave reads only C elements of rows it stores itself, before it
+            // stores them, so C may be D (in place).
+            const int ml = wm * C::WTM + i * 32 + r;
 #pragma unroll
             for (int j = 0; j < C::FN; ++j) {
                 u32x2 cv[4];
@@ -586,24 +652,18 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
                 }
             }
         }
-    }
-    compiler_fence();
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));   // this wave's LDS writes landed
-    compiler_fence();
-    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    constexpr int CPRW = C::WTN * 2 / 16;              // 16-byte chunks per sub-tile row
-    constexpr int RPI = 64 / CPRW;                     // rows per wave instruction
-    const __amdgpu_buffer_rsrc_t rd = make_rsrc(D + (size_t)m0 * N, (uint32_t)rows_a * N * 2u);
-    const int ec = lane % CPRW;
-    const int n = n0 + wn * C::WTN + ec * 8;
-    const bool n_ok = n < N;                           // N % 8 == 0: a chunk is all in or out
+        compiler_fence();
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));   // this wave's LDS writes landed
+        compiler_fence();
 #pragma unroll
-    for (int it = 0; it < C::WTM / RPI; ++it) {
-        const int r = it * RPI + lane / CPRW;
-        const u32x4 v = *(const u32x4 *)(epi + r * C::EPI_ROW + ec * 16);
-        const int ml = wm * C::WTM + r;                // row within the workgroup tile
-        const uint32_t off = n_ok ? (uint32_t)(ml * N + n) * 2u : kOutOfRange;
-        __builtin_amdgcn_raw_buffer_store_b128(v, rd, off, 0, kStoreStreaming);
+        for (int it = 0; it < 32 / RPI; ++it) {
+            const int rr = it * RPI + lane / CPRW;     // row within block i
+            const u32x4 v = *(const u32x4 *)(epi + rr * C::EPI_ROW + ec * 16);
+            const int ml = wm * C::WTM + i * 32 + rr;  // row within the workgroup tile
+            const uint32_t off = n_ok ? (uint32_t)(ml * N + n_st) * 2u : kOutOfRange;
+            __builtin_amdgcn_raw_buffer_store_b128(v, rd, off, 0, kStoreStreaming);
+        }
+        compiler_fence();
     }
 }
 

@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "gemm_kernel.hpp"
+#include "persistent_kernel.hpp"
 
 namespace {
 
@@ -29,18 +30,51 @@ typedef void (*gemm_kernel_fn)(const _Float16 *, const _Float16 *, const _Float1
                                int, int, int, float, float, int);
 
 template <class C>
+constexpr gemm_kernel_fn kernel_of()
+{
+    if constexpr (C::SCHED == 3)
+        return &sg::gemm_tn_persistent_kernel<C>;
+    else
+        return &sg::gemm_tn_kernel<C>;
+}
+
+// Workgroups of kernel `k` that the device can keep resident at once (CUs x
+// workgroups per CU), cached per device; 0 if the runtime cannot tell.
+int resident_capacity(const void *k, int threads, int (&cache)[16])
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (dev >= 0 && dev < 16 && cache[dev] > 0) return cache[dev];
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, threads, 0) != hipSuccess)
+        return 0;
+    const int cap = cus * per_cu;
+    if (dev >= 0 && dev < 16) cache[dev] = cap;
+    return cap;
+}
+
+template <class C>
 hipError_t launch(int M, int N, int K, float alpha, float beta, const void *A, const void *B,
                   const void *Cm, void *D, int kt_rot, hipStream_t stream)
 {
-    const gemm_kernel_fn kernel = &sg::gemm_tn_kernel<C>;   // fails to compile on drift
+    const gemm_kernel_fn kernel = kernel_of<C>();  // fails to compile on drift
     const long long tiles = (long long)((M + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
+    long long grid = tiles;
+    if constexpr (C::SCHED == 3) {
+        // one workgroup per resident slot; each loops over its output tiles
+        static int cache[16];
+        const int cap = resident_capacity(reinterpret_cast<const void *>(kernel), C::T, cache);
+        if (cap <= 0) return hipErrorInvalidConfiguration;
+        if (grid > cap) grid = cap;
+    }
     const _Float16 *a = static_cast<const _Float16 *>(A);
     const _Float16 *b = static_cast<const _Float16 *>(B);
     const _Float16 *c = static_cast<const _Float16 *>(Cm);
     _Float16 *d = static_cast<_Float16 *>(D);
     void *args[] = {&a, &b, &c, &d, &M, &N, &K, &alpha, &beta, &kt_rot};
     static_assert(sizeof(args) / sizeof(args[0]) == 10, "one entry per kernel parameter");
-    return hipLaunchKernel(reinterpret_cast<const void *>(kernel), dim3((unsigned)tiles),
+    return hipLaunchKernel(reinterpret_cast<const void *>(kernel), dim3((unsigned)grid),
                            dim3(C::T), args, 0, stream);
 }
 
@@ -49,7 +83,7 @@ constexpr Variant variant()
 {
     return Variant{{C::BM, C::BN, C::BK, C::S, C::NW, C::SCHED}, C::T, C::RING_BYTES, C::LDS_BYTES,
                    C::L,
-                   reinterpret_cast<const void *>(&sg::gemm_tn_kernel<C>), &launch<C>};
+                   reinterpret_cast<const void *>(kernel_of<C>()), &launch<C>};
 }
 
 // Compiled variants.  256x256 tiles carry the large square shapes (half the
@@ -82,6 +116,11 @@ const Variant kVariants[] = {
     variant<sg::Cfg<128, 128, 32, 3, 2, 2, 0>>(),
     variant<sg::Cfg<128, 128, 32, 4, 2, 2, 0>>(),
     variant<sg::Cfg<128, 128, 32, 5, 2, 2, 0>>(),
+    // persistent workgroups, one ring across output tiles (schedule 3)
+    variant<sg::Cfg<256, 256, 64, 2, 2, 4, 3>>(),
+    variant<sg::Cfg<128, 128, 64, 2, 2, 2, 3>>(),
+    variant<sg::Cfg<128, 128, 32, 2, 2, 2, 3>>(),
+    variant<sg::Cfg<128, 128, 32, 3, 2, 2, 3>>(),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -101,14 +140,15 @@ const Variant *find_variant(const sg_config *c)
 // CU, 128x128 ones do a quarter of the work at about 1.3x the cost per flop;
 // cost = rounds of 256 workgroups x per-workgroup work.  Large grids
 // (8192^3, 8000x7936x8200, 4096^3, 4096^2 x 128) pick 256x256x64, two
-// stages, 8 waves, cute order.  Small or skinny grids (2048^2 sweep,
-// 81920 x 256 x 256) pick 128x128x64, cute order, with the stage count of
-// the lesson's occupancy trade-off: three stages (96 KiB, one workgroup per
-// CU) when the grid is at most one workgroup per CU, else two stages
-// (64 KiB, two resident per CU) so a second workgroup hides latency.
-const Variant *select_variant(int M, int N, int K)
+// stages, 8 waves, cute order.  Small or skinny grids pick 128x128x64 with
+// the stage count of the lesson's occupancy trade-off: three stages (96 KiB,
+// one workgroup per CU) when the grid is at most one workgroup per CU
+// (2048^2 sweep); otherwise two stages (64 KiB, two resident per CU), and,
+// when K <= 1024 and there is no C operand, the persistent schedule, whose
+// ring runs on across output tiles (81920 x 256 x 256: -14 % time against
+// the tiled kernel; with long K loops the tiled kernel is 3-5 % faster).
+const Variant *select_variant(int M, int N, int K, bool with_c)
 {
-    (void)K;
     const long long t256 = (long long)((M + 255) / 256) * ((N + 255) / 256);
     const long long t128 = (long long)((M + 127) / 128) * ((N + 127) / 128);
     const double cost256 = (double)((t256 + 255) / 256) * 4.0;
@@ -118,6 +158,8 @@ const Variant *select_variant(int M, int N, int K)
         c = sg_config{256, 256, 64, 2, 8, 1};
     else if (t128 <= 256)
         c = sg_config{128, 128, 64, 3, 4, 1};
+    else if (K <= 1024 && !with_c)
+        c = sg_config{128, 128, 64, 2, 4, 3};
     else
         c = sg_config{128, 128, 64, 2, 4, 1};
     return find_variant(&c);
@@ -169,6 +211,8 @@ sg_status run(const Variant *v, int M, int N, int K, float alpha, float beta, co
     const long long tiles = (long long)((M + v->cfg.tile_m - 1) / v->cfg.tile_m) *
                             ((N + v->cfg.tile_n - 1) / v->cfg.tile_n);
     if (tiles * v->threads >= (1LL << 32)) return SG_ERR_SHAPE;
+    // the persistent kernel has no C operand
+    if (v->cfg.schedule == 3 && beta != 0.0f) return SG_ERR_UNSUPPORTED;
     // Rotate the K loop over 4 tile rows once the grid is more than one wave
     // of workgroups on the 256 CUs (measured: +14% at 8192^3, -2% at 4096^3
     // where all workgroups are resident and the operands fit in the 256 MB
@@ -188,7 +232,7 @@ sg_status gemm_fp16_tn_alpha(int M, int N, int K, float alpha, const void *A, co
 {
     const sg_status st = validate(M, N, K, A, B, D);
     if (st != SG_OK || M == 0 || N == 0) return st;
-    const Variant *v = select_variant(M, N, K);
+    const Variant *v = select_variant(M, N, K, false);
     if (!v) return SG_ERR_UNSUPPORTED;
     return run(v, M, N, K, alpha, 0.0f, A, B, nullptr, D, stream);
 }
@@ -200,7 +244,7 @@ sg_status gemm_fp16_tn_alpha_beta(int M, int N, int K, float alpha, float beta, 
     if (st != SG_OK) return st;
     st = validate_c(M, N, beta, Cm, D);
     if (st != SG_OK || M == 0 || N == 0) return st;
-    const Variant *v = select_variant(M, N, K);
+    const Variant *v = select_variant(M, N, K, beta != 0.0f);
     if (!v) return SG_ERR_UNSUPPORTED;
     return run(v, M, N, K, alpha, beta, A, B, Cm, D, stream);
 }
@@ -226,7 +270,7 @@ sg_status sg_select_config(int M, int N, int K, sg_config *out)
 {
     if (!out) return SG_ERR_NULL;
     if (M < 0 || N < 0 || K < 0) return SG_ERR_SHAPE;
-    const Variant *v = select_variant(M, N, K);
+    const Variant *v = select_variant(M, N, K, false);
     if (!v) return SG_ERR_UNSUPPORTED;
     *out = v->cfg;
     return SG_OK;
@@ -285,6 +329,18 @@ int sg_pipeline_wait_count(int stages, int loads_per_stage, int ntile, int k)
 {
     if (stages < 2 || loads_per_stage < 1 || ntile < 1 || k < 0 || k >= ntile) return -1;
     return sg::pipeline_wait_count(stages, loads_per_stage, ntile, k);
+}
+
+int sg_persistent_wait_count(int stages, int loads_per_stage, int stores_per_tile, int ntile,
+                             int total, int q)
+{
+    if (stages < 2 || stages > 3 || loads_per_stage < 1 || stores_per_tile < 0 || ntile < 1 ||
+        total < 1 || total % ntile != 0 || q < 0 || q >= total)
+        return -1;
+    if (q == 0) return loads_per_stage * ((stages == 3 && total > 1) ? 1 : 0);
+    const int g = q - 1;
+    return sg::persistent_wait_count(stages, loads_per_stage, stores_per_tile, ntile, total,
+                                     g / ntile, g % ntile);
 }
 
 const char *sg_status_string(sg_status status)

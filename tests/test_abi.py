@@ -17,7 +17,7 @@ S = _lib
 
 def test_every_declared_symbol_is_exported():
     declared = _lib.header_functions()
-    assert len(declared) == 11
+    assert len(declared) == 12
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
@@ -139,6 +139,28 @@ def test_wait_counts_match_the_ring_simulator():
     assert _lib.sg_pipeline_wait_count(3, 4, 4, 4) == -1
 
 
+def test_persistent_wait_counts_match_the_ring_simulator():
+    # loosest safe count per stream tile, found by the simulator with loads
+    # and epilogue stores on one in-order counter, against the kernel's formula
+    for stages in (2, 3):
+        for ntile in (1, 2, 3, 5):
+            for nout in (1, 2, 3):
+                for loads, stores in ((8, 8), (4, 6), (16, 16)):
+                    want = oracle.loosest_persistent_wait_counts(ntile, nout, stages, loads, stores)
+                    total = ntile * nout
+                    got = [_lib.sg_persistent_wait_count(stages, loads, stores, ntile, total, q)
+                           for q in range(total)]
+                    # never looser than the simulator allows; equal except for
+                    # the one documented case (three stages, one K tile per
+                    # output tile), where it may only be tighter
+                    assert all(0 <= a <= b for a, b in zip(got, want)), (stages, ntile, nout, got, want)
+                    if not (stages == 3 and ntile == 1):
+                        assert got == want, (stages, ntile, nout, loads, stores, got, want)
+    assert _lib.sg_persistent_wait_count(4, 8, 8, 2, 4, 0) == -1
+    assert _lib.sg_persistent_wait_count(3, 8, 8, 2, 5, 0) == -1
+    assert _lib.sg_persistent_wait_count(3, 8, 8, 2, 4, 4) == -1
+
+
 def test_config_table_and_lds_model():
     cfgs = _lib.configs()
     assert len(cfgs) == _lib.sg_num_configs() >= 8
@@ -165,9 +187,15 @@ def test_config_table_and_lds_model():
 
 def test_selection_returns_compiled_variants():
     for shape in [(256, 256, 256), (4096, 4096, 4096), (2048, 2048, 128), (4096, 4096, 128),
-                  (8192, 8192, 8192), (8000, 7936, 8200), (1, 8, 8)]:
+                  (8192, 8192, 8192), (8000, 7936, 8200), (1, 8, 8), (81920, 256, 256)]:
         c = _lib.sg_select_config(*shape)
         assert c.as_tuple() in {x.as_tuple() for x in _lib.configs()}
+    # the measured choices: big squares tiled 256x256x64, the skinny tall
+    # shape persistent 128x128x64, the one-wave sweep grid 128x128x64 S3
+    assert _lib.sg_select_config(8192, 8192, 8192).as_tuple() == (256, 256, 64, 2, 8, 1)
+    assert _lib.sg_select_config(81920, 256, 256).as_tuple() == (128, 128, 64, 2, 4, 3)
+    assert _lib.sg_select_config(2048, 2048, 2048).as_tuple() == (128, 128, 64, 3, 4, 1)
+    assert _lib.sg_select_config(81920, 256, 4096).as_tuple() == (128, 128, 64, 2, 4, 1)
 
 
 def _gpu_visible() -> bool:

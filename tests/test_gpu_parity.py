@@ -105,7 +105,8 @@ def test_every_variant_on_ragged_shapes(shape):
 
 @pytest.mark.parametrize("cfg", [None, (128, 128, 32, 3, 4, 1), (256, 256, 32, 5, 8, 1),
                                  (256, 256, 64, 2, 8, 1), (256, 256, 32, 3, 8, 0),
-                                 (128, 128, 64, 3, 4, 1), (256, 256, 64, 2, 8, 2)])
+                                 (128, 128, 64, 3, 4, 1), (256, 256, 64, 2, 8, 2),
+                                 (128, 128, 64, 2, 4, 3), (256, 256, 64, 2, 8, 3)])
 def test_tiny_shape_grid(cfg):
     # every M, N and K tail against every tile boundary of the variant
     say(f"[case] tiny grid cfg={cfg}")
@@ -124,13 +125,46 @@ def test_tiny_shape_grid(cfg):
                                        ((4352, 4104, 200), (256, 256, 64, 2, 8, 1)),
                                        ((2304, 2304, 520), (128, 128, 32, 4, 4, 1)),
                                        ((2304, 2312, 1000), (256, 256, 32, 3, 8, 0)),
-                                       ((4352, 4360, 336), (256, 256, 64, 2, 8, 2))])
+                                       ((4352, 4360, 336), (256, 256, 64, 2, 8, 2)),
+                                       ((4352, 4360, 336), (128, 128, 32, 3, 4, 3)),
+                                       ((4352, 4360, 200), (128, 128, 64, 2, 4, 3))])
 def test_rotated_k_loop_with_k_tail(shape, cfg):
     # more than 256 workgroups, so each tile row starts its K loop at a
     # rotated tile and the K-tail tile lands mid-sequence
     M, N, K = shape
     A, B = inputs.operands(M, N, K, 500 + K)
     full_check(A, B, config=cfg, label=f"rotated {shape}")
+
+
+PERSISTENT = [c for c in VARIANTS if c[5] == 3]
+
+
+@pytest.mark.parametrize("shape", [(4200, 4104, 200), (4200, 4104, 8), (4224, 4112, 72),
+                                   (2056, 4104, 136)])
+def test_persistent_workgroups_loop_over_tiles(shape):
+    # more output tiles than resident workgroups: each workgroup of the
+    # persistent schedule runs several tiles through one ring, with M, N and
+    # K tails, one-tile K loops (K = 8) and tiles whose K loop is shorter
+    # than the ring
+    M, N, K = shape
+    A, B = inputs.operands(M, N, K, 1100 + K)
+    say(f"[case] persistent {shape}")
+    ref = oracle.gemm_tn_f64(A, B)
+    assert PERSISTENT
+    for cfg in PERSISTENT:
+        say(f"[case] persistent {shape} {cfg}")
+        d = run_gemm(A, B, config=cfg).cpu().numpy()
+        rep = oracle.check(d, ref, K)
+        assert rep.ok, (cfg, str(rep))
+
+
+@pytest.mark.parametrize("cfg", [None] + PERSISTENT[:2])
+def test_k_zero_every_schedule(cfg):
+    say(f"[case] K=0 {cfg}")
+    A = np.zeros((1100, 0), np.float16)
+    B = np.zeros((1032, 0), np.float16)
+    d = run_gemm(A, B, config=cfg).cpu().numpy()
+    assert np.all(d.view(np.uint16) == 0)
 
 
 @pytest.mark.parametrize("shape", [(40, 16, 1 << 21), (8, 1 << 21, 8), (264, 24, (1 << 21) - 8)])
@@ -161,12 +195,16 @@ def test_empty_m_or_n_leaves_output_untouched():
     assert tuple(out.shape) == (0, 8)
 
 
-@pytest.mark.parametrize("cfg", [None, (128, 128, 32, 4, 4, 1), (256, 256, 32, 4, 8, 1),
-                                 (256, 256, 32, 4, 8, 0), (256, 256, 64, 2, 8, 2)])
-def test_canary_guard_bands(cfg):
+@pytest.mark.parametrize("cfg,shape", [(None, (300, 264, 136)), ((128, 128, 32, 4, 4, 1), (300, 264, 136)),
+                                       ((256, 256, 32, 4, 8, 1), (300, 264, 136)),
+                                       ((256, 256, 32, 4, 8, 0), (300, 264, 136)),
+                                       ((256, 256, 64, 2, 8, 2), (300, 264, 136)),
+                                       ((128, 128, 64, 2, 4, 3), (4200, 4104, 72)),
+                                       ((256, 256, 64, 2, 8, 3), (4200, 4104, 72))])
+def test_canary_guard_bands(cfg, shape):
     # D sits inside a larger buffer filled with a NaN pattern; nothing outside
     # D may change and every element of D must be written
-    M, N, K = 300, 264, 136
+    M, N, K = shape
     say(f"[case] canary cfg={cfg}")
     A, B = inputs.operands(M, N, K, 77)
     guard = 4096
@@ -189,9 +227,12 @@ def test_alpha_values(alpha):
     full_check(A, B, alpha=a32, label=f"alpha {alpha}")
 
 
-@pytest.mark.parametrize("shape", [(300, 264, 200), (4352, 520, 264), (256, 256, 0)])
+@pytest.mark.parametrize("shape", [(300, 264, 200), (4352, 520, 264), (256, 256, 0),
+                                   (20480, 256, 256)])
 @pytest.mark.parametrize("alpha,beta", [(1.0, 1.0), (0.5, -0.75), (-1.0, 0.3), (0.0, 2.0)])
 def test_beta_c(shape, alpha, beta):
+    # (20480, 256, 256): without C the library picks the persistent schedule;
+    # with C it must fall back to a tiled variant
     M, N, K = shape
     say(f"[case] beta {shape} alpha={alpha} beta={beta}")
     A, B = inputs.operands(M, N, K, 600 + M + K)
@@ -305,6 +346,20 @@ def test_tall_skinny_81920():
     A, B = inputs.workload("tall81920")
     d = run_gemm(A, B)
     sampled_check(A, B, d, None, "tall81920", seed=7)
+    for cfg in PERSISTENT:
+        d = run_gemm(A, B, config=cfg)
+        sampled_check(A, B, d, None, f"tall81920 {cfg}", seed=8)
+
+
+def test_attention_scores_persistent():
+    A, B = inputs.workload("attn_scores")
+    alpha = float(np.float32(1.0 / math.sqrt(128.0)))
+    ref = oracle.gemm_tn_f64(A, B, alpha)
+    for cfg in PERSISTENT:
+        say(f"[case] attn_scores {cfg}")
+        d = run_gemm(A, B, alpha=alpha, config=cfg).cpu().numpy()
+        rep = oracle.check(d, ref, 128)
+        assert rep.ok, (cfg, str(rep))
 
 
 def test_ragged8000():
