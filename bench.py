@@ -154,6 +154,12 @@ def launch_spread(fn, steps: int, flush=None):
     return ms[len(ms) // 2], ms[0]
 
 
+def takes(cfg, K: int) -> bool:
+    """Whether a compiled variant takes this K: the short-K schedule (4)
+    holds the whole K extent in its ring."""
+    return cfg.schedule != 4 or K <= cfg.tile_k * cfg.stages
+
+
 def variant_info(cfg):
     import stage_pipelined_mainloop_amd as sg
     st, info = sg.sg_query_config(cfg)
@@ -176,6 +182,8 @@ def mode_variants(args) -> int:
     b = torch.from_numpy(B).cuda()
     d = torch.empty((M, N), dtype=torch.float16, device="cuda")
     for c in sg.configs():
+        if not takes(c, K):
+            continue
         mean = time_launches(lambda: sg.gemm(a, b, out=d, alpha=alpha, config=c),
                              args.steps, args.warmup)
         t = 2.0 * M * N * K / (mean / 1e3) / 1e12
@@ -202,7 +210,7 @@ def mode_ksweep(args) -> int:
         M = N = inputs.KSWEEP_MN
         d = torch.empty((M, N), dtype=torch.float16, device="cuda")
         for c in sg.configs():
-            if (c.tile_m, c.tile_n, c.waves) not in ((128, 128, 4), (256, 256, 8)):
+            if (c.tile_m, c.tile_n, c.waves) not in ((128, 128, 4), (256, 256, 8)) or not takes(c, K):
                 continue
             mean = time_launches(lambda: sg.gemm(a, b, out=d, config=c), args.steps, args.warmup)
             t = 2.0 * M * N * K / (mean / 1e3) / 1e12

@@ -167,13 +167,13 @@ struct Cfg {
     static constexpr int EPI_ROW = WTN * 2 + 16;
     static constexpr int EPI_WAVE_BYTES = 32 * EPI_ROW;    // one 32-row block at a time
     static constexpr int EPI_BYTES = NW * EPI_WAVE_BYTES;
-    // Persistent schedule: the ring stays live during each output tile's
+    // Persistent and short-K schedules: the ring stays live during the
     // epilogue, so the staging area is separate and holds one 32-row block
     // of every wave's sub-tile at a time, rows unpadded (an 8-byte XOR
     // swizzle keeps the accesses conflict-free).
     static constexpr int EPI_BLOCK_WAVE_BYTES = 32 * WTN * 2;
     static constexpr int EPI_BLOCK_BYTES = NW * EPI_BLOCK_WAVE_BYTES;
-    static constexpr int LDS_BYTES = SCHED == 3 ? RING_BYTES + EPI_BLOCK_BYTES
+    static constexpr int LDS_BYTES = SCHED >= 3 ? RING_BYTES + EPI_BLOCK_BYTES
                                    : (RING_BYTES > EPI_BYTES ? RING_BYTES : EPI_BYTES);
     // Epilogue stores per lane per output tile: 16 bytes each, WTN * 2 / 16
     // lanes per sub-tile row.
@@ -184,9 +184,9 @@ struct Cfg {
     static constexpr int NB = BN * CPR / (64 * NW);
     static constexpr int L = NA + NB;
     static_assert(S >= 2, "a ring needs at least two slots");
-    static_assert(SCHED >= 0 && SCHED <= 3, "mainloop order");
+    static_assert(SCHED >= 0 && SCHED <= 4, "mainloop order");
     static_assert(SCHED != 3 || S == 2 || S == 3, "persistent ring: two or three slots");
-    static_assert(SCHED != 3 || WTN == 64, "persistent staging rows are 128 bytes");
+    static_assert(SCHED < 3 || WTN == 64, "unpadded staging rows are 128 bytes");
     static_assert(SCHED != 2 || (S == 2 && NW % 4 == 0 && (NW / 2) % 2 == 0 && BK == 64),
                   "ping-pong: two slots, two even wave groups, 128-byte rows");
     static_assert(NKS % 2 == 0, "fragment double buffer alternates per K step");
@@ -245,13 +245,63 @@ __device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, i
     tn = in_group / gm;
 }
 
+// One 32-row block of a wave's sub-tile (its FN 32x32 accumulators, rows
+// row0 .. row0+31 of the workgroup tile) to D = RNE16(alpha * acc), through
+// the wave's unpadded staging area: 128-byte rows of sixteen 8-byte slots,
+// slot c of row r at c ^ ((r >> 1) & 15), so the 32 rows of one write land on
+// 32 distinct bank pairs.  Wait for the LDS writes, read back 16 bytes per
+// lane along rows (a logical 16-byte chunk is an aligned slot pair, halves
+// swapped when the row's swizzle is odd) and store with the streaming policy.
+// Lane holds D[m][n .. n+3] for m = row (lane & 31) of each block and
+// n = 8 * g + 4 * (lane >> 5).  LDS runs one wave's accesses in order, so a
+// later block's writes cannot overtake these reads.
+template <class C>
+__device__ __forceinline__ void store_block_staged(const f32x16 (&blk)[C::FN], float alpha,
+                                                   char *epi, int lane,
+                                                   __amdgpu_buffer_rsrc_t rd, int row0, int n,
+                                                   bool n_ok, int N)
+{
+    static_assert(C::WTN == 64, "128-byte staging rows");
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const int half = lane >> 5;
+    const int wr = lane & 31;
+    const int wsw = (wr >> 1) & 15;
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const f32x16 &a = blk[j];
+            u32x2 packed;
+            packed[0] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(alpha * a[4 * g + 0])) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(alpha * a[4 * g + 1])) << 16);
+            packed[1] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(alpha * a[4 * g + 2])) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(alpha * a[4 * g + 3])) << 16);
+            const int slot8 = (8 * j + 2 * g + half) ^ wsw;
+            *(u32x2 *)(epi + wr * 128 + slot8 * 8) = packed;
+        }
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    compiler_fence();
+    const int ec = lane & 7;                           // 16-byte chunk of the row
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int r = it * 8 + (lane >> 3);
+        const int sw = (r >> 1) & 15;
+        u32x4 v = *(const u32x4 *)(epi + r * 128 + ((ec ^ (sw >> 1)) << 4));
+        if (sw & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+        const uint32_t off = n_ok ? (uint32_t)((row0 + r) * N + n) * 2u : kOutOfRange;
+        __builtin_amdgcn_raw_buffer_store_b128(v, rd, off, 0, kStoreStreaming);
+    }
+    compiler_fence();
+}
+
 template <class C>
 __global__ void __launch_bounds__(C::T)
 gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
                const _Float16 *Cm, _Float16 *D, int M, int N, int K, float alpha, float beta,
                int kt_rot)
 {
-    static_assert(C::SCHED <= 2, "schedule 3 is gemm_tn_persistent_kernel");
+    static_assert(C::SCHED <= 2, "schedules 3 and 4 have kernels of their own");
     // Cm and D may be the same buffer (in-place D = alpha A B^T + beta D): each
     // wave reads C only inside its own sub-tile and finishes those reads
     // before it stores, so they are not declared __restrict__.

@@ -67,20 +67,10 @@ gemm_tn_persistent_kernel(const _Float16 *__restrict__ A, const _Float16 *__rest
         kt0 = (kt_rot > 1 && ntile > 0) ? (tm % kt_rot) % ntile : 0;
     };
 
-    // ---- epilogue of one output tile: D = RNE16(alpha * acc), one rounding.
-    // Lane holds D[m][n .. n+3] for m = row (lane & 31) of each 32x32 block
-    // and n = 8 * g + 4 * half.  Per 32-row block: write it to this wave's
-    // staging area (128-byte rows of sixteen 8-byte slots; slot c of row r
-    // sits at c ^ ((r >> 1) & 15), so the 32 rows of one write land on 32
-    // distinct bank pairs), wait for the LDS writes, read back 16 bytes per
-    // lane along rows (a logical 16-byte chunk is an aligned slot pair, its
-    // halves swapped when the row's swizzle is odd) and store.  The area is
-    // private to the wave (no barrier); LDS executes one wave's accesses in
-    // order, so the next block's writes cannot overtake this block's reads.
+    // ---- epilogue of one output tile: D = RNE16(alpha * acc), one rounding,
+    // one 32-row block at a time through the wave's staging area beside the
+    // ring (store_block_staged; no barrier, the area is private to the wave).
     char *epi = smem + C::RING_BYTES + wave * C::EPI_BLOCK_WAVE_BYTES;
-    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    constexpr int RPI = 8;                         // rows per store instruction
-    const int ec = lane & 7;                       // 16-byte chunk of the row
     f32x16 acc[C::FM][C::FN];
     auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -92,40 +82,11 @@ gemm_tn_persistent_kernel(const _Float16 *__restrict__ A, const _Float16 *__rest
     };
     auto epilogue = [&](int m0, int n0, int rows_a) __attribute__((always_inline)) {
         const __amdgpu_buffer_rsrc_t rd = make_rsrc(D + (size_t)m0 * N, (uint32_t)rows_a * N * 2u);
-        const int n = n0 + wn * C::WTN + ec * 8;
+        const int n = n0 + wn * C::WTN + (lane & 7) * 8;
         const bool n_ok = n < N;                   // N % 8 == 0: a chunk is all in or out
-        const int wr = lane & 31;
-        const int wsw = (wr >> 1) & 15;
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i) {
-#pragma unroll
-            for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x16 &a = acc[i][j];
-                    u32x2 packed;
-                    packed[0] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(alpha * a[4 * g + 0])) |
-                                ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(alpha * a[4 * g + 1])) << 16);
-                    packed[1] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(alpha * a[4 * g + 2])) |
-                                ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(alpha * a[4 * g + 3])) << 16);
-                    const int slot8 = (8 * j + 2 * g + half) ^ wsw;
-                    *(u32x2 *)(epi + wr * 128 + slot8 * 8) = packed;
-                }
-            compiler_fence();
-            __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
-            compiler_fence();
-#pragma unroll
-            for (int it = 0; it < 32 / RPI; ++it) {
-                const int r = it * RPI + (lane >> 3);
-                const int sw = (r >> 1) & 15;
-                u32x4 v = *(const u32x4 *)(epi + r * 128 + ((ec ^ (sw >> 1)) << 4));
-                if (sw & 1) v = u32x4{v[2], v[3], v[0], v[1]};
-                const int ml = wm * C::WTM + i * 32 + r;
-                const uint32_t off = n_ok ? (uint32_t)(ml * N + n) * 2u : kOutOfRange;
-                __builtin_amdgcn_raw_buffer_store_b128(v, rd, off, 0, kStoreStreaming);
-            }
-            compiler_fence();
-        }
+        for (int i = 0; i < C::FM; ++i)
+            store_block_staged<C>(acc[i], alpha, epi, lane, rd, wm * C::WTM + i * 32, n, n_ok, N);
     };
 
     zero_acc();

@@ -8,6 +8,7 @@
 
 #include "gemm_kernel.hpp"
 #include "persistent_kernel.hpp"
+#include "shortk_kernel.hpp"
 
 namespace {
 
@@ -34,6 +35,8 @@ constexpr gemm_kernel_fn kernel_of()
 {
     if constexpr (C::SCHED == 3)
         return &sg::gemm_tn_persistent_kernel<C>;
+    else if constexpr (C::SCHED == 4)
+        return &sg::gemm_tn_shortk_kernel<C>;
     else
         return &sg::gemm_tn_kernel<C>;
 }
@@ -116,6 +119,8 @@ const Variant kVariants[] = {
     variant<sg::Cfg<128, 128, 32, 3, 2, 2, 0>>(),
     variant<sg::Cfg<128, 128, 32, 4, 2, 2, 0>>(),
     variant<sg::Cfg<128, 128, 32, 5, 2, 2, 0>>(),
+    // whole K extent in the ring, epilogue per row block (schedule 4, K <= S * BK)
+    variant<sg::Cfg<128, 128, 64, 2, 2, 2, 4>>(),
     // persistent workgroups, one ring across output tiles (schedule 3)
     variant<sg::Cfg<256, 256, 64, 2, 2, 4, 3>>(),
     variant<sg::Cfg<128, 128, 64, 2, 2, 2, 3>>(),
@@ -139,7 +144,7 @@ const Variant *find_variant(const sg_config *c)
 // Tile family by a wave-quantisation estimate: 256x256 workgroups run one per
 // CU, 128x128 ones do a quarter of the work at about 1.3x the cost per flop;
 // cost = rounds of 256 workgroups x per-workgroup work.  Large grids
-// (8192^3, 8000x7936x8200, 4096^3, 4096^2 x 128) pick 256x256x64, two
+// (8192^3, 8000x7936x8200, 4096^3) pick 256x256x64, two
 // stages, 8 waves, cute order.  Small or skinny grids pick 128x128x64 with
 // the stage count of the lesson's occupancy trade-off: three stages (96 KiB,
 // one workgroup per CU) when the grid is at most one workgroup per CU
@@ -147,6 +152,10 @@ const Variant *find_variant(const sg_config *c)
 // when K <= 1024 and there is no C operand, the persistent schedule, whose
 // ring runs on across output tiles (81920 x 256 x 256: -14 % time against
 // the tiled kernel; with long K loops the tiled kernel is 3-5 % faster).
+// Before all that: K <= 128 with more than one wave of 128x128 workgroups
+// and no C operand takes the short-K schedule, whose row-block epilogue
+// overlaps the write of D with the MFMAs (4096 x 4096 x 128: 10.4 us against
+// 11.0 for the tiled 256x256 kernel).
 const Variant *select_variant(int M, int N, int K, bool with_c)
 {
     const long long t256 = (long long)((M + 255) / 256) * ((N + 255) / 256);
@@ -154,7 +163,9 @@ const Variant *select_variant(int M, int N, int K, bool with_c)
     const double cost256 = (double)((t256 + 255) / 256) * 4.0;
     const double cost128 = (double)((t128 + 255) / 256) * 1.3;
     sg_config c;
-    if (cost256 <= cost128)
+    if (K <= 128 && t128 > 256 && !with_c)
+        c = sg_config{128, 128, 64, 2, 4, 4};
+    else if (cost256 <= cost128)
         c = sg_config{256, 256, 64, 2, 8, 1};
     else if (t128 <= 256)
         c = sg_config{128, 128, 64, 3, 4, 1};
@@ -211,8 +222,11 @@ sg_status run(const Variant *v, int M, int N, int K, float alpha, float beta, co
     const long long tiles = (long long)((M + v->cfg.tile_m - 1) / v->cfg.tile_m) *
                             ((N + v->cfg.tile_n - 1) / v->cfg.tile_n);
     if (tiles * v->threads >= (1LL << 32)) return SG_ERR_SHAPE;
-    // the persistent kernel has no C operand
-    if (v->cfg.schedule == 3 && beta != 0.0f) return SG_ERR_UNSUPPORTED;
+    // the persistent and short-K kernels have no C operand; the short-K
+    // kernel holds the whole K extent in its ring
+    if (v->cfg.schedule >= 3 && beta != 0.0f) return SG_ERR_UNSUPPORTED;
+    if (v->cfg.schedule == 4 && (long long)(K + v->cfg.tile_k - 1) / v->cfg.tile_k > v->cfg.stages)
+        return SG_ERR_UNSUPPORTED;
     // Rotate the K loop over 4 tile rows once the grid is more than one wave
     // of workgroups on the 256 CUs (measured: +14% at 8192^3, -2% at 4096^3
     // where all workgroups are resident and the operands fit in the 256 MB

@@ -105,6 +105,15 @@ def test_cfg_errors():
                               ctypes.byref(bad), None) == S.SG_ERR_UNSUPPORTED
     st, _ = _lib.sg_query_config(bad)
     assert st == S.SG_ERR_UNSUPPORTED
+    # the short-K schedule (4) holds the whole K extent in its ring: a longer
+    # K is refused before any HIP call (fake pointers never reach a launch)
+    for c in _lib.configs():
+        if c.schedule != 4:
+            continue
+        K = c.tile_k * c.stages + 8
+        st = L.gemm_fp16_tn_cfg(64, 64, K, 1.0, P, P + 0x1000000, P + 0x2000000,
+                                ctypes.byref(c), None)
+        assert st == S.SG_ERR_UNSUPPORTED, c
 
 
 def test_status_strings_are_stable():
@@ -196,6 +205,7 @@ def test_selection_returns_compiled_variants():
     assert _lib.sg_select_config(81920, 256, 256).as_tuple() == (128, 128, 64, 2, 4, 3)
     assert _lib.sg_select_config(2048, 2048, 2048).as_tuple() == (128, 128, 64, 3, 4, 1)
     assert _lib.sg_select_config(81920, 256, 4096).as_tuple() == (128, 128, 64, 2, 4, 1)
+    assert _lib.sg_select_config(4096, 4096, 128).as_tuple() == (128, 128, 64, 2, 4, 4)
 
 
 def _gpu_visible() -> bool:

@@ -82,6 +82,13 @@ def sampled_check(A, B, d_dev, alpha, label, seed=0):
 
 
 VARIANTS = [c.as_tuple() for c in sg.configs()]
+SHORTK = [c for c in VARIANTS if c[5] == 4]
+
+
+def runs(cfg, K):
+    """Whether a compiled variant takes this K: the short-K schedule (4)
+    needs the whole K extent in its ring (K <= stages * tile_k)."""
+    return cfg is None or cfg[5] != 4 or K <= cfg[2] * cfg[3]
 
 
 # ---------------------------------------------------------------------------
@@ -91,7 +98,8 @@ def test_square256_default_and_every_variant():
     A, B = inputs.workload("square256")
     full_check(A, B, label="square256 default")
     for cfg in VARIANTS:
-        full_check(A, B, config=cfg, label=f"square256 {cfg}")
+        if runs(cfg, 256):
+            full_check(A, B, config=cfg, label=f"square256 {cfg}")
 
 
 @pytest.mark.parametrize("shape", [(300, 264, 200), (257, 136, 40), (1, 8, 8), (129, 520, 1000),
@@ -100,13 +108,15 @@ def test_every_variant_on_ragged_shapes(shape):
     M, N, K = shape
     A, B = inputs.operands(M, N, K, 300 + M)
     for cfg in VARIANTS:
-        full_check(A, B, config=cfg, label=f"ragged {shape} {cfg}")
+        if runs(cfg, K):
+            full_check(A, B, config=cfg, label=f"ragged {shape} {cfg}")
 
 
 @pytest.mark.parametrize("cfg", [None, (128, 128, 32, 3, 4, 1), (256, 256, 32, 5, 8, 1),
                                  (256, 256, 64, 2, 8, 1), (256, 256, 32, 3, 8, 0),
                                  (128, 128, 64, 3, 4, 1), (256, 256, 64, 2, 8, 2),
-                                 (128, 128, 64, 2, 4, 3), (256, 256, 64, 2, 8, 3)])
+                                 (128, 128, 64, 2, 4, 3), (256, 256, 64, 2, 8, 3),
+                                 (128, 128, 64, 2, 4, 4)])
 def test_tiny_shape_grid(cfg):
     # every M, N and K tail against every tile boundary of the variant
     say(f"[case] tiny grid cfg={cfg}")
@@ -116,6 +126,8 @@ def test_tiny_shape_grid(cfg):
             for K in (8, 24, 40, 72, 136):
                 A = g.uniform(-1, 1, (M, K)).astype(np.float16)
                 B = g.uniform(-1, 1, (N, K)).astype(np.float16)
+                if not runs(cfg, K):
+                    continue
                 d = run_gemm(A, B, config=cfg).cpu().numpy()
                 rep = oracle.check(d, oracle.gemm_tn_f64(A, B), K)
                 assert rep.ok, (M, N, K, cfg, str(rep))
@@ -158,7 +170,7 @@ def test_persistent_workgroups_loop_over_tiles(shape):
         assert rep.ok, (cfg, str(rep))
 
 
-@pytest.mark.parametrize("cfg", [None] + PERSISTENT[:2])
+@pytest.mark.parametrize("cfg", [None] + PERSISTENT[:2] + SHORTK)
 def test_k_zero_every_schedule(cfg):
     say(f"[case] K=0 {cfg}")
     A = np.zeros((1100, 0), np.float16)
@@ -200,7 +212,9 @@ def test_empty_m_or_n_leaves_output_untouched():
                                        ((256, 256, 32, 4, 8, 0), (300, 264, 136)),
                                        ((256, 256, 64, 2, 8, 2), (300, 264, 136)),
                                        ((128, 128, 64, 2, 4, 3), (4200, 4104, 72)),
-                                       ((256, 256, 64, 2, 8, 3), (4200, 4104, 72))])
+                                       ((256, 256, 64, 2, 8, 3), (4200, 4104, 72)),
+                                       ((128, 128, 64, 2, 4, 4), (300, 264, 128)),
+                                       ((128, 128, 64, 2, 4, 4), (4200, 4104, 72))])
 def test_canary_guard_bands(cfg, shape):
     # D sits inside a larger buffer filled with a NaN pattern; nothing outside
     # D may change and every element of D must be written
@@ -328,7 +342,7 @@ def test_ksweep_every_stage_count(K):
     A, B = inputs.ksweep(K)
     a, b = to_dev(A), to_dev(B)
     for cfg in VARIANTS:
-        if cfg[:2] not in ((128, 128), (256, 256)):
+        if cfg[:2] not in ((128, 128), (256, 256)) or not runs(cfg, K):
             continue
         d = torch.full((2048, 2048), float("nan"), dtype=torch.float16, device=DEV)
         sg.gemm(a, b, out=d, config=cfg)
@@ -349,6 +363,24 @@ def test_tall_skinny_81920():
     for cfg in PERSISTENT:
         d = run_gemm(A, B, config=cfg)
         sampled_check(A, B, d, None, f"tall81920 {cfg}", seed=8)
+
+
+@pytest.mark.parametrize("shape", [(4096, 4096, 128), (1000, 1032, 120), (264, 8, 8), (520, 4104, 64)])
+def test_short_k_schedule(shape):
+    # whole K extent in the ring, epilogue per row block: K up to the ring,
+    # with M, N and K tails
+    M, N, K = shape
+    A, B = inputs.operands(M, N, K, 1300 + K, "normal")
+    alpha = float(np.float32(1.0 / math.sqrt(K)))
+    ref = oracle.gemm_tn_f64(A, B, alpha)
+    assert SHORTK
+    for cfg in SHORTK:
+        if not runs(cfg, K):
+            continue
+        say(f"[case] short-K {shape} {cfg}")
+        d = run_gemm(A, B, alpha=alpha, config=cfg).cpu().numpy()
+        rep = oracle.check(d, ref, K)
+        assert rep.ok, (cfg, str(rep))
 
 
 def test_attention_scores_persistent():
