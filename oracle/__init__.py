@@ -9,7 +9,8 @@ arithmetic.
 
 Contents:
   _native   fp16 codec, fp64 and exact (128-bit integer) GEMM evaluations,
-            written in plain C (oracle.c) and loaded with ctypes;
+            and the fp64 attention forward, written in plain C (oracle.c)
+            and loaded with ctypes;
   models    stage-count / LDS-footprint / occupancy model and the ring-buffer
             schedule simulator;
   check     the element-wise tolerance check.
@@ -19,7 +20,7 @@ docstring or source comment.  Parity is pinned by tests that check these
 functions against values the pages print, closed forms, brute force and an
 independent library routine, not against themselves.
 """
-from ._native import (build, f16_to_f64, f64_to_f16, gemm_tn_exact, gemm_tn_exact_beta,
+from ._native import (attention_f64, build, f16_to_f64, f64_to_f16, gemm_tn_exact, gemm_tn_exact_beta,
                       gemm_tn_f64, gemm_tn_f64_at, gemm_tn_f64_beta, gemm_tn_f64_rows,
                       num_threads)
 from .check import CheckReport, check, ulp16
@@ -29,7 +30,7 @@ from .models import (blocks_per_unit, lds_bytes, loosest_persistent_wait_counts,
                      simulate, simulate_loads)
 
 __all__ = [
-    "build", "f16_to_f64", "f64_to_f16", "gemm_tn_exact", "gemm_tn_exact_beta",
+    "attention_f64", "build", "f16_to_f64", "f64_to_f16", "gemm_tn_exact", "gemm_tn_exact_beta",
     "gemm_tn_f64", "gemm_tn_f64_beta",
     "gemm_tn_f64_at", "gemm_tn_f64_rows", "num_threads", "CheckReport", "check",
     "ulp16", "blocks_per_unit", "lds_bytes", "loosest_wait_counts", "minimum_stages",

@@ -73,6 +73,9 @@ def lib() -> ctypes.CDLL:
                                              ctypes.c_float, ctypes.c_float, u16p, u16p,
                                              ctypes.c_void_p, u16p]
         L.sgo_gemm_tn_exact_beta.restype = ctypes.c_int
+        L.sgo_attention_f64.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_float, u16p, u16p, u16p, u16p, ctypes.c_void_p]
+        L.sgo_attention_f64.restype = None
         L.sgo_num_threads.argtypes = []
         L.sgo_num_threads.restype = ctypes.c_int
         _lib = L
@@ -197,6 +200,32 @@ def gemm_tn_exact_beta(A, B, C, alpha: float = 1.0, beta: float = 0.0) -> np.nda
             raise ValueError(f"exact oracle refused the input (code {rc})")
     del keep
     return d.view(np.float16)
+
+
+def attention_f64(Q, K, V, alpha: float, with_bound: bool = False):
+    """O = RNE16(softmax(alpha * Q K^T) V), row-wise softmax, fp64 inside.
+
+    Q: (H, M, d) or (M, d); K, V: (H, N, d) or (N, d), fp16.  Returns O with
+    Q's shape (float16), and with `with_bound` also the per-element weight
+    sum_j p_j |v_jc| (float64)."""
+    q, k, v = _bits(Q), _bits(K), _bits(V)
+    squeeze = q.ndim == 2
+    if squeeze:
+        q, k, v = q[None], k[None], v[None]
+    H, M, d = q.shape
+    Hk, N, dk = k.shape
+    assert (Hk, dk) == (H, d) and v.shape == k.shape and N >= 1
+    q, k, v = (np.ascontiguousarray(x) for x in (q, k, v))
+    o = np.empty((H, M, d), np.uint16)
+    wb = np.empty((H, M, d), np.float64) if with_bound else None
+    if H and M and d:
+        lib().sgo_attention_f64(H, M, N, d, float(alpha), q, k, v, o,
+                                wb.ctypes.data if wb is not None else None)
+    o = o.view(np.float16)
+    if squeeze:
+        o = o[0]
+        wb = wb[0] if wb is not None else None
+    return (o, wb) if with_bound else o
 
 
 def num_threads() -> int:

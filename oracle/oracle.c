@@ -1,5 +1,6 @@
 /*
- * Plain CPU oracle for the half-precision TN GEMM  D = alpha * A * B^T.
+ * Plain CPU oracle for the half-precision TN GEMM  D = alpha * A * B^T, and
+ * for the attention forward O = softmax(alpha * Q K^T) V built on it.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing on the product path links, loads or
  * calls this file; only the test suite, the smoke check and the CPU-baseline
@@ -186,6 +187,59 @@ void sgo_gemm_tn_f64_rows(int N, int K, float alpha, const uint16_t *A,
             double s = dot_f64(A + (size_t)i * K, B + (size_t)j * K, K);
             Drows[(size_t)(i - r0) * N + j] = sgo_f64_to_f16(a64 * s);
         }
+}
+
+/* Attention forward of "CUDA operator notes 2", section "Softmax Attention":
+ * O = softmax(alpha * Q K^T) V with the softmax taken along each row, per head
+ * h of H.  Q is H x M x d, K and V are H x N x d, O is H x M x d, all
+ * row-major fp16.  For each output row: scores s_j = alpha * (q . k_j) in
+ * fp64 (products exact, sum in index order, then the fp32 alpha widened
+ * exactly), m = max_j s_j, w_j = exp(s_j - m), and
+ * O[c] = (sum_j w_j v_jc) / (sum_j w_j), rounded once to fp16.  When wbound is
+ * not NULL it receives, per output element, sum_j w_j |v_jc| / sum_j w_j: the
+ * weight of |V| behind that output, which the GPU tolerance uses.  N >= 1. */
+void sgo_attention_f64(int H, int M, int N, int d, float alpha, const uint16_t *Q,
+                       const uint16_t *K, const uint16_t *V, uint16_t *O, double *wbound)
+{
+    ensure_decode_table();
+    const double a64 = (double)alpha;
+    #pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)N);
+        double *num = (double *)malloc(sizeof(double) * (size_t)d);
+        double *wabs = (double *)malloc(sizeof(double) * (size_t)d);
+        #pragma omp for schedule(dynamic, 1) collapse(2)
+        for (int h = 0; h < H; ++h)
+            for (int i = 0; i < M; ++i) {
+                const uint16_t *q = Q + ((size_t)h * M + i) * d;
+                const uint16_t *kh = K + (size_t)h * N * d;
+                const uint16_t *vh = V + (size_t)h * N * d;
+                double m = -INFINITY;
+                for (int j = 0; j < N; ++j) {
+                    s[j] = a64 * dot_f64(q, kh + (size_t)j * d, d);
+                    if (s[j] > m) m = s[j];
+                }
+                double den = 0.0;
+                for (int c = 0; c < d; ++c) num[c] = wabs[c] = 0.0;
+                for (int j = 0; j < N; ++j) {
+                    const double w = exp(s[j] - m);
+                    den += w;
+                    for (int c = 0; c < d; ++c) {
+                        const double v = g_dec[vh[(size_t)j * d + c]];
+                        num[c] += w * v;
+                        wabs[c] += w * fabs(v);
+                    }
+                }
+                uint16_t *o = O + ((size_t)h * M + i) * d;
+                for (int c = 0; c < d; ++c) {
+                    o[c] = sgo_f64_to_f16(num[c] / den);
+                    if (wbound) wbound[((size_t)h * M + i) * d + c] = wabs[c] / den;
+                }
+            }
+        free(s);
+        free(num);
+        free(wabs);
+    }
 }
 
 int sgo_num_threads(void)
