@@ -163,6 +163,22 @@ int sg_pipeline_wait_count(int stages, int loads_per_stage, int ntile, int k);
 int sg_persistent_wait_count(int stages, int loads_per_stage, int stores_per_tile, int ntile,
                              int total, int q);
 
+/* Fused attention forward, "CUDA operator notes 2", section "Softmax
+ * Attention": O = softmax(alpha * Q K^T) V with the softmax along each row,
+ * for H independent heads.  Q is H x M x d, K and V are H x N x d, O is
+ * H x M x d; every head is row-major fp16 and the heads are stored one after
+ * another (head stride M * d or N * d elements).  The scores stay on chip:
+ * one pass over the keys with a running row maximum and sum (fp32), P V
+ * accumulated in fp32 from fp16 probabilities, O rounded once to fp16.
+ * alpha is fp32 (the page's 1/sqrt(d) is the caller's choice).
+ * Only d == 128 is compiled (SG_ERR_UNSUPPORTED otherwise).  H == 0 or
+ * M == 0: no work.  N == 0 with M > 0: SG_ERR_SHAPE (no keys to weight).
+ * Pointers: caller-owned device memory, 16-byte aligned (SG_ERR_ALIGN), O
+ * may not overlap Q, K or V (SG_ERR_ALIAS).  M, N <= 2^21.  Enqueues one
+ * kernel on `stream`; allocates and synchronises nothing. */
+sg_status attention_fp16_fwd(int H, int M, int N, int d, float alpha, const void *Q,
+                             const void *K, const void *V, void *O, void *stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *sg_status_string(sg_status status);
 

@@ -11,7 +11,8 @@ first call and a missing build raises.
 """
 from __future__ import annotations
 
-from ._lib import (SgConfig, SgConfigInfo, SgError, configs, gemm_fp16_tn, gemm_fp16_tn_alpha,
+from ._lib import (SgConfig, SgConfigInfo, SgError, attention_fp16_fwd, configs, gemm_fp16_tn,
+                   gemm_fp16_tn_alpha,
                    gemm_fp16_tn_alpha_beta, gemm_fp16_tn_cfg, sg_get_config, sg_minimum_stages, sg_num_configs,
                    sg_persistent_wait_count, sg_pipeline_wait_count, sg_query_config, sg_select_config,
                    sg_status_string)
@@ -62,8 +63,42 @@ def gemm(A, B, out=None, alpha: float | None = None, config=None, stream=None,
     return out
 
 
+def attention(Q, K, V, alpha: float | None = None, out=None, stream=None):
+    """O = softmax(alpha * Q K^T) V, softmax along each row, on the GPU.
+
+    Q: (H, M, d) or (M, d); K, V: (H, N, d) or (N, d); fp16 CUDA (HIP)
+    tensors, contiguous; d = 128.  alpha defaults to fp32(1 / sqrt(d)).
+    Returns O shaped like Q."""
+    import math
+
+    import torch
+
+    if Q.dtype != torch.float16 or K.dtype != torch.float16 or V.dtype != torch.float16:
+        raise TypeError("Q, K and V must be float16")
+    q3, k3, v3 = (x if x.dim() == 3 else x.unsqueeze(0) for x in (Q, K, V))
+    if q3.dim() != 3 or k3.shape != v3.shape or q3.shape[0] != k3.shape[0] \
+            or q3.shape[2] != k3.shape[2]:
+        raise ValueError(f"shapes {tuple(Q.shape)}, {tuple(K.shape)}, {tuple(V.shape)} do not match")
+    if not (Q.is_cuda and K.is_cuda and V.is_cuda):
+        raise ValueError("Q, K and V must be device tensors")
+    if not (Q.is_contiguous() and K.is_contiguous() and V.is_contiguous()):
+        raise ValueError("Q, K and V must be contiguous")
+    H, M, d = q3.shape
+    N = k3.shape[1]
+    if alpha is None:
+        alpha = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+    if out is None:
+        out = torch.empty_like(Q)
+    elif out.shape != Q.shape or out.dtype != torch.float16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float16 tensor shaped like Q")
+    s = (stream if stream is not None else torch.cuda.current_stream(Q.device)).cuda_stream
+    attention_fp16_fwd(H, M, N, d, float(alpha), Q.data_ptr(), K.data_ptr(), V.data_ptr(),
+                       out.data_ptr(), s)
+    return out
+
+
 __all__ = [
-    "gemm", "gemm_fp16_tn", "gemm_fp16_tn_alpha", "gemm_fp16_tn_alpha_beta", "gemm_fp16_tn_cfg",
+    "gemm", "attention", "attention_fp16_fwd", "gemm_fp16_tn", "gemm_fp16_tn_alpha", "gemm_fp16_tn_alpha_beta", "gemm_fp16_tn_cfg",
     "sg_select_config",
     "sg_num_configs", "sg_get_config", "sg_query_config", "sg_minimum_stages",
     "sg_pipeline_wait_count", "sg_persistent_wait_count", "sg_status_string", "configs", "SgConfig", "SgConfigInfo",

@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
         L.gemm_fp16_tn_alpha.restype = i
         L.gemm_fp16_tn_alpha_beta.argtypes = [i, i, i, f, f, vp, vp, vp, vp, vp]
         L.gemm_fp16_tn_alpha_beta.restype = i
+        L.attention_fp16_fwd.argtypes = [i, i, i, i, f, vp, vp, vp, vp, vp]
+        L.attention_fp16_fwd.restype = i
         L.gemm_fp16_tn_cfg.argtypes = [i, i, i, f, vp, vp, vp, ctypes.POINTER(SgConfig), vp]
         L.gemm_fp16_tn_cfg.restype = i
         L.sg_select_config.argtypes = [i, i, i, ctypes.POINTER(SgConfig)]
@@ -129,6 +131,12 @@ def gemm_fp16_tn_alpha_beta(M: int, N: int, K: int, alpha: float, beta: float, A
                             C: int, D: int, stream: int = 0) -> int:
     return _check(lib().gemm_fp16_tn_alpha_beta(M, N, K, alpha, beta, A, B, C, D, stream),
                   "gemm_fp16_tn_alpha_beta")
+
+
+def attention_fp16_fwd(H: int, M: int, N: int, d: int, alpha: float, Q: int, K: int, V: int,
+                       O: int, stream: int = 0) -> int:
+    return _check(lib().attention_fp16_fwd(H, M, N, d, alpha, Q, K, V, O, stream),
+                  "attention_fp16_fwd")
 
 
 def gemm_fp16_tn_cfg(M: int, N: int, K: int, alpha: float, A: int, B: int, D: int,

@@ -1,0 +1,278 @@
+// Fused attention forward O = softmax(alpha * Q K^T) V ("CUDA operator notes
+// 2", section "Softmax Attention": scores Q K^T / sqrt(d), a row-wise softmax,
+// then the product with V), for H independent heads with d = 128.
+//
+// The scores never leave the chip.  Each workgroup owns 128 query rows of one
+// head (4 waves, 32 rows each) and streams the head's keys in tiles of 64
+// through a two-slot LDS ring -- the stage-pipelined mainloop of "Lesson 6":
+// while tile j is consumed, tile j + 1's K rows arrive by LDS-DMA and its V
+// rows by ordinary loads -- and keeps a running row maximum m, row sum l and
+// output accumulator O (the online form of the softmax):
+//     S = Q K_j^T (MFMA, fp32), t = S * alpha * log2(e)
+//     m' = max(m, max_j t), O = O * 2^(m - m') + 2^(t - m') V_j, l likewise
+// and writes O / l once at the end.
+//
+// The P V product contracts over keys, which are rows of V, so each V tile is
+// written to LDS transposed (d x 64 keys) through registers, with the keys of
+// every 16-key group in the order the score accumulators hold them: the
+// fragment of probabilities a lane feeds to the MFMA then meets V values for
+// the same keys in the same order, without moving the probabilities.
+#pragma once
+
+#include "gemm_kernel.hpp"
+
+namespace sg {
+
+struct AttnCfg {
+    static constexpr int D = 128;                  // head dimension
+    static constexpr int BM = 128;                 // query rows per workgroup
+    static constexpr int BN = 64;                  // keys per tile
+    static constexpr int NW = 4;                   // waves, 32 query rows each
+    static constexpr int T = 64 * NW;
+    static constexpr int K_ROW = D * 2;            // 256-byte K rows
+    static constexpr int K_BYTES = BN * K_ROW;     // 16 KiB
+    static constexpr int VT_ROW = BN * 2;          // 128-byte V^T rows (one per d)
+    static constexpr int VT_BYTES = D * VT_ROW;    // 16 KiB
+    static constexpr int STAGE_BYTES = K_BYTES + VT_BYTES;
+    static constexpr int S = 2;                    // ring slots
+    static constexpr int LDS_BYTES = S * STAGE_BYTES;
+    static constexpr int KL = K_BYTES / (16 * T);  // K LDS-DMA loads per lane per tile
+    static_assert(KL * 16 * T == K_BYTES, "even K split");
+};
+
+// 16-byte chunk position of logical chunk c in K row r (16 chunks per row).
+__device__ __forceinline__ int k_chunk(int r, int c) { return c ^ (r & 15); }
+// 16-byte chunk position of logical chunk c in V^T row d (8 chunks per row).
+__device__ __forceinline__ int vt_chunk(int d, int c) { return c ^ ((d >> 1) & 7); }
+
+__global__ void __launch_bounds__(AttnCfg::T, 2)
+attention_fwd_kernel(const _Float16 *__restrict__ Q, const _Float16 *__restrict__ Kg,
+                     const _Float16 *__restrict__ V, _Float16 *__restrict__ O, int M, int N,
+                     float alpha)
+{
+    using C = AttnCfg;
+    __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int half = lane >> 5;
+    const int r32 = lane & 31;
+
+    const int row_blocks = (M + C::BM - 1) / C::BM;
+    const int h = blockIdx.x / row_blocks;
+    const int m0 = (blockIdx.x - h * row_blocks) * C::BM;
+    const int rows = (M - m0 < C::BM) ? (M - m0) : C::BM;
+    const _Float16 *qh = Q + ((size_t)h * M + m0) * C::D;
+    const _Float16 *kh = Kg + (size_t)h * N * C::D;
+    const _Float16 *vh = V + (size_t)h * N * C::D;
+    // buffer ranges cover only valid rows: rows past M or N read as zero
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qh, (uint32_t)rows * C::D * 2u);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kh, (uint32_t)N * C::D * 2u);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vh, (uint32_t)N * C::D * 2u);
+    const int ntiles = (N + C::BN - 1) / C::BN;
+
+    // ---- Q fragments of this wave's 32 rows, all of d, kept in VGPRs:
+    // step s holds Q[row][16 s + 8 half .. + 7]
+    const int qrow = wave * 32 + r32;
+    f16x8 qf[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+        qf[s] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rq, (uint32_t)(qrow * C::D + 16 * s + 8 * half) * 2u, 0, 0));
+
+    // ---- K tile j into slot: LDS-DMA, 1 KiB per wave instruction = 4 rows
+    // of 256 bytes; lane -> row lane / 16, position lane % 16, which holds
+    // logical chunk k_chunk(row, position) (the swizzle is its own inverse).
+    auto issue_k = [&](int j, int slot) {
+        char *base = smem + slot * C::STAGE_BYTES;
+#pragma unroll
+        for (int i = 0; i < C::KL; ++i) {
+            const int r = (i * C::NW + wave) * 4 + (lane >> 4);   // row within the tile
+            const int c = k_chunk(r, lane & 15);
+            const uint32_t off = (uint32_t)((j * C::BN + r) * C::D + c * 8) * 2u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rk, (__attribute__((address_space(3))) void *)(base + (i * C::NW + wave) * 1024),
+                16, off, 0, 0, 0);
+        }
+    };
+    // ---- V tile j: thread t loads keys 4 q4 .. 4 q4 + 3 (q4 = t % 16) of
+    // columns 8 dg .. 8 dg + 7 (dg = t / 16) into VGPRs ...
+    const int q4 = threadIdx.x & 15;
+    const int dg = threadIdx.x >> 4;
+    f16x8 vreg[4];
+    auto load_v = [&](int j) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            vreg[kk] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                                     rv, (uint32_t)((j * C::BN + 4 * q4 + kk) * C::D + 8 * dg) * 2u,
+                                                     0, 0));
+    };
+    // ... and writes them transposed: V^T row d gets these 4 keys as one
+    // 8-byte piece.  Within each 16-key group the order is keys
+    // 0-3, 8-11, 4-7, 12-15, so 16-byte logical chunk 2 G + hh of a row holds
+    // keys 16 G + {4 hh .. 4 hh + 3, 8 + 4 hh .. 8 + 4 hh + 3}.
+    auto write_vt = [&](int slot) {
+        char *base = smem + slot * C::STAGE_BYTES + C::K_BYTES;
+        const int G = q4 >> 2;
+        const int qp = ((q4 & 1) << 1) | ((q4 >> 1) & 1);   // 0,1,2,3 -> 0,2,1,3
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        u32x4 w[4];                                    // key kk's 8 values as 4 words
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) w[kk] = __builtin_bit_cast(u32x4, vreg[kk]);
+#pragma unroll
+        for (int dd = 0; dd < 8; ++dd) {
+            const int d = 8 * dg + dd;
+            const int sh = (dd & 1) * 16;              // column dd: half (dd & 1) of word dd / 2
+            u32x2 piece;
+            piece[0] = ((w[0][dd >> 1] >> sh) & 0xffffu) | (((w[1][dd >> 1] >> sh) & 0xffffu) << 16);
+            piece[1] = ((w[2][dd >> 1] >> sh) & 0xffffu) | (((w[3][dd >> 1] >> sh) & 0xffffu) << 16);
+            const int off = d * C::VT_ROW + (vt_chunk(d, 2 * G + (qp >> 1)) << 4) + ((qp & 1) << 3);
+            *(u32x2 *)(base + off) = piece;
+        }
+    };
+
+    auto barrier = [&]() {
+        compiler_fence();
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+        __builtin_amdgcn_s_barrier();
+        compiler_fence();
+    };
+
+    // ---- prologue: tile 0
+    issue_k(0, 0);
+    load_v(0);
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+    compiler_fence();
+    // the Q fragments count as produced here, after the wait: otherwise the
+    // compiler sinks their loads towards the loop and waits for them (and,
+    // vmcnt being in order, for the next tile's loads) inside every iteration
+#pragma unroll
+    for (int s = 0; s < 8; ++s) asm volatile("" : "+v"(qf[s]));
+    write_vt(0);
+    barrier();
+
+    const float c2 = alpha * 1.4426950408889634f;     // scores to base-2 exponents
+    float mrow = -__builtin_inff();                    // running max of t (row-wide)
+    float lsum = 0.0f;                                 // running sum, this lane's keys
+    f32x16 oacc[4];                                    // O[row][32 c + 8 g + 4 half + e]
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[c][e] = 0.0f;
+
+#pragma unroll 1
+    for (int j = 0; j < ntiles; ++j) {
+        const int slot = j & 1;
+        const bool more = j + 1 < ntiles;
+        if (more) {                                    // refill the other slot (read last in step j - 1)
+            issue_k(j + 1, slot ^ 1);
+            load_v(j + 1);
+        }
+        const char *kbase = smem + slot * C::STAGE_BYTES;
+        const char *vbase = kbase + C::K_BYTES;
+
+        // S = Q K_j^T: lane holds S[row][32 b + 8 g + 4 half + e] in sacc[b][4 g + e]
+        f32x16 sacc[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) sacc[b][e] = 0.0f;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const int key = 32 * b + r32;
+                const f16x8 kf = *(const f16x8 *)(kbase + key * C::K_ROW +
+                                                  (k_chunk(key, 2 * s + half) << 4));
+                sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[s], sacc[b], 0, 0, 0);
+            }
+        }
+
+        // online softmax for this lane's row (its keys; the partner lane
+        // lane ^ 32 holds the rest of the row)
+        const int kvalid = N - j * C::BN;              // keys of this tile below N
+        float tmax = -__builtin_inff();
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int key = 32 * b + 8 * (e >> 2) + 4 * half + (e & 3);
+                const float t = (key < kvalid) ? sacc[b][e] * c2 : -__builtin_inff();
+                sacc[b][e] = t;
+                tmax = __builtin_fmaxf(tmax, t);
+            }
+        const float other = __builtin_bit_cast(
+            float, __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __builtin_bit_cast(int, tmax)));
+        tmax = __builtin_fmaxf(tmax, other);
+        const float mnew = __builtin_fmaxf(mrow, tmax);   // finite: every tile has a key below N
+        const float scale = __builtin_amdgcn_exp2f(mrow - mnew);
+        mrow = mnew;
+        float psum = 0.0f;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float p = __builtin_amdgcn_exp2f(sacc[b][e] - mnew);
+                sacc[b][e] = p;
+                psum += p;
+            }
+        lsum = lsum * scale + psum;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) oacc[c][e] *= scale;
+
+        // O += P V_j: K step (b, t) covers keys 32 b + 16 t + {0..15}; this
+        // lane's 8 probabilities are sacc[b][8 t .. 8 t + 7] (keys
+        // 16 G + 4 half + {0..3} and 16 G + 8 + 4 half + {0..3}, G = 2 b + t),
+        // matched by logical V^T chunk 2 G + half.
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                f16x8 pf;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pf[e] = (_Float16)sacc[b][8 * t + e];
+                const int G = 2 * b + t;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int d = 32 * c + r32;
+                    const f16x8 vf = *(const f16x8 *)(vbase + d * C::VT_ROW +
+                                                      (vt_chunk(d, 2 * G + half) << 4));
+                    oacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf, oacc[c], 0, 0, 0);
+                }
+            }
+
+        if (more) {
+            // tile j + 1: V rows have arrived (and the K DMA); write V^T
+            compiler_fence();
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+            compiler_fence();
+            write_vt(slot ^ 1);
+        }
+        barrier();                                     // RAW for tile j + 1, WAR for slot
+    }
+
+    // ---- O / l, one rounding to fp16; lane stores 4 consecutive halves per
+    // (c, g); rows past M fall outside the buffer range and are dropped
+    const float lother = __builtin_bit_cast(
+        float, __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __builtin_bit_cast(int, lsum)));
+    const float inv = 1.0f / (lsum + lother);
+    const __amdgpu_buffer_rsrc_t ro =
+        make_rsrc(O + ((size_t)h * M + m0) * C::D, (uint32_t)rows * C::D * 2u);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            u32x2 packed;
+            packed[0] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(oacc[c][4 * g + 0] * inv)) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(oacc[c][4 * g + 1] * inv)) << 16);
+            packed[1] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(oacc[c][4 * g + 2] * inv)) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(oacc[c][4 * g + 3] * inv)) << 16);
+            const uint32_t off = (uint32_t)(qrow * C::D + 32 * c + 8 * g + 4 * half) * 2u;
+            __builtin_amdgcn_raw_buffer_store_b64(packed, ro, off, 0, 0);
+        }
+}
+
+}  // namespace sg

@@ -17,7 +17,7 @@ S = _lib
 
 def test_every_declared_symbol_is_exported():
     declared = _lib.header_functions()
-    assert len(declared) == 12
+    assert len(declared) == 13
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
@@ -114,6 +114,25 @@ def test_cfg_errors():
         st = L.gemm_fp16_tn_cfg(64, 64, K, 1.0, P, P + 0x1000000, P + 0x2000000,
                                 ctypes.byref(c), None)
         assert st == S.SG_ERR_UNSUPPORTED, c
+
+
+@pytest.mark.parametrize("args,status", [
+    ((-1, 8, 8, 128, P, P + 0x100000, P + 0x200000, P + 0x300000), S.SG_ERR_SHAPE),
+    ((1, 8, 8, 64, P, P + 0x100000, P + 0x200000, P + 0x300000), S.SG_ERR_UNSUPPORTED),
+    ((1, 8, 0, 128, P, P + 0x100000, P + 0x200000, P + 0x300000), S.SG_ERR_SHAPE),
+    ((1, 8, 8, 128, 0, P + 0x100000, P + 0x200000, P + 0x300000), S.SG_ERR_NULL),
+    ((1, 8, 8, 128, P, P + 0x100000, P + 0x200008, P + 0x300000), S.SG_ERR_ALIGN),
+    ((1, 8, 8, 128, P, P + 0x100000, P + 0x200000, P + 0x400), S.SG_ERR_ALIAS),   # O overlaps Q
+    ((1, 8, 8, 128, P, P + 0x100000, P + 0x200000, P + 0x200100), S.SG_ERR_ALIAS),  # O overlaps V
+    ((1, 8, (1 << 21) + 8, 128, P, P + (1 << 32), P + (1 << 33), P + (1 << 34)), S.SG_ERR_SHAPE),
+])
+def test_attention_argument_errors(args, status):
+    _must_be_rejected(status)
+    H, M, N, d, q, k, v, o = args
+    assert L.attention_fp16_fwd(H, M, N, d, 0.1, q, k, v, o, None) == status
+    # no work at all: H == 0 or M == 0 succeeds without touching anything
+    assert L.attention_fp16_fwd(0, 8, 8, 128, 0.1, P, P, P, P, None) == S.SG_OK
+    assert L.attention_fp16_fwd(2, 0, 8, 128, 0.1, P, P, P, P, None) == S.SG_OK
 
 
 def test_status_strings_are_stable():
