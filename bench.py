@@ -223,6 +223,44 @@ def mode_ksweep(args) -> int:
     return 0
 
 
+def mode_attention(args) -> int:
+    """The fused attention forward O = softmax(alpha Q K^T) V on H heads of
+    the attention-score shape (M = N = 4096, d = 128, N(0,1) inputs), next to
+    the unfused route on the same GPU: this library's GEMM for the scores,
+    then torch's softmax and batched product (one JSON line per head count)."""
+    import numpy as np
+    import torch
+
+    import stage_pipelined_mainloop_amd as sg
+    from stage_pipelined_mainloop_amd import inputs
+    M, N, d = 4096, 4096, 128
+    alpha = float(np.float32(1.0 / math.sqrt(d)))
+    for H in (1, args.heads):
+        q = torch.from_numpy(np.stack([inputs.matrix(M, d, 7000 + 3 * h, "normal") for h in range(H)])).cuda()
+        k = torch.from_numpy(np.stack([inputs.matrix(N, d, 7001 + 3 * h, "normal") for h in range(H)])).cuda()
+        v = torch.from_numpy(np.stack([inputs.matrix(N, d, 7002 + 3 * h, "normal") for h in range(H)])).cuda()
+        o = torch.empty_like(q)
+        fused = time_launches(lambda: sg.attention(q, k, v, alpha=alpha, out=o), args.steps, args.warmup)
+        s = torch.empty((H, M, N), dtype=torch.float16, device="cuda")
+
+        def unfused():
+            for h in range(H):
+                sg.gemm(q[h], k[h], out=s[h], alpha=alpha)
+            p = torch.softmax(s.float(), dim=-1).half()
+            return torch.bmm(p, v)
+        ref_ms = time_launches(unfused, max(3, args.steps // 5), 2)
+        flops = 4.0 * H * M * N * d
+        tf = flops / (fused / 1e3) / 1e12
+        print(json.dumps({"mode": "attention", "metric": "fused attention forward TFLOP/s (4 H M N d)",
+                          "heads": H, "M": M, "N": N, "d": d, "ms": round(fused, 4),
+                          "tflops": round(tf, 1),
+                          "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_TFLOPS,
+                                       "unit": "TFLOP/s", "frac": round(tf / PEAK_TFLOPS, 4)},
+                          "unfused_ms": round(ref_ms, 4),
+                          "unfused": "library GEMM for S, torch softmax (fp32) and bmm"}), flush=True)
+    return 0
+
+
 def mode_calibrate_copy(args) -> int:
     """A plain device copy of known size, for scaling the FETCH_SIZE and
     WRITE_SIZE counters: each launch reads and writes exactly 512 MiB."""
@@ -240,7 +278,7 @@ def mode_calibrate_copy(args) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--mode", default="bench",
-                    choices=["bench", "variants", "ksweep", "calibrate_copy"])
+                    choices=["bench", "variants", "ksweep", "calibrate_copy", "attention"])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
@@ -249,6 +287,7 @@ def main() -> int:
                     help="explicit variant tile_m,tile_n,tile_k,stages,waves,schedule")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--heads", type=int, default=16, help="heads for --mode attention")
     ap.add_argument("--cold", action="store_true",
                     help="also time single launches after a 512 MiB cache flush")
     args = ap.parse_args()
@@ -264,6 +303,8 @@ def main() -> int:
         return mode_ksweep(args)
     if args.mode == "calibrate_copy":
         return mode_calibrate_copy(args)
+    if args.mode == "attention":
+        return mode_attention(args)
 
     import numpy as np
     import torch
