@@ -34,10 +34,15 @@ HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 
 
+# the sources that decide which GEMM kernel runs and what it does (the
+# attention forward and the measurement probe are separate sources)
+GEMM_SOURCES = ("gemm_kernel.hpp", "persistent_kernel.hpp", "shortk_kernel.hpp", "stagegemm.hip")
+
+
 def kernel_source_sha() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "stage_pipelined_mainloop_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in GEMM_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]

@@ -30,7 +30,7 @@ FLAGS = [
 
 
 def sources() -> list[str]:
-    return [os.path.join(CSRC, "stagegemm.hip")]
+    return [os.path.join(CSRC, "stagegemm.hip"), os.path.join(CSRC, "attention.hip")]
 
 
 def probe_sources() -> list[str]:

@@ -6,11 +6,14 @@
 // head (4 waves, 32 rows each) and streams the head's keys in tiles of 64
 // through a two-slot LDS ring -- the stage-pipelined mainloop of "Lesson 6":
 // while tile j is consumed, tile j + 1's K rows arrive by LDS-DMA and its V
-// rows by ordinary loads -- and keeps a running row maximum m, row sum l and
-// output accumulator O (the online form of the softmax):
+// rows by ordinary loads -- and keeps a reference exponent m, a row sum l
+// and an output accumulator O (the online form of the softmax):
 //     S = Q K_j^T (MFMA, fp32), t = S * alpha * log2(e)
-//     m' = max(m, max_j t), O = O * 2^(m - m') + 2^(t - m') V_j, l likewise
-// and writes O / l once at the end.
+//     P = 2^(t - m), O += P V_j, l += sum P
+// and writes O / l once at the end.  The quotient does not depend on m, so m
+// only has to keep 2^(t - m) in range: it is raised (and O, l rescaled by
+// 2^(m - m')) when a row's tile maximum exceeds m by more than TAU, not on
+// every increase.  Probabilities then stay below 2^TAU, well inside fp16.
 //
 // The P V product contracts over keys, which are rows of V, so each V tile is
 // written to LDS transposed (d x 64 keys) through registers, with the keys of
@@ -38,6 +41,7 @@ struct AttnCfg {
     static constexpr int LDS_BYTES = S * STAGE_BYTES;
     static constexpr int KL = K_BYTES / (16 * T);  // K LDS-DMA loads per lane per tile
     static_assert(KL * 16 * T == K_BYTES, "even K split");
+    static constexpr float TAU = 8.0f;             // headroom of 2^(t - m), in exponent units
 };
 
 // 16-byte chunk position of logical chunk c in K row r (16 chunks per row).
@@ -45,6 +49,8 @@ __device__ __forceinline__ int k_chunk(int r, int c) { return c ^ (r & 15); }
 // 16-byte chunk position of logical chunk c in V^T row d (8 chunks per row).
 __device__ __forceinline__ int vt_chunk(int d, int c) { return c ^ ((d >> 1) & 7); }
 
+// NEG: alpha < 0, so the largest scaled score comes from the smallest score.
+template <bool NEG>
 __global__ void __launch_bounds__(AttnCfg::T, 2)
 attention_fwd_kernel(const _Float16 *__restrict__ Q, const _Float16 *__restrict__ Kg,
                      const _Float16 *__restrict__ V, _Float16 *__restrict__ O, int M, int N,
@@ -153,8 +159,11 @@ attention_fwd_kernel(const _Float16 *__restrict__ Q, const _Float16 *__restrict_
     barrier();
 
     const float c2 = alpha * 1.4426950408889634f;     // scores to base-2 exponents
-    float mrow = -__builtin_inff();                    // running max of t (row-wide)
+    float mref = -__builtin_inff();                    // reference exponent m (row-wide)
     float lsum = 0.0f;                                 // running sum, this lane's keys
+    // extreme of the raw scores that gives the largest t, and its identity
+    auto ext = [](float a, float b) { return NEG ? __builtin_fminf(a, b) : __builtin_fmaxf(a, b); };
+    const float none = NEG ? __builtin_inff() : -__builtin_inff();
     f32x16 oacc[4];                                    // O[row][32 c + 8 g + 4 half + e]
 #pragma unroll
     for (int c = 0; c < 4; ++c)
@@ -190,38 +199,60 @@ attention_fwd_kernel(const _Float16 *__restrict__ Q, const _Float16 *__restrict_
         }
 
         // online softmax for this lane's row (its keys; the partner lane
-        // lane ^ 32 holds the rest of the row)
+        // lane ^ 32 holds the rest of the row).  Keys past N exist only in
+        // the last tile.
         const int kvalid = N - j * C::BN;              // keys of this tile below N
-        float tmax = -__builtin_inff();
+        const bool ragged = kvalid < C::BN;            // uniform
+        auto key_of = [&](int b, int e) { return 32 * b + 8 * (e >> 2) + 4 * half + (e & 3); };
+        if (ragged) {
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    if (key_of(b, e) >= kvalid) sacc[b][e] = none;
+        }
+        float sx = none;
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int key = 32 * b + 8 * (e >> 2) + 4 * half + (e & 3);
-                const float t = (key < kvalid) ? sacc[b][e] * c2 : -__builtin_inff();
-                sacc[b][e] = t;
-                tmax = __builtin_fmaxf(tmax, t);
-            }
-        const float other = __builtin_bit_cast(
-            float, __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __builtin_bit_cast(int, tmax)));
-        tmax = __builtin_fmaxf(tmax, other);
-        const float mnew = __builtin_fmaxf(mrow, tmax);   // finite: every tile has a key below N
-        const float scale = __builtin_amdgcn_exp2f(mrow - mnew);
-        mrow = mnew;
+            for (int e = 0; e < 16; ++e) sx = ext(sx, sacc[b][e]);
+        sx = ext(sx, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                                                   (lane ^ 32) << 2, __builtin_bit_cast(int, sx))));
+        // largest t of the row in this tile (finite: the tile has a key below
+        // N); rounding is monotonic, so this is the largest rounded product
+        const float tmax = sx * c2;
+        const bool raise = tmax > mref + C::TAU;
+        if (__builtin_amdgcn_ballot_w64(raise)) {      // uniform: some row of the wave
+            const float mnew = raise ? tmax : mref;
+            const float scale = __builtin_amdgcn_exp2f(mref - mnew);   // 0 on the first tile
+            mref = mnew;
+            lsum *= scale;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) oacc[c][e] *= scale;
+        }
+        const float negm = -mref;
         float psum = 0.0f;
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const float p = __builtin_amdgcn_exp2f(sacc[b][e] - mnew);
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[b][e], c2, negm));
                 sacc[b][e] = p;
                 psum += p;
             }
-        lsum = lsum * scale + psum;
+        if (ragged) {                                  // alpha = 0 makes the masked t NaN
+            psum = 0.0f;
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+            for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) oacc[c][e] *= scale;
+                for (int e = 0; e < 16; ++e) {
+                    if (key_of(b, e) >= kvalid) sacc[b][e] = 0.0f;
+                    psum += sacc[b][e];
+                }
+        }
+        lsum += psum;
 
         // O += P V_j: K step (b, t) covers keys 32 b + 16 t + {0..15}; this
         // lane's 8 probabilities are sacc[b][8 t .. 8 t + 7] (keys

@@ -9,7 +9,6 @@
 #include "gemm_kernel.hpp"
 #include "persistent_kernel.hpp"
 #include "shortk_kernel.hpp"
-#include "attention_kernel.hpp"
 
 namespace {
 
@@ -344,41 +343,6 @@ int sg_pipeline_wait_count(int stages, int loads_per_stage, int ntile, int k)
 {
     if (stages < 2 || loads_per_stage < 1 || ntile < 1 || k < 0 || k >= ntile) return -1;
     return sg::pipeline_wait_count(stages, loads_per_stage, ntile, k);
-}
-
-sg_status attention_fp16_fwd(int H, int M, int N, int d, float alpha, const void *Q,
-                             const void *K, const void *V, void *O, void *stream)
-{
-    if (H < 0 || M < 0 || N < 0 || d < 0) return SG_ERR_SHAPE;
-    if (H == 0 || M == 0) return SG_OK;
-    if (d != sg::AttnCfg::D) return SG_ERR_UNSUPPORTED;
-    if (N == 0) return SG_ERR_SHAPE;                    // softmax over no keys
-    if (!Q || !K || !V || !O) return SG_ERR_NULL;
-    if (N > (1 << 21) || M > (1 << 21)) return SG_ERR_SHAPE;
-    if ((long long)H * M * d >= (1LL << 40) || (long long)H * N * d >= (1LL << 40))
-        return SG_ERR_SHAPE;
-    const uintptr_t all = reinterpret_cast<uintptr_t>(Q) | reinterpret_cast<uintptr_t>(K) |
-                          reinterpret_cast<uintptr_t>(V) | reinterpret_cast<uintptr_t>(O);
-    if (all & 15) return SG_ERR_ALIGN;
-    const size_t qbytes = (size_t)H * M * d * 2, kvbytes = (size_t)H * N * d * 2;
-    if (overlaps(O, qbytes, Q, qbytes) || overlaps(O, qbytes, K, kvbytes) ||
-        overlaps(O, qbytes, V, kvbytes))
-        return SG_ERR_ALIAS;
-    const long long blocks = (long long)H * ((M + sg::AttnCfg::BM - 1) / sg::AttnCfg::BM);
-    if (blocks >= (1LL << 31)) return SG_ERR_SHAPE;
-    typedef void (*attn_fn)(const _Float16 *, const _Float16 *, const _Float16 *, _Float16 *,
-                            int, int, float);
-    const attn_fn kernel = &sg::attention_fwd_kernel;   // fails to compile on drift
-    const _Float16 *q = static_cast<const _Float16 *>(Q);
-    const _Float16 *k = static_cast<const _Float16 *>(K);
-    const _Float16 *v = static_cast<const _Float16 *>(V);
-    _Float16 *o = static_cast<_Float16 *>(O);
-    void *args[] = {&q, &k, &v, &o, &M, &N, &alpha};
-    static_assert(sizeof(args) / sizeof(args[0]) == 7, "one entry per kernel parameter");
-    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(kernel),
-                                         dim3((unsigned)blocks), dim3(sg::AttnCfg::T), args, 0,
-                                         static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? SG_OK : SG_ERR_HIP;
 }
 
 int sg_persistent_wait_count(int stages, int loads_per_stage, int stores_per_tile, int ntile,

@@ -81,6 +81,24 @@ def test_flat_and_sharp_softmax(scale):
     check(Q, K, V, float(np.float32(scale)), f"scale {scale}")
 
 
+@pytest.mark.parametrize("alpha,N", [(-0.0884, 700), (-1.5, 130), (0.0, 100), (-0.0, 1)])
+def test_negative_and_zero_alpha(alpha, N):
+    # alpha < 0: the largest scaled score comes from the smallest score;
+    # alpha = 0 with a ragged last key tile: uniform weights over the N keys
+    Q, K, V = qkv(2, 160, N, 4111 + N)
+    check(Q, K, V, float(np.float32(alpha)), f"alpha {alpha} N={N}")
+
+
+@pytest.mark.parametrize("top", [4.0, 30.0])
+def test_growing_scores(top):
+    # key rows scaled up along the sequence, so a row's maximum keeps rising
+    # from tile to tile: by less than the rescale threshold (top 4) or far
+    # beyond it (top 30), both with and without a rescale of O
+    Q, K, V = qkv(1, 256, 1500, 4113 + int(top))
+    K = (K.astype(np.float64) * np.linspace(1.0, top, 1500)[None, :, None]).astype(np.float16)
+    check(Q, K, V, float(np.float32(1.0 / math.sqrt(128))), f"growing to x{top}")
+
+
 def test_attention_config_full():
     # the attention-score workload's Q and K (4096 x 128, N(0,1)) with a V of
     # the same shape, alpha = fp32(1/sqrt(128)); every output against the oracle
