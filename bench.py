@@ -245,7 +245,20 @@ def mode_attention(args) -> int:
         k = torch.from_numpy(np.stack([inputs.matrix(N, d, 7001 + 3 * h, "normal") for h in range(H)])).cuda()
         v = torch.from_numpy(np.stack([inputs.matrix(N, d, 7002 + 3 * h, "normal") for h in range(H)])).cuda()
         o = torch.empty_like(q)
-        fused = time_launches(lambda: sg.attention(q, k, v, alpha=alpha, out=o), args.steps, args.warmup)
+        splits = sg.attention_fp16_splits(H, M, N, d)
+        ws = torch.empty(max(sg.attention_fp16_workspace_bytes(H, M, N, d, splits), 16),
+                         dtype=torch.uint8, device="cuda")
+        stream = torch.cuda.current_stream().cuda_stream
+        ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr())
+
+        def fused_call(sp):
+            # the C entry directly: Python-side checks would cost more than
+            # the kernels at one head
+            return lambda: sg.attention_fp16_fwd_split(H, M, N, d, alpha, *ptrs, sp, ws.data_ptr(),
+                                                       ws.numel(), stream)
+        warm = max(args.warmup, 30)
+        fused = time_launches(fused_call(splits), args.steps, warm)
+        unsplit = time_launches(fused_call(1), args.steps, warm) if splits > 1 else fused
         s = torch.empty((H, M, N), dtype=torch.float16, device="cuda")
 
         def unfused():
@@ -257,7 +270,8 @@ def mode_attention(args) -> int:
         flops = 4.0 * H * M * N * d
         tf = flops / (fused / 1e3) / 1e12
         print(json.dumps({"mode": "attention", "metric": "fused attention forward TFLOP/s (4 H M N d)",
-                          "heads": H, "M": M, "N": N, "d": d, "ms": round(fused, 4),
+                          "heads": H, "M": M, "N": N, "d": d, "splits": splits, "ms": round(fused, 4),
+                          "ms_one_split": round(unsplit, 4),
                           "tflops": round(tf, 1),
                           "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_TFLOPS,
                                        "unit": "TFLOP/s", "frac": round(tf / PEAK_TFLOPS, 4)},

@@ -44,6 +44,8 @@
 #ifndef STAGEGEMM_H
 #define STAGEGEMM_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -178,6 +180,37 @@ int sg_persistent_wait_count(int stages, int loads_per_stage, int stores_per_til
  * kernel on `stream`; allocates and synchronises nothing. */
 sg_status attention_fp16_fwd(int H, int M, int N, int d, float alpha, const void *Q,
                              const void *K, const void *V, void *O, void *stream);
+
+/* Split-key form of attention_fp16_fwd, for grids too small to fill the
+ * device (one head of 4096 queries is 32 workgroups).  The keys of each head
+ * are cut into `splits` contiguous runs of 64-key tiles (at most one run per
+ * tile: a larger count is lowered to the number of key tiles); each run
+ * yields an unnormalised partial of O with its own reference exponent and
+ * row sum, written to `workspace` in fp32, and a second kernel merges the
+ * runs of every row with the same online-softmax identity ("CUDA operator
+ * notes 2", section "Softmax Attention"; the softmax does not depend on the
+ * constant subtracted before the exponential).  Same arguments, layouts and
+ * errors as attention_fp16_fwd, plus: splits >= 1 (SG_ERR_SHAPE otherwise);
+ * splits == 1 needs no workspace and is attention_fp16_fwd.  For splits > 1,
+ * `workspace` is caller-owned device memory of at least
+ * attention_fp16_workspace_bytes(H, M, N, d, splits) bytes (SG_ERR_SHAPE if
+ * smaller, SG_ERR_NULL if null), 16-byte aligned (SG_ERR_ALIGN), not
+ * overlapping Q, K, V or O (SG_ERR_ALIAS); its contents on entry do not
+ * matter and are scratch afterwards.  Enqueues two kernels on `stream`;
+ * calls that share a workspace must not overlap in time. */
+sg_status attention_fp16_fwd_split(int H, int M, int N, int d, float alpha, const void *Q,
+                                   const void *K, const void *V, void *O, int splits,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace attention_fp16_fwd_split needs: H * s * M * (d + 2) * 4
+ * with s = min(splits, key tiles); 0 when s <= 1 or the sizes are invalid. */
+size_t attention_fp16_workspace_bytes(int H, int M, int N, int d, int splits);
+
+/* The split count this library would use on the current device: 1 when
+ * H * ceil(M / 128) workgroups already reach two per compute unit, otherwise
+ * enough splits for that, with at least eight key tiles each.  -1 for invalid
+ * sizes (d != 128 included) or a failed device query. */
+int attention_fp16_splits(int H, int M, int N, int d);
 
 /* Human-readable name of a status code (static storage). */
 const char *sg_status_string(sg_status status);

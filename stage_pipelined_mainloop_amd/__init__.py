@@ -11,7 +11,8 @@ first call and a missing build raises.
 """
 from __future__ import annotations
 
-from ._lib import (SgConfig, SgConfigInfo, SgError, attention_fp16_fwd, configs, gemm_fp16_tn,
+from ._lib import (SgConfig, SgConfigInfo, SgError, attention_fp16_fwd, attention_fp16_fwd_split,
+                   attention_fp16_splits, attention_fp16_workspace_bytes, configs, gemm_fp16_tn,
                    gemm_fp16_tn_alpha,
                    gemm_fp16_tn_alpha_beta, gemm_fp16_tn_cfg, sg_get_config, sg_minimum_stages, sg_num_configs,
                    sg_persistent_wait_count, sg_pipeline_wait_count, sg_query_config, sg_select_config,
@@ -63,11 +64,16 @@ def gemm(A, B, out=None, alpha: float | None = None, config=None, stream=None,
     return out
 
 
-def attention(Q, K, V, alpha: float | None = None, out=None, stream=None):
+def attention(Q, K, V, alpha: float | None = None, out=None, stream=None, splits: int | None = None,
+              workspace=None):
     """O = softmax(alpha * Q K^T) V, softmax along each row, on the GPU.
 
     Q: (H, M, d) or (M, d); K, V: (H, N, d) or (N, d); fp16 CUDA (HIP)
     tensors, contiguous; d = 128.  alpha defaults to fp32(1 / sqrt(d)).
+    `splits` cuts the keys into that many runs merged afterwards (default:
+    the library's choice for the device, 1 when the heads already fill it);
+    with more than one, `workspace` (a device tensor of at least
+    attention_fp16_workspace_bytes bytes) is used, or one is allocated.
     Returns O shaped like Q."""
     import math
 
@@ -91,14 +97,33 @@ def attention(Q, K, V, alpha: float | None = None, out=None, stream=None):
         out = torch.empty_like(Q)
     elif out.shape != Q.shape or out.dtype != torch.float16 or not out.is_contiguous():
         raise ValueError("out must be a contiguous float16 tensor shaped like Q")
-    s = (stream if stream is not None else torch.cuda.current_stream(Q.device)).cuda_stream
-    attention_fp16_fwd(H, M, N, d, float(alpha), Q.data_ptr(), K.data_ptr(), V.data_ptr(),
-                       out.data_ptr(), s)
+    st = stream if stream is not None else torch.cuda.current_stream(Q.device)
+    if H == 0 or M == 0:
+        splits = 1
+    elif splits is None:
+        with torch.cuda.device(Q.device):
+            splits = attention_fp16_splits(H, M, N, d)
+        # -1 (sizes the library refuses): the call below reports why
+        splits = max(splits, 1)
+    need = attention_fp16_workspace_bytes(H, M, N, d, splits) if splits > 1 else 0
+    if need == 0:
+        attention_fp16_fwd_split(H, M, N, d, float(alpha), Q.data_ptr(), K.data_ptr(),
+                                 V.data_ptr(), out.data_ptr(), splits, 0, 0, st.cuda_stream)
+        return out
+    if workspace is None:
+        with torch.cuda.stream(st):
+            workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
+    elif not workspace.is_cuda or workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must be a device tensor of at least {need} bytes")
+    attention_fp16_fwd_split(H, M, N, d, float(alpha), Q.data_ptr(), K.data_ptr(), V.data_ptr(),
+                             out.data_ptr(), splits, workspace.data_ptr(),
+                             workspace.numel() * workspace.element_size(), st.cuda_stream)
     return out
 
 
 __all__ = [
-    "gemm", "attention", "attention_fp16_fwd", "gemm_fp16_tn", "gemm_fp16_tn_alpha", "gemm_fp16_tn_alpha_beta", "gemm_fp16_tn_cfg",
+    "gemm", "attention", "attention_fp16_fwd", "attention_fp16_fwd_split", "attention_fp16_splits",
+    "attention_fp16_workspace_bytes", "gemm_fp16_tn", "gemm_fp16_tn_alpha", "gemm_fp16_tn_alpha_beta", "gemm_fp16_tn_cfg",
     "sg_select_config",
     "sg_num_configs", "sg_get_config", "sg_query_config", "sg_minimum_stages",
     "sg_pipeline_wait_count", "sg_persistent_wait_count", "sg_status_string", "configs", "SgConfig", "SgConfigInfo",

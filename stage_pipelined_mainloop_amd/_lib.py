@@ -79,6 +79,12 @@ def lib() -> ctypes.CDLL:
         L.gemm_fp16_tn_alpha_beta.restype = i
         L.attention_fp16_fwd.argtypes = [i, i, i, i, f, vp, vp, vp, vp, vp]
         L.attention_fp16_fwd.restype = i
+        L.attention_fp16_fwd_split.argtypes = [i, i, i, i, f, vp, vp, vp, vp, i, vp, ctypes.c_size_t, vp]
+        L.attention_fp16_fwd_split.restype = i
+        L.attention_fp16_workspace_bytes.argtypes = [i, i, i, i, i]
+        L.attention_fp16_workspace_bytes.restype = ctypes.c_size_t
+        L.attention_fp16_splits.argtypes = [i, i, i, i]
+        L.attention_fp16_splits.restype = i
         L.gemm_fp16_tn_cfg.argtypes = [i, i, i, f, vp, vp, vp, ctypes.POINTER(SgConfig), vp]
         L.gemm_fp16_tn_cfg.restype = i
         L.sg_select_config.argtypes = [i, i, i, ctypes.POINTER(SgConfig)]
@@ -137,6 +143,22 @@ def attention_fp16_fwd(H: int, M: int, N: int, d: int, alpha: float, Q: int, K: 
                        O: int, stream: int = 0) -> int:
     return _check(lib().attention_fp16_fwd(H, M, N, d, alpha, Q, K, V, O, stream),
                   "attention_fp16_fwd")
+
+
+def attention_fp16_fwd_split(H: int, M: int, N: int, d: int, alpha: float, Q: int, K: int, V: int,
+                             O: int, splits: int, workspace: int, workspace_bytes: int,
+                             stream: int = 0) -> int:
+    return _check(lib().attention_fp16_fwd_split(H, M, N, d, alpha, Q, K, V, O, splits, workspace,
+                                                 workspace_bytes, stream),
+                  "attention_fp16_fwd_split")
+
+
+def attention_fp16_workspace_bytes(H: int, M: int, N: int, d: int, splits: int) -> int:
+    return lib().attention_fp16_workspace_bytes(H, M, N, d, splits)
+
+
+def attention_fp16_splits(H: int, M: int, N: int, d: int) -> int:
+    return lib().attention_fp16_splits(H, M, N, d)
 
 
 def gemm_fp16_tn_cfg(M: int, N: int, K: int, alpha: float, A: int, B: int, D: int,

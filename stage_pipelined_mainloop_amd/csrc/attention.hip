@@ -16,15 +16,11 @@ bool ranges_overlap(const void *p, size_t pbytes, const void *q, size_t qbytes)
     return pbytes && qbytes && a < b + qbytes && b < a + pbytes;
 }
 
-}  // namespace
-
-extern "C" {
-
-sg_status attention_fp16_fwd(int H, int M, int N, int d, float alpha, const void *Q,
-                             const void *K, const void *V, void *O, void *stream)
+// Checks shared by both entry points; SG_OK means "launch".
+sg_status check_args(int H, int M, int N, int d, const void *Q, const void *K, const void *V,
+                     const void *O)
 {
     if (H < 0 || M < 0 || N < 0 || d < 0) return SG_ERR_SHAPE;
-    if (H == 0 || M == 0) return SG_OK;
     if (d != sg::AttnCfg::D) return SG_ERR_UNSUPPORTED;
     if (N == 0) return SG_ERR_SHAPE;                    // softmax over no keys
     if (!Q || !K || !V || !O) return SG_ERR_NULL;
@@ -38,22 +34,114 @@ sg_status attention_fp16_fwd(int H, int M, int N, int d, float alpha, const void
     if (ranges_overlap(O, qbytes, Q, qbytes) || ranges_overlap(O, qbytes, K, kvbytes) ||
         ranges_overlap(O, qbytes, V, kvbytes))
         return SG_ERR_ALIAS;
-    const long long blocks = (long long)H * ((M + sg::AttnCfg::BM - 1) / sg::AttnCfg::BM);
+    return SG_OK;
+}
+
+int key_tiles(int N) { return (N + sg::AttnCfg::BN - 1) / sg::AttnCfg::BN; }
+
+size_t workspace_bytes(int H, int M, int splits)
+{
+    return (size_t)H * splits * M * (sg::AttnCfg::D + 2) * sizeof(float);
+}
+
+// splits == 1: O directly; otherwise the partials go to part_o / part_ml and
+// a second kernel merges them.
+sg_status launch(int H, int M, int N, float alpha, const void *Q, const void *K, const void *V,
+                 void *O, int splits, void *workspace, hipStream_t stream)
+{
+    const long long blocks =
+        (long long)H * ((M + sg::AttnCfg::BM - 1) / sg::AttnCfg::BM) * splits;
     if (blocks >= (1LL << 31)) return SG_ERR_SHAPE;
     typedef void (*attn_fn)(const _Float16 *, const _Float16 *, const _Float16 *, _Float16 *,
-                            int, int, float);
+                            float *, float *, int, int, float, int);
     const attn_fn kernel = alpha < 0.0f ? &sg::attention_fwd_kernel<true>
                                         : &sg::attention_fwd_kernel<false>;   // fails to compile on drift
     const _Float16 *q = static_cast<const _Float16 *>(Q);
     const _Float16 *k = static_cast<const _Float16 *>(K);
     const _Float16 *v = static_cast<const _Float16 *>(V);
     _Float16 *o = static_cast<_Float16 *>(O);
-    void *args[] = {&q, &k, &v, &o, &M, &N, &alpha};
-    static_assert(sizeof(args) / sizeof(args[0]) == 7, "one entry per kernel parameter");
-    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(kernel),
-                                         dim3((unsigned)blocks), dim3(sg::AttnCfg::T), args, 0,
-                                         static_cast<hipStream_t>(stream));
+    float *part_o = splits > 1 ? static_cast<float *>(workspace) : nullptr;
+    float *part_ml = splits > 1 ? part_o + (size_t)H * splits * M * sg::AttnCfg::D : nullptr;
+    void *args[] = {&q, &k, &v, &o, &part_o, &part_ml, &M, &N, &alpha, &splits};
+    static_assert(sizeof(args) / sizeof(args[0]) == 10, "one entry per kernel parameter");
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(kernel), dim3((unsigned)blocks),
+                                   dim3(sg::AttnCfg::T), args, 0, stream);
+    if (e != hipSuccess || splits == 1) return e == hipSuccess ? SG_OK : SG_ERR_HIP;
+
+    long long HM = (long long)H * M;
+    const long long cblocks = (HM * 32 + 255) / 256;
+    typedef void (*comb_fn)(const float *, const float *, _Float16 *, long long, int, int);
+    const comb_fn comb = &sg::attention_combine_kernel;
+    const float *cpo = part_o, *cpm = part_ml;
+    void *cargs[] = {&cpo, &cpm, &o, &HM, &M, &splits};
+    static_assert(sizeof(cargs) / sizeof(cargs[0]) == 6, "one entry per kernel parameter");
+    e = hipLaunchKernel(reinterpret_cast<const void *>(comb), dim3((unsigned)cblocks), dim3(256),
+                        cargs, 0, stream);
     return e == hipSuccess ? SG_OK : SG_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+sg_status attention_fp16_fwd(int H, int M, int N, int d, float alpha, const void *Q,
+                             const void *K, const void *V, void *O, void *stream)
+{
+    if (H < 0 || M < 0 || N < 0 || d < 0) return SG_ERR_SHAPE;
+    if (H == 0 || M == 0) return SG_OK;
+    const sg_status st = check_args(H, M, N, d, Q, K, V, O);
+    if (st != SG_OK) return st;
+    return launch(H, M, N, alpha, Q, K, V, O, 1, nullptr, static_cast<hipStream_t>(stream));
+}
+
+int attention_fp16_splits(int H, int M, int N, int d)
+{
+    if (H < 1 || M < 1 || N < 1 || d != sg::AttnCfg::D) return -1;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+        return -1;
+    // two workgroups per CU are resident; aim for that many, with at least
+    // eight key tiles per split so the ring's prologue, the partial write and
+    // the merge stay small next to the work (one head of 4096 x 4096 x 128:
+    // 8 splits 31.6 us, 16 splits 35.4, 4 splits 36.5, none 96)
+    const long long blocks = (long long)H * ((M + sg::AttnCfg::BM - 1) / sg::AttnCfg::BM);
+    const long long target = 2LL * cus;
+    if (blocks >= target) return 1;
+    long long splits = (target + blocks - 1) / blocks;
+    const long long most = key_tiles(N) / 8;
+    if (splits > most) splits = most;
+    return splits < 1 ? 1 : (int)splits;
+}
+
+size_t attention_fp16_workspace_bytes(int H, int M, int N, int d, int splits)
+{
+    if (H < 1 || M < 1 || N < 1 || d != sg::AttnCfg::D || splits <= 1) return 0;
+    if (splits > key_tiles(N)) splits = key_tiles(N);
+    return splits > 1 ? workspace_bytes(H, M, splits) : 0;
+}
+
+sg_status attention_fp16_fwd_split(int H, int M, int N, int d, float alpha, const void *Q,
+                                   const void *K, const void *V, void *O, int splits,
+                                   void *workspace, size_t workspace_bytes_given, void *stream)
+{
+    if (H < 0 || M < 0 || N < 0 || d < 0 || splits < 1) return SG_ERR_SHAPE;
+    if (H == 0 || M == 0) return SG_OK;
+    const sg_status st = check_args(H, M, N, d, Q, K, V, O);
+    if (st != SG_OK) return st;
+    if (splits > key_tiles(N)) splits = key_tiles(N);   // every split keeps a key tile
+    if (splits > 1) {
+        if (!workspace) return SG_ERR_NULL;
+        const size_t need = workspace_bytes(H, M, splits);
+        if (workspace_bytes_given < need) return SG_ERR_SHAPE;
+        if (reinterpret_cast<uintptr_t>(workspace) & 15) return SG_ERR_ALIGN;
+        const size_t qbytes = (size_t)H * M * d * 2, kvbytes = (size_t)H * N * d * 2;
+        if (ranges_overlap(workspace, need, Q, qbytes) || ranges_overlap(workspace, need, K, kvbytes) ||
+            ranges_overlap(workspace, need, V, kvbytes) || ranges_overlap(workspace, need, O, qbytes))
+            return SG_ERR_ALIAS;
+    }
+    return launch(H, M, N, alpha, Q, K, V, O, splits, workspace, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

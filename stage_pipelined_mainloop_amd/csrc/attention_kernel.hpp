@@ -26,6 +26,9 @@
 
 namespace sg {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 struct AttnCfg {
     static constexpr int D = 128;                  // head dimension
     static constexpr int BM = 128;                 // query rows per workgroup
@@ -50,11 +53,19 @@ __device__ __forceinline__ int k_chunk(int r, int c) { return c ^ (r & 15); }
 __device__ __forceinline__ int vt_chunk(int d, int c) { return c ^ ((d >> 1) & 7); }
 
 // NEG: alpha < 0, so the largest scaled score comes from the smallest score.
+//
+// With splits > 1 the keys are divided too: workgroup (head, row block,
+// split) takes a contiguous run of key tiles and, instead of O, writes its
+// unnormalised accumulator to part_o and its reference exponent and row sum
+// to part_ml; attention_combine_kernel then merges the splits of each row.
+// This gives a single head enough workgroups to fill the device.  Layouts
+// (fp32): part_o[(h * splits + sp) * M + row][D], part_ml[same index][2].
 template <bool NEG>
 __global__ void __launch_bounds__(AttnCfg::T, 2)
 attention_fwd_kernel(const _Float16 *__restrict__ Q, const _Float16 *__restrict__ Kg,
-                     const _Float16 *__restrict__ V, _Float16 *__restrict__ O, int M, int N,
-                     float alpha)
+                     const _Float16 *__restrict__ V, _Float16 *__restrict__ O,
+                     float *__restrict__ part_o, float *__restrict__ part_ml, int M, int N,
+                     float alpha, int splits)
 {
     using C = AttnCfg;
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
@@ -65,8 +76,10 @@ attention_fwd_kernel(const _Float16 *__restrict__ Q, const _Float16 *__restrict_
     const int r32 = lane & 31;
 
     const int row_blocks = (M + C::BM - 1) / C::BM;
-    const int h = blockIdx.x / row_blocks;
-    const int m0 = (blockIdx.x - h * row_blocks) * C::BM;
+    const int hb = blockIdx.x / splits;                // head-major row block
+    const int sp = blockIdx.x - hb * splits;
+    const int h = hb / row_blocks;
+    const int m0 = (hb - h * row_blocks) * C::BM;
     const int rows = (M - m0 < C::BM) ? (M - m0) : C::BM;
     const _Float16 *qh = Q + ((size_t)h * M + m0) * C::D;
     const _Float16 *kh = Kg + (size_t)h * N * C::D;
@@ -76,6 +89,9 @@ attention_fwd_kernel(const _Float16 *__restrict__ Q, const _Float16 *__restrict_
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kh, (uint32_t)N * C::D * 2u);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vh, (uint32_t)N * C::D * 2u);
     const int ntiles = (N + C::BN - 1) / C::BN;
+    // this split's key tiles [t_lo, t_hi): never empty, as splits <= ntiles
+    const int t_lo = (int)((long long)sp * ntiles / splits);
+    const int t_hi = (int)((long long)(sp + 1) * ntiles / splits);
 
     // ---- Q fragments of this wave's 32 rows, all of d, kept in VGPRs:
     // step s holds Q[row][16 s + 8 half .. + 7]
@@ -121,7 +137,6 @@ attention_fwd_kernel(const _Float16 *__restrict__ Q, const _Float16 *__restrict_
         char *base = smem + slot * C::STAGE_BYTES + C::K_BYTES;
         const int G = q4 >> 2;
         const int qp = ((q4 & 1) << 1) | ((q4 >> 1) & 1);   // 0,1,2,3 -> 0,2,1,3
-        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
         u32x4 w[4];                                    // key kk's 8 values as 4 words
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) w[kk] = __builtin_bit_cast(u32x4, vreg[kk]);
@@ -144,9 +159,9 @@ attention_fwd_kernel(const _Float16 *__restrict__ Q, const _Float16 *__restrict_
         compiler_fence();
     };
 
-    // ---- prologue: tile 0
-    issue_k(0, 0);
-    load_v(0);
+    // ---- prologue: the first tile
+    issue_k(t_lo, 0);
+    load_v(t_lo);
     compiler_fence();
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
     compiler_fence();
@@ -171,9 +186,9 @@ attention_fwd_kernel(const _Float16 *__restrict__ Q, const _Float16 *__restrict_
         for (int e = 0; e < 16; ++e) oacc[c][e] = 0.0f;
 
 #pragma unroll 1
-    for (int j = 0; j < ntiles; ++j) {
-        const int slot = j & 1;
-        const bool more = j + 1 < ntiles;
+    for (int j = t_lo; j < t_hi; ++j) {
+        const int slot = (j - t_lo) & 1;
+        const bool more = j + 1 < t_hi;
         if (more) {                                    // refill the other slot (read last in step j - 1)
             issue_k(j + 1, slot ^ 1);
             load_v(j + 1);
@@ -285,10 +300,37 @@ attention_fwd_kernel(const _Float16 *__restrict__ Q, const _Float16 *__restrict_
         barrier();                                     // RAW for tile j + 1, WAR for slot
     }
 
-    // ---- O / l, one rounding to fp16; lane stores 4 consecutive halves per
-    // (c, g); rows past M fall outside the buffer range and are dropped
     const float lother = __builtin_bit_cast(
         float, __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __builtin_bit_cast(int, lsum)));
+    if (splits > 1) {
+        // ---- partial of this split: O unnormalised, (m, l) of the row; rows
+        // past M fall outside the buffer ranges and are dropped
+        const size_t first = ((size_t)h * splits + sp) * M + m0;
+        const __amdgpu_buffer_rsrc_t rpo = make_rsrc(part_o + first * C::D, (uint32_t)rows * C::D * 4u);
+        const __amdgpu_buffer_rsrc_t rpm = make_rsrc(part_ml + first * 2, (uint32_t)rows * 8u);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                // whole-vector bit_cast: the same cast of a single vector
+                // element yields element 0's bits whatever the index
+                const f32x4 o4 = {oacc[c][4 * g], oacc[c][4 * g + 1], oacc[c][4 * g + 2],
+                                  oacc[c][4 * g + 3]};
+                const u32x4 v = __builtin_bit_cast(u32x4, o4);
+                const uint32_t off = (uint32_t)(qrow * C::D + 32 * c + 8 * g + 4 * half) * 4u;
+                __builtin_amdgcn_raw_buffer_store_b128(v, rpo, off, 0, 0);
+            }
+        if (half == 0) {
+            u32x2 ml;
+            ml[0] = __builtin_bit_cast(uint32_t, mref);
+            ml[1] = __builtin_bit_cast(uint32_t, lsum + lother);
+            __builtin_amdgcn_raw_buffer_store_b64(ml, rpm, (uint32_t)qrow * 8u, 0, 0);
+        }
+        return;
+    }
+
+    // ---- O / l, one conversion to fp16; lane stores 4 consecutive halves per
+    // (c, g); rows past M fall outside the buffer range and are dropped
     const float inv = 1.0f / (lsum + lother);
     const __amdgpu_buffer_rsrc_t ro =
         make_rsrc(O + ((size_t)h * M + m0) * C::D, (uint32_t)rows * C::D * 2u);
@@ -304,6 +346,44 @@ attention_fwd_kernel(const _Float16 *__restrict__ Q, const _Float16 *__restrict_
             const uint32_t off = (uint32_t)(qrow * C::D + 32 * c + 8 * g + 4 * half) * 2u;
             __builtin_amdgcn_raw_buffer_store_b64(packed, ro, off, 0, 0);
         }
+}
+
+// Merge of the key splits of each row (the same online-softmax identity
+// across splits): with m* the largest reference exponent of the row,
+//     O = sum_s 2^(m_s - m*) O_s / sum_s 2^(m_s - m*) l_s,
+// converted once to fp16.  32 threads per row, 4 columns (16 bytes) each;
+// HM = H * M rows in all.
+__global__ void __launch_bounds__(256)
+attention_combine_kernel(const float *__restrict__ part_o, const float *__restrict__ part_ml,
+                         _Float16 *__restrict__ O, long long HM, int M, int splits)
+{
+    using C = AttnCfg;
+    const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long hr = t >> 5;                       // h * M + row
+    if (hr >= HM) return;
+    const int col = (int)(t & 31) * 4;
+    const long long h = hr / M;
+    const long long row = hr - h * M;
+    const size_t first = (size_t)h * splits * M + row;   // index of split 0
+    float mx = -__builtin_inff();
+    for (int s = 0; s < splits; ++s) mx = __builtin_fmaxf(mx, part_ml[(first + (size_t)s * M) * 2]);
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float l = 0.0f;
+    for (int s = 0; s < splits; ++s) {
+        const size_t i = first + (size_t)s * M;
+        const float w = __builtin_amdgcn_exp2f(part_ml[i * 2] - mx);
+        l += w * part_ml[i * 2 + 1];
+        const f32x4 o = *(const f32x4 *)(part_o + i * C::D + col);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += w * o[e];
+    }
+    const float inv = 1.0f / l;
+    u32x2 packed;
+    packed[0] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(acc[0] * inv)) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(acc[1] * inv)) << 16);
+    packed[1] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(acc[2] * inv)) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(acc[3] * inv)) << 16);
+    *(u32x2 *)(O + hr * C::D + col) = packed;
 }
 
 }  // namespace sg

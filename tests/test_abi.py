@@ -17,7 +17,7 @@ S = _lib
 
 def test_every_declared_symbol_is_exported():
     declared = _lib.header_functions()
-    assert len(declared) == 13
+    assert len(declared) == 16
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
@@ -133,6 +133,43 @@ def test_attention_argument_errors(args, status):
     # no work at all: H == 0 or M == 0 succeeds without touching anything
     assert L.attention_fp16_fwd(0, 8, 8, 128, 0.1, P, P, P, P, None) == S.SG_OK
     assert L.attention_fp16_fwd(2, 0, 8, 128, 0.1, P, P, P, P, None) == S.SG_OK
+
+
+def test_attention_split_argument_errors():
+    q, k, v, o, w = P, P + 0x100000, P + 0x200000, P + 0x300000, P + 0x1000000
+    big = 1 << 30
+    F = L.attention_fp16_fwd_split
+    # the checks of the plain entry point come first
+    assert F(1, 8, 8, 64, 0.1, q, k, v, o, 1, 0, 0, None) == S.SG_ERR_UNSUPPORTED
+    assert F(1, 8, 8, 128, 0.1, q, k, v, q + 0x400, 2, w, big, None) == S.SG_ERR_ALIAS
+    assert F(1, 8, 8, 128, 0.1, q, k, v, o, 0, w, big, None) == S.SG_ERR_SHAPE      # splits < 1
+    assert F(1, 8, 8, 128, 0.1, q, k, v, o, -3, w, big, None) == S.SG_ERR_SHAPE
+    # N = 200: four key tiles, so two splits need a workspace
+    assert F(1, 8, 200, 128, 0.1, q, k, v, o, 2, 0, big, None) == S.SG_ERR_NULL
+    need = L.attention_fp16_workspace_bytes(1, 8, 200, 128, 2)
+    assert need == 1 * 2 * 8 * 130 * 4
+    assert F(1, 8, 200, 128, 0.1, q, k, v, o, 2, w, need - 1, None) == S.SG_ERR_SHAPE
+    assert F(1, 8, 200, 128, 0.1, q, k, v, o, 2, w + 8, need, None) == S.SG_ERR_ALIGN
+    assert F(1, 8, 200, 128, 0.1, q, k, v, o, 2, q, big, None) == S.SG_ERR_ALIAS
+    assert F(1, 8, 200, 128, 0.1, q, k, v, o, 2, o - need + 16, need, None) == S.SG_ERR_ALIAS
+    # no work at all
+    assert F(0, 8, 8, 128, 0.1, P, P, P, P, 4, 0, 0, None) == S.SG_OK
+    assert F(2, 0, 8, 128, 0.1, P, P, P, P, 4, 0, 0, None) == S.SG_OK
+
+
+def test_attention_workspace_bytes():
+    W = L.attention_fp16_workspace_bytes
+    assert W(1, 4096, 4096, 128, 16) == 16 * 4096 * 130 * 4
+    assert W(3, 100, 640, 128, 4) == 3 * 4 * 100 * 130 * 4
+    assert W(1, 10, 100, 128, 8) == 2 * 10 * 130 * 4      # two key tiles: two splits at most
+    assert W(1, 10, 64, 128, 8) == 0                      # one key tile: no split
+    assert W(1, 10, 100, 128, 1) == 0
+    assert W(1, 10, 100, 64, 2) == 0
+    assert W(0, 10, 100, 128, 2) == 0 and W(1, 10, 0, 128, 2) == 0
+    # invalid sizes are refused before any device query
+    assert L.attention_fp16_splits(1, 8, 8, 64) == -1
+    assert L.attention_fp16_splits(0, 8, 8, 128) == -1
+    assert L.attention_fp16_splits(1, 8, 0, 128) == -1
 
 
 def test_status_strings_are_stable():

@@ -36,18 +36,24 @@ def qkv(H, M, N, seed, scale=1.0):
     return Q, K, V
 
 
-def gpu_attention(Q, K, V, alpha):
+def gpu_attention(Q, K, V, alpha, splits=None):
     q, k, v = (torch.from_numpy(np.ascontiguousarray(x)).to(DEV) for x in (Q, K, V))
     o = torch.full(q.shape, float("nan"), dtype=torch.float16, device=DEV)
-    sg.attention(q, k, v, alpha=alpha, out=o)
+    ws = None
+    if splits is not None and splits > 1:
+        # scratch contents on entry must not matter
+        H, M, N = Q.shape[0], Q.shape[1], K.shape[1]
+        need = sg.attention_fp16_workspace_bytes(H, M, N, 128, splits)
+        ws = torch.full((max(need, 16) // 4,), float("nan"), dtype=torch.float32, device=DEV)
+    sg.attention(q, k, v, alpha=alpha, out=o, splits=splits, workspace=ws)
     torch.cuda.synchronize()
     return o.cpu().numpy()
 
 
-def check(Q, K, V, alpha, label):
+def check(Q, K, V, alpha, label, splits=None):
     N = K.shape[-2]
-    say(f"[case] attention {label} Q{Q.shape} N={N} alpha={alpha}")
-    O = gpu_attention(Q, K, V, alpha).astype(np.float64)
+    say(f"[case] attention {label} Q{Q.shape} N={N} alpha={alpha} splits={splits}")
+    O = gpu_attention(Q, K, V, alpha, splits).astype(np.float64)
     ref, w = oracle.attention_f64(Q, K, V, alpha, with_bound=True)
     ref = ref.astype(np.float64)
     assert np.all(np.isfinite(O)), label
@@ -99,12 +105,56 @@ def test_growing_scores(top):
     check(Q, K, V, float(np.float32(1.0 / math.sqrt(128))), f"growing to x{top}")
 
 
+@pytest.mark.parametrize("H,M,N,splits", [(1, 300, 1000, 1), (1, 300, 1000, 2), (1, 300, 1000, 5),
+                                          (2, 129, 65, 2), (1, 37, 200, 4), (1, 200, 130, 100),
+                                          (3, 256, 4096, 16), (1, 1, 1, 3)])
+def test_split_keys(H, M, N, splits):
+    # keys cut into runs merged afterwards; more splits than key tiles are
+    # lowered to one run per tile
+    Q, K, V = qkv(H, M, N, 4115 + M + N + splits)
+    check(Q, K, V, float(np.float32(1.0 / math.sqrt(128))), f"split {splits}", splits=splits)
+
+
+def test_split_growing_and_negative():
+    # runs with very different maxima (keys scaled up along the sequence),
+    # and alpha < 0
+    Q, K, V = qkv(1, 256, 1500, 4117)
+    K = (K.astype(np.float64) * np.linspace(1.0, 30.0, 1500)[None, :, None]).astype(np.float16)
+    check(Q, K, V, float(np.float32(1.0 / math.sqrt(128))), "split growing", splits=6)
+    check(Q, K, V, -0.0884, "split negative", splits=6)
+
+
+def test_split_choice_and_workspace_reuse():
+    # the library's choice on this device: one head of 4096 queries is 32
+    # row blocks, far from two per CU; sixteen heads already fill the device
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    s1 = sg.attention_fp16_splits(1, 4096, 4096, 128)
+    assert s1 == min(-(-2 * cus // 32), 64 // 8)
+    assert sg.attention_fp16_splits(16, 4096, 4096, 128) == (1 if 16 * 32 >= 2 * cus else s1)
+    # one workspace, two calls of different shapes back to back
+    need = sg.attention_fp16_workspace_bytes(2, 512, 2000, 128, 8)
+    ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device=DEV)
+    outs = []
+    for H, M, N in ((2, 512, 2000), (1, 100, 700)):
+        Q, K, V = qkv(H, M, N, 4119 + N)
+        q, k, v = (torch.from_numpy(x).to(DEV) for x in (Q, K, V))
+        o = sg.attention(q, k, v, alpha=0.09, splits=8, workspace=ws)
+        outs.append((o, Q, K, V))
+    torch.cuda.synchronize()
+    for o, Q, K, V in outs:
+        ref, w = oracle.attention_f64(Q, K, V, 0.09, with_bound=True)
+        bound = 2 * oracle.ulp16(np.abs(ref.astype(np.float64))) + 2 * (2.0 ** -11 + K.shape[1] * 2.0 ** -24) * w
+        assert np.all(np.abs(o.cpu().numpy().astype(np.float64) - ref.astype(np.float64)) <= bound)
+
+
 def test_attention_config_full():
     # the attention-score workload's Q and K (4096 x 128, N(0,1)) with a V of
     # the same shape, alpha = fp32(1/sqrt(128)); every output against the oracle
     Q, K = inputs.workload("attn_scores")
     V = inputs.matrix(4096, 128, 4105, "normal")
-    check(Q[None], K[None], V[None], float(np.float32(1.0 / math.sqrt(128))), "4096x4096x128")
+    for splits in (None, 1):
+        check(Q[None], K[None], V[None], float(np.float32(1.0 / math.sqrt(128))), "4096x4096x128",
+              splits=splits)
 
 
 def test_multi_head():
