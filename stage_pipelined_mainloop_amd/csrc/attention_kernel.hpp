@@ -5,8 +5,8 @@
 // The scores never leave the chip.  Each workgroup owns 128 query rows of one
 // head (4 waves, 32 rows each) and streams the head's keys in tiles of 64
 // through a two-slot LDS ring -- the stage-pipelined mainloop of "Lesson 6":
-// while tile j is consumed, tile j + 1's K rows arrive by LDS-DMA and its V
-// rows by ordinary loads -- and keeps a reference exponent m, a row sum l
+// while tile j is consumed, tile j + 1's K and V rows arrive by LDS-DMA --
+// and keeps a reference exponent m, a row sum l
 // and an output accumulator O (the online form of the softmax):
 //     S = Q K_j^T (MFMA, fp32), t = S * alpha * log2(e)
 //     P = 2^(t - m), O += P V_j, l += sum P
@@ -15,11 +15,15 @@
 // 2^(m - m')) when a row's tile maximum exceeds m by more than TAU, not on
 // every increase.  Probabilities then stay below 2^TAU, well inside fp16.
 //
-// The P V product contracts over keys, which are rows of V, so each V tile is
-// written to LDS transposed (d x 64 keys) through registers, with the keys of
-// every 16-key group in the order the score accumulators hold them: the
-// fragment of probabilities a lane feeds to the MFMA then meets V values for
-// the same keys in the same order, without moving the probabilities.
+// The P V product contracts over keys, which are rows of V: a lane's MFMA
+// operand needs one column of V over 8 keys.  V stays row-major in LDS and
+// the operand is read with the transposing LDS load (ds_read_b64_tr_b16): in
+// each group of 16 lanes, lane i receives element i % 4 of the 4-element
+// pieces addressed by lanes i / 4, i / 4 + 4, i / 4 + 8 and i / 4 + 12.  The
+// addresses are chosen so that the keys arrive in the order the score
+// accumulators hold them (keys 0-3, 8-11, 4-7, 12-15 of every 16), so the
+// fragment of probabilities a lane already holds is the other operand and
+// the probabilities never move between lanes.
 #pragma once
 
 #include "gemm_kernel.hpp"
@@ -37,20 +41,23 @@ struct AttnCfg {
     static constexpr int T = 64 * NW;
     static constexpr int K_ROW = D * 2;            // 256-byte K rows
     static constexpr int K_BYTES = BN * K_ROW;     // 16 KiB
-    static constexpr int VT_ROW = BN * 2;          // 128-byte V^T rows (one per d)
-    static constexpr int VT_BYTES = D * VT_ROW;    // 16 KiB
-    static constexpr int STAGE_BYTES = K_BYTES + VT_BYTES;
+    static constexpr int V_ROW = D * 2;            // 256-byte V rows
+    static constexpr int V_BYTES = BN * V_ROW;     // 16 KiB
+    static constexpr int STAGE_BYTES = K_BYTES + V_BYTES;
     static constexpr int S = 2;                    // ring slots
     static constexpr int LDS_BYTES = S * STAGE_BYTES;
     static constexpr int KL = K_BYTES / (16 * T);  // K LDS-DMA loads per lane per tile
-    static_assert(KL * 16 * T == K_BYTES, "even K split");
+    static_assert(KL * 16 * T == K_BYTES && K_BYTES == V_BYTES, "even K and V split");
     static constexpr float TAU = 8.0f;             // headroom of 2^(t - m), in exponent units
 };
 
 // 16-byte chunk position of logical chunk c in K row r (16 chunks per row).
 __device__ __forceinline__ int k_chunk(int r, int c) { return c ^ (r & 15); }
-// 16-byte chunk position of logical chunk c in V^T row d (8 chunks per row).
-__device__ __forceinline__ int vt_chunk(int d, int c) { return c ^ ((d >> 1) & 7); }
+// 16-byte chunk position of logical chunk c in V row r (16 chunks per row):
+// the transposing reads of one half-wave touch 4 consecutive rows (a multiple
+// of 4 apart) and 4 chunks 4 q .. 4 q + 3, which this places in 16 distinct
+// 16-byte bank groups.
+__device__ __forceinline__ int v_chunk(int r, int c) { return c ^ ((r & 3) << 2); }
 
 // NEG: alpha < 0, so the largest scaled score comes from the smallest score.
 //
@@ -117,40 +124,30 @@ attention_fwd_kernel(const _Float16 *__restrict__ Q, const _Float16 *__restrict_
                 16, off, 0, 0, 0);
         }
     };
-    // ---- V tile j: thread t loads keys 4 q4 .. 4 q4 + 3 (q4 = t % 16) of
-    // columns 8 dg .. 8 dg + 7 (dg = t / 16) into VGPRs ...
-    const int q4 = threadIdx.x & 15;
-    const int dg = threadIdx.x >> 4;
-    f16x8 vreg[4];
-    auto load_v = [&](int j) {
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-            vreg[kk] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                                                     rv, (uint32_t)((j * C::BN + 4 * q4 + kk) * C::D + 8 * dg) * 2u,
-                                                     0, 0));
-    };
-    // ... and writes them transposed: V^T row d gets these 4 keys as one
-    // 8-byte piece.  Within each 16-key group the order is keys
-    // 0-3, 8-11, 4-7, 12-15, so 16-byte logical chunk 2 G + hh of a row holds
-    // keys 16 G + {4 hh .. 4 hh + 3, 8 + 4 hh .. 8 + 4 hh + 3}.
-    auto write_vt = [&](int slot) {
+    // ---- V tile j into slot: the same LDS-DMA pattern with V's swizzle
+    auto issue_v = [&](int j, int slot) {
         char *base = smem + slot * C::STAGE_BYTES + C::K_BYTES;
-        const int G = q4 >> 2;
-        const int qp = ((q4 & 1) << 1) | ((q4 >> 1) & 1);   // 0,1,2,3 -> 0,2,1,3
-        u32x4 w[4];                                    // key kk's 8 values as 4 words
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) w[kk] = __builtin_bit_cast(u32x4, vreg[kk]);
-#pragma unroll
-        for (int dd = 0; dd < 8; ++dd) {
-            const int d = 8 * dg + dd;
-            const int sh = (dd & 1) * 16;              // column dd: half (dd & 1) of word dd / 2
-            u32x2 piece;
-            piece[0] = ((w[0][dd >> 1] >> sh) & 0xffffu) | (((w[1][dd >> 1] >> sh) & 0xffffu) << 16);
-            piece[1] = ((w[2][dd >> 1] >> sh) & 0xffffu) | (((w[3][dd >> 1] >> sh) & 0xffffu) << 16);
-            const int off = d * C::VT_ROW + (vt_chunk(d, 2 * G + (qp >> 1)) << 4) + ((qp & 1) << 3);
-            *(u32x2 *)(base + off) = piece;
+        for (int i = 0; i < C::KL; ++i) {
+            const int r = (i * C::NW + wave) * 4 + (lane >> 4);
+            const int c = v_chunk(r, lane & 15);
+            const uint32_t off = (uint32_t)((j * C::BN + r) * C::D + c * 8) * 2u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rv, (__attribute__((address_space(3))) void *)(base + (i * C::NW + wave) * 1024),
+                16, off, 0, 0, 0);
         }
     };
+    // ---- per-lane byte offsets of the transposing V reads within a V tile:
+    // as an address provider, lane l names key row 4 (l / 32) + (l % 16) / 4
+    // (plus 16 G + 8 i for 16-key group G, half i) and columns
+    // 32 c + 16 ((l / 16) % 2) + 4 (l % 4) .. + 3
+    int vrd[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int row = 4 * half + ((lane & 15) >> 2);
+        const int chunk = 4 * c + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+        vrd[c] = row * C::V_ROW + (v_chunk(row, chunk) << 4) + ((lane & 1) << 3);
+    }
 
     auto barrier = [&]() {
         compiler_fence();
@@ -161,7 +158,7 @@ attention_fwd_kernel(const _Float16 *__restrict__ Q, const _Float16 *__restrict_
 
     // ---- prologue: the first tile
     issue_k(t_lo, 0);
-    load_v(t_lo);
+    issue_v(t_lo, 0);
     compiler_fence();
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
     compiler_fence();
@@ -170,7 +167,6 @@ attention_fwd_kernel(const _Float16 *__restrict__ Q, const _Float16 *__restrict_
     // vmcnt being in order, for the next tile's loads) inside every iteration
 #pragma unroll
     for (int s = 0; s < 8; ++s) asm volatile("" : "+v"(qf[s]));
-    write_vt(0);
     barrier();
 
     const float c2 = alpha * 1.4426950408889634f;     // scores to base-2 exponents
@@ -191,7 +187,7 @@ attention_fwd_kernel(const _Float16 *__restrict__ Q, const _Float16 *__restrict_
         const bool more = j + 1 < t_hi;
         if (more) {                                    // refill the other slot (read last in step j - 1)
             issue_k(j + 1, slot ^ 1);
-            load_v(j + 1);
+            issue_v(j + 1, slot ^ 1);
         }
         const char *kbase = smem + slot * C::STAGE_BYTES;
         const char *vbase = kbase + C::K_BYTES;
@@ -272,7 +268,8 @@ attention_fwd_kernel(const _Float16 *__restrict__ Q, const _Float16 *__restrict_
         // O += P V_j: K step (b, t) covers keys 32 b + 16 t + {0..15}; this
         // lane's 8 probabilities are sacc[b][8 t .. 8 t + 7] (keys
         // 16 G + 4 half + {0..3} and 16 G + 8 + 4 half + {0..3}, G = 2 b + t),
-        // matched by logical V^T chunk 2 G + half.
+        // and the two transposing reads bring V at the same keys, column
+        // 32 c + lane % 32
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -283,20 +280,18 @@ attention_fwd_kernel(const _Float16 *__restrict__ Q, const _Float16 *__restrict_
                 const int G = 2 * b + t;
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    const int d = 32 * c + r32;
-                    const f16x8 vf = *(const f16x8 *)(vbase + d * C::VT_ROW +
-                                                      (vt_chunk(d, 2 * G + half) << 4));
+                    typedef short i16x4 __attribute__((ext_vector_type(4)));
+                    typedef short i16x8 __attribute__((ext_vector_type(8)));
+                    const char *p0 = vbase + vrd[c] + (16 * G) * C::V_ROW;
+                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) i16x4 *)(p0));
+                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) i16x4 *)(p0 + 8 * C::V_ROW));
+                    const f16x8 vf = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                     oacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf, oacc[c], 0, 0, 0);
                 }
             }
 
-        if (more) {
-            // tile j + 1: V rows have arrived (and the K DMA); write V^T
-            compiler_fence();
-            __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
-            compiler_fence();
-            write_vt(slot ^ 1);
-        }
         barrier();                                     // RAW for tile j + 1, WAR for slot
     }
 
