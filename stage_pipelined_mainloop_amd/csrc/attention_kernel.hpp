@@ -43,9 +43,9 @@ struct AttnCfg {
     static constexpr int K_BYTES = BN * K_ROW;     // 16 KiB
     static constexpr int V_ROW = D * 2;            // 256-byte V rows
     static constexpr int V_BYTES = BN * V_ROW;     // 16 KiB
-    static constexpr int STAGE_BYTES = K_BYTES + V_BYTES;
-    static constexpr int S = 2;                    // ring slots
-    static constexpr int LDS_BYTES = S * STAGE_BYTES;
+    static constexpr int S = 2;                    // slots of each ring (K and V)
+    static constexpr int V_OFFSET = S * K_BYTES;   // the V ring follows the K ring
+    static constexpr int LDS_BYTES = S * (K_BYTES + V_BYTES);
     static constexpr int KL = K_BYTES / (16 * T);  // K LDS-DMA loads per lane per tile
     static_assert(KL * 16 * T == K_BYTES && K_BYTES == V_BYTES, "even K and V split");
     static constexpr float TAU = 8.0f;             // headroom of 2^(t - m), in exponent units
@@ -58,6 +58,29 @@ __device__ __forceinline__ int k_chunk(int r, int c) { return c ^ (r & 15); }
 // of 4 apart) and 4 chunks 4 q .. 4 q + 3, which this places in 16 distinct
 // 16-byte bank groups.
 __device__ __forceinline__ int v_chunk(int r, int c) { return c ^ ((r & 3) << 2); }
+
+// Buffer resource words for `bytes` bytes from `base` (stride 0): reads past
+// the range return zero.
+__device__ __forceinline__ u32x4 rsrc_words(const void *base, uint32_t bytes)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, (uint32_t)kRsrcWord3};
+}
+
+// LDS-DMA of 16 bytes per lane to the wave's 1 KiB at LDS address `lds`
+// (lane l fills bytes 16 l .. 16 l + 15), issued through inline assembly.
+// The compiler cannot tell the transposing LDS reads apart from any pending
+// DMA target and would wait for every DMA in flight before each of them;
+// here it does not see these loads at all, and the kernel's own vmcnt(0)
+// before each barrier is what orders them.  (Loads the compiler does track
+// are waited for with counts that ignore these: at worst it waits longer.)
+__device__ __forceinline__ void dma16(const u32x4 &rsrc, uint32_t voff, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(rsrc)
+                 : "memory", "m0");
+}
 
 // NEG: alpha < 0, so the largest scaled score comes from the smallest score.
 //
@@ -82,9 +105,14 @@ attention_fwd_kernel(const _Float16 *__restrict__ Q, const _Float16 *__restrict_
     const int half = lane >> 5;
     const int r32 = lane & 31;
 
+    // Workgroups are dealt round-robin to the 8 XCDs; renumber them so each
+    // XCD takes a contiguous run (the same heads), whose K and V tiles its
+    // L2 then holds for all the row blocks reading them.
+    int pid = blockIdx.x;
+    if ((gridDim.x & 7) == 0) pid = (pid & 7) * (gridDim.x >> 3) + (pid >> 3);
     const int row_blocks = (M + C::BM - 1) / C::BM;
-    const int hb = blockIdx.x / splits;                // head-major row block
-    const int sp = blockIdx.x - hb * splits;
+    const int hb = pid / splits;                       // head-major row block
+    const int sp = pid - hb * splits;
     const int h = hb / row_blocks;
     const int m0 = (hb - h * row_blocks) * C::BM;
     const int rows = (M - m0 < C::BM) ? (M - m0) : C::BM;
@@ -93,8 +121,11 @@ attention_fwd_kernel(const _Float16 *__restrict__ Q, const _Float16 *__restrict_
     const _Float16 *vh = V + (size_t)h * N * C::D;
     // buffer ranges cover only valid rows: rows past M or N read as zero
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(qh, (uint32_t)rows * C::D * 2u);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kh, (uint32_t)N * C::D * 2u);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vh, (uint32_t)N * C::D * 2u);
+    const u32x4 rk = rsrc_words(kh, (uint32_t)N * C::D * 2u);
+    const u32x4 rv = rsrc_words(vh, (uint32_t)N * C::D * 2u);
+    // LDS address of the ring (an LDS offset, not a generic address)
+    const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(
+        (__attribute__((address_space(3))) char *)smem);
     const int ntiles = (N + C::BN - 1) / C::BN;
     // this split's key tiles [t_lo, t_hi): never empty, as splits <= ntiles
     const int t_lo = (int)((long long)sp * ntiles / splits);
@@ -113,28 +144,24 @@ attention_fwd_kernel(const _Float16 *__restrict__ Q, const _Float16 *__restrict_
     // of 256 bytes; lane -> row lane / 16, position lane % 16, which holds
     // logical chunk k_chunk(row, position) (the swizzle is its own inverse).
     auto issue_k = [&](int j, int slot) {
-        char *base = smem + slot * C::STAGE_BYTES;
+        const uint32_t base = lds0 + slot * C::K_BYTES;
 #pragma unroll
         for (int i = 0; i < C::KL; ++i) {
             const int r = (i * C::NW + wave) * 4 + (lane >> 4);   // row within the tile
             const int c = k_chunk(r, lane & 15);
             const uint32_t off = (uint32_t)((j * C::BN + r) * C::D + c * 8) * 2u;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rk, (__attribute__((address_space(3))) void *)(base + (i * C::NW + wave) * 1024),
-                16, off, 0, 0, 0);
+            dma16(rk, off, base + (i * C::NW + wave) * 1024);
         }
     };
     // ---- V tile j into slot: the same LDS-DMA pattern with V's swizzle
     auto issue_v = [&](int j, int slot) {
-        char *base = smem + slot * C::STAGE_BYTES + C::K_BYTES;
+        const uint32_t base = lds0 + C::V_OFFSET + slot * C::V_BYTES;
 #pragma unroll
         for (int i = 0; i < C::KL; ++i) {
             const int r = (i * C::NW + wave) * 4 + (lane >> 4);
             const int c = v_chunk(r, lane & 15);
             const uint32_t off = (uint32_t)((j * C::BN + r) * C::D + c * 8) * 2u;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rv, (__attribute__((address_space(3))) void *)(base + (i * C::NW + wave) * 1024),
-                16, off, 0, 0, 0);
+            dma16(rv, off, base + (i * C::NW + wave) * 1024);
         }
     };
     // ---- per-lane byte offsets of the transposing V reads within a V tile:
@@ -156,19 +183,6 @@ attention_fwd_kernel(const _Float16 *__restrict__ Q, const _Float16 *__restrict_
         compiler_fence();
     };
 
-    // ---- prologue: the first tile
-    issue_k(t_lo, 0);
-    issue_v(t_lo, 0);
-    compiler_fence();
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
-    compiler_fence();
-    // the Q fragments count as produced here, after the wait: otherwise the
-    // compiler sinks their loads towards the loop and waits for them (and,
-    // vmcnt being in order, for the next tile's loads) inside every iteration
-#pragma unroll
-    for (int s = 0; s < 8; ++s) asm volatile("" : "+v"(qf[s]));
-    barrier();
-
     const float c2 = alpha * 1.4426950408889634f;     // scores to base-2 exponents
     float mref = -__builtin_inff();                    // reference exponent m (row-wide)
     float lsum = 0.0f;                                 // running sum, this lane's keys
@@ -181,23 +195,14 @@ attention_fwd_kernel(const _Float16 *__restrict__ Q, const _Float16 *__restrict_
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[c][e] = 0.0f;
 
-#pragma unroll 1
-    for (int j = t_lo; j < t_hi; ++j) {
-        const int slot = (j - t_lo) & 1;
-        const bool more = j + 1 < t_hi;
-        if (more) {                                    // refill the other slot (read last in step j - 1)
-            issue_k(j + 1, slot ^ 1);
-            issue_v(j + 1, slot ^ 1);
-        }
-        const char *kbase = smem + slot * C::STAGE_BYTES;
-        const char *vbase = kbase + C::K_BYTES;
-
-        // S = Q K_j^T: lane holds S[row][32 b + 8 g + 4 half + e] in sacc[b][4 g + e]
-        f32x16 sacc[2];
+    // S = Q K^T of the tile in K slot `slot`: lane holds
+    // S[row][32 b + 8 g + 4 half + e] in sa[b][4 g + e]
+    auto scores = [&](int slot, f32x16 (&sa)[2]) {
+        const char *kbase = smem + slot * C::K_BYTES;
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) sacc[b][e] = 0.0f;
+            for (int e = 0; e < 16; ++e) sa[b][e] = 0.0f;
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
 #pragma unroll
@@ -205,94 +210,139 @@ attention_fwd_kernel(const _Float16 *__restrict__ Q, const _Float16 *__restrict_
                 const int key = 32 * b + r32;
                 const f16x8 kf = *(const f16x8 *)(kbase + key * C::K_ROW +
                                                   (k_chunk(key, 2 * s + half) << 4));
-                sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[s], sacc[b], 0, 0, 0);
+                sa[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[s], sa[b], 0, 0, 0);
             }
         }
+    };
 
-        // online softmax for this lane's row (its keys; the partner lane
-        // lane ^ 32 holds the rest of the row).  Keys past N exist only in
-        // the last tile.
-        const int kvalid = N - j * C::BN;              // keys of this tile below N
+    // The online softmax in two halves, for this lane's row (its keys; the
+    // partner lane lane ^ 32 holds the rest of the row).  Keys at or past
+    // kvalid exist only in the last tile.
+    auto key_of = [&](int b, int e) { return 32 * b + 8 * (e >> 2) + 4 * half + (e & 3); };
+    // (1) Before a tile's probabilities: raise m where the row's maximum t in
+    // the tile passed it by more than TAU and scale l to the new m; O is
+    // scaled by the returned factor before the tile's P V, when the returned
+    // flag says some row of the wave raised m (rarely, after the first tile).
+    auto decide = [&](const f32x16 (&sa)[2], int kvalid, float &scale) -> bool {
         const bool ragged = kvalid < C::BN;            // uniform
-        auto key_of = [&](int b, int e) { return 32 * b + 8 * (e >> 2) + 4 * half + (e & 3); };
-        if (ragged) {
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-#pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    if (key_of(b, e) >= kvalid) sacc[b][e] = none;
-        }
         float sx = none;
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) sx = ext(sx, sacc[b][e]);
+            for (int e = 0; e < 16; ++e)
+                sx = ext(sx, (ragged && key_of(b, e) >= kvalid) ? none : sa[b][e]);
         sx = ext(sx, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
                                                    (lane ^ 32) << 2, __builtin_bit_cast(int, sx))));
         // largest t of the row in this tile (finite: the tile has a key below
         // N); rounding is monotonic, so this is the largest rounded product
         const float tmax = sx * c2;
         const bool raise = tmax > mref + C::TAU;
-        if (__builtin_amdgcn_ballot_w64(raise)) {      // uniform: some row of the wave
-            const float mnew = raise ? tmax : mref;
-            const float scale = __builtin_amdgcn_exp2f(mref - mnew);   // 0 on the first tile
-            mref = mnew;
-            lsum *= scale;
+        const float mnew = raise ? tmax : mref;
+        scale = raise ? __builtin_amdgcn_exp2f(mref - mnew) : 1.0f;   // 0 on the first tile
+        mref = mnew;
+        lsum *= scale;
+        return __builtin_amdgcn_ballot_w64(raise) != 0;   // uniform
+    };
+    auto rescale = [&](bool any, float scale) {
+        if (any) {
 #pragma unroll
             for (int c = 0; c < 4; ++c)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) oacc[c][e] *= scale;
         }
+    };
+    // (2) The probabilities 2^(t - m), added to l and returned as fp16 MFMA
+    // fragments: fragment 2 b + t holds sa[b][8 t .. 8 t + 7].
+    auto probs = [&](const f32x16 (&sa)[2], int kvalid, f16x8 (&pf)[4]) {
+        const bool ragged = kvalid < C::BN;            // uniform
         const float negm = -mref;
         float psum = 0.0f;
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[b][e], c2, negm));
-                sacc[b][e] = p;
-                psum += p;
-            }
-        if (ragged) {                                  // alpha = 0 makes the masked t NaN
-            psum = 0.0f;
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    if (key_of(b, e) >= kvalid) sacc[b][e] = 0.0f;
-                    psum += sacc[b][e];
+                for (int e = 0; e < 8; ++e) {
+                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[b][8 * t + e], c2, negm));
+                    if (ragged && key_of(b, 8 * t + e) >= kvalid) p = 0.0f;   // alpha = 0: t is NaN there
+                    psum += p;
+                    pf[2 * b + t][e] = (_Float16)p;
                 }
-        }
         lsum += psum;
+    };
 
-        // O += P V_j: K step (b, t) covers keys 32 b + 16 t + {0..15}; this
-        // lane's 8 probabilities are sacc[b][8 t .. 8 t + 7] (keys
-        // 16 G + 4 half + {0..3} and 16 G + 8 + 4 half + {0..3}, G = 2 b + t),
-        // and the two transposing reads bring V at the same keys, column
-        // 32 c + lane % 32
+    // O += P V for the tile in V slot `slot`: K step f covers keys
+    // 16 f + {0..15}; this lane's probabilities pf[f] are keys
+    // 16 f + 4 half + {0..3} and 16 f + 8 + 4 half + {0..3}, and the two
+    // transposing reads bring V at the same keys, column 32 c + lane % 32
+    auto pv = [&](int slot, const f16x8 (&pf)[4]) {
+        const char *vbase = smem + C::V_OFFSET + slot * C::V_BYTES;
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int f = 0; f < 4; ++f)
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                f16x8 pf;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) pf[e] = (_Float16)sacc[b][8 * t + e];
-                const int G = 2 * b + t;
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    typedef short i16x4 __attribute__((ext_vector_type(4)));
-                    typedef short i16x8 __attribute__((ext_vector_type(8)));
-                    const char *p0 = vbase + vrd[c] + (16 * G) * C::V_ROW;
-                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) i16x4 *)(p0));
-                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) i16x4 *)(p0 + 8 * C::V_ROW));
-                    const f16x8 vf = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                    oacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf, oacc[c], 0, 0, 0);
-                }
+            for (int c = 0; c < 4; ++c) {
+                typedef short i16x4 __attribute__((ext_vector_type(4)));
+                const char *p0 = vbase + vrd[c] + (16 * f) * C::V_ROW;
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4 *)(p0));
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4 *)(p0 + 8 * C::V_ROW));
+                const f16x8 vf = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                oacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[f], oacc[c], 0, 0, 0);
             }
+    };
+    // ---- prologue: K and V of the first tile, K of the second; scores of
+    // the first tile
+    issue_k(t_lo, 0);
+    issue_v(t_lo, 0);
+    if (t_lo + 1 < t_hi) issue_k(t_lo + 1, 1);
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+    compiler_fence();
+    // the Q fragments count as produced here, after the wait: otherwise the
+    // compiler sinks their loads towards the loop and waits for them (and,
+    // vmcnt being in order, for the next tile's loads) inside every iteration
+#pragma unroll
+    for (int s = 0; s < 8; ++s) asm volatile("" : "+v"(qf[s]));
+    barrier();
+    f32x16 sacc[2];
+    scores(0, sacc);
+    float scale;
+    bool any = decide(sacc, N - t_lo * C::BN, scale);
+    barrier();                                         // K slot 0 is refilled next
 
-        barrier();                                     // RAW for tile j + 1, WAR for slot
+    // ---- steady state, software-pipelined.  Step j: tile j's
+    // probabilities, tile j + 1's scores (K runs one tile ahead of V), tile
+    // j's P V, then m for tile j + 1 -- one branch-free stretch for the
+    // scheduler to interleave; the rare rescale of O that m calls for comes
+    // first in the next step.  K_{j+2}
+    // goes to the K slot K_j held (read for S_j in the step before), V_{j+1}
+    // to the V slot V_{j-1} held; both are waited for at the step's closing
+    // barrier, which is also the WAR fence for the next refills.
+    auto step = [&](int j, int kvalid_next) {
+        const int cur = (j - t_lo) & 1;
+        rescale(any, scale);
+        if (j + 2 < t_hi) issue_k(j + 2, cur);
+        issue_v(j + 1, cur ^ 1);
+        f16x8 pf[4];
+        probs(sacc, C::BN, pf);
+        f32x16 snext[2];
+        scores(cur ^ 1, snext);
+        pv(cur, pf);
+        any = decide(snext, kvalid_next, scale);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) sacc[b] = snext[b];
+        barrier();                                     // RAW for K_{j+2}, V_{j+1}; WAR for both slots
+    };
+#pragma unroll 1
+    for (int j = t_lo; j < t_hi - 2; ++j) step(j, C::BN);
+    if (t_hi - t_lo >= 2) step(t_hi - 2, N - (t_hi - 1) * C::BN);   // next is the last tile
+    {   // ---- the last tile (the only one that can be ragged)
+        const int j = t_hi - 1;
+        rescale(any, scale);
+        f16x8 pf[4];
+        probs(sacc, N - j * C::BN, pf);
+        pv((j - t_lo) & 1, pf);
     }
 
     const float lother = __builtin_bit_cast(
