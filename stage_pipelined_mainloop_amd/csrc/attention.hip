@@ -21,7 +21,7 @@ sg_status check_args(int H, int M, int N, int d, const void *Q, const void *K, c
                      const void *O)
 {
     if (H < 0 || M < 0 || N < 0 || d < 0) return SG_ERR_SHAPE;
-    if (d != sg::AttnCfg::D) return SG_ERR_UNSUPPORTED;
+    if (d != sg::AttnCfg<4>::D) return SG_ERR_UNSUPPORTED;
     if (N == 0) return SG_ERR_SHAPE;                    // softmax over no keys
     if (!Q || !K || !V || !O) return SG_ERR_NULL;
     if (N > (1 << 21) || M > (1 << 21)) return SG_ERR_SHAPE;
@@ -37,35 +37,56 @@ sg_status check_args(int H, int M, int N, int d, const void *Q, const void *K, c
     return SG_OK;
 }
 
-int key_tiles(int N) { return (N + sg::AttnCfg::BN - 1) / sg::AttnCfg::BN; }
+int key_tiles(int N) { return (N + sg::AttnCfg<4>::BN - 1) / sg::AttnCfg<4>::BN; }
 
 size_t workspace_bytes(int H, int M, int splits)
 {
-    return (size_t)H * splits * M * (sg::AttnCfg::D + 2) * sizeof(float);
+    return (size_t)H * splits * M * (sg::AttnCfg<4>::D + 2) * sizeof(float);
 }
 
+// Compute units of the current device (cached per device; 0 if the query
+// fails).
+int device_cus()
+{
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev < 64 && cache[dev] > 0) return cache[dev];
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    if (dev < 64) cache[dev] = cus;
+    return cus;
+}
+
+long long row_blocks(int M, int bm) { return (M + bm - 1) / bm; }
+
 // splits == 1: O directly; otherwise the partials go to part_o / part_ml and
-// a second kernel merges them.
+// a second kernel merges them.  Unsplit calls whose 256-row workgroups fill
+// every CU take the 8-wave kernel, all others the 4-wave one.
 sg_status launch(int H, int M, int N, float alpha, const void *Q, const void *K, const void *V,
                  void *O, int splits, void *workspace, hipStream_t stream)
 {
-    const long long blocks =
-        (long long)H * ((M + sg::AttnCfg::BM - 1) / sg::AttnCfg::BM) * splits;
+    const bool wide = splits == 1 && H * row_blocks(M, sg::AttnCfg<8>::BM) >= device_cus() &&
+                      device_cus() > 0;
+    const int bm = wide ? sg::AttnCfg<8>::BM : sg::AttnCfg<4>::BM;
+    const long long blocks = (long long)H * row_blocks(M, bm) * splits;
     if (blocks >= (1LL << 31)) return SG_ERR_SHAPE;
     typedef void (*attn_fn)(const _Float16 *, const _Float16 *, const _Float16 *, _Float16 *,
                             float *, float *, int, int, float, int);
-    const attn_fn kernel = alpha < 0.0f ? &sg::attention_fwd_kernel<true>
-                                        : &sg::attention_fwd_kernel<false>;   // fails to compile on drift
+    const attn_fn kernel =
+        wide ? (alpha < 0.0f ? &sg::attention_fwd_kernel<true, 8> : &sg::attention_fwd_kernel<false, 8>)
+             : (alpha < 0.0f ? &sg::attention_fwd_kernel<true, 4> : &sg::attention_fwd_kernel<false, 4>);
     const _Float16 *q = static_cast<const _Float16 *>(Q);
     const _Float16 *k = static_cast<const _Float16 *>(K);
     const _Float16 *v = static_cast<const _Float16 *>(V);
     _Float16 *o = static_cast<_Float16 *>(O);
     float *part_o = splits > 1 ? static_cast<float *>(workspace) : nullptr;
-    float *part_ml = splits > 1 ? part_o + (size_t)H * splits * M * sg::AttnCfg::D : nullptr;
+    float *part_ml = splits > 1 ? part_o + (size_t)H * splits * M * sg::AttnCfg<4>::D : nullptr;
     void *args[] = {&q, &k, &v, &o, &part_o, &part_ml, &M, &N, &alpha, &splits};
     static_assert(sizeof(args) / sizeof(args[0]) == 10, "one entry per kernel parameter");
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(kernel), dim3((unsigned)blocks),
-                                   dim3(sg::AttnCfg::T), args, 0, stream);
+                                   dim3(64 * (wide ? 8 : 4)), args, 0, stream);
     if (e != hipSuccess || splits == 1) return e == hipSuccess ? SG_OK : SG_ERR_HIP;
 
     long long HM = (long long)H * M;
@@ -96,17 +117,14 @@ sg_status attention_fp16_fwd(int H, int M, int N, int d, float alpha, const void
 
 int attention_fp16_splits(int H, int M, int N, int d)
 {
-    if (H < 1 || M < 1 || N < 1 || d != sg::AttnCfg::D) return -1;
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus < 1)
-        return -1;
+    if (H < 1 || M < 1 || N < 1 || d != sg::AttnCfg<4>::D) return -1;
+    const int cus = device_cus();
+    if (cus < 1) return -1;
     // two workgroups per CU are resident; aim for that many, with at least
     // eight key tiles per split so the ring's prologue, the partial write and
     // the merge stay small next to the work (one head of 4096 x 4096 x 128:
     // 8 splits 31.6 us, 16 splits 35.4, 4 splits 36.5, none 96)
-    const long long blocks = (long long)H * ((M + sg::AttnCfg::BM - 1) / sg::AttnCfg::BM);
+    const long long blocks = (long long)H * ((M + sg::AttnCfg<4>::BM - 1) / sg::AttnCfg<4>::BM);
     const long long target = 2LL * cus;
     if (blocks >= target) return 1;
     long long splits = (target + blocks - 1) / blocks;
@@ -117,7 +135,7 @@ int attention_fp16_splits(int H, int M, int N, int d)
 
 size_t attention_fp16_workspace_bytes(int H, int M, int N, int d, int splits)
 {
-    if (H < 1 || M < 1 || N < 1 || d != sg::AttnCfg::D || splits <= 1) return 0;
+    if (H < 1 || M < 1 || N < 1 || d != sg::AttnCfg<4>::D || splits <= 1) return 0;
     if (splits > key_tiles(N)) splits = key_tiles(N);
     return splits > 1 ? workspace_bytes(H, M, splits) : 0;
 }

@@ -2,8 +2,9 @@
 // 2", section "Softmax Attention": scores Q K^T / sqrt(d), a row-wise softmax,
 // then the product with V), for H independent heads with d = 128.
 //
-// The scores never leave the chip.  Each workgroup owns 128 query rows of one
-// head (4 waves, 32 rows each) and streams the head's keys in tiles of 64
+// The scores never leave the chip.  Each workgroup owns 128 or 256 query rows
+// of one head (4 or 8 waves, 32 rows each) and streams the head's keys in
+// tiles of 64
 // through a two-slot LDS ring -- the stage-pipelined mainloop of "Lesson 6":
 // while tile j is consumed, tile j + 1's K and V rows arrive by LDS-DMA --
 // and keeps a reference exponent m, a row sum l
@@ -33,11 +34,12 @@ namespace sg {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+template <int NWAVES>
 struct AttnCfg {
     static constexpr int D = 128;                  // head dimension
-    static constexpr int BM = 128;                 // query rows per workgroup
+    static constexpr int BM = 32 * NWAVES;         // query rows per workgroup
     static constexpr int BN = 64;                  // keys per tile
-    static constexpr int NW = 4;                   // waves, 32 query rows each
+    static constexpr int NW = NWAVES;              // waves, 32 query rows each
     static constexpr int T = 64 * NW;
     static constexpr int K_ROW = D * 2;            // 256-byte K rows
     static constexpr int K_BYTES = BN * K_ROW;     // 16 KiB
@@ -90,14 +92,19 @@ __device__ __forceinline__ void dma16(const u32x4 &rsrc, uint32_t voff, uint32_t
 // to part_ml; attention_combine_kernel then merges the splits of each row.
 // This gives a single head enough workgroups to fill the device.  Layouts
 // (fp32): part_o[(h * splits + sp) * M + row][D], part_ml[same index][2].
-template <bool NEG>
-__global__ void __launch_bounds__(AttnCfg::T, 2)
+//
+// NWAVES: 4 (128 query rows, two workgroups per CU) or 8 (256 rows, one per
+// CU).  Both keep 8 waves on a CU; with 8 per workgroup every K and V tile
+// is fetched into LDS once for twice the rows, which halves the DMA traffic
+// per flop (measured -5 % time on 16 heads of 4096 x 4096).
+template <bool NEG, int NWAVES>
+__global__ void __launch_bounds__(64 * NWAVES, 8 / NWAVES)
 attention_fwd_kernel(const _Float16 *__restrict__ Q, const _Float16 *__restrict__ Kg,
                      const _Float16 *__restrict__ V, _Float16 *__restrict__ O,
                      float *__restrict__ part_o, float *__restrict__ part_ml, int M, int N,
                      float alpha, int splits)
 {
-    using C = AttnCfg;
+    using C = AttnCfg<NWAVES>;
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
     const int lane = threadIdx.x & 63;
@@ -402,7 +409,7 @@ __global__ void __launch_bounds__(256)
 attention_combine_kernel(const float *__restrict__ part_o, const float *__restrict__ part_ml,
                          _Float16 *__restrict__ O, long long HM, int M, int splits)
 {
-    using C = AttnCfg;
+    using C = AttnCfg<4>;
     const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
     const long long hr = t >> 5;                       // h * M + row
     if (hr >= HM) return;

@@ -147,6 +147,36 @@ def test_split_choice_and_workspace_reuse():
         assert np.all(np.abs(o.cpu().numpy().astype(np.float64) - ref.astype(np.float64)) <= bound)
 
 
+@pytest.mark.parametrize("H,M,N", [(64, 1024, 300), (256, 200, 77), (260, 129, 64)])
+def test_wide_workgroups(H, M, N):
+    # grids whose 256-row workgroups fill every CU take the 8-wave kernel
+    # (ragged M inside a 256-row block included)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert H * -(-M // 256) >= cus
+    Q, K, V = qkv(H, M, N, 4121 + H)
+    check(Q, K, V, float(np.float32(1.0 / math.sqrt(128))), f"wide {H}x{M}x{N}")
+    check(Q, K, V, -0.07, f"wide {H}x{M}x{N} alpha<0")
+
+
+def test_sixteen_heads_sampled_rows():
+    # the 16-head 4096 x 4096 x 128 shape the bench times: every output
+    # finite, 48 sampled rows per head against the oracle
+    H, M, N = 16, 4096, 4096
+    Q, K, V = qkv(H, M, N, 4123)
+    alpha = float(np.float32(1.0 / math.sqrt(128)))
+    say(f"[case] attention 16 heads full, sampled rows")
+    O = gpu_attention(Q, K, V, alpha).astype(np.float64)
+    assert np.all(np.isfinite(O))
+    g = np.random.Generator(np.random.PCG64(4125))
+    rows = np.sort(np.concatenate([[0, 255, 256, M - 1], g.choice(M, 44, replace=False)]))
+    ref, w = oracle.attention_f64(np.ascontiguousarray(Q[:, rows]), K, V, alpha, with_bound=True)
+    ref = ref.astype(np.float64)
+    bound = 2 * oracle.ulp16(np.abs(ref)) + 2 * (2.0 ** -11 + N * 2.0 ** -24) * w
+    err = np.abs(O[:, rows] - ref)
+    say(f"         max |err| {err.max():.3g}, max |err| / bound {float((err / bound).max()):.3f}")
+    assert np.all(err <= bound)
+
+
 def test_attention_config_full():
     # the attention-score workload's Q and K (4096 x 128, N(0,1)) with a V of
     # the same shape, alpha = fp32(1/sqrt(128)); every output against the oracle
