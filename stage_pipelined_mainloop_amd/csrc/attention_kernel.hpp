@@ -417,17 +417,36 @@ attention_combine_kernel(const float *__restrict__ part_o, const float *__restri
     const long long h = hr / M;
     const long long row = hr - h * M;
     const size_t first = (size_t)h * splits * M + row;   // index of split 0
+    // one online pass, four runs per round so their loads are in flight together
     float mx = -__builtin_inff();
-    for (int s = 0; s < splits; ++s) mx = __builtin_fmaxf(mx, part_ml[(first + (size_t)s * M) * 2]);
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     float l = 0.0f;
-    for (int s = 0; s < splits; ++s) {
-        const size_t i = first + (size_t)s * M;
-        const float w = __builtin_amdgcn_exp2f(part_ml[i * 2] - mx);
-        l += w * part_ml[i * 2 + 1];
-        const f32x4 o = *(const f32x4 *)(part_o + i * C::D + col);
+    for (int s0 = 0; s0 < splits; s0 += 4) {
+        float ms[4], ls[4];
+        f32x4 os[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] += w * o[e];
+        for (int u = 0; u < 4; ++u) {
+            const size_t i = first + (size_t)(s0 + u < splits ? s0 + u : s0) * M;
+            typedef float f32x2 __attribute__((ext_vector_type(2)));
+            const f32x2 ml = *(const f32x2 *)(part_ml + i * 2);
+            ms[u] = s0 + u < splits ? ml[0] : -__builtin_inff();
+            ls[u] = ml[1];
+            os[u] = *(const f32x4 *)(part_o + i * C::D + col);
+        }
+        const float mr = __builtin_fmaxf(__builtin_fmaxf(ms[0], ms[1]), __builtin_fmaxf(ms[2], ms[3]));
+        const float mnew = __builtin_fmaxf(mx, mr);
+        const float keep = __builtin_amdgcn_exp2f(mx - mnew);   // 0 in the first round
+        l *= keep;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] *= keep;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float w = __builtin_amdgcn_exp2f(ms[u] - mnew);   // 0 for the padding runs
+            l += w * ls[u];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] += w * os[u][e];
+        }
+        mx = mnew;
     }
     const float inv = 1.0f / l;
     u32x2 packed;
