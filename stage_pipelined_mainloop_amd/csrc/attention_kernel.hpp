@@ -4,11 +4,10 @@
 //
 // The scores never leave the chip.  Each workgroup owns 128 or 256 query rows
 // of one head (4 or 8 waves, 32 rows each) and streams the head's keys in
-// tiles of 64
-// through a two-slot LDS ring -- the stage-pipelined mainloop of "Lesson 6":
-// while tile j is consumed, tile j + 1's K and V rows arrive by LDS-DMA --
-// and keeps a reference exponent m, a row sum l
-// and an output accumulator O (the online form of the softmax):
+// tiles of 64 through two-slot LDS rings for K and V, filled by LDS-DMA one
+// and two tiles ahead -- the stage-pipelined mainloop of "Lesson 6" -- and
+// keeps a reference exponent m, a row sum l and an output accumulator O (the
+// online form of the softmax):
 //     S = Q K_j^T (MFMA, fp32), t = S * alpha * log2(e)
 //     P = 2^(t - m), O += P V_j, l += sum P
 // and writes O / l once at the end.  The quotient does not depend on m, so m

@@ -206,3 +206,66 @@ def test_empty_and_unsupported():
     q64 = torch.zeros((1, 8, 64), dtype=torch.float16, device=DEV)
     with pytest.raises(sg.SgError):
         sg.attention(q64, q64, q64)
+
+
+def test_graph_replays_match_eager():
+    # no allocation, memset or host synchronisation on the launch path (the
+    # split call's workspace is the caller's): captured into a HIP graph,
+    # replays with eager work between them reproduce the eager result bit for
+    # bit, for the 4-wave, 8-wave and split kernels
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for (H, M, N, splits) in [(2, 300, 700, 1), (cus, 256, 200, 1), (1, 512, 2048, 4)]:
+        say(f"[case] attention graph H={H} M={M} N={N} splits={splits}")
+        Q, K, V = qkv(H, M, N, 4127 + N)
+        q, k, v = (torch.from_numpy(x).to(DEV) for x in (Q, K, V))
+        need = max(sg.attention_fp16_workspace_bytes(H, M, N, 128, splits), 16)
+        ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+        eager = sg.attention(q, k, v, alpha=0.09, splits=splits, workspace=ws)
+        torch.cuda.synchronize()
+        out = torch.empty_like(eager)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            sg.attention(q, k, v, alpha=0.09, out=out, splits=splits, workspace=ws)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            sg.attention(q, k, v, alpha=0.09, out=out, splits=splits, workspace=ws)
+        for r in range(4):
+            out.fill_(float("nan"))
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), (H, M, N, splits, r)
+            tmp = sg.attention(q, k, v, alpha=0.09, splits=splits, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(tmp.view(torch.int16), eager.view(torch.int16))
+
+
+def test_two_streams_concurrently():
+    # a split call and a wide call on two streams at once, each with its own
+    # workspace, both match the oracle
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    Q1, K1, V1 = qkv(1, 1024, 3000, 4129)
+    Q2, K2, V2 = qkv(cus, 256, 100, 4131)
+    d1 = [torch.from_numpy(x).to(DEV) for x in (Q1, K1, V1)]
+    d2 = [torch.from_numpy(x).to(DEV) for x in (Q2, K2, V2)]
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    ws1 = torch.empty(sg.attention_fp16_workspace_bytes(1, 1024, 3000, 128, 6), dtype=torch.uint8, device=DEV)
+    outs = []
+    torch.cuda.synchronize()
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            o1 = sg.attention(*d1, alpha=0.1, splits=6, workspace=ws1)
+        with torch.cuda.stream(s2):
+            o2 = sg.attention(*d2, alpha=0.1)
+        outs.append((o1, o2))
+        s1.synchronize()                               # ws1 is reused by the next round
+    torch.cuda.synchronize()
+    for (Q, K, V), idx in (((Q1, K1, V1), 0), ((Q2, K2, V2), 1)):
+        ref, w = oracle.attention_f64(Q, K, V, 0.1, with_bound=True)
+        ref = ref.astype(np.float64)
+        bound = 2 * oracle.ulp16(np.abs(ref)) + 2 * (2.0 ** -11 + K.shape[1] * 2.0 ** -24) * w
+        for pair in outs:
+            err = np.abs(pair[idx].cpu().numpy().astype(np.float64) - ref)
+            assert np.all(err <= bound), idx
