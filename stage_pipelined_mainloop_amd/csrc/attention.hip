@@ -67,11 +67,13 @@ long long row_blocks(int M, int bm) { return (M + bm - 1) / bm; }
 sg_status launch(int H, int M, int N, float alpha, const void *Q, const void *K, const void *V,
                  void *O, int splits, void *workspace, hipStream_t stream)
 {
-    const bool wide = splits == 1 && H * row_blocks(M, sg::AttnCfg<8>::BM) >= device_cus() &&
-                      device_cus() > 0;
+    // the 4-wave grid is the larger one: bound it before any HIP call
+    if ((long long)H * row_blocks(M, sg::AttnCfg<4>::BM) * splits >= (1LL << 31))
+        return SG_ERR_SHAPE;
+    const int cus = splits == 1 ? device_cus() : 0;
+    const bool wide = cus > 0 && H * row_blocks(M, sg::AttnCfg<8>::BM) >= cus;
     const int bm = wide ? sg::AttnCfg<8>::BM : sg::AttnCfg<4>::BM;
     const long long blocks = (long long)H * row_blocks(M, bm) * splits;
-    if (blocks >= (1LL << 31)) return SG_ERR_SHAPE;
     typedef void (*attn_fn)(const _Float16 *, const _Float16 *, const _Float16 *, _Float16 *,
                             float *, float *, int, int, float, int);
     const attn_fn kernel =
@@ -120,10 +122,10 @@ int attention_fp16_splits(int H, int M, int N, int d)
     if (H < 1 || M < 1 || N < 1 || d != sg::AttnCfg<4>::D) return -1;
     const int cus = device_cus();
     if (cus < 1) return -1;
-    // two workgroups per CU are resident; aim for that many, with at least
-    // eight key tiles per split so the ring's prologue, the partial write and
-    // the merge stay small next to the work (one head of 4096 x 4096 x 128:
-    // 8 splits 31.6 us, 16 splits 35.4, 4 splits 36.5, none 96)
+    // two 4-wave workgroups per CU are resident; aim for that many, with at
+    // least eight key tiles per split so the ring's prologue, the partial
+    // write and the merge stay small next to the work (one head of
+    // 4096 x 4096 x 128 measured fastest at 8 splits, ahead of 4 and 16)
     const long long blocks = (long long)H * ((M + sg::AttnCfg<4>::BM - 1) / sg::AttnCfg<4>::BM);
     const long long target = 2LL * cus;
     if (blocks >= target) return 1;
