@@ -100,6 +100,18 @@ def mfma_ceiling(a, b, target_ms: float = 20.0):
     return L.sg_probe_mfma_ceiling_flops(blocks, iters) / (e0.elapsed_time(e1) / 1e3) / 1e12
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (first processor in /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(A, B, target_s: float):
     import oracle
     M, K = A.shape
@@ -114,7 +126,7 @@ def cpu_baseline(A, B, target_s: float):
     dt = time.perf_counter() - t0
     flops = 2.0 * rows * N * K
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu_model(),
             "sample": f"rows 0..{rows - 1} of D ({rows} x {N} outputs, K={K}), fp64 accumulation, "
                       f"{dt:.1f} s wall"}
 
