@@ -206,9 +206,11 @@ sg_status attention_fp16_fwd_split(int H, int M, int N, int d, float alpha, cons
  * with s = min(splits, key tiles); 0 when s <= 1 or the sizes are invalid. */
 size_t attention_fp16_workspace_bytes(int H, int M, int N, int d, int splits);
 
-/* The split count this library would use on the current device: 1 when
- * H * ceil(M / 128) workgroups already reach two per compute unit, otherwise
- * enough splits for that, with at least eight key tiles each.  -1 for invalid
+/* The split count this library would use on the current device: the count
+ * (1 to min(64, key tiles)) that minimises a cost model of the forward (about
+ * one 64-key tile per microsecond per compute unit, bounded below by one
+ * workgroup's own tiles) plus the merge (a fixed cost and the fp32 partials'
+ * traffic).  1 whenever the heads already fill the device.  -1 for invalid
  * sizes (d != 128 included) or a failed device query. */
 int attention_fp16_splits(int H, int M, int N, int d);
 

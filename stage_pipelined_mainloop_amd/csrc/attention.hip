@@ -122,17 +122,29 @@ int attention_fp16_splits(int H, int M, int N, int d)
     if (H < 1 || M < 1 || N < 1 || d != sg::AttnCfg<4>::D) return -1;
     const int cus = device_cus();
     if (cus < 1) return -1;
-    // two 4-wave workgroups per CU are resident; aim for that many, with at
-    // least eight key tiles per split so the ring's prologue, the partial
-    // write and the merge stay small next to the work (one head of
-    // 4096 x 4096 x 128 measured fastest at 8 splits, ahead of 4 and 16)
+    // A cost model fitted to one box's timings of 4-wave workgroups (128
+    // rows, d = 128): a CU runs about one 64-key tile per microsecond, shared
+    // by the workgroups it holds, so the forward takes
+    //     max(tiles per workgroup, all tiles / CUs) microseconds,
+    // and a split call adds the merge: about 4 us (its launch and the partial
+    // epilogue) plus writing and reading the fp32 partials at about 5 TB/s.
+    // The split count with the smallest estimate wins (ties: fewer splits).
+    // It reproduces the fastest measured count on one head at 1024 to 4096
+    // keys (8), four heads at 2048 (4) and sixteen heads at 512 to 4096 (1).
+    constexpr double kTileUs = 1.0, kMergeUs = 4.0, kBytesPerUs = 5.0e6;
     const long long blocks = (long long)H * ((M + sg::AttnCfg<4>::BM - 1) / sg::AttnCfg<4>::BM);
-    const long long target = 2LL * cus;
-    if (blocks >= target) return 1;
-    long long splits = (target + blocks - 1) / blocks;
-    const long long most = key_tiles(N) / 8;
-    if (splits > most) splits = most;
-    return splits < 1 ? 1 : (int)splits;
+    const int tiles = key_tiles(N);
+    int best_s = 1;
+    double best = 0.0;
+    for (int s = 1; s <= tiles && s <= 64; ++s) {
+        const long long per_wg = (tiles + s - 1) / s;
+        const double work = (double)blocks * s * per_wg / cus;
+        double t = kTileUs * (per_wg > work ? (double)per_wg : work);
+        if (s > 1) t += kMergeUs + 2.0 * (double)workspace_bytes(H, M, s) / kBytesPerUs;
+        if (s == 1 || t < best) { best = t; best_s = s; }
+        if (blocks * s >= 4LL * cus) break;            // more splits only add partials
+    }
+    return best_s;
 }
 
 size_t attention_fp16_workspace_bytes(int H, int M, int N, int d, int splits)
