@@ -108,3 +108,61 @@ def test_heads_are_independent():
     for h in range(4):
         assert np.array_equal(O[h].view(np.uint16),
                               oracle.attention_f64(Q[h], K[h], V[h], 0.3).view(np.uint16))
+
+
+def _exact_rounded(Q, K, V, alpha):
+    """O rounded once to fp16 from a 60-digit evaluation of the definition
+    (decimal module: exact products and sums of the fp16 inputs, exp to 60
+    digits); None where the value lies within 1e-12 (relative) of an fp16
+    rounding midpoint, where the oracle's fp64 evaluation (error far below
+    that) may legitimately round either way."""
+    import decimal
+    from decimal import Decimal
+    ctx = decimal.Context(prec=60)
+    M, d = Q.shape
+    N = K.shape[0]
+    a = Decimal(float(alpha))
+    out = np.empty((M, d), dtype=object)
+    for i in range(M):
+        s = [ctx.multiply(a, sum((Decimal(float(Q[i, c])) * Decimal(float(K[j, c])) for c in range(d)),
+                                 Decimal(0))) for j in range(N)]
+        m = max(s)
+        w = [ctx.exp(ctx.subtract(sj, m)) for sj in s]
+        tot = sum(w, Decimal(0))
+        for c in range(d):
+            v = ctx.divide(sum((ctx.multiply(w[j], Decimal(float(V[j, c]))) for j in range(N)), Decimal(0)), tot)
+            h = np.float16(float(v))                  # RNE of the nearest double
+            # the two fp16 neighbours of v and their midpoint, exactly
+            up = np.nextafter(h, np.float16(np.inf))
+            dn = np.nextafter(h, np.float16(-np.inf))
+            for other in (up, dn):
+                mid = (Decimal(float(h)) + Decimal(float(other))) / 2
+                if abs(v - mid) <= abs(v) * Decimal("1e-12"):
+                    h = None
+                    break
+            out[i, c] = h
+    return out
+
+
+@pytest.mark.parametrize("seed,alpha", [(3019, 1 / math.sqrt(8)), (3021, 0.9), (3023, -0.6), (3025, 4.0),
+                                        (3027, 0.0)])
+def test_equals_correctly_rounded_exact_value(seed, alpha):
+    # the oracle's fp64 evaluation rounds to the same fp16 as a 60-digit
+    # evaluation of the definition, element by element (flat, sharp and
+    # negative-alpha softmaxes; any dropped term, wrong sign or index breaks it)
+    g = np.random.Generator(np.random.PCG64(seed))
+    M, N, d = 4, 6, 8
+    Q = g.standard_normal((M, d)).astype(np.float16)
+    K = g.standard_normal((N, d)).astype(np.float16)
+    V = g.standard_normal((N, d)).astype(np.float16)
+    a32 = float(np.float32(alpha))
+    O = oracle.attention_f64(Q, K, V, a32)
+    ex = _exact_rounded(Q, K, V, a32)
+    decided = 0
+    for i in range(M):
+        for c in range(d):
+            if ex[i, c] is None:
+                continue
+            decided += 1
+            assert O[i, c].view(np.uint16) == ex[i, c].view(np.uint16), (i, c, O[i, c], ex[i, c])
+    assert decided >= M * d - 2
