@@ -74,7 +74,15 @@ typedef enum sg_status {
  *      output tiles whose K tiles stream through one ring (order 1 within
  *      each), so the next tile's loads overlap this tile's last MFMAs and
  *      epilogue; two or three stages, D = alpha * A * B^T only (the C
- *      operand of gemm_fp16_tn_alpha_beta selects another variant). */
+ *      operand of gemm_fp16_tn_alpha_beta selects another variant);
+ *   4  short K: the whole K extent (K <= stages * tile_k) loaded into the
+ *      ring at once, then each wave's row blocks computed and stored in
+ *      turn; D = alpha * A * B^T only (SG_ERR_UNSUPPORTED for a longer K or
+ *      with a C operand);
+ *   5  order 1 on 16x16x32 MFMAs instead of 32x32x16 (tile_k 64): the same
+ *      LDS traffic per flop, a different balance between clock and MFMA
+ *      occupancy under the power limit.  Compiled for comparison; the
+ *      library's own choice never takes it. */
 typedef struct sg_config {
     int tile_m;
     int tile_n;

@@ -56,6 +56,7 @@ namespace sg {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // gfx9 buffer resource word 3 (raw 32-bit data format, no swizzle).
@@ -144,11 +145,20 @@ __device__ __forceinline__ int swz(int r)
 // SCHED selects the mainloop order: 0 = the three-phase order of "Lesson 6"
 // (wait, barrier, refill, compute), 1 = the cute page's order with the next
 // tile's first fragments prefetched across the barrier, 2 = ping-pong of two
-// wave groups (one computes while the other reads and refills).
+// wave groups (one computes while the other reads and refills), 3 =
+// persistent, 4 = short K, 5 = order 1 on 16x16x32 MFMAs.
+//
+// MFMA shape.  Orders 0-4 use v_mfma_f32_32x32x16_f16 (32x32 blocks, K steps
+// of 16); order 5 uses v_mfma_f32_16x16x32_f16 (16x16 blocks, K steps of
+// 32).  The LDS bytes read per flop are the same (a fragment is 1 KiB either
+// way), but under the power limit the 16x16x32 form sustains more
+// throughput on the same operands (measured 1867 against 1628 TFLOP/s in an
+// MFMA-only loop on uniform [-1, 1] fp16 data).
 template <int BM_, int BN_, int BK_, int S_, int WM_, int WN_, int SCHED_ = 1>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_, WM = WM_, WN = WN_;
     static constexpr int SCHED = SCHED_;
+    static constexpr bool MF16 = SCHED == 5;        // 16x16x32 MFMAs
     static constexpr int NW = WM * WN;              // wavefronts
     static constexpr int T = 64 * NW;               // threads
     static constexpr int WTM = BM / WM;             // wave sub-tile
@@ -157,7 +167,11 @@ struct Cfg {
     static constexpr int FN = WTN / 32;
     static constexpr int RB = BK * 2;               // LDS row bytes
     static constexpr int CPR = BK / 8;              // 16-byte chunks per row
-    static constexpr int NKS = BK / 16;             // MFMA K steps per tile
+    static constexpr int KSTEP = MF16 ? 32 : 16;    // K depth of one MFMA
+    static constexpr int NKS = BK / KSTEP;          // MFMA K steps per tile
+    static constexpr int MB = MF16 ? 16 : 32;       // rows of one MFMA block
+    static constexpr int AM = WTM / MB;             // MFMA blocks per wave
+    static constexpr int AN = WTN / MB;
     static constexpr int A_BYTES = BM * RB;
     static constexpr int B_BYTES = BN * RB;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
@@ -173,7 +187,8 @@ struct Cfg {
     // swizzle keeps the accesses conflict-free).
     static constexpr int EPI_BLOCK_WAVE_BYTES = 32 * WTN * 2;
     static constexpr int EPI_BLOCK_BYTES = NW * EPI_BLOCK_WAVE_BYTES;
-    static constexpr int LDS_BYTES = SCHED >= 3 ? RING_BYTES + EPI_BLOCK_BYTES
+    static constexpr bool OWN_STAGING = SCHED == 3 || SCHED == 4;   // staging beside the ring
+    static constexpr int LDS_BYTES = OWN_STAGING ? RING_BYTES + EPI_BLOCK_BYTES
                                    : (RING_BYTES > EPI_BYTES ? RING_BYTES : EPI_BYTES);
     // Epilogue stores per lane per output tile: 16 bytes each, WTN * 2 / 16
     // lanes per sub-tile row.
@@ -184,9 +199,10 @@ struct Cfg {
     static constexpr int NB = BN * CPR / (64 * NW);
     static constexpr int L = NA + NB;
     static_assert(S >= 2, "a ring needs at least two slots");
-    static_assert(SCHED >= 0 && SCHED <= 4, "mainloop order");
+    static_assert(SCHED >= 0 && SCHED <= 5, "mainloop order");
+    static_assert(!MF16 || BK == 64, "16x16x32 order: two K steps of 32 per tile");
     static_assert(SCHED != 3 || S == 2 || S == 3, "persistent ring: two or three slots");
-    static_assert(SCHED < 3 || WTN == 64, "unpadded staging rows are 128 bytes");
+    static_assert(!OWN_STAGING || WTN == 64, "unpadded staging rows are 128 bytes");
     static_assert(SCHED != 2 || (S == 2 && NW % 4 == 0 && (NW / 2) % 2 == 0 && BK == 64),
                   "ping-pong: two slots, two even wave groups, 128-byte rows");
     static_assert(NKS % 2 == 0, "fragment double buffer alternates per K step");
@@ -301,7 +317,7 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
                const _Float16 *Cm, _Float16 *D, int M, int N, int K, float alpha, float beta,
                int kt_rot)
 {
-    static_assert(C::SCHED <= 2, "schedules 3 and 4 have kernels of their own");
+    static_assert(C::SCHED <= 2 || C::SCHED == 5, "schedules 3 and 4 have kernels of their own");
     // Cm and D may be the same buffer (in-place D = alpha A B^T + beta D): each
     // wave reads C only inside its own sub-tile and finishes those reads
     // before it stores, so they are not declared __restrict__.
@@ -372,42 +388,50 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
     };
 
     // ---- per-lane fragment read offsets within a slot (bytes), per MFMA K step
-    const int half = lane >> 5;                      // which 8-wide K group of the step
-    const int ra_row = wm * C::WTM + (lane & 31);
-    const int rb_row = wn * C::WTN + (lane & 31);
+    // 32x32x16: lane reads row lane % 32 of a block, 8-wide K group lane / 32;
+    // 16x16x32: row lane % 16, K group lane / 16 (four per 32-deep step)
+    const int half = lane >> 5;
+    const int ra_row = wm * C::WTM + (lane & (C::MB - 1));
+    const int rb_row = wn * C::WTN + (lane & (C::MB - 1));
     int fa[C::NKS], fb[C::NKS];
 #pragma unroll
     for (int ks = 0; ks < C::NKS; ++ks) {
-        const int c = 2 * ks + half;
+        const int c = C::MF16 ? 4 * ks + (lane >> 4) : 2 * ks + half;
         fa[ks] = ra_row * C::RB + ((c ^ swz<C::CPR>(ra_row)) << 4);
         fb[ks] = C::A_BYTES + rb_row * C::RB + ((c ^ swz<C::CPR>(rb_row)) << 4);
     }
 
-    f32x16 acc[C::FM][C::FN];
+    using Acc = std::conditional_t<C::MF16, f32x4v, f32x16>;
+    constexpr int ACC_N = C::MF16 ? 4 : 16;
+    Acc acc[C::AM][C::AN];
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i)
+    for (int i = 0; i < C::AM; ++i)
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j)
+        for (int j = 0; j < C::AN; ++j)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+            for (int e = 0; e < ACC_N; ++e) acc[i][j][e] = 0.0f;
 
     // LDS -> VGPR fragments of one MFMA K step, and the MFMAs of one K step.
     // Read order follows first use by mfma_step: A0, all of B, then A1...
-    auto read_frags = [&](f16x8 (&ra)[C::FM], f16x8 (&rb)[C::FN], const char *sbase, int ks) {
+    auto read_frags = [&](f16x8 (&ra)[C::AM], f16x8 (&rb)[C::AN], const char *sbase, int ks) {
         ra[0] = *(const f16x8 *)(sbase + fa[ks]);
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j)
-            rb[j] = *(const f16x8 *)(sbase + fb[ks] + j * 32 * C::RB);
+        for (int j = 0; j < C::AN; ++j)
+            rb[j] = *(const f16x8 *)(sbase + fb[ks] + j * C::MB * C::RB);
 #pragma unroll
-        for (int i = 1; i < C::FM; ++i)
-            ra[i] = *(const f16x8 *)(sbase + fa[ks] + i * 32 * C::RB);
+        for (int i = 1; i < C::AM; ++i)
+            ra[i] = *(const f16x8 *)(sbase + fa[ks] + i * C::MB * C::RB);
     };
-    auto mfma_step = [&](const f16x8 (&ra)[C::FM], const f16x8 (&rb)[C::FN]) {
+    auto mfma_step = [&](const f16x8 (&ra)[C::AM], const f16x8 (&rb)[C::AN]) {
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i)
+        for (int i = 0; i < C::AM; ++i)
 #pragma unroll
-            for (int j = 0; j < C::FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(rb[j], ra[i], acc[i][j], 0, 0, 0);
+            for (int j = 0; j < C::AN; ++j) {
+                if constexpr (C::MF16)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(rb[j], ra[i], acc[i][j], 0, 0, 0);
+                else
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(rb[j], ra[i], acc[i][j], 0, 0, 0);
+            }
     };
     // Wait for this lane's loads of tile `t` (and its own LDS reads), then a
     // workgroup barrier: tile t is visible to every wave and every read
@@ -450,7 +474,7 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
             const char *sbase = smem + slot * C::STAGE_BYTES;
 #pragma unroll
             for (int ks = 0; ks < C::NKS; ++ks) {
-                f16x8 ra[C::FM], rb[C::FN];
+                f16x8 ra[C::AM], rb[C::AN];
                 read_frags(ra, rb, sbase, ks);
                 mfma_step(ra, rb);
             }
@@ -518,7 +542,7 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
             __builtin_amdgcn_sched_barrier(0);
             compiler_fence();
         };
-        f16x8 fra[C::NKS][C::FM], frb[C::NKS][C::FN];
+        f16x8 fra[C::NKS][C::AM], frb[C::NKS][C::AN];
         // tile 0 (already issued by the prologue) complete and visible
         compiler_fence();
         wait_vm_lgkm0<0>();
@@ -555,7 +579,7 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
         // last MFMAs of tile k, so LDS latency hides under them.  The refill
         // of slot (k-1) mod S is issued at the first step of tile k: every
         // read of that slot was issued before the previous barrier.
-        f16x8 ra0[C::FM], rb0[C::FN], ra1[C::FM], rb1[C::FN];
+        f16x8 ra0[C::AM], rb0[C::AN], ra1[C::AM], rb1[C::AN];
         // One K tile.  MODE: 2 = steady state (a next tile exists and tile
         // k+S-1 is issued), 1 = drain (a next tile exists, nothing issued),
         // 0 = the last tile.  The modes are separate loops so that every K
@@ -570,11 +594,11 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
 #pragma unroll
             for (int ks = 0; ks < C::NKS; ++ks) {
                 // NKS is even, so step ks uses buffer ks & 1 in every tile
-                f16x8(&cra)[C::FM] = (ks & 1) ? ra1 : ra0;
-                f16x8(&crb)[C::FN] = (ks & 1) ? rb1 : rb0;
-                f16x8(&nra)[C::FM] = (ks & 1) ? ra0 : ra1;
-                f16x8(&nrb)[C::FN] = (ks & 1) ? rb0 : rb1;
-                int nreads = C::FM + C::FN;
+                f16x8(&cra)[C::AM] = (ks & 1) ? ra1 : ra0;
+                f16x8(&crb)[C::AN] = (ks & 1) ? rb1 : rb0;
+                f16x8(&nra)[C::AM] = (ks & 1) ? ra0 : ra1;
+                f16x8(&nrb)[C::AN] = (ks & 1) ? rb0 : rb1;
+                int nreads = C::AM + C::AN;
                 if (ks == C::NKS - 1) {
                     if constexpr (MODE == 2) {
                         sync_tile_steady();
@@ -598,7 +622,7 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
                 mfma_step(cra, crb);
                 // order: LDS read, MFMA, [LDS-DMA], LDS read, MFMA, ...
 #pragma unroll
-                for (int m = 0; m < C::FM * C::FN; ++m) {
+                for (int m = 0; m < C::AM * C::AN; ++m) {
                     if (m < nreads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                     if (m < nissue) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
@@ -622,8 +646,8 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
 
     // ---- epilogue ("cute(9) multistage_gemm", section 7.2: registers ->
     // shared memory -> global, so the global writes are row-contiguous).
-    // Lane holds D[m][n .. n+3] for m = row (lane & 31) of each 32x32 block
-    // and n = 8 * g + 4 * half.  Per 32-row block i of its sub-tile, each
+    // Lane holds D[m][n .. n+3]: 4 consecutive columns of one row per
+    // accumulator group (the pieces below).  Per 32-row block i of its sub-tile, each
     // wave converts alpha * acc (+ beta * C) to fp16 (one rounding), writes
     // the block into a private LDS region, waits for those writes, reads it
     // back row by row and stores 16 bytes per lane: every store instruction
@@ -657,48 +681,70 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
     const bool with_c = beta != 0.0f;
     const __amdgpu_buffer_rsrc_t rc =
         make_rsrc(with_c ? Cm + (size_t)m0 * N : D, with_c ? (uint32_t)rows_a * N * 2u : 0u);
+    // Piece p (4 per 32-column group) of 32-row block i: this lane's row r of
+    // the block, column c of the wave's sub-tile and its 4 accumulators.
+    // 32x32 blocks: p = (j, g), r = lane % 32, c = 32 j + 8 g + 4 half.
+    // 16x16 blocks: p = (h, jj) over the block's two 16-row halves and the
+    // 16-column groups, r = 16 h + lane % 16, c = 16 jj + 4 (lane / 16).
+    constexpr int PIECES = 4 * C::FN;
+    auto piece = [&](int i, int p, int &r, int &c, float (&v)[4]) {
+        if constexpr (C::MF16) {
+            const int hh = p / C::AN, jj = p % C::AN;
+            r = 16 * hh + (lane & 15);
+            c = 16 * jj + 4 * (lane >> 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = acc[2 * i + hh][jj][e];
+        } else {
+            const int j = p / 4, g = p % 4;
+            r = lane & 31;
+            c = 32 * j + 8 * g + 4 * half;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
+        }
+    };
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) {
-        const int r = lane & 31;                       // row within block i (and staging row)
         if (!with_c) {
             // D = RNE16(alpha * acc): one rounding of the exact product (the
             // compiler emits v_fma_mixlo_f16); C is not read.
 #pragma unroll
-            for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x16 &a = acc[i][j];
-                    stage4(r, j * 32 + 8 * g + 4 * half, alpha * a[4 * g + 0],
-                           alpha * a[4 * g + 1], alpha * a[4 * g + 2], alpha * a[4 * g + 3]);
-                }
+            for (int p = 0; p < PIECES; ++p) {
+                int r, c;
+                float v[4];
+                piece(i, p, r, c, v);
+                stage4(r, c, alpha * v[0], alpha * v[1], alpha * v[2], alpha * v[3]);
+            }
         } else {
             // D = RNE16(alpha * acc + beta * C) ("CUDA operator notes 2",
             // "GEMM"): C is read in the accumulator layout (4 halves per lane
-            // and group), combined in fp32 and rounded once to fp16.  Each
+            // and piece), combined in fp32 and rounded once to fp16.  Each
             // wave reads only C elements of rows it stores itself, before it
             // stores them, so C may be D (in place).
-            const int ml = wm * C::WTM + i * 32 + r;
+            // four pieces at a time: their C loads, then their staging
 #pragma unroll
-            for (int j = 0; j < C::FN; ++j) {
+            for (int p0 = 0; p0 < PIECES; p0 += 4) {
                 u32x2 cv[4];
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int n = n0 + wn * C::WTN + j * 32 + 8 * g + 4 * half;
+                for (int q = 0; q < 4; ++q) {
+                    int r, c;
+                    float v[4];
+                    piece(i, p0 + q, r, c, v);
+                    const int ml = wm * C::WTM + i * 32 + r;
+                    const int n = n0 + wn * C::WTN + c;
                     const uint32_t off = (n < N) ? (uint32_t)(ml * N + n) * 2u : kOutOfRange;
-                    cv[g] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rc, off, 0, 0));
+                    cv[q] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rc, off, 0, 0));
                 }
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x16 &a = acc[i][j];
-                    const float c0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(cv[g][0] & 0xffffu));
-                    const float c1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(cv[g][0] >> 16));
-                    const float c2 = (float)__builtin_bit_cast(_Float16, (uint16_t)(cv[g][1] & 0xffffu));
-                    const float c3 = (float)__builtin_bit_cast(_Float16, (uint16_t)(cv[g][1] >> 16));
-                    stage4(r, j * 32 + 8 * g + 4 * half,
-                           __builtin_fmaf(beta, c0, alpha * a[4 * g + 0]),
-                           __builtin_fmaf(beta, c1, alpha * a[4 * g + 1]),
-                           __builtin_fmaf(beta, c2, alpha * a[4 * g + 2]),
-                           __builtin_fmaf(beta, c3, alpha * a[4 * g + 3]));
+                for (int q = 0; q < 4; ++q) {
+                    int r, c;
+                    float v[4];
+                    piece(i, p0 + q, r, c, v);
+                    const float c0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(cv[q][0] & 0xffffu));
+                    const float c1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(cv[q][0] >> 16));
+                    const float c2 = (float)__builtin_bit_cast(_Float16, (uint16_t)(cv[q][1] & 0xffffu));
+                    const float c3 = (float)__builtin_bit_cast(_Float16, (uint16_t)(cv[q][1] >> 16));
+                    stage4(r, c, __builtin_fmaf(beta, c0, alpha * v[0]), __builtin_fmaf(beta, c1, alpha * v[1]),
+                           __builtin_fmaf(beta, c2, alpha * v[2]), __builtin_fmaf(beta, c3, alpha * v[3]));
                 }
             }
         }

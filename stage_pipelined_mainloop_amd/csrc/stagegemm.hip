@@ -119,6 +119,8 @@ const Variant kVariants[] = {
     variant<sg::Cfg<128, 128, 32, 3, 2, 2, 0>>(),
     variant<sg::Cfg<128, 128, 32, 4, 2, 2, 0>>(),
     variant<sg::Cfg<128, 128, 32, 5, 2, 2, 0>>(),
+    // cute-page order on 16x16x32 MFMAs (schedule 5)
+    variant<sg::Cfg<256, 256, 64, 2, 2, 4, 5>>(),
     // whole K extent in the ring, epilogue per row block (schedule 4, K <= S * BK)
     variant<sg::Cfg<128, 128, 64, 2, 2, 2, 4>>(),
     // persistent workgroups, one ring across output tiles (schedule 3)
@@ -224,7 +226,7 @@ sg_status run(const Variant *v, int M, int N, int K, float alpha, float beta, co
     if (tiles * v->threads >= (1LL << 32)) return SG_ERR_SHAPE;
     // the persistent and short-K kernels have no C operand; the short-K
     // kernel holds the whole K extent in its ring
-    if (v->cfg.schedule >= 3 && beta != 0.0f) return SG_ERR_UNSUPPORTED;
+    if ((v->cfg.schedule == 3 || v->cfg.schedule == 4) && beta != 0.0f) return SG_ERR_UNSUPPORTED;
     if (v->cfg.schedule == 4 && (long long)(K + v->cfg.tile_k - 1) / v->cfg.tile_k > v->cfg.stages)
         return SG_ERR_UNSUPPORTED;
     // Rotate the K loop over 4 tile rows once the grid is more than one wave

@@ -118,7 +118,7 @@ def test_every_variant_on_ragged_shapes(shape):
                                  (256, 256, 64, 2, 8, 1), (256, 256, 32, 3, 8, 0),
                                  (128, 128, 64, 3, 4, 1), (256, 256, 64, 2, 8, 2),
                                  (128, 128, 64, 2, 4, 3), (256, 256, 64, 2, 8, 3),
-                                 (128, 128, 64, 2, 4, 4)])
+                                 (128, 128, 64, 2, 4, 4), (256, 256, 64, 2, 8, 5)])
 def test_tiny_shape_grid(cfg):
     # every M, N and K tail against every tile boundary of the variant
     say(f"[case] tiny grid cfg={cfg}")
