@@ -61,9 +61,10 @@ def load_traffic(workload: str):
     return t.get("hbm_bytes_per_launch")
 
 
-def mfma_ceiling(a, b, target_ms: float = 20.0):
+def mfma_ceiling(a, b, target_ms: float = 20.0, shape16: bool = False):
     """TFLOP/s of pure fp16 MFMAs on fragments of the workload's own inputs
-    (libsgprobe.so): the power-limited ceiling for this operand data."""
+    (libsgprobe.so): the power-limited ceiling for this operand data, with
+    32x32x16 MFMAs (or 16x16x32 with shape16)."""
     import ctypes
 
     import torch
@@ -73,6 +74,8 @@ def mfma_ceiling(a, b, target_ms: float = 20.0):
                                         ctypes.c_longlong, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_void_p, ctypes.c_void_p]
     L.sg_probe_mfma_ceiling.restype = ctypes.c_int
+    L.sg_probe_mfma_ceiling_shape.argtypes = [ctypes.c_int] + L.sg_probe_mfma_ceiling.argtypes
+    L.sg_probe_mfma_ceiling_shape.restype = ctypes.c_int
     L.sg_probe_mfma_ceiling_flops.argtypes = [ctypes.c_int, ctypes.c_int]
     L.sg_probe_mfma_ceiling_flops.restype = ctypes.c_double
     blocks = 1024
@@ -80,8 +83,8 @@ def mfma_ceiling(a, b, target_ms: float = 20.0):
     stream = torch.cuda.current_stream(a.device)
 
     def run(iters):
-        rc = L.sg_probe_mfma_ceiling(a.data_ptr(), a.numel(), b.data_ptr(), b.numel(), blocks,
-                                     iters, sink.data_ptr(), stream.cuda_stream)
+        rc = L.sg_probe_mfma_ceiling_shape(int(shape16), a.data_ptr(), a.numel(), b.data_ptr(),
+                                           b.numel(), blocks, iters, sink.data_ptr(), stream.cuda_stream)
         if rc != 0:
             raise RuntimeError(f"mfma ceiling probe failed to launch ({rc})")
 
@@ -430,6 +433,8 @@ def main() -> int:
         ceil = mfma_ceiling(a, b)
         out["config"]["mfma_ceiling_tflops"] = round(ceil, 1)
         out["config"]["frac_of_mfma_ceiling"] = round(achieved / ceil, 4)
+        # the same loop on 16x16x32 MFMAs, which draw less power per flop
+        out["config"]["mfma_ceiling_16x16x32_tflops"] = round(mfma_ceiling(a, b, shape16=True), 1)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(A, B, args.cpu_seconds)
     print(json.dumps(out), flush=True)
