@@ -178,8 +178,10 @@ int sg_persistent_wait_count(int stages, int loads_per_stage, int stores_per_til
  * for H independent heads.  Q is H x M x d, K and V are H x N x d, O is
  * H x M x d; every head is row-major fp16 and the heads are stored one after
  * another (head stride M * d or N * d elements).  The scores stay on chip:
- * one pass over the keys with a running row maximum and sum (fp32), P V
- * accumulated in fp32 from fp16 probabilities, O rounded once to fp16.
+ * one pass over the keys with a running reference exponent per row (raised
+ * when the row's maximum passes it by more than 2^8; the quotient does not
+ * depend on it) and a running row sum in fp32, P V accumulated in fp32 from
+ * fp16 probabilities, O / l converted once to fp16.
  * alpha is fp32 (the page's 1/sqrt(d) is the caller's choice).
  * Only d == 128 is compiled (SG_ERR_UNSUPPORTED otherwise).  H == 0 or
  * M == 0: no work.  N == 0 with M > 0: SG_ERR_SHAPE (no keys to weight).
