@@ -34,8 +34,8 @@ def gemm(A, B, out=None, alpha: float | None = None, config=None, stream=None,
         raise TypeError("A and B must be float16")
     if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[1]:
         raise ValueError(f"shapes {tuple(A.shape)} and {tuple(B.shape)} do not form A @ B.T")
-    if not (A.is_cuda and B.is_cuda):
-        raise ValueError("A and B must be device tensors")
+    if not (A.is_cuda and B.is_cuda) or A.device != B.device:
+        raise ValueError("A and B must be device tensors on the same device")
     if not (A.is_contiguous() and B.is_contiguous()):
         raise ValueError("A and B must be contiguous (row-major)")
     M, K = A.shape
@@ -85,8 +85,8 @@ def attention(Q, K, V, alpha: float | None = None, out=None, stream=None, splits
     if q3.dim() != 3 or k3.shape != v3.shape or q3.shape[0] != k3.shape[0] \
             or q3.shape[2] != k3.shape[2]:
         raise ValueError(f"shapes {tuple(Q.shape)}, {tuple(K.shape)}, {tuple(V.shape)} do not match")
-    if not (Q.is_cuda and K.is_cuda and V.is_cuda):
-        raise ValueError("Q, K and V must be device tensors")
+    if not (Q.is_cuda and K.is_cuda and V.is_cuda) or not (Q.device == K.device == V.device):
+        raise ValueError("Q, K and V must be device tensors on the same device")
     if not (Q.is_contiguous() and K.is_contiguous() and V.is_contiguous()):
         raise ValueError("Q, K and V must be contiguous")
     H, M, d = q3.shape
@@ -95,8 +95,9 @@ def attention(Q, K, V, alpha: float | None = None, out=None, stream=None, splits
         alpha = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
     if out is None:
         out = torch.empty_like(Q)
-    elif out.shape != Q.shape or out.dtype != torch.float16 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float16 tensor shaped like Q")
+    elif (out.shape != Q.shape or out.dtype != torch.float16 or not out.is_contiguous()
+          or out.device != Q.device):
+        raise ValueError("out must be a contiguous float16 tensor shaped like Q, on Q's device")
     st = stream if stream is not None else torch.cuda.current_stream(Q.device)
     if H == 0 or M == 0:
         splits = 1
@@ -107,17 +108,20 @@ def attention(Q, K, V, alpha: float | None = None, out=None, stream=None, splits
         splits = max(splits, 1)
     need = attention_fp16_workspace_bytes(H, M, N, d, splits) if splits > 1 else 0
     if need == 0:
-        attention_fp16_fwd_split(H, M, N, d, float(alpha), Q.data_ptr(), K.data_ptr(),
-                                 V.data_ptr(), out.data_ptr(), splits, 0, 0, st.cuda_stream)
+        with torch.cuda.device(Q.device):              # the launcher queries the current device
+            attention_fp16_fwd_split(H, M, N, d, float(alpha), Q.data_ptr(), K.data_ptr(),
+                                     V.data_ptr(), out.data_ptr(), splits, 0, 0, st.cuda_stream)
         return out
     if workspace is None:
         with torch.cuda.stream(st):
             workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
-    elif not workspace.is_cuda or workspace.numel() * workspace.element_size() < need:
-        raise ValueError(f"workspace must be a device tensor of at least {need} bytes")
-    attention_fp16_fwd_split(H, M, N, d, float(alpha), Q.data_ptr(), K.data_ptr(), V.data_ptr(),
-                             out.data_ptr(), splits, workspace.data_ptr(),
-                             workspace.numel() * workspace.element_size(), st.cuda_stream)
+    elif (not workspace.is_cuda or workspace.device != Q.device
+          or workspace.numel() * workspace.element_size() < need):
+        raise ValueError(f"workspace must be a tensor of at least {need} bytes on Q's device")
+    with torch.cuda.device(Q.device):
+        attention_fp16_fwd_split(H, M, N, d, float(alpha), Q.data_ptr(), K.data_ptr(), V.data_ptr(),
+                                 out.data_ptr(), splits, workspace.data_ptr(),
+                                 workspace.numel() * workspace.element_size(), st.cuda_stream)
     return out
 
 
