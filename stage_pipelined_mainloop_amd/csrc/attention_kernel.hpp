@@ -371,7 +371,7 @@ attention_fwd_kernel(const _Float16 *__restrict__ Q, const _Float16 *__restrict_
                 const uint32_t off = (uint32_t)(qrow * C::D + 32 * c + 8 * g + 4 * half) * 4u;
                 __builtin_amdgcn_raw_buffer_store_b128(v, rpo, off, 0, 0);
             }
-        if (half == 0) {
+        if (__lane_id() < 32) {                        // recomputed: keeping `half` live spills
             u32x2 ml;
             ml[0] = __builtin_bit_cast(uint32_t, mref);
             ml[1] = __builtin_bit_cast(uint32_t, lsum + lother);
