@@ -159,6 +159,7 @@ struct Cfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_, WM = WM_, WN = WN_;
     static constexpr int SCHED = SCHED_;
     static constexpr bool MF16 = SCHED == 5;        // 16x16x32 MFMAs
+    static constexpr int ORDER = SCHED == 5 ? 1 : SCHED;   // mainloop order
     static constexpr int NW = WM * WN;              // wavefronts
     static constexpr int T = 64 * NW;               // threads
     static constexpr int WTM = BM / WM;             // wave sub-tile
@@ -465,7 +466,7 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
 
     int slot = 0;                                    // slot of tile k
     int wslot = C::S - 1;                            // slot of tile k+S-1
-    if constexpr (C::SCHED == 0) {
+    if constexpr (C::ORDER == 0) {
         // ---- "Lesson 6" three-phase order: wait, barrier, refill, compute.
 #pragma unroll 1
         for (int k = 0; k < ntile; ++k) {
@@ -481,7 +482,7 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
             slot = (slot + 1 == C::S) ? 0 : slot + 1;
             wslot = (wslot + 1 == C::S) ? 0 : wslot + 1;
         }
-    } else if constexpr (C::SCHED == 2) {
+    } else if constexpr (C::ORDER == 2) {
         // ---- Ping-pong.  The two waves sharing a SIMD belong to different
         // groups (waves are dealt to SIMDs round-robin): G0 = waves 0..NG-1,
         // G1 = waves NG..NW-1.  Time is cut into phases, each ending in one
