@@ -327,8 +327,9 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); "
-              "the path shards into independent output tiles, see the design notes",
+        print(f"bench.py measures one GPU (asked for {args.gpus}): the GEMM shards into "
+              "independent output tiles (split M, broadcast B) with no exchange during "
+              "compute, so N GPUs each run this one-GPU step on their share",
               file=sys.stderr)
         return 2
     if args.mode == "variants":
