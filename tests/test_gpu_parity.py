@@ -216,7 +216,8 @@ def test_empty_m_or_n_leaves_output_untouched():
                                        ((128, 128, 64, 2, 4, 3), (4200, 4104, 72)),
                                        ((256, 256, 64, 2, 8, 3), (4200, 4104, 72)),
                                        ((128, 128, 64, 2, 4, 4), (300, 264, 128)),
-                                       ((128, 128, 64, 2, 4, 4), (4200, 4104, 72))])
+                                       ((128, 128, 64, 2, 4, 4), (4200, 4104, 72)),
+                                       ((256, 256, 64, 2, 8, 5), (300, 264, 136))])
 def test_canary_guard_bands(cfg, shape):
     # D sits inside a larger buffer filled with a NaN pattern; nothing outside
     # D may change and every element of D must be written
