@@ -82,7 +82,9 @@ typedef enum sg_status {
  *   5  order 1 on 16x16x32 MFMAs instead of 32x32x16 (tile_k 64): the same
  *      LDS traffic per flop, a different balance between clock and MFMA
  *      occupancy under the power limit.  Compiled for comparison; the
- *      library's own choice never takes it. */
+ *      library's own choice never takes it;
+ *   7  order 2 (ping-pong wave groups) on 16x16x32 MFMAs (tile_k 64, two
+ *      stages): the library's choice for 256 x 256 tiles. */
 typedef struct sg_config {
     int tile_m;
     int tile_n;

@@ -8,7 +8,8 @@
 //
 //   * One workgroup per BM x BN output tile; NW = WM x WN wavefronts of 64
 //     lanes, each owning a (BM/WM) x (BN/WN) sub-tile built from 32x32 MFMA
-//     blocks (v_mfma_f32_32x32x16_f16, fp32 accumulators).
+//     blocks (v_mfma_f32_32x32x16_f16, fp32 accumulators) or from 16x16 ones
+//     (v_mfma_f32_16x16x32_f16, schedules 5 and 7; see "MFMA shape" below).
 //   * An S-slot ring in LDS.  Each slot holds one K step: A rows [BM x BK] and
 //     B rows [BN x BK], both K-contiguous (the TN layout needs no transpose).
 //   * Global -> LDS copies are LDS-DMA buffer loads (buffer_load_dwordx4 ...
@@ -148,18 +149,24 @@ __device__ __forceinline__ int swz(int r)
 // wave groups (one computes while the other reads and refills), 3 =
 // persistent, 4 = short K, 5 = order 1 on 16x16x32 MFMAs.
 //
-// MFMA shape.  Orders 0-4 use v_mfma_f32_32x32x16_f16 (32x32 blocks, K steps
-// of 16); order 5 uses v_mfma_f32_16x16x32_f16 (16x16 blocks, K steps of
-// 32).  The LDS bytes read per flop are the same (a fragment is 1 KiB either
-// way), but under the power limit the 16x16x32 form sustains more
-// throughput on the same operands (measured 1867 against 1628 TFLOP/s in an
-// MFMA-only loop on uniform [-1, 1] fp16 data).
+// MFMA shape.  Schedules 0-4 use v_mfma_f32_32x32x16_f16 (32x32 blocks, K
+// steps of 16); schedules 5 and 7 use v_mfma_f32_16x16x32_f16 (16x16 blocks,
+// K steps of 32) in the mainloop order of schedule 1 and 2 respectively.  The
+// LDS bytes read per flop are the same (a fragment is 1 KiB either way), but
+// under the power limit the 16x16x32 form sustains more throughput on the
+// same operands (measured 1867 against 1628 TFLOP/s in an MFMA-only loop on
+// uniform [-1, 1] fp16 data).  With order 1 that gain is eaten by the
+// fragment reads, which the waves of a workgroup issue all at once; with the
+// ping-pong order one wave group reads while the other multiplies, and the
+// 8192^3 GEMM runs about 7 % faster than order 1 on 32x32x16 blocks
+// (clock 1.78 against 1.39 GHz under the counters, MFMA busy 74 against
+// 85 %).
 template <int BM_, int BN_, int BK_, int S_, int WM_, int WN_, int SCHED_ = 1>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_, WM = WM_, WN = WN_;
     static constexpr int SCHED = SCHED_;
-    static constexpr bool MF16 = SCHED == 5;        // 16x16x32 MFMAs
-    static constexpr int ORDER = SCHED == 5 ? 1 : SCHED;   // mainloop order
+    static constexpr bool MF16 = SCHED == 5 || SCHED == 7;   // 16x16x32 MFMAs
+    static constexpr int ORDER = SCHED == 5 ? 1 : SCHED == 7 ? 2 : SCHED;   // mainloop order
     static constexpr int NW = WM * WN;              // wavefronts
     static constexpr int T = 64 * NW;               // threads
     static constexpr int WTM = BM / WM;             // wave sub-tile
@@ -200,11 +207,11 @@ struct Cfg {
     static constexpr int NB = BN * CPR / (64 * NW);
     static constexpr int L = NA + NB;
     static_assert(S >= 2, "a ring needs at least two slots");
-    static_assert(SCHED >= 0 && SCHED <= 5, "mainloop order");
+    static_assert(SCHED >= 0 && SCHED <= 7 && SCHED != 6, "mainloop order");
     static_assert(!MF16 || BK == 64, "16x16x32 order: two K steps of 32 per tile");
     static_assert(SCHED != 3 || S == 2 || S == 3, "persistent ring: two or three slots");
     static_assert(!OWN_STAGING || WTN == 64, "unpadded staging rows are 128 bytes");
-    static_assert(SCHED != 2 || (S == 2 && NW % 4 == 0 && (NW / 2) % 2 == 0 && BK == 64),
+    static_assert(ORDER != 2 || (S == 2 && NW % 4 == 0 && (NW / 2) % 2 == 0 && BK == 64),
                   "ping-pong: two slots, two even wave groups, 128-byte rows");
     static_assert(NKS % 2 == 0, "fragment double buffer alternates per K step");
     static_assert(BK == 32 || BK == 64, "BK");
@@ -318,7 +325,7 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
                const _Float16 *Cm, _Float16 *D, int M, int N, int K, float alpha, float beta,
                int kt_rot)
 {
-    static_assert(C::SCHED <= 2 || C::SCHED == 5, "schedules 3 and 4 have kernels of their own");
+    static_assert(C::SCHED <= 2 || C::SCHED >= 5, "schedules 3 and 4 have kernels of their own");
     // Cm and D may be the same buffer (in-place D = alpha A B^T + beta D): each
     // wave reads C only inside its own sub-tile and finishes those reads
     // before it stores, so they are not declared __restrict__.

@@ -257,7 +257,7 @@ def test_selection_returns_compiled_variants():
         assert c.as_tuple() in {x.as_tuple() for x in _lib.configs()}
     # the measured choices: big squares tiled 256x256x64, the skinny tall
     # shape persistent 128x128x64, the one-wave sweep grid 128x128x64 S3
-    assert _lib.sg_select_config(8192, 8192, 8192).as_tuple() == (256, 256, 64, 2, 8, 1)
+    assert _lib.sg_select_config(8192, 8192, 8192).as_tuple() == (256, 256, 64, 2, 8, 7)
     assert _lib.sg_select_config(81920, 256, 256).as_tuple() == (128, 128, 64, 2, 4, 3)
     assert _lib.sg_select_config(2048, 2048, 2048).as_tuple() == (128, 128, 64, 3, 4, 1)
     assert _lib.sg_select_config(81920, 256, 4096).as_tuple() == (128, 128, 64, 2, 4, 1)

@@ -118,7 +118,8 @@ def test_every_variant_on_ragged_shapes(shape):
                                  (256, 256, 64, 2, 8, 1), (256, 256, 32, 3, 8, 0),
                                  (128, 128, 64, 3, 4, 1), (256, 256, 64, 2, 8, 2),
                                  (128, 128, 64, 2, 4, 3), (256, 256, 64, 2, 8, 3),
-                                 (128, 128, 64, 2, 4, 4), (256, 256, 64, 2, 8, 5)])
+                                 (128, 128, 64, 2, 4, 4), (256, 256, 64, 2, 8, 5),
+                                 (256, 256, 64, 2, 8, 7)])
 def test_tiny_shape_grid(cfg):
     # every M, N and K tail against every tile boundary of the variant
     say(f"[case] tiny grid cfg={cfg}")
@@ -137,6 +138,7 @@ def test_tiny_shape_grid(cfg):
 
 @pytest.mark.parametrize("shape,cfg", [((4352, 4352, 264), None),
                                        ((4352, 4104, 200), (256, 256, 64, 2, 8, 1)),
+                                       ((4352, 4104, 200), (256, 256, 64, 2, 8, 7)),
                                        ((2304, 2304, 520), (128, 128, 32, 4, 4, 1)),
                                        ((2304, 2312, 1000), (256, 256, 32, 3, 8, 0)),
                                        ((4352, 4360, 336), (256, 256, 64, 2, 8, 2)),
@@ -217,7 +219,8 @@ def test_empty_m_or_n_leaves_output_untouched():
                                        ((256, 256, 64, 2, 8, 3), (4200, 4104, 72)),
                                        ((128, 128, 64, 2, 4, 4), (300, 264, 128)),
                                        ((128, 128, 64, 2, 4, 4), (4200, 4104, 72)),
-                                       ((256, 256, 64, 2, 8, 5), (300, 264, 136))])
+                                       ((256, 256, 64, 2, 8, 5), (300, 264, 136)),
+                                       ((256, 256, 64, 2, 8, 7), (300, 264, 136))])
 def test_canary_guard_bands(cfg, shape):
     # D sits inside a larger buffer filled with a NaN pattern; nothing outside
     # D may change and every element of D must be written
@@ -245,11 +248,12 @@ def test_alpha_values(alpha):
 
 
 @pytest.mark.parametrize("shape", [(300, 264, 200), (4352, 520, 264), (256, 256, 0),
-                                   (20480, 256, 256)])
+                                   (20480, 256, 256), (3848, 3840, 136)])
 @pytest.mark.parametrize("alpha,beta", [(1.0, 1.0), (0.5, -0.75), (-1.0, 0.3), (0.0, 2.0)])
 def test_beta_c(shape, alpha, beta):
     # (20480, 256, 256): without C the library picks the persistent schedule;
-    # with C it must fall back to a tiled variant
+    # with C it must fall back to a tiled variant.  (3848, 3840, 136) takes
+    # the 256 x 256 tiles, with M and N tails.
     M, N, K = shape
     say(f"[case] beta {shape} alpha={alpha} beta={beta}")
     A, B = inputs.operands(M, N, K, 600 + M + K)
