@@ -84,7 +84,13 @@ typedef enum sg_status {
  *      occupancy under the power limit.  Compiled for comparison; the
  *      library's own choice never takes it;
  *   7  order 2 (ping-pong wave groups) on 16x16x32 MFMAs (tile_k 64, two
- *      stages): the library's choice for 256 x 256 tiles. */
+ *      stages).  Compiled for comparison;
+ *   8  order 7 with the LDS-DMA loads split between the two wave groups:
+ *      the first group loads A tiles, the second B tiles, each in its own
+ *      fragment-read phase.  A keeps stages - 1 ring slots and B keeps
+ *      `stages` (stages = 3: 64 + 96 KiB for 256 x 256 x 64 tiles), which
+ *      gives the second group's loads two phases to land.  The library's
+ *      choice for 256 x 256 tiles. */
 typedef struct sg_config {
     int tile_m;
     int tile_n;

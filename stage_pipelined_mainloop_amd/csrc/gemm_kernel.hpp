@@ -150,8 +150,9 @@ __device__ __forceinline__ int swz(int r)
 // persistent, 4 = short K, 5 = order 1 on 16x16x32 MFMAs.
 //
 // MFMA shape.  Schedules 0-4 use v_mfma_f32_32x32x16_f16 (32x32 blocks, K
-// steps of 16); schedules 5 and 7 use v_mfma_f32_16x16x32_f16 (16x16 blocks,
-// K steps of 32) in the mainloop order of schedule 1 and 2 respectively.  The
+// steps of 16); schedules 5, 7 and 8 use v_mfma_f32_16x16x32_f16 (16x16
+// blocks, K steps of 32) in the mainloop order of schedule 1, 2 and the
+// split-load form of 2 (order 8) respectively.  The
 // LDS bytes read per flop are the same (a fragment is 1 KiB either way), but
 // under the power limit the 16x16x32 form sustains more throughput on the
 // same operands (measured 1867 against 1628 TFLOP/s in an MFMA-only loop on
@@ -160,12 +161,14 @@ __device__ __forceinline__ int swz(int r)
 // ping-pong order one wave group reads while the other multiplies, and the
 // 8192^3 GEMM runs about 7 % faster than order 1 on 32x32x16 blocks
 // (clock 1.78 against 1.39 GHz under the counters, MFMA busy 74 against
-// 85 %).
+// 85 %).  Order 8 then removes the ping-pong's remaining stall (the LDS-DMA
+// issues of a whole tile in one read phase) and reaches MFMA busy 80 % at
+// the same clock.
 template <int BM_, int BN_, int BK_, int S_, int WM_, int WN_, int SCHED_ = 1>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_, WM = WM_, WN = WN_;
     static constexpr int SCHED = SCHED_;
-    static constexpr bool MF16 = SCHED == 5 || SCHED == 7;   // 16x16x32 MFMAs
+    static constexpr bool MF16 = SCHED == 5 || SCHED == 7 || SCHED == 8;   // 16x16x32 MFMAs
     static constexpr int ORDER = SCHED == 5 ? 1 : SCHED == 7 ? 2 : SCHED;   // mainloop order
     static constexpr int NW = WM * WN;              // wavefronts
     static constexpr int T = 64 * NW;               // threads
@@ -183,7 +186,8 @@ struct Cfg {
     static constexpr int A_BYTES = BM * RB;
     static constexpr int B_BYTES = BN * RB;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-    static constexpr int RING_BYTES = S * STAGE_BYTES;
+    // Order 8 keeps S - 1 slots of A and S slots of B.
+    static constexpr int RING_BYTES = ORDER == 8 ? (S - 1) * A_BYTES + S * B_BYTES : S * STAGE_BYTES;
     // Epilogue staging: each wave's WTM x WTN fp16 sub-tile, rows padded by
     // 16 bytes (row stride 9 x 16 B for 128-byte rows) against bank conflicts.
     static constexpr int EPI_ROW = WTN * 2 + 16;
@@ -207,12 +211,14 @@ struct Cfg {
     static constexpr int NB = BN * CPR / (64 * NW);
     static constexpr int L = NA + NB;
     static_assert(S >= 2, "a ring needs at least two slots");
-    static_assert(SCHED >= 0 && SCHED <= 7 && SCHED != 6, "mainloop order");
+    static_assert(SCHED >= 0 && SCHED <= 8 && SCHED != 6, "mainloop order");
     static_assert(!MF16 || BK == 64, "16x16x32 order: two K steps of 32 per tile");
     static_assert(SCHED != 3 || S == 2 || S == 3, "persistent ring: two or three slots");
     static_assert(!OWN_STAGING || WTN == 64, "unpadded staging rows are 128 bytes");
     static_assert(ORDER != 2 || (S == 2 && NW % 4 == 0 && (NW / 2) % 2 == 0 && BK == 64),
                   "ping-pong: two slots, two even wave groups, 128-byte rows");
+    static_assert(ORDER != 8 || (S == 3 && NW % 4 == 0 && (NW / 2) % 2 == 0 && BK == 64 && BM == BN),
+                  "split-load ping-pong: A ring of two slots, B ring of three, square tiles");
     static_assert(NKS % 2 == 0, "fragment double buffer alternates per K step");
     static_assert(BK == 32 || BK == 64, "BK");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile is whole 32x32 blocks");
@@ -421,14 +427,18 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
 
     // LDS -> VGPR fragments of one MFMA K step, and the MFMAs of one K step.
     // Read order follows first use by mfma_step: A0, all of B, then A1...
-    auto read_frags = [&](f16x8 (&ra)[C::AM], f16x8 (&rb)[C::AN], const char *sbase, int ks) {
-        ra[0] = *(const f16x8 *)(sbase + fa[ks]);
+    auto read_frags_ab = [&](f16x8 (&ra)[C::AM], f16x8 (&rb)[C::AN], const char *abase,
+                             const char *bbase, int ks) {
+        ra[0] = *(const f16x8 *)(abase + fa[ks]);
 #pragma unroll
         for (int j = 0; j < C::AN; ++j)
-            rb[j] = *(const f16x8 *)(sbase + fb[ks] + j * C::MB * C::RB);
+            rb[j] = *(const f16x8 *)(bbase + fb[ks] + j * C::MB * C::RB);
 #pragma unroll
         for (int i = 1; i < C::AM; ++i)
-            ra[i] = *(const f16x8 *)(sbase + fa[ks] + i * C::MB * C::RB);
+            ra[i] = *(const f16x8 *)(abase + fa[ks] + i * C::MB * C::RB);
+    };
+    auto read_frags = [&](f16x8 (&ra)[C::AM], f16x8 (&rb)[C::AN], const char *sbase, int ks) {
+        read_frags_ab(ra, rb, sbase, sbase, ks);
     };
     auto mfma_step = [&](const f16x8 (&ra)[C::AM], const f16x8 (&rb)[C::AN]) {
 #pragma unroll
@@ -466,10 +476,12 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
         compiler_fence();
     };
 
-    // ---- prologue: tiles 0 .. S-2
+    // ---- prologue: tiles 0 .. S-2 (order 8 has a prologue of its own)
+    if constexpr (C::ORDER != 8) {
 #pragma unroll
-    for (int t = 0; t < C::S - 1; ++t)
-        if (t < ntile) issue(t, t);
+        for (int t = 0; t < C::S - 1; ++t)
+            if (t < ntile) issue(t, t);
+    }
 
     int slot = 0;                                    // slot of tile k
     int wslot = C::S - 1;                            // slot of tile k+S-1
@@ -577,6 +589,108 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
             __builtin_amdgcn_s_setprio(0);
             if (grp == 0) __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
             barrier();
+        }
+        if (grp == 0) barrier();                   // G0 idles in the last phase
+    } else if constexpr (C::ORDER == 8) {
+        // ---- Ping-pong with the loads split between the groups.  The phases
+        // are those of order 2, but G0 loads only A tiles and G1 only B
+        // tiles, each group in its own read phase and after its fragment
+        // reads, so each read phase issues half of a tile's LDS-DMA.  (In
+        // order 2, G0 issues the whole tile: the LDS-DMA path accepts an
+        // instruction only as fast as it moves 16 bytes per lane, so those
+        // issues held G0's read phase well past the other group's MFMAs.)
+        // A ring: two slots, tile j in slot j % 2.  B ring: three slots,
+        // tile j in slot j % 3.
+        //   G0, read phase of tile j (phase 2j): A(j+1) into slot (j+1) % 2,
+        //     which held A(j-1), last read in phases 2j-2 and 2j-1 (WAR);
+        //     complete by G0's vmcnt(0) at the end of phase 2j+1 (RAW:
+        //     first read in phase 2j+2).
+        //   G1, read phase of tile j (phase 2j+1): B(j+2) into slot
+        //     (j+2) % 3, which held B(j-1), last read in phases 2j-2 and
+        //     2j-1 (WAR); B(j+1), issued one read phase earlier, complete by
+        //     the vmcnt at the end of this phase (RAW: first read in phase
+        //     2j+2), B(j+2) may stay in flight.
+        // The prologue loads A(0), B(0) and B(1).
+        constexpr int NG = C::NW / 2;
+        const int grp = wave / NG;                 // wave-uniform
+        const int gw = wave - grp * NG;
+        constexpr int NLG = C::BM * C::CPR / (64 * NG);   // loads per wave per operand tile
+        static_assert(NLG * 64 * NG == C::BM * C::CPR, "split");
+        const int pr0 = gw * 8 + (lane >> 3);
+        const int pc = (lane & 7) ^ swz<C::CPR>(pr0);
+        const uint32_t p_base = (uint32_t)(pr0 * K + pc * 8) * 2u;
+        const uint32_t p_step = (uint32_t)(NG * 8) * (uint32_t)K * 2u;
+        char *const b_ring = smem + 2 * C::A_BYTES;
+        // One operand tile t of `rs` into `dst` by this group's waves.
+        auto issue_op = [&](const __amdgpu_buffer_rsrc_t &rs, int t, char *dst) {
+            int kt = t + kt0;
+            if (kt >= ntile) kt -= ntile;
+            const int kbase = kt * C::BK;
+            const bool valid = pc * 8 < K - kbase;
+            const uint32_t v = valid ? p_base + (uint32_t)kbase * 2u : kOutOfRange;
+            const uint32_t step = valid ? p_step : 0u;
+#pragma unroll
+            for (int i = 0; i < NLG; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rs, (__attribute__((address_space(3))) void *)(dst + (i * NG + gw) * 1024),
+                    16, v + (uint32_t)i * step, 0, 0, 0);
+        };
+        auto barrier = [&]() {
+            compiler_fence();
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            compiler_fence();
+        };
+        if (ntile > 0) {
+            if (grp == 0) {
+                issue_op(ra, 0, smem);
+            } else {
+                issue_op(rb, 0, b_ring);
+                if (ntile > 1) issue_op(rb, 1, b_ring + C::B_BYTES);
+            }
+        }
+        f16x8 fra[C::NKS][C::AM], frb[C::NKS][C::AN];
+        compiler_fence();
+        wait_vm_lgkm0<0>();
+        barrier();
+        if (grp == 1) barrier();                   // G1 idles in phase 0
+        int bslot = 0;                             // B slot of tile j
+#pragma unroll 1
+        for (int j = 0; j < ntile; ++j) {
+            // read phase of tile j
+            const char *abase = smem + (j & 1) * C::A_BYTES;
+            const char *bbase = b_ring - C::A_BYTES + bslot * C::B_BYTES;   // fb holds + A_BYTES
+#pragma unroll
+            for (int ks = 0; ks < C::NKS; ++ks) read_frags_ab(fra[ks], frb[ks], abase, bbase, ks);
+            compiler_fence();
+            __builtin_amdgcn_sched_barrier(0);
+            const int b2 = bslot == 0 ? 2 : bslot - 1;   // (j + 2) % 3
+            if (grp == 0) {
+                if (j + 1 < ntile) issue_op(ra, j + 1, smem + ((j + 1) & 1) * C::A_BYTES);
+                compiler_fence();
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+            } else if (j + 2 < ntile) {
+                issue_op(rb, j + 2, b_ring + b2 * C::B_BYTES);
+                compiler_fence();
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm(NLG, 0));
+            } else {
+                compiler_fence();
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+            }
+            barrier();
+            // MFMA phase of tile j, at raised priority as in order 2
+            __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int ks = 0; ks < C::NKS; ++ks) mfma_step(fra[ks], frb[ks]);
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(0);
+            if (grp == 0) __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+            barrier();
+            bslot = bslot == 2 ? 0 : bslot + 1;
         }
         if (grp == 0) barrier();                   // G0 idles in the last phase
     } else {

@@ -121,8 +121,10 @@ const Variant kVariants[] = {
     variant<sg::Cfg<128, 128, 32, 5, 2, 2, 0>>(),
     // cute-page order on 16x16x32 MFMAs (schedule 5)
     variant<sg::Cfg<256, 256, 64, 2, 2, 4, 5>>(),
-    // ping-pong wave groups on 16x16x32 MFMAs (schedule 7)
+    // ping-pong wave groups on 16x16x32 MFMAs (schedule 7), and with the
+    // loads split between the groups (schedule 8: A ring of 2, B ring of 3)
     variant<sg::Cfg<256, 256, 64, 2, 2, 4, 7>>(),
+    variant<sg::Cfg<256, 256, 64, 3, 2, 4, 8>>(),
     // whole K extent in the ring, epilogue per row block (schedule 4, K <= S * BK)
     variant<sg::Cfg<128, 128, 64, 2, 2, 2, 4>>(),
     // persistent workgroups, one ring across output tiles (schedule 3)
@@ -148,9 +150,10 @@ const Variant *find_variant(const sg_config *c)
 // Tile family by a wave-quantisation estimate: 256x256 workgroups run one per
 // CU, 128x128 ones do a quarter of the work at about 1.3x the cost per flop;
 // cost = rounds of 256 workgroups x per-workgroup work.  Large grids
-// (8192^3, 8000x7936x8200, 4096^3) pick 256x256x64, two stages, 8 waves,
-// ping-pong wave groups on 16x16x32 MFMAs (6-7 % less time than the cute
-// order on 32x32x16 blocks on all three).  Small or skinny grids pick 128x128x64 with
+// (8192^3, 8000x7936x8200, 4096^3) pick 256x256x64, 8 waves, ping-pong wave
+// groups on 16x16x32 MFMAs with the loads split between the groups
+// (schedule 8: 5-12 % less time than schedule 7, which itself takes 6-7 %
+// less than the cute order on 32x32x16 blocks).  Small or skinny grids pick 128x128x64 with
 // the stage count of the lesson's occupancy trade-off: three stages (96 KiB,
 // one workgroup per CU) when the grid is at most one workgroup per CU
 // (2048^2 sweep); otherwise two stages (64 KiB, two resident per CU), and,
@@ -171,7 +174,7 @@ const Variant *select_variant(int M, int N, int K, bool with_c)
     if (K <= 128 && t128 > 256 && !with_c)
         c = sg_config{128, 128, 64, 2, 4, 4};
     else if (cost256 <= cost128)
-        c = sg_config{256, 256, 64, 2, 8, 7};
+        c = sg_config{256, 256, 64, 3, 8, 8};
     else if (t128 <= 256)
         c = sg_config{128, 128, 64, 3, 4, 1};
     else if (K <= 1024 && !with_c)

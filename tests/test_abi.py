@@ -240,6 +240,9 @@ def test_config_table_and_lds_model():
         st, info = _lib.sg_query_config(c)
         assert st in (S.SG_OK, S.SG_ERR_HIP)
         lds = oracle.lds_bytes(c.tile_m, c.tile_n, c.tile_k, c.stages)
+        if c.schedule == 8:
+            # A keeps one slot fewer than B
+            lds -= oracle.lds_bytes(c.tile_m, c.tile_n, c.tile_k, 1) - c.tile_n * c.tile_k * 2
         assert info.lds_bytes == lds <= 160 * 1024
         assert lds <= info.lds_total_bytes <= 160 * 1024
         assert info.wg_per_cu_lds == oracle.blocks_per_unit(info.lds_total_bytes, 160 * 1024)
@@ -257,7 +260,7 @@ def test_selection_returns_compiled_variants():
         assert c.as_tuple() in {x.as_tuple() for x in _lib.configs()}
     # the measured choices: big squares tiled 256x256x64, the skinny tall
     # shape persistent 128x128x64, the one-wave sweep grid 128x128x64 S3
-    assert _lib.sg_select_config(8192, 8192, 8192).as_tuple() == (256, 256, 64, 2, 8, 7)
+    assert _lib.sg_select_config(8192, 8192, 8192).as_tuple() == (256, 256, 64, 3, 8, 8)
     assert _lib.sg_select_config(81920, 256, 256).as_tuple() == (128, 128, 64, 2, 4, 3)
     assert _lib.sg_select_config(2048, 2048, 2048).as_tuple() == (128, 128, 64, 3, 4, 1)
     assert _lib.sg_select_config(81920, 256, 4096).as_tuple() == (128, 128, 64, 2, 4, 1)

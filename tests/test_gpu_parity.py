@@ -119,7 +119,7 @@ def test_every_variant_on_ragged_shapes(shape):
                                  (128, 128, 64, 3, 4, 1), (256, 256, 64, 2, 8, 2),
                                  (128, 128, 64, 2, 4, 3), (256, 256, 64, 2, 8, 3),
                                  (128, 128, 64, 2, 4, 4), (256, 256, 64, 2, 8, 5),
-                                 (256, 256, 64, 2, 8, 7)])
+                                 (256, 256, 64, 2, 8, 7), (256, 256, 64, 3, 8, 8)])
 def test_tiny_shape_grid(cfg):
     # every M, N and K tail against every tile boundary of the variant
     say(f"[case] tiny grid cfg={cfg}")
@@ -139,6 +139,7 @@ def test_tiny_shape_grid(cfg):
 @pytest.mark.parametrize("shape,cfg", [((4352, 4352, 264), None),
                                        ((4352, 4104, 200), (256, 256, 64, 2, 8, 1)),
                                        ((4352, 4104, 200), (256, 256, 64, 2, 8, 7)),
+                                       ((4352, 4104, 200), (256, 256, 64, 3, 8, 8)),
                                        ((2304, 2304, 520), (128, 128, 32, 4, 4, 1)),
                                        ((2304, 2312, 1000), (256, 256, 32, 3, 8, 0)),
                                        ((4352, 4360, 336), (256, 256, 64, 2, 8, 2)),
@@ -220,7 +221,8 @@ def test_empty_m_or_n_leaves_output_untouched():
                                        ((128, 128, 64, 2, 4, 4), (300, 264, 128)),
                                        ((128, 128, 64, 2, 4, 4), (4200, 4104, 72)),
                                        ((256, 256, 64, 2, 8, 5), (300, 264, 136)),
-                                       ((256, 256, 64, 2, 8, 7), (300, 264, 136))])
+                                       ((256, 256, 64, 2, 8, 7), (300, 264, 136)),
+                                       ((256, 256, 64, 3, 8, 8), (300, 264, 136))])
 def test_canary_guard_bands(cfg, shape):
     # D sits inside a larger buffer filled with a NaN pattern; nothing outside
     # D may change and every element of D must be written
