@@ -491,3 +491,202 @@ def loosest_persistent_wait_counts(ntile: int, ntiles_out: int, stages: int,
             best = n
         counts.append(best)
     return counts
+
+
+# --------------------------------------------------------------------------
+# Two wave groups, one ring per operand
+#
+# The same RAW and WAR rules ("Lesson 6", sections 2-3), for a workgroup
+# whose waves form groups that run different programs between common
+# barriers, with the A and B tiles in rings of their own.  Each group is
+# represented by one of its waves (every wave of a group runs the same
+# program, and the load counter is per wave).  The simulator cuts every
+# program at its barriers; the pieces with the same barrier count form one
+# epoch, and ops of different groups within an epoch have no order.  So:
+#   WAR   an issue into a slot conflicts with any read of that slot in the
+#         same epoch, by any group (reads complete before the reader's next
+#         barrier, so reads of earlier epochs are safe);
+#   RAW   a read needs every counted load of that tile, from every group,
+#         retired by a wait in an earlier epoch;
+#   each group computes tiles 0..ntile-1 in order, from fragments of that
+#   tile that it read; nothing is in flight at the end; every group passes
+#   the same number of barriers.
+
+@dataclass
+class GroupOp:
+    kind: str            # "issue", "wait", "sync", "read", "compute"
+    operand: str = ""    # "A" or "B"
+    tile: int = -1
+    slot: int = -1
+    n: int = 0           # issue: counted loads; wait: loads that may stay outstanding
+
+
+def simulate_groups(programs: dict, ntile: int, slots: dict, parts) -> SimResult:
+    """Replay the per-group programs `programs` ({name: [GroupOp]}).
+    `slots[operand]` is the ring depth of that operand and `parts(operand,
+    tile)` the number of counted loads (summed over the represented waves)
+    that make the tile complete."""
+    res = SimResult(ok=True)
+
+    def err(msg):
+        res.ok = False
+        res.errors.append(msg)
+
+    segs = {}
+    for g, prog in programs.items():
+        cur, lst = [], []
+        for op in prog:
+            if op.kind == "sync":
+                lst.append(cur)
+                cur = []
+            else:
+                cur.append(op)
+        lst.append(cur)
+        segs[g] = lst
+    nseg = {len(v) for v in segs.values()}
+    if len(nseg) != 1:
+        err(f"groups pass different numbers of barriers: "
+            f"{ {g: len(v) - 1 for g, v in segs.items()} }")
+        return res
+    nepoch = nseg.pop()
+
+    ring = {o: [None] * slots[o] for o in slots}
+    issued = {}                         # (operand, tile) -> counted loads issued
+    retired = {}                        # (operand, tile) -> counted loads retired
+    retire_epoch = {}                   # (operand, tile) -> epoch of the last retirement
+    home = {}                           # (operand, tile) -> slot
+    outstanding = {g: [] for g in programs}
+    frags = {g: {} for g in programs}
+    computed = {g: [] for g in programs}
+    read_once = set()
+
+    for e in range(nepoch):
+        reads_now = []                  # (operand, slot, group)
+        issues_now = []                 # (operand, slot, tile, group)
+        for g in programs:
+            for op in segs[g][e]:
+                if op.kind == "issue":
+                    key = (op.operand, op.tile)
+                    if not (0 <= op.tile < ntile):
+                        err(f"{g}: issue of {op.operand} tile {op.tile} outside 0..{ntile - 1}")
+                        continue
+                    if key in read_once or (key in home and home[key] != op.slot):
+                        err(f"{g}: {op.operand} tile {op.tile} loaded twice")
+                    if key not in home:
+                        home[key] = op.slot
+                        ring[op.operand][op.slot] = op.tile
+                    issued[key] = issued.get(key, 0) + op.n
+                    outstanding[g].extend([key] * op.n)
+                    issues_now.append((op.operand, op.slot, op.tile, g))
+                    res.issued.append((op.operand, op.tile, op.slot))
+                elif op.kind == "wait":
+                    while len(outstanding[g]) > max(op.n, 0):
+                        key = outstanding[g].pop(0)
+                        retired[key] = retired.get(key, 0) + 1
+                        retire_epoch[key] = e
+                elif op.kind == "read":
+                    key = (op.operand, op.tile)
+                    held = ring[op.operand][op.slot]
+                    reads_now.append((op.operand, op.slot, g))
+                    read_once.add(key)
+                    res.reads.append((op.operand, op.slot, held, g))
+                    if held != op.tile:
+                        err(f"{g}: read of {op.operand} tile {op.tile} from slot {op.slot}, "
+                            f"which holds tile {held}")
+                    elif (issued.get(key, 0) != parts(op.operand, op.tile)
+                          or retired.get(key, 0) != parts(op.operand, op.tile)
+                          or retire_epoch.get(key, e) >= e):
+                        err(f"RAW: {g} read {op.operand} tile {op.tile} from slot {op.slot} "
+                            f"before all its loads were retired and published")
+                    frags[g][op.operand] = held
+                elif op.kind == "compute":
+                    f = frags[g]
+                    if f.get("A") != op.tile or f.get("B") != op.tile:
+                        err(f"{g}: compute of tile {op.tile} with fragments of A tile "
+                            f"{f.get('A')} and B tile {f.get('B')}")
+                    computed[g].append(op.tile)
+                else:
+                    raise ValueError(op.kind)
+        for (o, s, t, g) in issues_now:
+            clash = sorted({rg for (ro, rs, rg) in reads_now if ro == o and rs == s})
+            if clash:
+                err(f"WAR: {g} refilled {o} slot {s} with tile {t} in the epoch in which "
+                    f"{', '.join(clash)} read it")
+        res.max_in_flight = max(res.max_in_flight,
+                                max((len(set(v)) for v in outstanding.values()), default=0))
+    for g in programs:
+        if computed[g] != list(range(ntile)):
+            err(f"{g}: computed tiles {computed[g]}, not 0..{ntile - 1} in order")
+        if outstanding[g]:
+            err(f"{g}: {len(outstanding[g])} loads still in flight at the end")
+    for o in slots:
+        for t in range(ntile):
+            if issued.get((o, t), 0) != parts(o, t):
+                err(f"{o} tile {t}: {issued.get((o, t), 0)} loads issued, {parts(o, t)} expected")
+    return res
+
+
+def schedule_pingpong(ntile: int, loads: int):
+    """Ping-pong of two wave groups over one ring of two slots that holds A
+    and B tile j in slot j mod 2.  Phase 2j: G0 issues all loads of tile j+1
+    (`loads` per operand per wave), then reads tile j; G1 computes tile j-1.
+    Phase 2j+1: G0 computes tile j and retires its loads; G1 reads tile j.
+    Tile 0 is loaded by both groups (half of each operand each) before the
+    first barrier.  Returns (programs, slots, parts)."""
+    h = loads // 2
+    g0, g1 = [], []
+    if ntile > 0:
+        for prog in (g0, g1):
+            prog += [GroupOp("issue", "A", 0, 0, h), GroupOp("issue", "B", 0, 0, h)]
+    for prog in (g0, g1):
+        prog += [GroupOp("wait", n=0), GroupOp("sync")]
+    g1.append(GroupOp("sync"))
+    for j in range(ntile):
+        if j + 1 < ntile:
+            g0 += [GroupOp("issue", "A", j + 1, (j + 1) % 2, loads),
+                   GroupOp("issue", "B", j + 1, (j + 1) % 2, loads)]
+        for prog in (g0, g1):
+            prog += [GroupOp("read", "A", j, j % 2), GroupOp("read", "B", j, j % 2)]
+        g0 += [GroupOp("sync"), GroupOp("compute", tile=j), GroupOp("wait", n=0), GroupOp("sync")]
+        g1 += [GroupOp("sync"), GroupOp("compute", tile=j), GroupOp("sync")]
+    g0.append(GroupOp("sync"))
+    return {"G0": g0, "G1": g1}, {"A": 2, "B": 2}, (lambda o, t: 2 * h if t == 0 else loads)
+
+
+def schedule_split_pingpong(ntile: int, loads: int, a_slots: int = 2, b_slots: int = 3,
+                            a_ahead: int = 1, b_ahead: int = 2, g0_keep: int = 0,
+                            g1_keep: int | None = None):
+    """The ping-pong with the loads split between the groups: G0 loads A
+    tiles only, G1 B tiles only, `loads` per wave per tile, each after its
+    fragment reads.  A tile j lives in slot j mod a_slots, B tile j in slot
+    j mod b_slots.  Phase 2j: G0 reads tile j, issues A(j + a_ahead); G1
+    computes tile j-1.  Phase 2j+1: G0 computes tile j and waits until at
+    most g0_keep loads remain; G1 reads tile j, issues B(j + b_ahead) and
+    waits until at most g1_keep remain (default: the loads just issued).
+    Before the first barrier G0 loads A tiles 0..a_ahead-1 and G1 B tiles
+    0..b_ahead-1.  The defaults are the kernel's protocol; the parameters
+    exist to plant mistakes.  Returns (programs, slots, parts)."""
+    g0, g1 = [], []
+    for t in range(min(a_ahead, ntile)):
+        g0.append(GroupOp("issue", "A", t, t % a_slots, loads))
+    for t in range(min(b_ahead, ntile)):
+        g1.append(GroupOp("issue", "B", t, t % b_slots, loads))
+    for prog in (g0, g1):
+        prog += [GroupOp("wait", n=0), GroupOp("sync")]
+    g1.append(GroupOp("sync"))
+    for j in range(ntile):
+        for prog in (g0, g1):
+            prog += [GroupOp("read", "A", j, j % a_slots), GroupOp("read", "B", j, j % b_slots)]
+        ta, tb = j + a_ahead, j + b_ahead
+        if ta < ntile:
+            g0.append(GroupOp("issue", "A", ta, ta % a_slots, loads))
+        g0 += [GroupOp("sync"), GroupOp("compute", tile=j), GroupOp("wait", n=g0_keep),
+               GroupOp("sync")]
+        if tb < ntile:
+            g1.append(GroupOp("issue", "B", tb, tb % b_slots, loads))
+            g1.append(GroupOp("wait", n=loads if g1_keep is None else g1_keep))
+        else:
+            g1.append(GroupOp("wait", n=0))
+        g1 += [GroupOp("sync"), GroupOp("compute", tile=j), GroupOp("sync")]
+    g0.append(GroupOp("sync"))
+    return {"G0": g0, "G1": g1}, {"A": a_slots, "B": b_slots}, (lambda o, t: loads)

@@ -279,3 +279,23 @@ def _gpu_visible() -> bool:
 def test_launch_without_device_reports_hip_error():
     # all validation passes, so the library tries to launch and HIP refuses
     assert L.gemm_fp16_tn(8, 8, 8, P, P + 0x100000, P + 0x200000, None) == S.SG_ERR_HIP
+
+
+def test_split_pingpong_variant_matches_the_simulated_protocol():
+    # the compiled split-load ping-pong keeps one A slot fewer than B slots
+    # and loads one operand tile per wave group in loads_per_stage loads per
+    # wave; that protocol passes the two-group hazard simulator
+    from oracle.models import schedule_split_pingpong, simulate_groups
+    cfg = _lib.SgConfig(256, 256, 64, 3, 8, 8)
+    st, info = _lib.sg_query_config(cfg)
+    assert st in (S.SG_OK, S.SG_ERR_HIP)
+    op_tile = cfg.tile_m * cfg.tile_k * 2
+    a_slots = cfg.stages - 1
+    assert info.lds_bytes == a_slots * op_tile + cfg.stages * op_tile == 160 * 1024
+    loads = info.loads_per_stage
+    assert loads * 16 * 64 * (cfg.waves // 2) == op_tile      # one group moves one operand tile
+    for ntile in range(1, 8):
+        progs, slots, parts = schedule_split_pingpong(ntile, loads, a_slots=a_slots,
+                                                      b_slots=cfg.stages)
+        r = simulate_groups(progs, ntile, slots, parts)
+        assert r.ok, (ntile, r.errors)

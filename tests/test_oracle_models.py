@@ -7,8 +7,9 @@ import os
 import pytest
 
 import oracle
-from oracle.models import (Op, schedule_cute_loads, schedule_cute_multistage, schedule_three_phase,
-                           simulate, simulate_loads)
+from oracle.models import (Op, schedule_cute_loads, schedule_cute_multistage, schedule_pingpong,
+                           schedule_split_pingpong, schedule_three_phase, simulate,
+                           simulate_groups, simulate_loads)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -169,3 +170,47 @@ def test_cute_order_with_counted_loads_catches_a_loose_wait():
         loose[t] += 1
         r = simulate_loads(schedule_cute_loads(ntile, stages, 2, L, loose), ntile, stages, 2, L)
         assert not r.ok and any(e.startswith("RAW") for e in r.errors), t
+
+
+# ---- two wave groups, one ring per operand
+
+@pytest.mark.parametrize("ntile", range(0, 10))
+def test_group_schedules_are_hazard_free(ntile):
+    for make in (schedule_pingpong, schedule_split_pingpong):
+        progs, slots, parts = make(ntile, 8)
+        r = simulate_groups(progs, ntile, slots, parts)
+        assert r.ok, (make.__name__, ntile, r.errors)
+
+
+@pytest.mark.parametrize("plant,expect", [
+    (dict(b_slots=2), "WAR"),        # B ring too shallow for loads two tiles ahead
+    (dict(b_ahead=3), "WAR"),        # B loaded three tiles ahead into a three-slot ring
+    (dict(a_ahead=2), "WAR"),        # A loaded two tiles ahead into a two-slot ring
+    (dict(b_ahead=1), "RAW"),        # B loaded only one tile ahead: lands in the phase it is read
+    (dict(g1_keep=16), "RAW"),       # G1 keeps two B tiles in flight
+    (dict(g0_keep=1), "RAW"),        # G0 leaves one load of the next A tile unretired
+])
+def test_split_pingpong_planted_mistakes_are_caught(plant, expect):
+    progs, slots, parts = schedule_split_pingpong(6, 8, **plant)
+    r = simulate_groups(progs, 6, slots, parts)
+    assert not r.ok
+    assert any(e.startswith(expect) for e in r.errors), r.errors
+
+
+def test_split_pingpong_group1_wait_is_the_loosest_safe():
+    # G1 may keep exactly the B tile it just issued in flight, no load more
+    results = []
+    for keep in (8, 9):
+        progs, slots, parts = schedule_split_pingpong(6, 8, g1_keep=keep)
+        results.append(simulate_groups(progs, 6, slots, parts).ok)
+    assert results == [True, False]
+
+
+def test_group_simulator_catches_barrier_mismatch_and_missing_loads():
+    progs, slots, parts = schedule_split_pingpong(4, 8)
+    del progs["G0"][-1]                                   # G0 skips its last barrier
+    assert any("barriers" in e for e in simulate_groups(progs, 4, slots, parts).errors)
+    progs, slots, parts = schedule_pingpong(3, 8)
+    progs["G0"] = [o for o in progs["G0"] if not (o.kind == "issue" and o.operand == "B" and o.tile == 2)]
+    r = simulate_groups(progs, 3, slots, parts)
+    assert not r.ok and any("B tile 2" in e for e in r.errors)
