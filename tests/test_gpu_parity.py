@@ -175,7 +175,8 @@ def test_persistent_workgroups_loop_over_tiles(shape):
         assert rep.ok, (cfg, str(rep))
 
 
-@pytest.mark.parametrize("cfg", [None] + PERSISTENT[:2] + SHORTK)
+@pytest.mark.parametrize("cfg", [None] + PERSISTENT[:2] + SHORTK +
+                         [(256, 256, 64, 2, 8, 7), (256, 256, 64, 3, 8, 8)])
 def test_k_zero_every_schedule(cfg):
     say(f"[case] K=0 {cfg}")
     A = np.zeros((1100, 0), np.float16)
@@ -184,15 +185,18 @@ def test_k_zero_every_schedule(cfg):
     assert np.all(d.view(np.uint16) == 0)
 
 
-@pytest.mark.parametrize("shape", [(40, 16, 1 << 21), (8, 1 << 21, 8), (264, 24, (1 << 21) - 8)])
-def test_maximum_k_and_n(shape):
+@pytest.mark.parametrize("shape,cfg", [((40, 16, 1 << 21), None), ((8, 1 << 21, 8), None),
+                                       ((264, 24, (1 << 21) - 8), None),
+                                       ((264, 24, (1 << 21) - 8), (256, 256, 64, 3, 8, 8))])
+def test_maximum_k_and_n(shape, cfg):
     # K and N at the documented limit 2^21: per-workgroup buffer ranges and
-    # offsets come closest to 2^31 here
+    # offsets come closest to 2^31 here (the last case with 256-row A and B
+    # ranges of the split-load ping-pong: 1 GiB each)
     M, N, K = shape
     g = np.random.Generator(np.random.PCG64(901))
     A = g.uniform(-1, 1, (M, K)).astype(np.float16)
     B = g.uniform(-1, 1, (N, K)).astype(np.float16)
-    full_check(A, B, label=f"limit {shape}")
+    full_check(A, B, config=cfg, label=f"limit {shape}")
 
 
 def test_k_zero_writes_zeros():
