@@ -147,40 +147,48 @@ const Variant *find_variant(const sg_config *c)
 }
 
 // Choice from the measured sweeps (MI355X, fp16 uniform[-1,1] inputs).
-// Tile family by a wave-quantisation estimate: 256x256 workgroups run one per
-// CU, 128x128 ones do a quarter of the work at about 1.3x the cost per flop;
-// cost = rounds of 256 workgroups x per-workgroup work.  Large grids
-// (8192^3, 8000x7936x8200, 4096^3) pick 256x256x64, 8 waves, ping-pong wave
-// groups on 16x16x32 MFMAs with the loads split between the groups
-// (schedule 8: 5-12 % less time than schedule 7, which itself takes 6-7 %
-// less than the cute order on 32x32x16 blocks).  Small or skinny grids pick 128x128x64 with
-// the stage count of the lesson's occupancy trade-off: three stages (96 KiB,
-// one workgroup per CU) when the grid is at most one workgroup per CU
-// (2048^2 sweep); otherwise two stages (64 KiB, two resident per CU), and,
-// when K <= 1024 and there is no C operand, the persistent schedule, whose
-// ring runs on across output tiles (81920 x 256 x 256: -14 % time against
-// the tiled kernel; with long K loops the tiled kernel is 3-5 % faster).
-// Before all that: K <= 128 with more than one wave of 128x128 workgroups
-// and no C operand takes the short-K schedule, whose row-block epilogue
-// overlaps the write of D with the MFMAs (4096 x 4096 x 128: 10.4 us against
-// 11.0 for the tiled 256x256 kernel).
+// First, K <= 128 with more than one wave of 128x128 workgroups and no C
+// operand takes the short-K schedule, whose row-block epilogue overlaps the
+// write of D with the MFMAs (4096 x 4096 x 128: 10.4 us against 11.0 for
+// the tiled 256x256 kernel).  Otherwise the cheapest of these, in units of
+// one full round of 256 workgroups of the 256x256 kernel:
+//   256x256x64, schedule 8 (one workgroup per CU)    1.00 per round of 256
+//   128x128x64 S2, schedule 1 (two per CU)           0.66 per round of 512
+//   128x128x64 S3, schedule 1 (one per CU)           0.42 per round of 256
+//   128x128x64 S2 persistent (K <= 1024, no C)       0.9 x the S2 figure
+// A partial round costs 0.75 + 0.25 x its fill: its workgroups still run
+// the whole K loop, only with less contention.  Fitted to interleaved
+// timings at K = 4096 (2560^2 ... 6144^2, 16384 x 1024, 81920 x 256) and
+// 8192 (2048^2, 2560^2); it picks the faster family at every one of them,
+// and at K = 1024 and 512 it is within 2 % of the best choice.  The
+// persistent factor comes from the tall shape 81920 x 256 x 256 (21.3 us
+// against 23.7 tiled and 25.1 for 256x256 tiles).
+double rounds(long long tiles, long long per_round)
+{
+    const long long full = tiles / per_round;
+    const long long rest = tiles % per_round;
+    return (double)full + (rest ? 0.75 + 0.25 * (double)rest / (double)per_round : 0.0);
+}
+
 const Variant *select_variant(int M, int N, int K, bool with_c)
 {
     const long long t256 = (long long)((M + 255) / 256) * ((N + 255) / 256);
     const long long t128 = (long long)((M + 127) / 128) * ((N + 127) / 128);
-    const double cost256 = (double)((t256 + 255) / 256) * 4.0;
-    const double cost128 = (double)((t128 + 255) / 256) * 1.3;
     sg_config c;
-    if (K <= 128 && t128 > 256 && !with_c)
+    if (K <= 128 && t128 > 256 && !with_c) {
         c = sg_config{128, 128, 64, 2, 4, 4};
-    else if (cost256 <= cost128)
+    } else {
+        const double c256 = rounds(t256, 256);
+        const double c2 = 0.66 * rounds(t128, 512);
+        const double c3 = 0.42 * rounds(t128, 256);
+        const bool persistent = K <= 1024 && !with_c && t128 > 256;
+        const double cp = persistent ? 0.9 * c2 : 1e300;
         c = sg_config{256, 256, 64, 3, 8, 8};
-    else if (t128 <= 256)
-        c = sg_config{128, 128, 64, 3, 4, 1};
-    else if (K <= 1024 && !with_c)
-        c = sg_config{128, 128, 64, 2, 4, 3};
-    else
-        c = sg_config{128, 128, 64, 2, 4, 1};
+        double best = c256;
+        if (c3 < best) { best = c3; c = sg_config{128, 128, 64, 3, 4, 1}; }
+        if (c2 < best) { best = c2; c = sg_config{128, 128, 64, 2, 4, 1}; }
+        if (cp < best) { best = cp; c = sg_config{128, 128, 64, 2, 4, 3}; }
+    }
     return find_variant(&c);
 }
 
