@@ -75,6 +75,10 @@ __device__ __forceinline__ u32x4 rsrc_words(const void *base, uint32_t bytes)
 // here it does not see these loads at all, and the kernel's own vmcnt(0)
 // before each barrier is what orders them.  (Loads the compiler does track
 // are waited for with counts that ignore these: at worst it waits longer.)
+// m0 is written and consumed inside the same statement.  The compiler warns
+// that a reserved register in a clobber list may not be preserved; nothing
+// else in these kernels uses m0 (checked in the generated code), so no value
+// of its own lives across the statement.
 __device__ __forceinline__ void dma16(const u32x4 &rsrc, uint32_t voff, uint32_t lds)
 {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
