@@ -480,3 +480,16 @@ def test_ragged8000():
     say("[case] full ragged8000 (oracle on all 63.5M outputs)")
     rep = oracle.check(d.cpu().numpy(), oracle.gemm_tn_f64(A, B), 8200)
     assert rep.ok, str(rep)
+
+
+@pytest.mark.parametrize("shape", [(3072, 3080, 520), (40960, 256, 2056), (2600, 2560, 1032)])
+def test_selection_refit_shapes(shape):
+    # shapes whose tile family the fitted round-cost model decides: mid-size
+    # squares and a tall shape with a long K loop go to the 256x256
+    # split-load ping-pong, 2600 x 2560 to 128x128 tiles; every element
+    M, N, K = shape
+    A, B = inputs.operands(M, N, K, 1500 + K)
+    cfg = sg._lib.sg_select_config(M, N, K).as_tuple()
+    want = (128, 128, 64, 2, 4, 1) if M == 2600 else (256, 256, 64, 3, 8, 8)
+    assert cfg == want, (shape, cfg)
+    full_check(A, B, label=f"refit {shape} -> {cfg}")
