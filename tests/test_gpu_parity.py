@@ -250,7 +250,9 @@ def test_canary_guard_bands(cfg, shape):
 def test_alpha_values(alpha):
     A, B = inputs.operands(384, 392, 520, 91)
     a32 = float(np.float32(alpha))
-    full_check(A, B, alpha=a32, label=f"alpha {alpha}")
+    # the library's choice, and the large-shape kernel on the same operands
+    for cfg in (None, (256, 256, 64, 3, 8, 8)):
+        full_check(A, B, alpha=a32, config=cfg, label=f"alpha {alpha} {cfg}")
 
 
 @pytest.mark.parametrize("shape", [(300, 264, 200), (4352, 520, 264), (256, 256, 0),
