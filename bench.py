@@ -315,7 +315,8 @@ def main() -> int:
                     choices=["bench", "variants", "ksweep", "calibrate_copy", "attention"])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed launches first (default: about 100 ms of them, at least 30)")
     ap.add_argument("--workload", default="square8192")
     ap.add_argument("--config", default=None,
                     help="explicit variant tile_m,tile_n,tile_k,stages,waves,schedule")
@@ -325,6 +326,9 @@ def main() -> int:
     ap.add_argument("--cold", action="store_true",
                     help="also time single launches after a 512 MiB cache flush")
     args = ap.parse_args()
+    auto_warmup = args.warmup is None
+    if auto_warmup:
+        args.warmup = 30
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU (asked for {args.gpus}): the GEMM shards into "
@@ -360,6 +364,18 @@ def main() -> int:
     def step():
         sg.gemm(a, b, out=d, alpha=alpha, config=cfg)
 
+    if auto_warmup:
+        # about 100 ms of launches, so that the clock has settled before the
+        # timed steps even for a kernel of a few microseconds
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+        tw = time.perf_counter()
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+        per = (time.perf_counter() - tw) / 10
+        args.warmup = max(30, min(20000, int(0.1 / max(per, 1e-6))))
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
