@@ -682,7 +682,8 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
                 __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
             }
             barrier();
-            // MFMA phase of tile j, at raised priority as in order 2
+            // MFMA phase of tile j, at raised priority as in order 2 (here
+            // measured neutral: the reading wave seldom competes for issue)
             __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int ks = 0; ks < C::NKS; ++ks) mfma_step(fra[ks], frb[ks]);

@@ -268,6 +268,8 @@ def test_selection_returns_compiled_variants():
     assert _lib.sg_select_config(3072, 3072, 4096).as_tuple() == (256, 256, 64, 3, 8, 8)
     assert _lib.sg_select_config(6144, 6144, 4096).as_tuple() == (256, 256, 64, 3, 8, 8)
     assert _lib.sg_select_config(4096, 4096, 128).as_tuple() == (128, 128, 64, 2, 4, 4)
+    assert _lib.sg_select_config(2048, 2048, 128).as_tuple() == (128, 128, 64, 2, 4, 4)
+    assert _lib.sg_select_config(2048, 2048, 512).as_tuple() == (128, 128, 64, 3, 4, 1)
 
 
 def _gpu_visible() -> bool:
