@@ -451,7 +451,10 @@ def main() -> int:
         out["config"]["mfma_ceiling_tflops"] = round(ceil, 1)
         out["config"]["frac_of_mfma_ceiling"] = round(achieved / ceil, 4)
         # the same loop on 16x16x32 MFMAs, which draw less power per flop
-        out["config"]["mfma_ceiling_16x16x32_tflops"] = round(mfma_ceiling(a, b, shape16=True), 1)
+        # (the shape the large-shape kernel uses)
+        ceil16 = mfma_ceiling(a, b, shape16=True)
+        out["config"]["mfma_ceiling_16x16x32_tflops"] = round(ceil16, 1)
+        out["config"]["frac_of_mfma_ceiling_16x16x32"] = round(achieved / ceil16, 4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(A, B, args.cpu_seconds)
     print(json.dumps(out), flush=True)
