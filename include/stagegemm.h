@@ -144,8 +144,9 @@ sg_status gemm_fp16_tn_cfg(int M, int N, int K, float alpha, const void *A,
 
 /* The variant gemm_fp16_tn (and gemm_fp16_tn_alpha) would run for this
  * shape (no pointers needed).  gemm_fp16_tn_alpha_beta with beta != 0 runs
- * the same variant unless it is persistent (schedule 3): then the tiled
- * variant of the same tile and stage count. */
+ * the same variant unless it is persistent (schedule 3) or short-K
+ * (schedule 4), which take no C operand: the choice is then made among the
+ * tiled variants only, by the same cost model. */
 sg_status sg_select_config(int M, int N, int K, sg_config *out);
 
 /* Enumerate the compiled variants: index 0 .. sg_num_configs()-1. */
