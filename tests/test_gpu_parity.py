@@ -495,3 +495,22 @@ def test_selection_refit_shapes(shape):
     want = (128, 128, 64, 2, 4, 1) if M == 2600 else (256, 256, 64, 3, 8, 8)
     assert cfg == want, (shape, cfg)
     full_check(A, B, label=f"refit {shape} -> {cfg}")
+
+
+def test_random_shapes_variants_and_alpha():
+    # seeded random cases beyond the fixed grids: any M, N and K tail, any
+    # compiled variant that takes the K, any alpha; every element
+    g = np.random.Generator(np.random.PCG64(4242))
+    for case in range(40):
+        M = int(g.integers(1, 700))
+        N = 8 * int(g.integers(1, 80))
+        K = 8 * int(g.integers(0, 80))
+        cands = [c for c in VARIANTS if runs(c, K)]
+        cfg = cands[int(g.integers(0, len(cands)))]
+        alpha = float(np.float32(g.choice([1.0, 0.5, -1.25, 1.0 / 3.0, 2.0 ** -7])))
+        A = g.uniform(-1, 1, (M, K)).astype(np.float16)
+        B = g.uniform(-1, 1, (N, K)).astype(np.float16)
+        say(f"[case] random {case}: {M}x{N}x{K} cfg={cfg} alpha={alpha}")
+        d = run_gemm(A, B, alpha, cfg).cpu().numpy()
+        rep = oracle.check(d, oracle.gemm_tn_f64(A, B, alpha), K)
+        assert rep.ok, (case, M, N, K, cfg, alpha, str(rep))
