@@ -272,3 +272,18 @@ def test_two_streams_concurrently():
         for pair in outs:
             err = np.abs(pair[idx].cpu().numpy().astype(np.float64) - ref)
             assert np.all(err <= bound), idx
+
+
+def test_random_shapes_alpha_and_splits():
+    # seeded random cases: heads, ragged M and N, alpha of either sign and
+    # size, the library's split count or a random one up to the key tiles
+    g = np.random.Generator(np.random.PCG64(4343))
+    for case in range(24):
+        H = int(g.integers(1, 4))
+        M = int(g.integers(1, 420))
+        N = int(g.integers(1, 900))
+        alpha = float(np.float32(g.choice([1.0 / math.sqrt(128), -1.0 / math.sqrt(128), 0.02, -0.3])))
+        ntiles = (N + 63) // 64
+        splits = None if g.integers(0, 3) == 0 else int(g.integers(1, min(ntiles, 8) + 1))
+        Q, K, V = qkv(H, M, N, 5000 + case, scale=float(g.choice([0.5, 1.0, 2.0])))
+        check(Q, K, V, alpha, f"random {case}", splits=splits)
