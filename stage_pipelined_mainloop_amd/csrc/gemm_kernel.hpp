@@ -9,7 +9,8 @@
 //   * One workgroup per BM x BN output tile; NW = WM x WN wavefronts of 64
 //     lanes, each owning a (BM/WM) x (BN/WN) sub-tile built from 32x32 MFMA
 //     blocks (v_mfma_f32_32x32x16_f16, fp32 accumulators) or from 16x16 ones
-//     (v_mfma_f32_16x16x32_f16, schedules 5 and 7; see "MFMA shape" below).
+//     (v_mfma_f32_16x16x32_f16, schedules 5, 7 and 8; see "MFMA shape"
+//     below).
 //   * An S-slot ring in LDS.  Each slot holds one K step: A rows [BM x BK] and
 //     B rows [BN x BK], both K-contiguous (the TN layout needs no transpose).
 //   * Global -> LDS copies are LDS-DMA buffer loads (buffer_load_dwordx4 ...
@@ -147,7 +148,9 @@ __device__ __forceinline__ int swz(int r)
 // (wait, barrier, refill, compute), 1 = the cute page's order with the next
 // tile's first fragments prefetched across the barrier, 2 = ping-pong of two
 // wave groups (one computes while the other reads and refills), 3 =
-// persistent, 4 = short K, 5 = order 1 on 16x16x32 MFMAs.
+// persistent, 4 = short K, 5 = order 1 on 16x16x32 MFMAs, 7 = order 2 on
+// 16x16x32 MFMAs, 8 = order 7 with the LDS-DMA loads split between the two
+// wave groups (A ring of S - 1 slots, B ring of S; "order 8" below).
 //
 // MFMA shape.  Schedules 0-4 use v_mfma_f32_32x32x16_f16 (32x32 blocks, K
 // steps of 16); schedules 5, 7 and 8 use v_mfma_f32_16x16x32_f16 (16x16
