@@ -263,7 +263,7 @@ def test_two_streams_concurrently():
         with torch.cuda.stream(s2):
             o2 = sg.attention(*d2, alpha=0.1)
         outs.append((o1, o2))
-        s1.synchronize()                               # ws1 is reused by the next round
+        s1.synchronize()                               # ws1 is reused by the next iteration
     torch.cuda.synchronize()
     for (Q, K, V), idx in (((Q1, K1, V1), 0), ((Q2, K2, V2), 1)):
         ref, w = oracle.attention_f64(Q, K, V, 0.1, with_bound=True)
