@@ -412,12 +412,15 @@ def test_graph_replays_match_eager():
 
 
 def test_two_streams_concurrently():
-    # independent calls on two streams at once (including two persistent
-    # launches competing for the same CUs) each match the oracle
+    # independent calls on three streams at once (two persistent launches
+    # competing for the same CUs, and the split-load ping-pong, whose
+    # workgroups take a whole CU's LDS) each match the oracle
     A1, B1 = inputs.operands(20480, 256, 256, 1601)
     A2, B2 = inputs.operands(2048, 2048, 1024, 1603)
+    A3, B3 = inputs.operands(3072, 3080, 520, 1605)
     a1, b1, a2, b2 = to_dev(A1), to_dev(B1), to_dev(A2), to_dev(B2)
-    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    a3, b3 = to_dev(A3), to_dev(B3)
+    s1, s2, s3 = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
     outs = []
     torch.cuda.synchronize()
     for _ in range(3):
@@ -425,13 +428,18 @@ def test_two_streams_concurrently():
             o1 = sg.gemm(a1, b1)
         with torch.cuda.stream(s2):
             o2 = sg.gemm(a2, b2)
-        outs.append((o1, o2))
+        with torch.cuda.stream(s3):
+            o3 = sg.gemm(a3, b3)
+        outs.append((o1, o2, o3))
     torch.cuda.synchronize()
+    assert sg._lib.sg_select_config(3072, 3080, 520).as_tuple() == (256, 256, 64, 3, 8, 8)
     ref1 = oracle.gemm_tn_f64(A1, B1)
     ref2 = oracle.gemm_tn_f64(A2, B2)
-    for o1, o2 in outs:
+    ref3 = oracle.gemm_tn_f64(A3, B3)
+    for o1, o2, o3 in outs:
         assert oracle.check(o1.cpu().numpy(), ref1, 256).ok
         assert oracle.check(o2.cpu().numpy(), ref2, 1024).ok
+        assert oracle.check(o3.cpu().numpy(), ref3, 520).ok
 
 
 def test_tall_skinny_81920():
