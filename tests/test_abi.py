@@ -304,3 +304,19 @@ def test_split_pingpong_variant_matches_the_simulated_protocol():
                                                       b_slots=cfg.stages)
         r = simulate_groups(progs, ntile, slots, parts)
         assert r.ok, (ntile, r.errors)
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    # no fallback of any kind: without the built library every entry point
+    # raises, and the Python front end refuses host tensors outright
+    monkeypatch.setattr(_lib, "LIB_PATH", "/nonexistent/libstagegemm.so")
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.lib()
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.gemm_fp16_tn(8, 8, 8, 0, 0, 0, None)
+    import torch
+    import stage_pipelined_mainloop_amd as sg
+    a = torch.zeros((8, 8), dtype=torch.float16)
+    with pytest.raises(ValueError, match="device tensors"):
+        sg.gemm(a, a)
