@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "attention_kernel.hpp"
 
 namespace {
@@ -45,17 +47,21 @@ size_t workspace_bytes(int H, int M, int splits)
 }
 
 // Compute units of the current device (cached per device; 0 if the query
-// fails).
+// fails).  Host threads that fill the cache at once write the same value,
+// through an atomic.
 int device_cus()
 {
-    static int cache[64];
+    static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
-    if (dev < 64 && cache[dev] > 0) return cache[dev];
+    if (dev < 64) {
+        const int hit = cache[dev].load(std::memory_order_relaxed);
+        if (hit > 0) return hit;
+    }
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
-    if (dev < 64) cache[dev] = cus;
+    if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
     return cus;
 }
 

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "gemm_kernel.hpp"
 #include "persistent_kernel.hpp"
 #include "shortk_kernel.hpp"
@@ -42,18 +44,23 @@ constexpr gemm_kernel_fn kernel_of()
 }
 
 // Workgroups of kernel `k` that the device can keep resident at once (CUs x
-// workgroups per CU), cached per device; 0 if the runtime cannot tell.
-int resident_capacity(const void *k, int threads, int (&cache)[16])
+// workgroups per CU), cached per device; 0 if the runtime cannot tell.  Calls
+// from several host threads may fill the cache at once: each writes the same
+// value, through an atomic.
+int resident_capacity(const void *k, int threads, std::atomic<int> (&cache)[16])
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
-    if (dev >= 0 && dev < 16 && cache[dev] > 0) return cache[dev];
+    if (dev >= 0 && dev < 16) {
+        const int hit = cache[dev].load(std::memory_order_relaxed);
+        if (hit > 0) return hit;
+    }
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, threads, 0) != hipSuccess)
         return 0;
     const int cap = cus * per_cu;
-    if (dev >= 0 && dev < 16) cache[dev] = cap;
+    if (dev >= 0 && dev < 16) cache[dev].store(cap, std::memory_order_relaxed);
     return cap;
 }
 
@@ -66,7 +73,7 @@ hipError_t launch(int M, int N, int K, float alpha, float beta, const void *A, c
     long long grid = tiles;
     if constexpr (C::SCHED == 3) {
         // one workgroup per resident slot; each loops over its output tiles
-        static int cache[16];
+        static std::atomic<int> cache[16];
         const int cap = resident_capacity(reinterpret_cast<const void *>(kernel), C::T, cache);
         if (cap <= 0) return hipErrorInvalidConfiguration;
         if (grid > cap) grid = cap;
