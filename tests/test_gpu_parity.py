@@ -384,8 +384,10 @@ def test_graph_replays_match_eager():
     # the launch path makes no allocation, memset or host synchronisation, so
     # it can be captured into a HIP graph: replays, with eager work between
     # them, must reproduce the eager result bit for bit (tiled, persistent
-    # and short-K kernels)
-    for (M, N, K) in [(4096, 4096, 512), (2048, 1024, 512), (20480, 256, 256), (4096, 2048, 128)]:
+    # and short-K kernels, and the 256^3 call that bench.py replays from a
+    # graph)
+    for (M, N, K) in [(4096, 4096, 512), (2048, 1024, 512), (20480, 256, 256), (4096, 2048, 128),
+                      (256, 256, 256)]:
         say(f"[case] graph {M}x{N}x{K}")
         A, B = inputs.operands(M, N, K, 1500 + K)
         a, b = to_dev(A), to_dev(B)
@@ -400,7 +402,8 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            sg.gemm(a, b, out=out)
+            for _ in range(3):                 # several steps in one graph
+                sg.gemm(a, b, out=out)
         for r in range(4):
             out.fill_(float("nan"))
             g.replay()
