@@ -414,6 +414,50 @@ def test_graph_replays_match_eager():
             assert torch.equal(tmp.view(torch.int16), eager.view(torch.int16))
 
 
+def test_calls_from_several_host_threads():
+    # host threads, each on its own stream, call the tiled (split-load
+    # ping-pong), persistent, short-K and attention entry points at once; the
+    # launchers share only per-device caches, and every result must equal the
+    # one the same call gives alone, bit for bit
+    import threading
+    cases = [((3072, 3080, 520), 1701), ((20480, 256, 256), 1703), ((4096, 2048, 128), 1705)]
+    ops = []
+    for (M, N, K), seed in cases:
+        A, B = inputs.operands(M, N, K, seed)
+        a, b = to_dev(A), to_dev(B)
+        ops.append(lambda a=a, b=b: sg.gemm(a, b))
+    gen = torch.Generator().manual_seed(1707)
+    q, k, v = (torch.randn((4, 512, 128), generator=gen).half().cuda() for _ in range(3))
+    ops.append(lambda: sg.attention(q, k, v, splits=2))
+    alone = []
+    for op in ops:
+        alone.append(op())
+        torch.cuda.synchronize()
+    results, errors = {}, []
+
+    def worker(i):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                outs = [ops[i]() for _ in range(4)]
+            s.synchronize()
+            results[i] = outs
+        except Exception as e:             # reported from the main thread
+            errors.append((i, repr(e)))
+
+    say("[case] host threads")
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(ops))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not any(t.is_alive() for t in threads)
+    assert not errors, errors
+    for i, ref in enumerate(alone):
+        for r, out in enumerate(results[i]):
+            assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), (i, r)
+
+
 def test_two_streams_concurrently():
     # independent calls on three streams at once (two persistent launches
     # competing for the same CUs, and the split-load ping-pong, whose
