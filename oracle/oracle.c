@@ -130,6 +130,15 @@ static double dot_f64(const uint16_t *arow, const uint16_t *brow, int K)
     return sum;
 }
 
+/* alpha * s in fp64 (exact: 24 x 53 bits fit unless s has more than 29
+ * significant bits, and then one fp64 rounding far below fp16's), plus +0 so
+ * that an exactly zero value is +0 for either sign of alpha: the value of an
+ * exactly zero real sum has no sign, and round-to-nearest gives +0 for it. */
+static double scaled_sum(double a64, double s)
+{
+    return a64 * s + 0.0;
+}
+
 /* D[i][j] = RNE16( alpha * sum_k A[i][k] * B[j][k] ), all row-major. */
 void sgo_gemm_tn_f64(int M, int N, int K, float alpha,
                      const uint16_t *A, const uint16_t *B, uint16_t *D)
@@ -140,7 +149,7 @@ void sgo_gemm_tn_f64(int M, int N, int K, float alpha,
     for (int i = 0; i < M; ++i)
         for (int j = 0; j < N; ++j) {
             double s = dot_f64(A + (size_t)i * K, B + (size_t)j * K, K);
-            D[(size_t)i * N + j] = sgo_f64_to_f16(a64 * s);
+            D[(size_t)i * N + j] = sgo_f64_to_f16(scaled_sum(a64, s));
         }
 }
 
@@ -158,7 +167,7 @@ void sgo_gemm_tn_f64_beta(int M, int N, int K, float alpha, float beta,
         for (int j = 0; j < N; ++j) {
             double s = a64 * dot_f64(A + (size_t)i * K, B + (size_t)j * K, K);
             if (beta != 0.0f) s += b64 * g_dec[C[(size_t)i * N + j]];   /* beta*c exact */
-            D[(size_t)i * N + j] = sgo_f64_to_f16(s);
+            D[(size_t)i * N + j] = sgo_f64_to_f16(s + 0.0);   /* exact zero -> +0 */
         }
 }
 
@@ -171,7 +180,7 @@ void sgo_gemm_tn_f64_at(int K, float alpha, const uint16_t *A, const uint16_t *B
     #pragma omp parallel for schedule(dynamic, 64)
     for (long t = 0; t < count; ++t) {
         double s = dot_f64(A + (size_t)rows[t] * K, B + (size_t)cols[t] * K, K);
-        out[t] = sgo_f64_to_f16(a64 * s);
+        out[t] = sgo_f64_to_f16(scaled_sum(a64, s));
     }
 }
 
@@ -185,7 +194,7 @@ void sgo_gemm_tn_f64_rows(int N, int K, float alpha, const uint16_t *A,
     for (int i = r0; i < r1; ++i)
         for (int j = 0; j < N; ++j) {
             double s = dot_f64(A + (size_t)i * K, B + (size_t)j * K, K);
-            Drows[(size_t)(i - r0) * N + j] = sgo_f64_to_f16(a64 * s);
+            Drows[(size_t)(i - r0) * N + j] = sgo_f64_to_f16(scaled_sum(a64, s));
         }
 }
 

@@ -69,17 +69,18 @@ def test_exact_matches_rational_brute_force(seed):
 
 
 @pytest.mark.parametrize("kind", ["uniform", "wide"])
-def test_f64_equals_exact_on_all_tiny_shapes(kind):
+@pytest.mark.parametrize("alpha", [1.0, -1.0, -0.375])
+def test_f64_equals_exact_on_all_tiny_shapes(kind, alpha):
+    # bit patterns, so the sign of every zero is compared too (K = 0 included)
     g = np.random.Generator(np.random.PCG64(7))
     for M in range(1, 9):
         for N in range(1, 9):
             for K in range(0, 9):
                 A = _rand_f16(g, (M, K), kind)
                 B = _rand_f16(g, (N, K), kind)
-                d1 = oracle.gemm_tn_f64(A, B)
-                d2 = oracle.gemm_tn_exact(A, B)
-                # values equal (+0 and -0 compare equal)
-                assert np.array_equal(d1.astype(np.float64), d2.astype(np.float64)), (M, N, K)
+                d1 = oracle.gemm_tn_f64(A, B, alpha)
+                d2 = oracle.gemm_tn_exact(A, B, alpha)
+                assert np.array_equal(d1.view(np.uint16), d2.view(np.uint16)), (M, N, K, alpha)
 
 
 def test_f64_equals_exact_random_shapes_to_64():
@@ -88,10 +89,40 @@ def test_f64_equals_exact_random_shapes_to_64():
         M, N, K = (int(v) for v in g.integers(1, 65, size=3))
         A = _rand_f16(g, (M, K))
         B = _rand_f16(g, (N, K))
-        alpha = float(np.float32(g.choice([1.0, 0.125, 1 / math.sqrt(128)])))
+        alpha = float(np.float32(g.choice([1.0, 0.125, 1 / math.sqrt(128), -0.5, -3.0])))
         d1 = oracle.gemm_tn_f64(A, B, alpha)
         d2 = oracle.gemm_tn_exact(A, B, alpha)
-        assert np.array_equal(d1.astype(np.float64), d2.astype(np.float64)), (M, N, K)
+        assert np.array_equal(d1.view(np.uint16), d2.view(np.uint16)), (M, N, K, alpha)
+
+
+@pytest.mark.parametrize("alpha", [1.0, -1.0, -0.125, 0.0, -0.0])
+def test_exactly_zero_sums_are_plus_zero(alpha):
+    # The real sum 0 has no sign and round-to-nearest gives +0 for it, for any
+    # alpha: the empty sum (K = 0), an all-zero row, signed zeros in the
+    # operands and a row whose products cancel exactly.  A nonzero negative
+    # value too small for binary16 still rounds to -0.
+    A = np.zeros((4, 8), np.float16)
+    A[1] = -0.0
+    A[2] = [0, 1, -1, 2, -2, 0.5, -0.5, 0]        # products with B row 0 cancel
+    A[3, 0] = np.float16(2.0 ** -14)
+    B = np.zeros((2, 8), np.float16)
+    B[0] = 1.0
+    B[1, 0] = np.float16(-2.0 ** -14)             # A[3] . B[1] = -2^-28
+    want = np.zeros((4, 2), np.uint16)
+    if alpha != 0:
+        want[3, 0] = np.float16(alpha * 2.0 ** -14).view(np.uint16)   # exact in binary16
+        if alpha > 0:
+            want[3, 1] = 0x8000                   # -2^-28 * alpha rounds to -0
+    for f in (oracle.gemm_tn_f64, oracle.gemm_tn_exact):
+        d = f(A, B, alpha).view(np.uint16)
+        assert np.array_equal(d, want), (alpha, d, want)
+        d0 = f(np.zeros((3, 0), np.float16), np.zeros((5, 0), np.float16), alpha)
+        assert np.array_equal(d0.view(np.uint16), np.zeros((3, 5), np.uint16)), alpha
+    # beta: alpha * 0 = -0 and beta * c = -0 still give +0
+    C = np.full((2, 2), -0.0, np.float16)
+    for f in (oracle.gemm_tn_f64_beta, oracle.gemm_tn_exact_beta):
+        d = f(A[:2], B, C, alpha, 1.0).view(np.uint16)
+        assert np.array_equal(d, np.zeros((2, 2), np.uint16)), (alpha, d)
 
 
 def test_f64_against_numpy_matmul():
