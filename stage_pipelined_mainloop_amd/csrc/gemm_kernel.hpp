@@ -278,6 +278,16 @@ __device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, i
     tn = in_group / gm;
 }
 
+// alpha * acc as one fused operation with a +0 addend: the product is exact
+// inside the fma and the +0 turns an exactly zero product (alpha < 0 times a
+// zero sum) into +0, the value round-to-nearest gives the real sum 0; no other
+// value changes.  The compiler folds it with the conversion to fp16 into
+// v_fma_mixlo_f16.
+__device__ __forceinline__ float scale_acc(float alpha, float acc)
+{
+    return __builtin_fmaf(alpha, acc, 0.0f);
+}
+
 // One 32-row block of a wave's sub-tile (its FN 32x32 accumulators, rows
 // row0 .. row0+31 of the workgroup tile) to D = RNE16(alpha * acc), through
 // the wave's unpadded staging area: 128-byte rows of sixteen 8-byte slots,
@@ -305,10 +315,10 @@ __device__ __forceinline__ void store_block_staged(const f32x16 (&blk)[C::FN], f
         for (int g = 0; g < 4; ++g) {
             const f32x16 &a = blk[j];
             u32x2 packed;
-            packed[0] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(alpha * a[4 * g + 0])) |
-                        ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(alpha * a[4 * g + 1])) << 16);
-            packed[1] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(alpha * a[4 * g + 2])) |
-                        ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(alpha * a[4 * g + 3])) << 16);
+            packed[0] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)scale_acc(alpha, a[4 * g + 0])) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)scale_acc(alpha, a[4 * g + 1])) << 16);
+            packed[1] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)scale_acc(alpha, a[4 * g + 2])) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)scale_acc(alpha, a[4 * g + 3])) << 16);
             const int slot8 = (8 * j + 2 * g + half) ^ wsw;
             *(u32x2 *)(epi + wr * 128 + slot8 * 8) = packed;
         }
@@ -838,7 +848,8 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
                 int r, c;
                 float v[4];
                 piece(i, p, r, c, v);
-                stage4(r, c, alpha * v[0], alpha * v[1], alpha * v[2], alpha * v[3]);
+                stage4(r, c, scale_acc(alpha, v[0]), scale_acc(alpha, v[1]), scale_acc(alpha, v[2]),
+                       scale_acc(alpha, v[3]));
             }
         } else {
             // D = RNE16(alpha * acc + beta * C) ("CUDA operator notes 2",
@@ -869,8 +880,11 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
                     const float c1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(cv[q][0] >> 16));
                     const float c2 = (float)__builtin_bit_cast(_Float16, (uint16_t)(cv[q][1] & 0xffffu));
                     const float c3 = (float)__builtin_bit_cast(_Float16, (uint16_t)(cv[q][1] >> 16));
-                    stage4(r, c, __builtin_fmaf(beta, c0, alpha * v[0]), __builtin_fmaf(beta, c1, alpha * v[1]),
-                           __builtin_fmaf(beta, c2, alpha * v[2]), __builtin_fmaf(beta, c3, alpha * v[3]));
+                    // a zero product is +0 here, so an exactly zero total is +0 too
+                    stage4(r, c, __builtin_fmaf(beta, c0, scale_acc(alpha, v[0])),
+                           __builtin_fmaf(beta, c1, scale_acc(alpha, v[1])),
+                           __builtin_fmaf(beta, c2, scale_acc(alpha, v[2])),
+                           __builtin_fmaf(beta, c3, scale_acc(alpha, v[3])));
                 }
             }
         }

@@ -6,11 +6,10 @@ expected values come only from oracle/.  Bound per element:
 |D - D_ref| <= 2 ulp16(|D_ref|) + 1e-4 sqrt(K), every element finite.
 
 Small shapes, and the full-size workloads 4096^3, 8192^3 (the benchmarked
-call), 8000x7936x8200, 4096x4096x128 and 81920x256x256, are compared element
-by element in full.  The K-sweep runs every stage count of both tile
-families at full size and is compared on whole sampled rows and columns,
-chosen to cross every tile boundary, plus a check that every element is
-finite.
+call), 8000x7936x8200, 4096x4096x128, 81920x256x256 and the K-sweep
+(M = N = 2048, every K, every stage count of both tile families), are
+compared element by element in full.  Exactly zero sums are compared by bit
+pattern (+0 for either sign of alpha).
 """
 import math
 import sys
@@ -175,14 +174,41 @@ def test_persistent_workgroups_loop_over_tiles(shape):
         assert rep.ok, (cfg, str(rep))
 
 
+@pytest.mark.parametrize("alpha", [None, -1.0, -0.375])
 @pytest.mark.parametrize("cfg", [None] + PERSISTENT[:2] + SHORTK +
                          [(256, 256, 64, 2, 8, 7), (256, 256, 64, 3, 8, 8)])
-def test_k_zero_every_schedule(cfg):
-    say(f"[case] K=0 {cfg}")
+def test_k_zero_every_schedule(cfg, alpha):
+    # the empty sum is +0 (bit pattern 0) for either sign of alpha
+    say(f"[case] K=0 {cfg} alpha={alpha}")
     A = np.zeros((1100, 0), np.float16)
     B = np.zeros((1032, 0), np.float16)
-    d = run_gemm(A, B, config=cfg).cpu().numpy()
+    d = run_gemm(A, B, alpha=alpha, config=cfg).cpu().numpy()
     assert np.all(d.view(np.uint16) == 0)
+
+
+@pytest.mark.parametrize("alpha", [-1.0, -0.375, 1.0])
+def test_zero_sums_are_plus_zero_every_variant(alpha):
+    # rows whose sum is exactly zero (all-zero, signed zeros, products that
+    # cancel) must give the oracle's bit patterns (+0) for negative alpha too;
+    # the other rows are compared within the tolerance
+    M, N, K = 300, 264, 136
+    A, B = inputs.operands(M, N, K, 1901)
+    A[5] = 0.0
+    A[70] = -0.0
+    A[171] = 0.0
+    A[171, :8] = [1, -1, 0.5, -0.5, 0.25, -0.25, 2, -2]      # cancels against B's first...
+    B[:, :8] = np.float16(0.75)                              # ...8 columns of equal value
+    ref = oracle.gemm_tn_f64(A, B, alpha)
+    zero_rows = [5, 70, 171]
+    assert np.all(ref[zero_rows].view(np.uint16) == 0)
+    for cfg in [None] + VARIANTS:
+        if not runs(cfg, K):
+            continue
+        say(f"[case] zero sums alpha={alpha} {cfg}")
+        d = run_gemm(A, B, alpha=alpha, config=cfg).cpu().numpy()
+        assert np.array_equal(d[zero_rows].view(np.uint16), ref[zero_rows].view(np.uint16)), cfg
+        rep = oracle.check(d, ref, K)
+        assert rep.ok, (cfg, str(rep))
 
 
 @pytest.mark.parametrize("shape,cfg", [((40, 16, 1 << 21), None), ((8, 1 << 21, 8), None),
@@ -358,15 +384,21 @@ def test_square4096():
 
 @pytest.mark.parametrize("K", inputs.KSWEEP_K)
 def test_ksweep_every_stage_count(K):
+    # every element of every variant (each stage count of both tile
+    # families, and the library's own choice) against one oracle run per K
     A, B = inputs.ksweep(K)
     a, b = to_dev(A), to_dev(B)
-    for cfg in VARIANTS:
-        if cfg[:2] not in ((128, 128), (256, 256)) or not runs(cfg, K):
+    say(f"[case] ksweep K={K}: oracle on all 4.2M outputs")
+    ref = oracle.gemm_tn_f64(A, B)
+    for cfg in [None] + VARIANTS:
+        if cfg is not None and (cfg[:2] not in ((128, 128), (256, 256)) or not runs(cfg, K)):
             continue
+        say(f"[case] ksweep K={K} {cfg}")
         d = torch.full((2048, 2048), float("nan"), dtype=torch.float16, device=DEV)
         sg.gemm(a, b, out=d, config=cfg)
         torch.cuda.synchronize()
-        sampled_check(A, B, d, None, f"ksweep K={K} {cfg}", seed=K)
+        rep = oracle.check(d.cpu().numpy(), ref, K)
+        assert rep.ok, (K, cfg, str(rep))
 
 
 def test_square8192():
