@@ -35,10 +35,11 @@
  *   - M, N, K >= 0.  M == 0 or N == 0 is a no-op returning SG_OK; K == 0
  *     writes +0 to all of D (the empty sum).
  *   - K % 8 == 0 and N % 8 == 0 (rows are whole 16-byte chunks), and A, B, D
- *     16-byte aligned; otherwise SG_ERR_ALIGN.  M is unrestricted.  Tails in
- *     M, N and K that are not tile multiples are handled inside the kernel.
- *   - K <= 2^21, N <= 2^21, every matrix below 2^40 elements and the launch
- *     below 2^32 threads; otherwise SG_ERR_SHAPE.
+ *     16-byte aligned; otherwise SG_ERR_ALIGN.  M needs no multiple.  Tails
+ *     in M, N and K that are not tile multiples are handled inside the
+ *     kernel.
+ *   - K <= 2^21, N <= 2^21, M <= 2^31 - 257, every matrix below 2^40
+ *     elements and the launch below 2^32 threads; otherwise SG_ERR_SHAPE.
  *   - D must not overlap A or B (SG_ERR_ALIAS).
  */
 #ifndef STAGEGEMM_H

@@ -200,6 +200,9 @@ const Variant *select_variant(int M, int N, int K, bool with_c)
     return find_variant(&c);
 }
 
+// Largest M: tile counts (M + tile_m - 1) / tile_m stay within int.
+constexpr int kMaxM = 0x7fffffff - 256;
+
 bool overlaps(const void *p, size_t pbytes, const void *q, size_t qbytes)
 {
     const uintptr_t a = reinterpret_cast<uintptr_t>(p);
@@ -215,6 +218,9 @@ sg_status validate(int M, int N, int K, const void *A, const void *B, const void
     if (!D) return SG_ERR_NULL;
     if (K > 0 && (!A || !B)) return SG_ERR_NULL;
     if (K > (1 << 21) || N > (1 << 21)) return SG_ERR_SHAPE;
+    // tile counts and tile origins are computed in int: (M + 255) / 256
+    // must not overflow
+    if (M > kMaxM) return SG_ERR_SHAPE;
     const long long lim = 1LL << 40;
     if ((long long)M * K >= lim || (long long)M * N >= lim) return SG_ERR_SHAPE;
     if ((K & 7) || (N & 7)) return SG_ERR_ALIGN;

@@ -54,6 +54,10 @@ def _must_be_rejected(status):
     ((8, 8, (1 << 21) + 8, P, P + 0x10000000, P + 0x20000000), S.SG_ERR_SHAPE),
     ((8, (1 << 21) + 8, 8, P, P + 0x10000000, P + 0x20000000), S.SG_ERR_SHAPE),
     ((1 << 30, 8, 1 << 11, P, P + (1 << 44), P + (1 << 45)), S.SG_ERR_SHAPE),  # M*K >= 2^40
+    # M just past the limit where (M + 255) / 256 still fits an int; M*K and
+    # M*N are far below 2^40 here, so only the M bound rejects it
+    ((0x7fffffff - 255, 8, 8, P, P + (1 << 40), P + (1 << 41)), S.SG_ERR_SHAPE),
+    ((0x7fffffff, 8, 8, P, P + (1 << 40), P + (1 << 41)), S.SG_ERR_SHAPE),
 ])
 def test_argument_errors(args, status):
     _must_be_rejected(status)
