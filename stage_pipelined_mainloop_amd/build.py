@@ -12,7 +12,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libstagegemm.so")
 PROBE_LIB = os.path.join(PKG, "libsgprobe.so")
-RESOURCES = os.path.join(PKG, "kernel_resources.txt")
+# compiler remarks (registers, LDS, occupancy per kernel): a build log, kept
+# out of the source tree's history under the ignored build/ directory
+RESOURCES = os.path.join(ROOT, "build", "kernel_resources.txt")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -38,10 +40,52 @@ def probe_sources() -> list[str]:
     return [os.path.join(CSRC, "mfma_ceiling.hip")]
 
 
+def check_m0_confined() -> int:
+    """The attention kernels issue their LDS-DMA through inline assembly that
+    writes m0 (the LDS address register of the instruction) and lists it as
+    clobbered.  The compiler does not preserve a reserved register across
+    such a statement, so the DMA is safe only while no compiler-generated code
+    in that translation unit uses m0.  Compile it to assembly and check that
+    every m0 operand lies inside an inline-assembly region; raise otherwise
+    (for instance after a compiler update).  Returns the number of m0
+    operands found, all inside the DMA statements."""
+    out_dir = os.path.join(ROOT, "build")
+    os.makedirs(out_dir, exist_ok=True)
+    asm = os.path.join(out_dir, "attention.s")
+    cmd = [HIPCC, *[f for f in FLAGS if f not in ("-shared", "-fPIC")], "--cuda-device-only",
+           "-S", "-I", INCLUDE, "-I", CSRC, os.path.join(CSRC, "attention.hip"), "-o", asm]
+    p = subprocess.run(cmd, capture_output=True, text=True)
+    if p.returncode != 0:
+        sys.stderr.write(p.stdout + p.stderr)
+        raise RuntimeError("hipcc failed compiling attention.hip to assembly")
+    inside, found, stray = False, 0, []
+    with open(asm) as f:
+        for n, line in enumerate(f, 1):
+            if ";;#ASMSTART" in line:
+                inside = True
+                continue
+            if ";;#ASMEND" in line:
+                inside = False
+                continue
+            code = line.split(";", 1)[0]
+            if re.search(r"\bm0\b", code):
+                if inside:
+                    found += 1
+                else:
+                    stray.append(f"{n}: {line.strip()}")
+    if stray:
+        raise RuntimeError("compiler-generated code uses m0 in attention.hip, which the inline "
+                           "LDS-DMA clobbers:\n" + "\n".join(stray[:20]))
+    if found == 0:
+        raise RuntimeError("no m0 operand found in the attention DMA statements: the check "
+                           "no longer sees them")
+    return found
+
+
 def build(verbose: bool = False) -> str:
     """Compile every HIP source into libstagegemm.so next to this file and
     record per-kernel register / LDS / occupancy remarks in
-    kernel_resources.txt.  Always recompiles."""
+    build/kernel_resources.txt.  Always recompiles."""
     tmp = LIB + ".tmp"
     cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC,
            "-Rpass-analysis=kernel-resource-usage", *sources(), "-o", tmp]
@@ -51,6 +95,7 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed building libstagegemm.so")
     os.replace(tmp, LIB)
     remarks = [ln for ln in p.stderr.splitlines() if "remark:" in ln]
+    os.makedirs(os.path.dirname(RESOURCES), exist_ok=True)
     with open(RESOURCES, "w") as f:
         f.write("\n".join(_clean(r) for r in remarks) + "\n")
     tmp = PROBE_LIB + ".tmp"
@@ -59,6 +104,7 @@ def build(verbose: bool = False) -> str:
         sys.stderr.write(p2.stdout + p2.stderr)
         raise RuntimeError("hipcc failed building libsgprobe.so")
     os.replace(tmp, PROBE_LIB)
+    check_m0_confined()
     if verbose:
         sys.stdout.write(p.stderr)
     return LIB

@@ -77,8 +77,9 @@ __device__ __forceinline__ u32x4 rsrc_words(const void *base, uint32_t bytes)
 // are waited for with counts that ignore these: at worst it waits longer.)
 // m0 is written and consumed inside the same statement.  The compiler warns
 // that a reserved register in a clobber list may not be preserved; nothing
-// else in these kernels uses m0 (checked in the generated code), so no value
-// of its own lives across the statement.
+// else in this translation unit uses m0, so no value of its own lives across
+// the statement.  Every build checks that in the generated assembly (every m0
+// operand must sit inside an inline-assembly region) and fails otherwise.
 __device__ __forceinline__ void dma16(const u32x4 &rsrc, uint32_t voff, uint32_t lds)
 {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
