@@ -23,14 +23,26 @@ CFLAGS = ["-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off"
           "-Wall", "-Wextra"]
 
 
-def build(force: bool = True) -> str:
-    """Compile oracle.c into liboracle.so next to it and return the path."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
-        cmd = ["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"]
+# Address and undefined-behaviour sanitizers for a checking build of the same
+# source (run by the test suite with the sanitizer runtimes preloaded).
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                  "-fno-omit-frame-pointer", "-g"]
+
+# A test run may point the loader at another build of oracle.c (the
+# sanitized one) through this variable.
+LIBRARY_ENV = "SGO_LIBRARY"
+
+
+def build(force: bool = True, out: str | None = None, sanitize: bool = False) -> str:
+    """Compile oracle.c into liboracle.so next to it (or into `out`) and
+    return the path.  sanitize=True adds SANITIZE_FLAGS."""
+    target = out or _LIB
+    if force or not os.path.exists(target):
+        tmp = target + ".tmp"
+        cmd = ["gcc", *CFLAGS, *(SANITIZE_FLAGS if sanitize else []), _SRC, "-o", tmp, "-lm"]
         subprocess.run(cmd, check=True)
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, target)
+    return target
 
 
 _lib = None
@@ -39,9 +51,10 @@ _lib = None
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
+        path = os.environ.get(LIBRARY_ENV) or _LIB
+        if path == _LIB and not os.path.exists(_LIB):
             build(force=True)
-        L = ctypes.CDLL(_LIB)
+        L = ctypes.CDLL(path)
         u16p = np.ctypeslib.ndpointer(np.uint16, flags="C_CONTIGUOUS")
         f64p = np.ctypeslib.ndpointer(np.float64, flags="C_CONTIGUOUS")
         i32p = np.ctypeslib.ndpointer(np.int32, flags="C_CONTIGUOUS")
