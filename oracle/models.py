@@ -185,49 +185,56 @@ def simulate(ops: list[Op], ntile: int, stages: int, nfrag: int,
 
 
 def schedule_cute_multistage(ntile: int, stages: int, nfrag: int) -> list[Op]:
-    """The ring schedule of the multistage kernel walked through in
-    "cute(9) multistage_gemm" sections 5 and 6: prologue of S-1 batches, one
-    fence per batch; then per K tile and per K fragment: at the last fragment
-    wait until at most S-2 batches are in flight, barrier, advance the read
-    slot; prefetch the next fragment; at the first fragment issue the next
-    global tile (if any remain) and fence unconditionally; compute.  The
-    prologue only issues tiles that exist (the page assumes ntile >= S-1).
-    The page has two K fragments per tile; with one the prefetch would
-    overwrite the fragment about to be used, so nfrag >= 2 is required."""
+    """Ring schedule of the multistage kernel of "cute(9) multistage_gemm",
+    sections 5, 6 and 8, rebuilt from the rules those sections state:
+
+      * tile j always lives in slot j mod S;
+      * each global load forms one commit group, closed by a fence; a group
+        is committed even when no tile is left to load, so wait counts stay
+        in step (section 8);
+      * the prologue commits the groups of tiles 0 .. S-2 (section 5: S-1,
+        not S, so the first refill has a free slot);
+      * a tile becomes readable after a wait that leaves at most S-2 groups
+        pending and a block-wide barrier; the same barrier ends every read of
+        the slot that the next refill overwrites;
+      * fragments are double-buffered in registers: while fragment f of tile
+        t is multiplied, fragment f+1 is fetched -- at the last fragment that
+        is fragment 0 of tile t+1, so the wait and barrier for tile t+1 come
+        first (section 9: the read slot advances there);
+      * the refill of tile t+S-1 is issued at the first fragment of tile t.
+
+    The prologue only loads tiles that exist (the page assumes ntile >= S-1).
+    With one fragment per tile the fetch would overwrite the fragment about to
+    be used, so nfrag >= 2 is required (the page has two)."""
     if nfrag < 2:
         raise ValueError("the walked-through schedule needs at least two fragments per tile")
     ops: list[Op] = []
-    itile_to_read = 0
-    ismem_read = 0
-    ismem_write = 0
-    for _ in range(stages - 1):
-        if itile_to_read < ntile:
-            ops.append(Op("issue", tile=itile_to_read, slot=ismem_write))
+
+    def commit(tile: int) -> None:
+        if tile < ntile:
+            ops.append(Op("issue", tile=tile, slot=tile % stages))
         ops.append(Op("fence"))
-        itile_to_read += 1
-        ismem_write += 1
-    itile_to_read = min(itile_to_read, ntile)
-    ismem_write %= stages
-    ops.append(Op("wait", n=stages - 2))
-    ops.append(Op("sync"))
+
+    def publish() -> None:
+        ops.append(Op("wait", n=stages - 2))
+        ops.append(Op("sync"))
+
+    for tile in range(stages - 1):
+        commit(tile)
+    publish()
     # Fragment registers are named by the fragment index; which tile's data a
     # fragment holds is what the compute check verifies.
-    ops.append(Op("read", slot=ismem_read, frag=0))
-    for itile in range(ntile):
-        for ik in range(nfrag):
-            ik_next = (ik + 1) % nfrag
-            if ik == nfrag - 1:
-                ops.append(Op("wait", n=stages - 2))
-                ops.append(Op("sync"))
-                ismem_read = (ismem_read + 1) % stages
-            ops.append(Op("read", slot=ismem_read, frag=ik_next))
-            if ik == 0:
-                if itile_to_read < ntile:
-                    ops.append(Op("issue", tile=itile_to_read, slot=ismem_write))
-                    itile_to_read += 1
-                    ismem_write = (ismem_write + 1) % stages
-                ops.append(Op("fence"))
-            ops.append(Op("compute", tile=itile, frag=ik))
+    ops.append(Op("read", slot=0, frag=0))
+    for t in range(ntile):
+        for f in range(nfrag):
+            last = f == nfrag - 1
+            if last:
+                publish()
+            source = t + 1 if last else t      # at the very end: a read nobody uses
+            ops.append(Op("read", slot=source % stages, frag=(f + 1) % nfrag))
+            if f == 0:
+                commit(t + stages - 1)
+            ops.append(Op("compute", tile=t, frag=f))
     return ops
 
 
