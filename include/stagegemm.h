@@ -135,6 +135,46 @@ sg_status gemm_fp16_tn_alpha_beta(int M, int N, int K, float alpha, float beta,
                                   const void *A, const void *B, const void *C, void *D,
                                   void *stream);
 
+/* Split-K form of gemm_fp16_tn_alpha, for grids that leave compute units
+ * idle: fewer 256 x 256 output tiles than one round of resident workgroups
+ * (one per compute unit), or a last round that is only partly full
+ * ("cute(9) multistage_gemm", section 11.3, names split-K as the remedy for
+ * too few output tiles).  Output tiles that fill whole rounds are computed
+ * as by the tiled schedule 8; each remaining tile is cut along K into
+ * `splits` contiguous runs of 64-deep K tiles (fewer if K has fewer tiles,
+ * at most 16), each run computed by its own workgroup through the same
+ * stage-pipelined mainloop, which writes the run's fp32 partial tile to the
+ * workspace.  A second kernel then adds the runs of every cut tile in run
+ * order (so the result does not depend on which run finished first),
+ * multiplies by alpha and rounds once to fp16.
+ *
+ * Workspace: caller-owned device memory, 16-byte aligned (SG_ERR_ALIGN), of
+ * at least gemm_fp16_tn_splitk_workspace_bytes(M, N, K, splits) bytes
+ * (SG_ERR_SHAPE if smaller, SG_ERR_NULL if NULL when needed), not
+ * overlapping A, B or D (SG_ERR_ALIAS).  Its contents on entry do not
+ * matter and are scratch afterwards; calls that share a workspace must not
+ * overlap in time.  splits == 1, or a shape with nothing to split, needs no
+ * workspace and runs gemm_fp16_tn_alpha.  splits < 1: SG_ERR_SHAPE.  The
+ * split plan depends on the current device's resident workgroup count, which
+ * is read from the runtime (a query that changes nothing on the device):
+ * errors that depend on the plan (workspace NULL, too small or overlapping)
+ * are found after that query, all others before any HIP call.  Other rules
+ * as gemm_fp16_tn.  Enqueues two kernels on `stream` (one when nothing is
+ * split). */
+sg_status gemm_fp16_tn_splitk(int M, int N, int K, float alpha, const void *A, const void *B,
+                              void *D, int splits, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/* Workspace bytes gemm_fp16_tn_splitk needs on the current device: one fp32
+ * 256 x 256 partial tile per run of each cut tile.  0 when nothing is split,
+ * for invalid sizes, or when the device cannot be queried. */
+size_t gemm_fp16_tn_splitk_workspace_bytes(int M, int N, int K, int splits);
+
+/* The split count the library would use for this shape on the current
+ * device (1: the plain call is the better choice).  -1 for invalid sizes or
+ * a failed device query. */
+int gemm_fp16_tn_splitk_splits(int M, int N, int K);
+
 /* As gemm_fp16_tn_alpha, but runs the named compiled variant instead of the
  * one the library would choose (used by the stage-count sweep).
  * SG_ERR_UNSUPPORTED if no such variant is compiled; SG_ERR_NULL if cfg is

@@ -14,20 +14,49 @@ from __future__ import annotations
 from ._lib import (SgConfig, SgConfigInfo, SgError, attention_fp16_fwd, attention_fp16_fwd_split,
                    attention_fp16_splits, attention_fp16_workspace_bytes, configs, gemm_fp16_tn,
                    gemm_fp16_tn_alpha,
-                   gemm_fp16_tn_alpha_beta, gemm_fp16_tn_cfg, sg_get_config, sg_minimum_stages, sg_num_configs,
+                   gemm_fp16_tn_alpha_beta, gemm_fp16_tn_cfg, gemm_fp16_tn_splitk,
+                   gemm_fp16_tn_splitk_splits, gemm_fp16_tn_splitk_workspace_bytes, sg_get_config,
+                   sg_minimum_stages, sg_num_configs,
                    sg_persistent_wait_count, sg_pipeline_wait_count, sg_query_config, sg_select_config,
                    sg_status_string)
 
+# Split-K workspaces kept per (device, stream) and reused: calls on one
+# stream never overlap, calls on different streams get different buffers.
+_split_workspaces: dict = {}
+
+
+def split_workspace(device, stream, nbytes: int):
+    """A device buffer of at least `nbytes` for split-K calls on `stream` (a
+    torch.cuda.Stream), reused across calls.  Under HIP-graph capture a fresh
+    buffer is allocated from the graph's pool each time."""
+    import torch
+    if torch.cuda.is_current_stream_capturing():
+        with torch.cuda.stream(stream):
+            return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    key = (torch.device(device).index, stream.cuda_stream)
+    buf = _split_workspaces.get(key)
+    if buf is None or buf.numel() < nbytes:
+        with torch.cuda.stream(stream):
+            buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _split_workspaces[key] = buf
+    return buf
+
 
 def gemm(A, B, out=None, alpha: float | None = None, config=None, stream=None,
-         beta: float | None = None, C=None):
+         beta: float | None = None, C=None, splits: int | None = None, workspace=None):
     """D = alpha * A @ B.T (+ beta * C) on the GPU for fp16 CUDA (HIP) tensors.
 
     A: (M, K), B: (N, K), out: (M, N) or None (allocated).  `config` picks a
     compiled variant (SgConfig or a 6-tuple) instead of the library's choice.
     With a non-zero `beta`, C is an (M, N) fp16 tensor (it may be `out`
     itself for an in-place update).  `stream` is a torch.cuda.Stream
-    (default: the current stream)."""
+    (default: the current stream).
+
+    Without config or C, the call may split output tiles along K
+    (gemm_fp16_tn_splitk): `splits` sets the count (default: the library's
+    choice for the shape; 1 = never).  Its `workspace` (a device tensor of at
+    least gemm_fp16_tn_splitk_workspace_bytes bytes) is allocated once per
+    stream when not given."""
     import torch
 
     if A.dtype != torch.float16 or B.dtype != torch.float16:
@@ -57,10 +86,29 @@ def gemm(A, B, out=None, alpha: float | None = None, config=None, stream=None,
                                 a, b, C.data_ptr(), d, s)
     elif config is not None:
         gemm_fp16_tn_cfg(M, N, K, 1.0 if alpha is None else float(alpha), a, b, d, config, s)
-    elif alpha is None:
-        gemm_fp16_tn(M, N, K, a, b, d, s)
     else:
-        gemm_fp16_tn_alpha(M, N, K, float(alpha), a, b, d, s)
+        st = stream if stream is not None else torch.cuda.current_stream(A.device)
+        need = 0
+        if M > 0 and N > 0 and K > 0 and (splits is None or splits > 1):
+            with torch.cuda.device(A.device):          # the library queries the current device
+                if splits is None:
+                    splits = max(gemm_fp16_tn_splitk_splits(M, N, K), 1)
+                if splits > 1:
+                    need = gemm_fp16_tn_splitk_workspace_bytes(M, N, K, splits)
+        if need > 0:
+            if workspace is None:
+                workspace = split_workspace(A.device, st, need)
+            elif (not workspace.is_cuda or workspace.device != A.device
+                  or workspace.numel() * workspace.element_size() < need):
+                raise ValueError(f"workspace must be a tensor of at least {need} bytes on A's device")
+            with torch.cuda.device(A.device):
+                gemm_fp16_tn_splitk(M, N, K, 1.0 if alpha is None else float(alpha), a, b, d, splits,
+                                    workspace.data_ptr(),
+                                    workspace.numel() * workspace.element_size(), s)
+        elif alpha is None:
+            gemm_fp16_tn(M, N, K, a, b, d, s)
+        else:
+            gemm_fp16_tn_alpha(M, N, K, float(alpha), a, b, d, s)
     return out
 
 
@@ -128,6 +176,8 @@ def attention(Q, K, V, alpha: float | None = None, out=None, stream=None, splits
 __all__ = [
     "gemm", "attention", "attention_fp16_fwd", "attention_fp16_fwd_split", "attention_fp16_splits",
     "attention_fp16_workspace_bytes", "gemm_fp16_tn", "gemm_fp16_tn_alpha", "gemm_fp16_tn_alpha_beta", "gemm_fp16_tn_cfg",
+    "gemm_fp16_tn_splitk", "gemm_fp16_tn_splitk_splits", "gemm_fp16_tn_splitk_workspace_bytes",
+    "split_workspace",
     "sg_select_config",
     "sg_num_configs", "sg_get_config", "sg_query_config", "sg_minimum_stages",
     "sg_pipeline_wait_count", "sg_persistent_wait_count", "sg_status_string", "configs", "SgConfig", "SgConfigInfo",

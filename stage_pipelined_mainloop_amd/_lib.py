@@ -85,6 +85,12 @@ def lib() -> ctypes.CDLL:
         L.attention_fp16_workspace_bytes.restype = ctypes.c_size_t
         L.attention_fp16_splits.argtypes = [i, i, i, i]
         L.attention_fp16_splits.restype = i
+        L.gemm_fp16_tn_splitk.argtypes = [i, i, i, f, vp, vp, vp, i, vp, ctypes.c_size_t, vp]
+        L.gemm_fp16_tn_splitk.restype = i
+        L.gemm_fp16_tn_splitk_workspace_bytes.argtypes = [i, i, i, i]
+        L.gemm_fp16_tn_splitk_workspace_bytes.restype = ctypes.c_size_t
+        L.gemm_fp16_tn_splitk_splits.argtypes = [i, i, i]
+        L.gemm_fp16_tn_splitk_splits.restype = i
         L.gemm_fp16_tn_cfg.argtypes = [i, i, i, f, vp, vp, vp, ctypes.POINTER(SgConfig), vp]
         L.gemm_fp16_tn_cfg.restype = i
         L.sg_select_config.argtypes = [i, i, i, ctypes.POINTER(SgConfig)]
@@ -166,6 +172,20 @@ def gemm_fp16_tn_cfg(M: int, N: int, K: int, alpha: float, A: int, B: int, D: in
     c = cfg if isinstance(cfg, SgConfig) else SgConfig(*cfg)
     return _check(lib().gemm_fp16_tn_cfg(M, N, K, alpha, A, B, D, ctypes.byref(c), stream),
                   "gemm_fp16_tn_cfg")
+
+
+def gemm_fp16_tn_splitk(M: int, N: int, K: int, alpha: float, A: int, B: int, D: int, splits: int,
+                        workspace: int, workspace_bytes: int, stream: int = 0) -> int:
+    return _check(lib().gemm_fp16_tn_splitk(M, N, K, alpha, A, B, D, splits, workspace,
+                                            workspace_bytes, stream), "gemm_fp16_tn_splitk")
+
+
+def gemm_fp16_tn_splitk_workspace_bytes(M: int, N: int, K: int, splits: int) -> int:
+    return int(lib().gemm_fp16_tn_splitk_workspace_bytes(M, N, K, splits))
+
+
+def gemm_fp16_tn_splitk_splits(M: int, N: int, K: int) -> int:
+    return int(lib().gemm_fp16_tn_splitk_splits(M, N, K))
 
 
 def sg_select_config(M: int, N: int, K: int) -> SgConfig:

@@ -262,11 +262,13 @@ __device__ __forceinline__ void wait_tile(int j)
 // Grid position -> output tile.  Workgroups are dealt round-robin to the 8
 // XCDs; renumber so each XCD receives a contiguous run of tiles, then walk
 // the run in groups of GM tile-rows so concurrently resident workgroups of
-// one XCD share A and B panels in that XCD's L2.
-__device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, int &tm, int &tn)
+// one XCD share A and B panels in that XCD's L2.  The renumbering applies to
+// grid positions below `renumber` (the whole grid for the tiled kernels; the
+// data-parallel part of a split-K grid) when that count is a multiple of 8.
+__device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, int renumber,
+                                            int &tm, int &tn)
 {
-    const int total = tiles_m * tiles_n;
-    if ((total & 7) == 0) pid = (pid & 7) * (total >> 3) + (pid >> 3);
+    if ((renumber & 7) == 0 && pid < renumber) pid = (pid & 7) * (renumber >> 3) + (pid >> 3);
     constexpr int GM = 4;
     const int per_group = GM * tiles_n;
     const int group = pid / per_group;
@@ -338,13 +340,32 @@ __device__ __forceinline__ void store_block_staged(const f32x16 (&blk)[C::FN], f
     compiler_fence();
 }
 
-template <class C>
-__global__ void __launch_bounds__(C::T)
-gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
-               const _Float16 *Cm, _Float16 *D, int M, int N, int K, float alpha, float beta,
-               int kt_rot)
+// Work of a split-K launch (schedule 8 only).  Grid positions below
+// dp_tiles compute whole output tiles, as the tiled kernel does.  The
+// remaining L = tiles - dp_tiles output tiles are each cut into `splits`
+// contiguous runs of K tiles; run p of cut tile t is grid position
+// dp_tiles + q, where the pieces are numbered q' = p * L + t (K run first)
+// and q' is dealt to the 8 XCDs in contiguous blocks, so an XCD's pieces
+// share one K run and neighbouring output tiles.  Each piece writes its fp32
+// partial tile, row-major, to part[(t * splits + p) * BM * BN ...] and ends;
+// split_reduce_kernel, launched after it on the same stream, adds the runs
+// of every cut tile in run order and writes D.
+struct SplitWork {
+    float *part;          // L * splits partial tiles of BM * BN fp32
+    int dp_tiles;
+    int splits;
+};
+
+// The mainloop and epilogue of one workgroup (or, for a split piece, the
+// mainloop and the write of its partial tile).
+template <class C, bool SPLIT>
+__device__ __forceinline__ void gemm_tn_body(const _Float16 *__restrict__ A,
+                                             const _Float16 *__restrict__ B, const _Float16 *Cm,
+                                             _Float16 *D, int M, int N, int K, float alpha,
+                                             float beta, int kt_rot, const SplitWork &sw)
 {
     static_assert(C::SCHED <= 2 || C::SCHED >= 5, "schedules 3 and 4 have kernels of their own");
+    static_assert(!SPLIT || C::ORDER == 8, "split-K runs the split-load ping-pong");
     // Cm and D may be the same buffer (in-place D = alpha A B^T + beta D): each
     // wave reads C only inside its own sub-tile and finishes those reads
     // before it stores, so they are not declared __restrict__.
@@ -357,8 +378,32 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
 
     const int tiles_m = (M + C::BM - 1) / C::BM;
     const int tiles_n = (N + C::BN - 1) / C::BN;
+    const int ntile = (K + C::BK - 1) / C::BK;
+    // This workgroup's output tile (linear id in the grouped walk) and its
+    // run of K tiles [kfirst, kfirst + nk).
+    int tile_id = blockIdx.x;
+    int renumber = tiles_m * tiles_n;
+    int kfirst = 0, nk = ntile;
+    bool partial = false;
+    int krun = 0, ltile = 0;
+    if constexpr (SPLIT) {
+        renumber = sw.dp_tiles;
+        if ((int)blockIdx.x >= sw.dp_tiles) {
+            const int L = tiles_m * tiles_n - sw.dp_tiles;
+            const int G = L * sw.splits;
+            int q = blockIdx.x - sw.dp_tiles;
+            if ((G & 7) == 0) q = (q & 7) * (G >> 3) + (q >> 3);
+            krun = q / L;
+            ltile = q - krun * L;
+            tile_id = sw.dp_tiles + ltile;
+            renumber = 0;
+            kfirst = (int)((long long)krun * ntile / sw.splits);
+            nk = (int)((long long)(krun + 1) * ntile / sw.splits) - kfirst;
+            partial = true;
+        }
+    }
     int tm, tn;
-    tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    tile_coords(tile_id, tiles_m, tiles_n, renumber, tm, tn);
     const int m0 = tm * C::BM;
     const int n0 = tn * C::BN;
     const int rows_a = (M - m0 < C::BM) ? (M - m0) : C::BM;
@@ -367,15 +412,15 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + (size_t)m0 * K, (uint32_t)rows_a * K * 2u);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + (size_t)n0 * K, (uint32_t)rows_b * K * 2u);
 
-    const int ntile = (K + C::BK - 1) / C::BK;
     // K-loop rotation.  With a power-of-two row stride every row of a K tile
     // sits at the same offset modulo the memory-channel interleave, so tiles
     // fetched in lockstep by all workgroups of an XCD queue on one channel.
     // Workgroup row tm starts its K loop at tile (tm mod kt_rot): workgroups
     // sharing an A panel stay in lockstep, the others spread over kt_rot
     // channels.  The sum is the same set of products in a different order.
-    int kt0 = 0;
-    if (kt_rot > 1 && ntile > 0) kt0 = (tm % kt_rot) % ntile;
+    // A split piece runs its K tiles in order from kfirst.
+    int kt0 = kfirst;
+    if (!partial && kt_rot > 1 && ntile > 0) kt0 = (tm % kt_rot) % ntile;
 
     // ---- per-lane LDS-DMA source offsets.  Wave load i of an operand fills
     // LDS chunks q = (i*NW + wave)*64 + lane: row r = q / CPR, position
@@ -634,7 +679,8 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
         const uint32_t p_base = (uint32_t)(pr0 * K + pc * 8) * 2u;
         const uint32_t p_step = (uint32_t)(NG * 8) * (uint32_t)K * 2u;
         char *const b_ring = smem + 2 * C::A_BYTES;
-        // One operand tile t of `rs` into `dst` by this group's waves.
+        // Operand tile t (the t-th of this workgroup's nk K tiles) of `rs`
+        // into `dst` by this group's waves.
         auto issue_op = [&](const __amdgpu_buffer_rsrc_t &rs, int t, char *dst) {
             int kt = t + kt0;
             if (kt >= ntile) kt -= ntile;
@@ -655,12 +701,12 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
             __builtin_amdgcn_sched_barrier(0);
             compiler_fence();
         };
-        if (ntile > 0) {
+        if (nk > 0) {
             if (grp == 0) {
                 issue_op(ra, 0, smem);
             } else {
                 issue_op(rb, 0, b_ring);
-                if (ntile > 1) issue_op(rb, 1, b_ring + C::B_BYTES);
+                if (nk > 1) issue_op(rb, 1, b_ring + C::B_BYTES);
             }
         }
         f16x8 fra[C::NKS][C::AM], frb[C::NKS][C::AN];
@@ -670,7 +716,7 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
         if (grp == 1) barrier();                   // G1 idles in phase 0
         int bslot = 0;                             // B slot of tile j
 #pragma unroll 1
-        for (int j = 0; j < ntile; ++j) {
+        for (int j = 0; j < nk; ++j) {
             // read phase of tile j
             const char *abase = smem + (j & 1) * C::A_BYTES;
             const char *bbase = b_ring - C::A_BYTES + bslot * C::B_BYTES;   // fb holds + A_BYTES
@@ -680,11 +726,11 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
             __builtin_amdgcn_sched_barrier(0);
             const int b2 = bslot == 0 ? 2 : bslot - 1;   // (j + 2) % 3
             if (grp == 0) {
-                if (j + 1 < ntile) issue_op(ra, j + 1, smem + ((j + 1) & 1) * C::A_BYTES);
+                if (j + 1 < nk) issue_op(ra, j + 1, smem + ((j + 1) & 1) * C::A_BYTES);
                 compiler_fence();
                 __builtin_amdgcn_sched_barrier(0);
                 __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
-            } else if (j + 2 < ntile) {
+            } else if (j + 2 < nk) {
                 issue_op(rb, j + 2, b_ring + b2 * C::B_BYTES);
                 compiler_fence();
                 __builtin_amdgcn_sched_barrier(0);
@@ -777,6 +823,30 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
 #pragma unroll 1
             for (; k < ntile - 1; ++k) tile(k, std::integral_constant<int, 1>{});
             tile(ntile - 1, std::integral_constant<int, 0>{});
+        }
+    }
+
+    // ---- split-K piece: its fp32 partial tile, row-major, with the
+    // streaming cache policy (read once, by the reduction kernel), and done.
+    // Block (i, j) of a wave holds rows 16 i + (lane % 16) and columns
+    // 16 j + 4 (lane / 16) .. + 3 of the wave's sub-tile (operands swapped,
+    // as in the epilogue): 64-byte row pieces of 16 rows per instruction.
+    if constexpr (SPLIT) {
+        if (partial) {
+            typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+            const __amdgpu_buffer_rsrc_t rw = make_rsrc(
+                sw.part + (size_t)(ltile * sw.splits + krun) * (C::BM * C::BN),
+                (uint32_t)(C::BM * C::BN * 4));
+            const int r0 = wm * C::WTM + (lane & 15);
+            const int c0 = wn * C::WTN + 4 * (lane >> 4);
+#pragma unroll
+            for (int i = 0; i < C::AM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::AN; ++j)
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        __builtin_bit_cast(u32x4, acc[i][j]), rw,
+                        (uint32_t)(((r0 + 16 * i) * C::BN + c0 + 16 * j) * 4), 0, kStoreStreaming);
+            return;
         }
     }
 
@@ -901,6 +971,69 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
         }
         compiler_fence();
     }
+}
+
+template <class C>
+__global__ void __launch_bounds__(C::T)
+gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
+               const _Float16 *Cm, _Float16 *D, int M, int N, int K, float alpha, float beta,
+               int kt_rot)
+{
+    gemm_tn_body<C, false>(A, B, Cm, D, M, N, K, alpha, beta, kt_rot,
+                           SplitWork{nullptr, 0, 1});
+}
+
+// Split-K form of schedule 8 (see SplitWork): D = alpha * A * B^T, no C.
+template <class C>
+__global__ void __launch_bounds__(C::T)
+gemm_tn_split_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
+                     _Float16 *D, int M, int N, int K, float alpha, int kt_rot, float *part,
+                     int dp_tiles, int splits)
+{
+    gemm_tn_body<C, true>(A, B, nullptr, D, M, N, K, alpha, 0.0f, kt_rot,
+                          SplitWork{part, dp_tiles, splits});
+}
+
+// Second kernel of a split-K call: for every cut tile, the sum of its runs'
+// partials in run order 0 .. splits-1 (so the result does not depend on
+// which run finished first), scaled by alpha and rounded once to fp16, into
+// D.  Each thread handles 8 consecutive columns of one row (two 16-byte
+// loads per run, one 16-byte store); BM * BN / 2048 workgroups of 256
+// threads per cut tile.  Rows past M and columns past N are not stored
+// (N % 8 == 0: 8 columns are all in or all out).
+template <int BM, int BN>
+__global__ void __launch_bounds__(256)
+split_reduce_kernel(const float *__restrict__ part, _Float16 *__restrict__ D, int M, int N,
+                    float alpha, int dp_tiles, int splits)
+{
+    constexpr int PER_TILE = BM * BN / (256 * 8);
+    const int lt = blockIdx.x / PER_TILE;
+    const int e = ((blockIdx.x - lt * PER_TILE) * 256 + threadIdx.x) * 8;   // element in the tile
+    const int tiles_m = (M + BM - 1) / BM;
+    const int tiles_n = (N + BN - 1) / BN;
+    int tm, tn;
+    tile_coords(dp_tiles + lt, tiles_m, tiles_n, 0, tm, tn);
+    const int m = tm * BM + e / BN;
+    const int n = tn * BN + e % BN;
+    if (m >= M || n >= N) return;
+    const f32x4v *src = reinterpret_cast<const f32x4v *>(part + (size_t)lt * splits * (BM * BN) + e);
+    f32x4v lo = src[0], hi = src[1];
+#pragma unroll 1
+    for (int p = 1; p < splits; ++p) {
+        const f32x4v *q = src + (size_t)p * (BM * BN / 4);
+        lo += q[0];
+        hi += q[1];
+    }
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 out;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        const float a0 = scale_acc(alpha, h < 2 ? lo[2 * h] : hi[2 * h - 4]);
+        const float a1 = scale_acc(alpha, h < 2 ? lo[2 * h + 1] : hi[2 * h - 3]);
+        out[h] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a0) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a1) << 16);
+    }
+    __builtin_nontemporal_store(out, reinterpret_cast<u32x4 *>(D + (size_t)m * N + n));
 }
 
 }  // namespace sg

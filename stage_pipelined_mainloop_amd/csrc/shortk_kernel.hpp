@@ -39,7 +39,7 @@ gemm_tn_shortk_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict
     const int tiles_m = (M + C::BM - 1) / C::BM;
     const int tiles_n = (N + C::BN - 1) / C::BN;
     int tm, tn;
-    tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    tile_coords(blockIdx.x, tiles_m, tiles_n, tiles_m * tiles_n, tm, tn);
     const int m0 = tm * C::BM;
     const int n0 = tn * C::BN;
     const int rows_a = (M - m0 < C::BM) ? (M - m0) : C::BM;

@@ -178,11 +178,14 @@ double rounds(long long tiles, long long per_round)
     return (double)full + (rest ? 0.75 + 0.25 * (double)rest / (double)per_round : 0.0);
 }
 
-const Variant *select_variant(int M, int N, int K, bool with_c)
+// The library's choice and its cost in rounds of the 256x256 kernel (0 for
+// the short-K schedule, which the split form never competes with).
+const Variant *select_variant(int M, int N, int K, bool with_c, double *cost = nullptr)
 {
     const long long t256 = (long long)((M + 255) / 256) * ((N + 255) / 256);
     const long long t128 = (long long)((M + 127) / 128) * ((N + 127) / 128);
     sg_config c;
+    double best = 0.0;
     if (K <= 128 && t128 >= 256 && !with_c) {
         c = sg_config{128, 128, 64, 2, 4, 4};
     } else {
@@ -192,16 +195,109 @@ const Variant *select_variant(int M, int N, int K, bool with_c)
         const bool persistent = K <= 1024 && !with_c && t128 > 256;
         const double cp = persistent ? 0.9 * c2 : 1e300;
         c = sg_config{256, 256, 64, 3, 8, 8};
-        double best = c256;
+        best = c256;
         if (c3 < best) { best = c3; c = sg_config{128, 128, 64, 3, 4, 1}; }
         if (c2 < best) { best = c2; c = sg_config{128, 128, 64, 2, 4, 1}; }
         if (cp < best) { best = cp; c = sg_config{128, 128, 64, 2, 4, 3}; }
     }
+    if (cost) *cost = best;
     return find_variant(&c);
 }
 
 // Largest M: tile counts (M + tile_m - 1) / tile_m stay within int.
 constexpr int kMaxM = 0x7fffffff - 256;
+
+// ---- split-K form of schedule 8 (gemm_fp16_tn_splitk).  Output tiles that
+// fill whole rounds of resident workgroups run as in the tiled kernel; the
+// rest -- every tile when there are fewer than one round -- are cut along K
+// into `splits` runs computed by separate workgroups, whose fp32 partials a
+// second kernel adds up (sg::SplitWork, sg::split_reduce_kernel).
+using SplitCfg = sg::Cfg<256, 256, 64, 3, 2, 4, 8>;
+constexpr size_t kSplitTileBytes = (size_t)SplitCfg::BM * SplitCfg::BN * 4;
+constexpr int kMaxSplits = 16;
+
+struct SplitPlan {
+    int tiles = 0;       // output tiles
+    int dp_tiles = 0;    // computed whole
+    int left = 0;        // cut along K
+    int splits = 1;      // runs per cut tile (1: nothing is split)
+    long long grid = 0;
+    size_t bytes = 0;        // workspace: the partial tiles (0 when nothing is split)
+};
+
+// Resident workgroups of the split kernel on the current device (one per
+// CU), cached per device; 0 if the runtime cannot tell.
+int split_capacity()
+{
+    static std::atomic<int> cache[16];
+    return resident_capacity(reinterpret_cast<const void *>(&sg::gemm_tn_split_kernel<SplitCfg>),
+                             SplitCfg::T, cache);
+}
+
+SplitPlan plan_split(int M, int N, int K, int splits, int capacity)
+{
+    SplitPlan p;
+    p.tiles = ((M + SplitCfg::BM - 1) / SplitCfg::BM) * ((N + SplitCfg::BN - 1) / SplitCfg::BN);
+    const int ntile = (K + SplitCfg::BK - 1) / SplitCfg::BK;
+    int s = splits < ntile ? splits : ntile;       // every run holds at least one K tile
+    if (s > kMaxSplits) s = kMaxSplits;
+    const int left = p.tiles >= capacity ? p.tiles % capacity : p.tiles;
+    if (s <= 1 || left == 0 || capacity <= 0) {
+        p.dp_tiles = p.tiles;
+        p.grid = p.tiles;
+        return p;
+    }
+    p.left = left;
+    p.dp_tiles = p.tiles - left;
+    p.splits = s;
+    p.grid = (long long)p.dp_tiles + (long long)left * s;
+    p.bytes = (size_t)left * s * kSplitTileBytes;
+    return p;
+}
+
+// The split count the library uses (1: none), from a time model in
+// microseconds fitted to interleaved timings of both forms on MI355X:
+//   * a round of `capacity` 256x256 workgroups takes 1.55 us per 64-deep K
+//     tile plus 3 us (prologue, epilogue and launch): 4096^3, 64 K tiles,
+//     measures about 99 us;
+//   * the plain call costs select_variant's rounds times that round time;
+//   * the split call costs its whole-tile rounds, then ceil(pieces /
+//     capacity) rounds of ceil(ntile / s) K tiles, then the reduction: about
+//     2 us plus the partial tiles (L * s * 256 KiB) written and read back at
+//     about 4.6 MB per us.
+// Measured against it (us, plain / best split): 2048^2 x 16384 141.6 / 115.8
+// (s = 4), 2048^2 x 8192 73.8 / 71.4, 4352^2 x 4096 164.3 / 134.9,
+// 6144^2 x 4096 259.6 / 243.4, 1024^2 x 8192 55.4 / 34.6; plain stays
+// faster at 2048^2 x 2048 (21.0 / 35.5), 2560^2 x 4096, 3072^2 x 4096,
+// 4096 x 2048 x 4096 and 81920 x 256 x 256, where the model keeps it.
+int choose_splits(int M, int N, int K, int capacity)
+{
+    const SplitPlan whole = plan_split(M, N, K, 1, capacity);
+    const int left = whole.tiles >= capacity ? whole.tiles % capacity : whole.tiles;
+    const int ntile = (K + SplitCfg::BK - 1) / SplitCfg::BK;
+    if (left == 0 || ntile < 2 || capacity <= 0) return 1;
+    const double k_tile_us = 1.55, round_us = 3.0, reduce_us = 2.0, partial_mb_per_us = 4.6;
+    const double full_round = ntile * k_tile_us + round_us;
+    double plain_rounds = 0.0;
+    select_variant(M, N, K, false, &plain_rounds);
+    if (plain_rounds <= 0.0) return 1;                 // short K: never split
+    const double plain = plain_rounds * full_round;
+    const double dp = (double)(whole.tiles / capacity) * full_round;   // whole-tile rounds
+    int best_s = 1;
+    double best = plain;
+    for (int s = 2; s <= kMaxSplits && s <= ntile; ++s) {
+        const long long pieces = (long long)left * s;
+        const double piece_rounds = (double)((pieces + capacity - 1) / capacity);
+        const double run = ((ntile + s - 1) / s) * k_tile_us + round_us;
+        const double mb = (double)pieces * (double)kSplitTileBytes / 1e6;
+        const double t = dp + piece_rounds * run + reduce_us + mb / partial_mb_per_us;
+        if (t < best) {
+            best = t;
+            best_s = s;
+        }
+    }
+    return best_s;
+}
 
 bool overlaps(const void *p, size_t pbytes, const void *q, size_t qbytes)
 {
@@ -267,6 +363,31 @@ sg_status run(const Variant *v, int M, int N, int K, float alpha, float beta, co
     return e == hipSuccess ? SG_OK : SG_ERR_HIP;
 }
 
+sg_status launch_split(const SplitPlan &p, int M, int N, int K, float alpha, const void *A,
+                       const void *B, void *D, void *workspace, void *stream)
+{
+    const _Float16 *a = static_cast<const _Float16 *>(A);
+    const _Float16 *b = static_cast<const _Float16 *>(B);
+    _Float16 *d = static_cast<_Float16 *>(D);
+    float *part = static_cast<float *>(workspace);
+    int dp = p.dp_tiles, splits = p.splits;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    // the whole-tile part keeps the tiled kernel's K rotation when it spans
+    // more than one round
+    int kt_rot = dp > 256 ? 4 : 1;
+    void *args[] = {&a, &b, &d, &M, &N, &K, &alpha, &kt_rot, &part, &dp, &splits};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&sg::gemm_tn_split_kernel<SplitCfg>),
+                                   dim3((unsigned)p.grid), dim3(SplitCfg::T), args, 0, st);
+    if (e != hipSuccess) return SG_ERR_HIP;
+    const float *cpart = part;
+    void *rargs[] = {&cpart, &d, &M, &N, &alpha, &dp, &splits};
+    constexpr int per_tile = SplitCfg::BM * SplitCfg::BN / (256 * 8);
+    e = hipLaunchKernel(
+        reinterpret_cast<const void *>(&sg::split_reduce_kernel<SplitCfg::BM, SplitCfg::BN>),
+        dim3((unsigned)(p.left * per_tile)), dim3(256), rargs, 0, st);
+    return e == hipSuccess ? SG_OK : SG_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -308,6 +429,50 @@ sg_status gemm_fp16_tn_cfg(int M, int N, int K, float alpha, const void *A, cons
     if (!v) return SG_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return SG_OK;
     return run(v, M, N, K, alpha, 0.0f, A, B, nullptr, D, stream);
+}
+
+int gemm_fp16_tn_splitk_splits(int M, int N, int K)
+{
+    if (M <= 0 || N <= 0 || K < 0 || M > kMaxM || K > (1 << 21) || N > (1 << 21)) return -1;
+    if (K == 0) return 1;
+    const int cap = split_capacity();
+    if (cap <= 0) return -1;
+    return choose_splits(M, N, K, cap);
+}
+
+size_t gemm_fp16_tn_splitk_workspace_bytes(int M, int N, int K, int splits)
+{
+    if (M <= 0 || N <= 0 || K <= 0 || splits < 1 || M > kMaxM || K > (1 << 21) || N > (1 << 21))
+        return 0;
+    const int cap = split_capacity();
+    if (cap <= 0) return 0;
+    return plan_split(M, N, K, splits, cap).bytes;
+}
+
+sg_status gemm_fp16_tn_splitk(int M, int N, int K, float alpha, const void *A, const void *B,
+                              void *D, int splits, void *workspace, size_t workspace_bytes,
+                              void *stream)
+{
+    sg_status st = validate(M, N, K, A, B, D);
+    if (st != SG_OK) return st;
+    if (splits < 1) return SG_ERR_SHAPE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 15) return SG_ERR_ALIGN;
+    if (M == 0 || N == 0) return SG_OK;
+    if (splits == 1 || K == 0) return gemm_fp16_tn_alpha(M, N, K, alpha, A, B, D, stream);
+    // the plan depends on the device's resident workgroup count (a runtime
+    // query that changes nothing on the device)
+    const int cap = split_capacity();
+    if (cap <= 0) return SG_ERR_HIP;
+    const SplitPlan p = plan_split(M, N, K, splits, cap);
+    if (p.splits == 1) return gemm_fp16_tn_alpha(M, N, K, alpha, A, B, D, stream);
+    if (p.grid * SplitCfg::T >= (1LL << 32)) return SG_ERR_SHAPE;
+    if (!workspace) return SG_ERR_NULL;
+    if (workspace_bytes < p.bytes) return SG_ERR_SHAPE;
+    if (overlaps(workspace, p.bytes, A, (size_t)M * K * 2) ||
+        overlaps(workspace, p.bytes, B, (size_t)N * K * 2) ||
+        overlaps(workspace, p.bytes, D, (size_t)M * N * 2))
+        return SG_ERR_ALIAS;
+    return launch_split(p, M, N, K, alpha, A, B, D, workspace, stream);
 }
 
 sg_status sg_select_config(int M, int N, int K, sg_config *out)

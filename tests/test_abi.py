@@ -17,7 +17,7 @@ S = _lib
 
 def test_every_declared_symbol_is_exported():
     declared = _lib.header_functions()
-    assert len(declared) == 16
+    assert len(declared) == 19
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
@@ -159,6 +159,28 @@ def test_attention_split_argument_errors():
     # no work at all
     assert F(0, 8, 8, 128, 0.1, P, P, P, P, 4, 0, 0, None) == S.SG_OK
     assert F(2, 0, 8, 128, 0.1, P, P, P, P, 4, 0, 0, None) == S.SG_OK
+
+
+def test_splitk_argument_errors():
+    a, b, d, w = P, P + 0x100000, P + 0x200000, P + 0x1000000
+    F = L.gemm_fp16_tn_splitk
+    # the plain entry point's checks come first
+    assert F(-1, 8, 8, 1.0, a, b, d, 2, w, 1 << 30, None) == S.SG_ERR_SHAPE
+    assert F(8, 8, 12, 1.0, a, b, d, 2, w, 1 << 30, None) == S.SG_ERR_ALIGN
+    assert F(8, 8, 8, 1.0, a, b, a + 0x40, 2, w, 1 << 30, None) == S.SG_ERR_ALIAS
+    assert F(0x7fffffff, 8, 8, 1.0, a, b, d, 2, w, 1 << 30, None) == S.SG_ERR_SHAPE
+    # then its own, before any HIP call
+    assert F(8, 8, 8, 1.0, a, b, d, 0, w, 1 << 30, None) == S.SG_ERR_SHAPE       # splits < 1
+    assert F(8, 8, 8, 1.0, a, b, d, -2, w, 1 << 30, None) == S.SG_ERR_SHAPE
+    assert F(8, 8, 8, 1.0, a, b, d, 2, w + 8, 1 << 30, None) == S.SG_ERR_ALIGN   # 16-byte aligned
+    # nothing to compute: no launch, no workspace needed
+    assert F(0, 8, 8, 1.0, a, b, d, 4, 0, 0, None) == S.SG_OK
+    assert F(8, 0, 8, 1.0, a, b, d, 4, 0, 0, None) == S.SG_OK
+    # invalid sizes are refused before any device query
+    assert L.gemm_fp16_tn_splitk_workspace_bytes(-1, 8, 8, 2) == 0
+    assert L.gemm_fp16_tn_splitk_workspace_bytes(8, 8, 8, 0) == 0
+    assert L.gemm_fp16_tn_splitk_splits(8, -8, 8) == -1
+    assert L.gemm_fp16_tn_splitk_splits(8, 8, (1 << 21) + 8) == -1
 
 
 def test_attention_workspace_bytes():
