@@ -10,11 +10,24 @@ Prints ONE JSON line (rank 0):
                events around the back-to-back timed launches, on the stream
                they are launched on; when the host enqueues launches no
                faster than they run, the steps are captured once as a HIP
-               graph that the timed region replays); traffic = HBM
-               bytes per launch from the committed rocprofv3 counter summary,
-               or null if the kernel source changed since it was taken
+               graph that the timed region replays); traffic = bytes per
+               launch that leave L2 (FETCH_SIZE and WRITE_SIZE, scaled by a
+               plain copy of known size) from the committed rocprofv3
+               summary, or null if the kernel source changed since it was
+               taken.  Requests leaving L2 may still hit the memory-side
+               Infinity Cache, so this bounds the HBM bytes from above
   cpu_baseline the CPU oracle timed on a bounded row sample of the same
                workload, on this host's cores
+  per_config   every other workload of the measurement plan (256^3, 4096^3,
+               the attention-score shape, the ragged shape, the tall-skinny
+               shape and the M = N = 2048 stage sweep), each with its own
+               roofline and CPU baseline; the sweep also per stage count
+
+Other modes: variants, ksweep (every compiled variant), attention (the
+fused forward), calibrate_copy (the copy the traffic counters are scaled
+by), stage_model (T_copy and T_compute of the stage-count formula) and
+trace_summary (a kernel trace of this script averaged over exactly the
+timed dispatches).
 """
 from __future__ import annotations
 
@@ -311,10 +324,315 @@ def mode_calibrate_copy(args) -> int:
     return 0
 
 
+def variant_name(cfg, splits: int = 1) -> str:
+    v = "x".join(str(x) for x in cfg.as_tuple()[:3]) + f" S{cfg.stages} w{cfg.waves} sched{cfg.schedule}"
+    return v + (f" split-K x{splits}" if splits > 1 else "")
+
+
+def library_call(M: int, N: int, K: int, a, b, d, alpha):
+    """The library's choice for this shape as one launch function (split-K
+    with its workspace when the library picks it), its description and the
+    split count."""
+    import torch
+
+    import stage_pipelined_mainloop_amd as sg
+    s = max(sg.gemm_fp16_tn_splitk_splits(M, N, K), 1)
+    need = sg.gemm_fp16_tn_splitk_workspace_bytes(M, N, K, s) if s > 1 else 0
+    stream = torch.cuda.current_stream().cuda_stream
+    al = 1.0 if alpha is None else float(alpha)
+    ptrs = (a.data_ptr(), b.data_ptr(), d.data_ptr())
+    if need > 0:
+        ws = torch.zeros(need, dtype=torch.uint8, device=a.device)
+
+        def fn():
+            sg.gemm_fp16_tn_splitk(M, N, K, al, *ptrs, s, ws.data_ptr(), need, stream)
+        fn.workspace = ws
+        # the split-K form runs the split-load ping-pong (schedule 8)
+        return fn, variant_name(sg.SgConfig(256, 256, 64, 3, 8, 8), s), s
+
+    def fn():
+        sg.gemm_fp16_tn_alpha(M, N, K, al, *ptrs, stream)
+    return fn, variant_name(sg.sg_select_config(M, N, K)), 1
+
+
+def timed_mean_ms(fn, target_ms: float = 40.0, min_launches: int = 20):
+    """Mean launch time of `fn` back to back: about target_ms of warm-up, then
+    about target_ms timed between one pair of HIP events.  Launch-bound calls
+    (the host enqueues no faster than they run) are replayed from a captured
+    HIP graph, as in the headline measurement.  Returns (ms, launch kind)."""
+    import torch
+    for _ in range(10):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(20):
+        fn()
+    enq = (time.perf_counter() - t0) / 20
+    torch.cuda.synchronize()
+    per = (time.perf_counter() - t0) / 20
+    n = max(min_launches, min(5000, int(target_ms / 1e3 / max(per, 1e-6))))
+    if enq > 0.9 * per:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n):
+                fn()
+        g.replay()
+        g.replay()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n, "graph"
+    return time_launches(fn, n, n), "eager"
+
+
+def roofline_of(M: int, N: int, K: int, ms: float, workload: str | None = None) -> dict:
+    """MFMA roofline above the ridge (about 315 flop/B), HBM below it, with
+    the algorithmic work 2MNK flop or 2(MK + NK + MN) bytes per launch."""
+    flops = 2.0 * M * N * K
+    algo_bytes = 2.0 * (M * K + N * K + M * N)
+    traffic = load_traffic(workload) if workload else None
+    ridge = PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if flops / algo_bytes < ridge:
+        gbs = algo_bytes / (ms / 1e3) / 1e9
+        return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+    tf = flops / (ms / 1e3) / 1e12
+    return {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / PEAK_TFLOPS, 4), "traffic": traffic}
+
+
+def cpu_baseline_full(A, B, min_s: float = 0.5):
+    """The oracle on the whole (small) problem, repeated for at least min_s."""
+    import oracle
+    M, K = A.shape
+    N = B.shape[0]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.gemm_tn_f64(A, B)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_s:
+            break
+    return {"value": 2.0 * M * N * K * reps / dt / 1e12, "unit": "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle", "cpu": cpu_model(),
+            "sample": f"all {M} x {N} outputs (K={K}), {reps} runs, {dt:.2f} s wall"}
+
+
+def per_config(args) -> dict:
+    """Every workload of the measurement plan besides the headline: the
+    library's choice timed on one GPU with its roofline, next to the oracle
+    timed on this host on a bounded sample of the same workload; the stage
+    sweep also per stage count (LDS bytes and workgroups per CU from the
+    library's query)."""
+    import numpy as np
+    import torch
+
+    import stage_pipelined_mainloop_amd as sg
+    from stage_pipelined_mainloop_amd import inputs
+    res = {}
+    cpu_s = args.config_cpu_seconds
+    for name in ("square256", "square4096", "attn_scores", "ragged8000", "tall81920"):
+        M, N, K, dist, seed = inputs.WORKLOADS[name]
+        A, B = inputs.workload(name)
+        alpha = float(np.float32(1.0 / math.sqrt(K))) if name == "attn_scores" else None
+        a, b = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+        d = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        fn, vname, s = library_call(M, N, K, a, b, d, alpha)
+        ms, kind = timed_mean_ms(fn)
+        entry = {"M": M, "N": N, "K": K, "dist": dist, "variant": vname, "launch": kind,
+                 "kernel_us": round(ms * 1e3, 2),
+                 "tflops": round(2.0 * M * N * K / (ms / 1e3) / 1e12, 1),
+                 "roofline": roofline_of(M, N, K, ms, name)}
+        if not args.no_cpu_baseline:
+            entry["cpu_baseline"] = (cpu_baseline_full(A, B) if M * N * K <= 1 << 26
+                                     else cpu_baseline(A, B, cpu_s))
+        res[name] = entry
+        print(f"[bench] {name}: {entry['kernel_us']} us, {entry['variant']}", file=sys.stderr,
+              flush=True)
+        del a, b, d, fn
+    # stage sweep: M = N = 2048, every K; the library's choice and the best
+    # compiled variant at each stage count of the 128x128 (4 waves) and
+    # 256x256 (8 waves) families
+    sweep = {"M": inputs.KSWEEP_MN, "N": inputs.KSWEEP_MN, "K": {}}
+    M = N = inputs.KSWEEP_MN
+    for K in inputs.KSWEEP_K:
+        A, B = inputs.ksweep(K)
+        a, b = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+        d = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        fn, vname, s = library_call(M, N, K, a, b, d, None)
+        ms, kind = timed_mean_ms(fn, target_ms=20.0)
+        per_k = {"library": {"variant": vname, "kernel_us": round(ms * 1e3, 2),
+                             "roofline": roofline_of(M, N, K, ms)}, "by_stages": {}}
+        for c in sg.configs():
+            if (c.tile_m, c.tile_n, c.waves) not in ((128, 128, 4), (256, 256, 8)) or not takes(c, K):
+                continue
+            cms, _ = timed_mean_ms(lambda: sg.gemm(a, b, out=d, config=c), target_ms=5.0,
+                                   min_launches=10)
+            key = str(c.stages)
+            best = per_k["by_stages"].get(key)
+            if best is None or cms * 1e3 < best["kernel_us"]:
+                info = variant_info(c)
+                per_k["by_stages"][key] = {
+                    "variant": variant_name(c), "kernel_us": round(cms * 1e3, 2),
+                    "tflops": round(2.0 * M * N * K / (cms / 1e3) / 1e12, 1),
+                    "frac": roofline_of(M, N, K, cms)["frac"],
+                    "lds_ring_bytes": info["lds_bytes"], "lds_total_bytes": info["lds_total_bytes"],
+                    "wg_per_cu": info["wg_per_cu"]}
+        bs = min(per_k["by_stages"].items(), key=lambda kv: kv[1]["kernel_us"])
+        per_k["best_fixed_stage_count"] = {"stages": int(bs[0]), **bs[1]}
+        if not args.no_cpu_baseline:
+            per_k["cpu_baseline"] = cpu_baseline(A, B, cpu_s / 2)
+        sweep["K"][str(K)] = per_k
+        print(f"[bench] ksweep K={K}: {per_k['library']['kernel_us']} us, {vname}", file=sys.stderr,
+              flush=True)
+        del a, b, d, fn
+    res["ksweep"] = sweep
+    return res
+
+
+def mode_stage_model(args) -> int:
+    """The stage-count model of "Lesson 6", section 4, evaluated for the
+    256 x 256 x 64 tile of the large-shape kernel on this GPU: T_copy (one K
+    tile's LDS-DMA loads, issue to completion, every CU copying at once) and
+    T_compute (one K tile's MFMAs per wave) in shader clock cycles from the
+    probe library, S_min = ceil(T_copy / T_compute) + 1 from the library's
+    sg_minimum_stages, and the LDS footprint and workgroups per CU of every
+    ring depth at this tile next to the ring the kernel uses."""
+    import ctypes
+    import statistics
+
+    import numpy as np
+    import torch
+
+    import stage_pipelined_mainloop_amd as sg
+    from stage_pipelined_mainloop_amd import inputs
+    so = os.path.join(ROOT, "stage_pipelined_mainloop_amd", "libsgprobe.so")
+    P = ctypes.CDLL(so)
+    P.sg_probe_stage_timing.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p,
+                                        ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    P.sg_probe_stage_timing.restype = ctypes.c_int
+    M, N, K, dist, seed = inputs.WORKLOADS[args.workload]
+    A, B = inputs.workload(args.workload)
+    a, b = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tiles_m = M // 256
+    blocks = min(cus, tiles_m * (N // 256))
+    ntile = K // 64
+    out = torch.zeros(blocks * 32, dtype=torch.int64, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def run():
+        rc = P.sg_probe_stage_timing(a.data_ptr(), M, b.data_ptr(), N, K, tiles_m, blocks, ntile,
+                                     out.data_ptr(), stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"stage probe failed to launch ({rc})")
+    for _ in range(3):
+        run()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    r = out.view(blocks, 8, 4).cpu().numpy().astype(np.float64)
+    copy_w = r[:, :, 0] / r[:, :, 2]              # per wave, cycles per K tile
+    comp_w = r[:, :, 1] / r[:, :, 2]
+    copy = copy_w.ravel()
+    comp = comp_w.ravel()
+    # a workgroup's tile is ready when its last wave's loads are, and its
+    # MFMAs are done when its last wave's are
+    copy_wg = copy_w.max(axis=1)
+    comp_wg = comp_w.max(axis=1)
+
+    def stats(x):
+        return {"median": round(float(np.median(x)), 1), "mean": round(float(x.mean()), 1),
+                "p10": round(float(np.percentile(x, 10)), 1), "p90": round(float(np.percentile(x, 90)), 1)}
+    t_copy = statistics.median(copy.tolist())
+    t_comp = statistics.median(comp.tolist())
+    s_min = sg.sg_minimum_stages(int(round(t_copy)), int(round(t_comp)))
+    t_copy_wg = float(np.median(copy_wg))
+    t_comp_wg = float(np.median(comp_wg))
+    s_min_wg = sg.sg_minimum_stages(int(round(t_copy_wg)), int(round(t_comp_wg)))
+    stage_bytes = (256 + 256) * 64 * 2
+    rings = [{"stages": st, "lds_bytes": st * stage_bytes,
+              "wg_per_cu_lds": (160 * 1024) // (st * stage_bytes)} for st in range(2, 6)]
+    _, info = sg.sg_query_config(sg.SgConfig(256, 256, 64, 3, 8, 8))
+    print(json.dumps({
+        "mode": "stage_model", "workload": args.workload, "tile": "256x256x64",
+        "workgroups": blocks, "k_tiles_timed": ntile, "probe_ms": round(e0.elapsed_time(e1), 3),
+        "T_copy_cycles": stats(copy), "T_compute_cycles": stats(comp),
+        "copy_over_compute": round(t_copy / t_comp, 3),
+        "S_min": s_min, "formula": "ceil(T_copy / T_compute) + 1 (medians over waves)",
+        "per_workgroup": {"T_copy_cycles": stats(copy_wg), "T_compute_cycles": stats(comp_wg),
+                          "copy_over_compute": round(t_copy_wg / t_comp_wg, 3), "S_min": s_min_wg,
+                          "statistic": "slowest wave of each workgroup, median over workgroups"},
+        "rings_of_whole_stages": rings,
+        "kernel_ring": {"A_slots": 2, "B_slots": 3, "lds_bytes": info.lds_bytes,
+                        "wg_per_cu": info.wg_per_cu,
+                        "tiles_in_flight_ahead": {"A": 1, "B": 2}}}), flush=True)
+    return 0
+
+
+def mode_trace_summary(args) -> int:
+    """Summarise a rocprofv3 kernel trace (CSV) of a bench.py run, given that
+    run's JSON line: per kernel, dispatches and mean duration over all of
+    them; for the step's kernel, the mean over exactly the timed dispatches
+    (config.trace_window of the JSON line) and the roofline figure it gives,
+    to set beside the run's own event timing.  Host-only, no GPU."""
+    import csv
+    import statistics
+    line = None
+    with open(args.bench_log) as f:
+        for ln in f:
+            ln = ln.strip()
+            if ln.startswith("{") and '"metric"' in ln:
+                line = json.loads(ln)
+    if line is None:
+        print(f"no bench JSON line in {args.bench_log}", file=sys.stderr)
+        return 1
+    cfgd = line["config"]
+    M, N, K = cfgd["M"], cfgd["N"], cfgd["K"]
+    win = cfgd["trace_window"]
+    per = {}
+    with open(args.trace) as f:
+        for row in csv.DictReader(f):
+            dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3   # us
+            per.setdefault(row["Kernel_Name"], []).append((int(row["Start_Timestamp"]), dur))
+    print("| kernel | dispatches | mean us (all) | median us | min us |")
+    print("|---|---|---|---|---|")
+    for name, v in sorted(per.items(), key=lambda kv: -sum(d for _, d in kv[1])):
+        ds = [d for _, d in v]
+        print(f"| `{name[:90]}` | {len(ds)} | {statistics.mean(ds):.2f} | "
+              f"{statistics.median(ds):.2f} | {min(ds):.2f} |")
+    hot = max(per, key=lambda k: sum(d for _, d in per[k]))
+    seq = [d for _, d in sorted(per[hot])]
+    window = seq[win["first"]:win["first"] + win["count"]]
+    if len(window) != win["count"]:
+        print(f"trace holds {len(seq)} dispatches of the step kernel; window {win} incomplete",
+              file=sys.stderr)
+        return 1
+    mean_us = statistics.mean(window)
+    roof = roofline_of(M, N, K, mean_us / 1e3)
+    bench_us = cfgd["kernel_ms_mean"] * 1e3
+    print()
+    print(f"Timed window: dispatches {win['first']}..{win['first'] + win['count'] - 1} of `{hot[:90]}`: "
+          f"mean {mean_us:.2f} us -> {roof['achieved']} {roof['unit']}, frac {roof['frac']} "
+          f"(bench events: {bench_us:.2f} us, frac {line['roofline']['frac']}; "
+          f"trace / events = {mean_us / bench_us:.4f})")
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--mode", default="bench",
-                    choices=["bench", "variants", "ksweep", "calibrate_copy", "attention"])
+                    choices=["bench", "variants", "ksweep", "calibrate_copy", "attention",
+                             "trace_summary", "stage_model"])
+    ap.add_argument("--trace", default=None, help="kernel-trace CSV for --mode trace_summary")
+    ap.add_argument("--bench-log", default=None, help="that run's output for --mode trace_summary")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=None,
@@ -323,6 +641,10 @@ def main() -> int:
     ap.add_argument("--config", default=None,
                     help="explicit variant tile_m,tile_n,tile_k,stages,waves,schedule")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--config-cpu-seconds", type=float, default=2.0,
+                    help="oracle seconds per sampled CPU baseline of the other workloads")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="time only the headline workload (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--heads", type=int, default=16, help="heads for --mode attention")
     ap.add_argument("--cold", action="store_true",
@@ -341,6 +663,10 @@ def main() -> int:
               "compute, so N GPUs each run this one-GPU step on their share",
               file=sys.stderr)
         return 2
+    if args.mode == "trace_summary":
+        return mode_trace_summary(args)
+    if args.mode == "stage_model":
+        return mode_stage_model(args)
     if args.mode == "variants":
         return mode_variants(args)
     if args.mode == "ksweep":
@@ -364,10 +690,13 @@ def main() -> int:
     b = torch.from_numpy(B).to(dev)
     d = torch.empty((M, N), dtype=torch.float16, device=dev)
     cfg = tuple(int(x) for x in args.config.split(",")) if args.config else None
-    chosen = sg.SgConfig(*cfg) if cfg else sg.sg_select_config(M, N, K)
+    if cfg:
+        vname = variant_name(sg.SgConfig(*cfg))
 
-    def step():
-        sg.gemm(a, b, out=d, alpha=alpha, config=cfg)
+        def step():
+            sg.gemm(a, b, out=d, alpha=alpha, config=cfg)
+    else:
+        step, vname, _ = library_call(M, N, K, a, b, d, alpha)
 
     for _ in range(10):
         step()
@@ -433,7 +762,7 @@ def main() -> int:
     achieved = flops / mean_launch_s / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
-                "traffic": load_traffic(args.workload)}
+                "traffic": load_traffic(args.workload), "traffic_kind": "l2_egress_bytes"}
     algo_bytes = 2.0 * (M * K + N * K + M * N)
     ridge = PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)          # ~315 flop/B
     if flops / algo_bytes < ridge:
@@ -441,7 +770,7 @@ def main() -> int:
         gbs = algo_bytes / mean_launch_s / 1e9
         roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                    "traffic": load_traffic(args.workload)}
+                    "traffic": load_traffic(args.workload), "traffic_kind": "l2_egress_bytes"}
 
     out = {
         "metric": METRIC,
@@ -458,13 +787,17 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": args.workload, "M": M, "N": N, "K": K, "dist": dist,
                    "alpha": alpha if alpha is not None else 1.0,
-                   "variant": "x".join(str(v) for v in chosen.as_tuple()[:3])
-                              + f" S{chosen.stages} w{chosen.waves} sched{chosen.schedule}",
+                   "variant": vname,
                    "pct_of_fp16_peak": round(100.0 * value / PEAK_TFLOPS, 2),
                    "launch": "one HIP graph of the timed steps" if graph is not None else "eager",
                    "kernel_ms_mean": round(mean_launch_s * 1e3, 4),
                    "kernel_ms_median_single": round(med_ms, 4),
-                   "kernel_ms_min_single": round(min_ms, 4)},
+                   "kernel_ms_min_single": round(min_ms, 4),
+                   # dispatches of the step's kernel in this process before the
+                   # timed ones (calibration, warm-up, graph check): a kernel
+                   # trace of this run averages dispatches [first, first + steps)
+                   "trace_window": {"first": 60 + args.warmup + (args.steps if graph is not None else 0),
+                                    "count": args.steps}},
         "roofline": roofline,
         "cpu_baseline": None,
     }
@@ -482,6 +815,9 @@ def main() -> int:
         out["config"]["frac_of_mfma_ceiling_16x16x32"] = round(achieved / ceil16, 4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(A, B, args.cpu_seconds)
+    if not args.no_per_config:
+        del a, b, d, step
+        out["per_config"] = per_config(args)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -9,6 +9,19 @@
 // v_mfma_f32_32x32x16_f16 (or 16 independent 16x16 accumulators through
 // v_mfma_f32_16x16x32_f16: the same flops per loop) with a different operand
 // pair per MFMA; no memory traffic inside the timed loop.
+//
+// A second probe times the two quantities of the stage-count model of
+// "Lesson 6: Shared Memory layout and async pipeline", section 4 --
+// S_min = ceil(T_copy / T_compute) + 1 -- for the 256 x 256 x 64 tile of the
+// large-shape GEMM kernel, in shader clock cycles (s_memtime), with one
+// 512-thread workgroup per CU on every CU:
+//   T_copy     from the issue of one K tile's LDS-DMA loads (A and B, 64 KiB
+//              per workgroup, 16 bytes per lane per load as in the GEMM) to
+//              their completion (vmcnt 0), with every CU copying at once and
+//              nothing else in flight;
+//   T_compute  the MFMAs of one K tile: each of the 8 waves issues the 64
+//              v_mfma_f32_16x16x32_f16 of its 128 x 64 sub-tile from
+//              registers, timed from a workgroup barrier to the last issue.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -86,9 +99,122 @@ mfma_ceiling16_kernel(const f16x8 *__restrict__ a, const f16x8 *__restrict__ b, 
     sink[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+// Stage-model probe (see the file comment).  Workgroup w reads the A rows of
+// tile row (w % tiles_m) and the B rows of tile column (w / tiles_m) of an
+// M x K and N x K row-major fp16 pair (M, N >= 256 * those counts, K a
+// multiple of 64, ntile <= K / 64).  out[w * 8 + wave] receives, per wave,
+// {copy cycles summed over the ntile K tiles, compute cycles summed, ntile,
+// a value that keeps the MFMA results live} as four 64-bit words.
+__global__ void __launch_bounds__(512)
+stage_timing_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, int K,
+                    int tiles_m, int ntile, unsigned long long *__restrict__ out)
+{
+    __shared__ __attribute__((aligned(1024))) char lds[65536];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tm = blockIdx.x % tiles_m;
+    const int tn = blockIdx.x / tiles_m;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<_Float16 *>(A + (size_t)tm * 256 * K), (short)0, 256 * K * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<_Float16 *>(B + (size_t)tn * 256 * K), (short)0, 256 * K * 2, 0x00020000);
+    // load j (0..3) of this wave fills LDS chunk q = (j * 8 + wave) * 64 + lane
+    // of an operand: row q / 8, 16-byte column q % 8 of the 128-byte K slice
+    f16x8 fa[4], fb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        fa[i] = *(const f16x8 *)(A + (size_t)(tm * 256 + wave * 32 + i * 8 + (lane >> 3)) * K + (lane & 7) * 8);
+        fb[i] = *(const f16x8 *)(B + (size_t)(tn * 256 + wave * 32 + i * 8 + (lane >> 3)) * K + (lane & 7) * 8);
+    }
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.0f;
+    unsigned long long copy = 0, compute = 0;
+    for (int t = 0; t < ntile; ++t) {
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        const unsigned long long c0 = __builtin_amdgcn_s_memtime();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int q = (j * 8 + wave) * 64 + lane;
+            const uint32_t off = (uint32_t)(((q >> 3) * K + t * 64 + (q & 7) * 8) * 2);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ra, (__attribute__((address_space(3))) void *)(lds + (j * 8 + wave) * 1024), 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rb, (__attribute__((address_space(3))) void *)(lds + 32768 + (j * 8 + wave) * 1024), 16, off, 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+        __builtin_amdgcn_sched_barrier(0);
+        const unsigned long long c1 = __builtin_amdgcn_s_memtime();
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        const unsigned long long m0 = __builtin_amdgcn_s_memtime();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[j], fa[(i + ks) & 3], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        const unsigned long long m1 = __builtin_amdgcn_s_memtime();
+        __builtin_amdgcn_sched_barrier(0);
+        copy += c1 - c0;
+        compute += m1 - m0;
+    }
+    float sum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sum += acc[i][j][e];
+    // one lane per wave records; the LDS contents feed the live value too
+    sum += (float)*(const _Float16 *)(lds + lane * 16);
+    if (lane == 0) {
+        unsigned long long *o = out + ((size_t)blockIdx.x * 8 + wave) * 4;
+        o[0] = copy;
+        o[1] = compute;
+        o[2] = (unsigned long long)ntile;
+        o[3] = (unsigned long long)__builtin_bit_cast(uint32_t, sum);
+    }
+}
+
 }  // namespace
 
 extern "C" {
+
+// Stage-model probe launch: `blocks` workgroups (one per CU is the intended
+// use) over an M x K (A) and N x K (B) fp16 pair with M >= 256 * tiles_m and
+// N >= 256 * ceil(blocks / tiles_m); K a positive multiple of 64 below 2^21;
+// 1 <= ntile <= K / 64; out: device buffer of blocks * 32 64-bit words.
+// Returns a hipError_t value (hipErrorInvalidValue for arguments outside
+// these bounds, checked here before the launch).
+int sg_probe_stage_timing(const void *A, long long M, const void *B, long long N, int K,
+                          int tiles_m, int blocks, int ntile, void *out, void *stream)
+{
+    if (!A || !B || !out || K <= 0 || (K & 63) || K > (1 << 21) || tiles_m <= 0 || blocks <= 0 ||
+        ntile <= 0 || ntile > K / 64)
+        return (int)hipErrorInvalidValue;
+    const long long tiles_n = (blocks + tiles_m - 1) / tiles_m;
+    if (M < 256LL * tiles_m || N < 256LL * tiles_n || 256LL * K * 2 >= (1LL << 31))
+        return (int)hipErrorInvalidValue;
+    const _Float16 *a = static_cast<const _Float16 *>(A);
+    const _Float16 *b = static_cast<const _Float16 *>(B);
+    unsigned long long *o = static_cast<unsigned long long *>(out);
+    void *args[] = {&a, &b, &K, &tiles_m, &ntile, &o};
+    return (int)hipLaunchKernel(reinterpret_cast<const void *>(&stage_timing_kernel), dim3(blocks),
+                                dim3(512), args, 0, static_cast<hipStream_t>(stream));
+}
+
 
 // Flops one launch performs: blocks x 4 waves x iters x 16 x 8 MFMAs of
 // 2 * 32 * 32 * 16 flop.

@@ -163,7 +163,7 @@ def test_split_graph_replays_and_streams():
     # replays of a captured split call (two kernels; its workspace from the
     # graph's pool) and calls on two streams at once, each with its own
     # cached workspace, all equal to the eager result bit for bit
-    M, N, K = 2048, 2048, 2048
+    M, N, K = 2048, 2048, 8192
     A, B = inputs.operands(M, N, K, 2601)
     a, b = to_dev(A), to_dev(B)
     assert sg.gemm_fp16_tn_splitk_splits(M, N, K) > 1
