@@ -175,6 +175,23 @@ size_t gemm_fp16_tn_splitk_workspace_bytes(int M, int N, int K, int splits);
  * a failed device query. */
 int gemm_fp16_tn_splitk_splits(int M, int N, int K);
 
+/* gemm_fp16_tn_splitk without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP-graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The partial tiles live in a fixed
+ * 64 MiB device array of the library's own (256 fp32 partial tiles of
+ * 256 x 256, one round of split pieces on a 256-CU device), which every GPU
+ * the library runs on holds until the process ends; its address is looked
+ * up once per device.  This call allocates and frees nothing and calls no
+ * allocating library routine.  A plan whose partials exceed the array
+ * (gemm_fp16_tn_splitk_workspace_bytes(M, N, K, splits) > 64 MiB) is
+ * rejected with SG_ERR_SHAPE before any launch.  Every call on one GPU
+ * shares the array: calls that overlap in time on one GPU (two streams, two
+ * host threads) race and may return wrong results; serialise them.  Nothing
+ * in the array needs to be zero.  Other arguments, rules and errors as
+ * gemm_fp16_tn_splitk. */
+sg_status gemm_fp16_tn_splitk_noalloc(int M, int N, int K, float alpha, const void *A,
+                                      const void *B, void *D, int splits, void *stream);
+
 /* As gemm_fp16_tn_alpha, but runs the named compiled variant instead of the
  * one the library would choose (used by the stage-count sweep).
  * SG_ERR_UNSUPPORTED if no such variant is compiled; SG_ERR_NULL if cfg is

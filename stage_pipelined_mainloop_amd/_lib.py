@@ -87,6 +87,8 @@ def lib() -> ctypes.CDLL:
         L.attention_fp16_splits.restype = i
         L.gemm_fp16_tn_splitk.argtypes = [i, i, i, f, vp, vp, vp, i, vp, ctypes.c_size_t, vp]
         L.gemm_fp16_tn_splitk.restype = i
+        L.gemm_fp16_tn_splitk_noalloc.argtypes = [i, i, i, f, vp, vp, vp, i, vp]
+        L.gemm_fp16_tn_splitk_noalloc.restype = i
         L.gemm_fp16_tn_splitk_workspace_bytes.argtypes = [i, i, i, i]
         L.gemm_fp16_tn_splitk_workspace_bytes.restype = ctypes.c_size_t
         L.gemm_fp16_tn_splitk_splits.argtypes = [i, i, i]
@@ -178,6 +180,12 @@ def gemm_fp16_tn_splitk(M: int, N: int, K: int, alpha: float, A: int, B: int, D:
                         workspace: int, workspace_bytes: int, stream: int = 0) -> int:
     return _check(lib().gemm_fp16_tn_splitk(M, N, K, alpha, A, B, D, splits, workspace,
                                             workspace_bytes, stream), "gemm_fp16_tn_splitk")
+
+
+def gemm_fp16_tn_splitk_noalloc(M: int, N: int, K: int, alpha: float, A: int, B: int, D: int,
+                                splits: int, stream: int = 0) -> int:
+    return _check(lib().gemm_fp16_tn_splitk_noalloc(M, N, K, alpha, A, B, D, splits, stream),
+                  "gemm_fp16_tn_splitk_noalloc")
 
 
 def gemm_fp16_tn_splitk_workspace_bytes(M: int, N: int, K: int, splits: int) -> int:

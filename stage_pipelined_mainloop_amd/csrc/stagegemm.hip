@@ -12,6 +12,13 @@
 #include "persistent_kernel.hpp"
 #include "shortk_kernel.hpp"
 
+// Scratch of the allocation-free split-K entry point: the partial tiles of
+// one round of 256 split pieces (256 x 256 x 256 fp32 = 64 MiB), a fixed
+// device array that each GPU the library runs on holds until the process
+// ends.  Host code never uses this name as an address: the device address is
+// looked up per device with hipGetSymbolAddress (scratch_address below).
+static __device__ __align__(256) float scratch[256 * 256 * 256];
+
 namespace {
 
 typedef hipError_t (*launch_fn)(int M, int N, int K, float alpha, float beta, const void *A,
@@ -388,6 +395,22 @@ sg_status launch_split(const SplitPlan &p, int M, int N, int K, float alpha, con
     return e == hipSuccess ? SG_OK : SG_ERR_HIP;
 }
 
+// Device address of `scratch` on the current device, looked up once per
+// device (the array has its own address on every GPU); nullptr if the
+// runtime cannot tell.  Threads may race to fill the cache: each stores the
+// same value.
+void *scratch_address()
+{
+    static std::atomic<void *> cache[16];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return nullptr;
+    void *p = cache[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    cache[dev].store(p, std::memory_order_release);
+    return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -473,6 +496,25 @@ sg_status gemm_fp16_tn_splitk(int M, int N, int K, float alpha, const void *A, c
         overlaps(workspace, p.bytes, D, (size_t)M * N * 2))
         return SG_ERR_ALIAS;
     return launch_split(p, M, N, K, alpha, A, B, D, workspace, stream);
+}
+
+sg_status gemm_fp16_tn_splitk_noalloc(int M, int N, int K, float alpha, const void *A,
+                                      const void *B, void *D, int splits, void *stream)
+{
+    sg_status st = validate(M, N, K, A, B, D);
+    if (st != SG_OK) return st;
+    if (splits < 1) return SG_ERR_SHAPE;
+    if (M == 0 || N == 0) return SG_OK;
+    if (splits == 1 || K == 0) return gemm_fp16_tn_alpha(M, N, K, alpha, A, B, D, stream);
+    const int cap = split_capacity();
+    if (cap <= 0) return SG_ERR_HIP;
+    const SplitPlan p = plan_split(M, N, K, splits, cap);
+    if (p.splits == 1) return gemm_fp16_tn_alpha(M, N, K, alpha, A, B, D, stream);
+    if (p.grid * SplitCfg::T >= (1LL << 32)) return SG_ERR_SHAPE;
+    if (p.bytes > sizeof(scratch)) return SG_ERR_SHAPE;    // more partials than the array holds
+    void *ws = scratch_address();
+    if (!ws) return SG_ERR_HIP;
+    return launch_split(p, M, N, K, alpha, A, B, D, ws, stream);
 }
 
 sg_status sg_select_config(int M, int N, int K, sg_config *out)
