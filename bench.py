@@ -231,9 +231,11 @@ def mode_variants(args) -> int:
 
 
 def mode_ksweep(args) -> int:
-    """M = N = 2048, K in the sweep list, every compiled stage count of the
-    128x128x32 and 256x256x32 (8-wave) tiles; LDS bytes and occupancy from
-    the library's query."""
+    """M = N = 2048, K in the sweep list: the library's choice (split-K when
+    it picks it), then every compiled stage count of the 128x128 (4 waves)
+    and 256x256 (8 waves) tiles; LDS bytes and occupancy from the library's
+    query.  Each line records how many kernel dispatches it made, so a
+    kernel trace or counter pass of this mode can be mapped back to it."""
     import torch
 
     import stage_pipelined_mainloop_amd as sg
@@ -244,17 +246,26 @@ def mode_ksweep(args) -> int:
         b = torch.from_numpy(B).cuda()
         M = N = inputs.KSWEEP_MN
         d = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        fn, vname, s = library_call(M, N, K, a, b, d, None)
+        entries = [("library", vname, fn, 2 if s > 1 else 1, None)]
         for c in sg.configs():
             if (c.tile_m, c.tile_n, c.waves) not in ((128, 128, 4), (256, 256, 8)) or not takes(c, K):
                 continue
-            mean = time_launches(lambda: sg.gemm(a, b, out=d, config=c), args.steps, args.warmup)
+            entries.append(("variant", variant_name(c),
+                            (lambda c=c: sg.gemm(a, b, out=d, config=c)), 1, c))
+        for kind, name, f, kernels, c in entries:
+            mean = time_launches(f, args.steps, args.warmup)
             t = 2.0 * M * N * K / (mean / 1e3) / 1e12
             gbs = 2.0 * (M * K + N * K + M * N) / (mean / 1e3) / 1e9
-            print(json.dumps({"mode": "ksweep", "M": M, "N": N, "K": K,
-                              "variant": c.as_tuple(), "ms_mean": round(mean, 4),
-                              "tflops": round(t, 1), "pct_peak": round(100 * t / PEAK_TFLOPS, 2),
-                              "hbm_gbs_compulsory": round(gbs, 1),
-                              "info": variant_info(c)}), flush=True)
+            line = {"mode": "ksweep", "M": M, "N": N, "K": K, "kind": kind, "variant": name,
+                    "ms_mean": round(mean, 4), "tflops": round(t, 1),
+                    "pct_peak": round(100 * t / PEAK_TFLOPS, 2), "hbm_gbs_compulsory": round(gbs, 1),
+                    "launches": args.warmup + args.steps, "warmup": args.warmup,
+                    "kernels_per_call": kernels}
+            if c is not None:
+                line["config"] = c.as_tuple()
+                line["info"] = variant_info(c)
+            print(json.dumps(line), flush=True)
     return 0
 
 
@@ -342,7 +353,7 @@ def library_call(M: int, N: int, K: int, a, b, d, alpha):
     al = 1.0 if alpha is None else float(alpha)
     ptrs = (a.data_ptr(), b.data_ptr(), d.data_ptr())
     if need > 0:
-        ws = torch.zeros(need, dtype=torch.uint8, device=a.device)
+        ws = torch.empty(need, dtype=torch.uint8, device=a.device)   # contents do not matter
 
         def fn():
             sg.gemm_fp16_tn_splitk(M, N, K, al, *ptrs, s, ws.data_ptr(), need, stream)
@@ -577,6 +588,249 @@ def mode_stage_model(args) -> int:
     return 0
 
 
+def _pmc(path: str, name_filter: str = "_ZN2sg"):
+    """Rows of a rocprofv3 counter CSV for this library's kernels, grouped by
+    dispatch: {dispatch id: (kernel name, {counter: value}, duration ns)}."""
+    import csv
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if name_filter not in r["Kernel_Name"]:
+                continue
+            d = out.setdefault(int(r["Dispatch_Id"]), [r["Kernel_Name"], {}, 0])
+            d[1][r["Counter_Name"]] = d[1].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            if "End_Timestamp" in r and r["End_Timestamp"]:
+                d[2] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    return out
+
+
+def _glob1(pattern: str):
+    import glob
+    f = sorted(glob.glob(pattern, recursive=True))
+    return f[0] if f else None
+
+
+def _copy_scales(prof_dir: str):
+    """FETCH_SIZE / WRITE_SIZE scale factors from the calibration copy passes
+    (512 MiB read and written per launch)."""
+    scale = {}
+    for key, counter in (("copy_fetch", "FETCH_SIZE"), ("copy_write", "WRITE_SIZE")):
+        rows = _pmc(_glob1(f"{prof_dir}/**/{key}_counter_collection.csv"), "")
+        vals = [c[counter] for _, (n, c, _d) in rows.items() if counter in c and "opy" in n]
+        if not vals:
+            vals = [max(c.get(counter, 0.0) for _, (n, c, _d) in rows.items())]
+        scale[counter] = (512 * 1024 * 1024) / (max(vals) * 1024)
+    return scale
+
+
+SQ_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE "
+               "SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_WAVES SQ_INSTS_LDS GRBM_GUI_ACTIVE")
+
+
+def mode_profile_summary(args) -> int:
+    """Turn one workload's profiling runs into profiles/<kernel>_<workload>.md
+    and profiles/traffic_<workload>.json (which the bench line reads):
+    a kernel trace of `python bench.py --workload W --no-per-config
+    --no-cpu-baseline` averaged over exactly its timed dispatches, and three
+    counter passes of the same command with --steps 5 --warmup 1 (FETCH_SIZE,
+    WRITE_SIZE, and the SQ counters), scaled by the calibration copy's passes.
+    Host-only, no GPU.  Expects in --prof-dir: trace_<W>/ (kernel trace and
+    stats CSVs), trace_<W>.log (that run's output), <W>_fetch, <W>_write,
+    <W>_sq, copy_fetch, copy_write counter CSVs."""
+    import csv
+    import statistics
+    w, pdir = args.workload, args.prof_dir
+    scale = _copy_scales(pdir)
+    with open(f"{pdir}/trace_{w}.log") as f:
+        b = json.loads([ln for ln in f if ln.startswith("{")][-1])
+    M, N, K = b["config"]["M"], b["config"]["N"], b["config"]["K"]
+    win = b["config"]["trace_window"]
+    trace = _glob1(f"{pdir}/trace_{w}/**/*kernel_trace.csv")
+    per = {}
+    with open(trace) as f:
+        for r in csv.DictReader(f):
+            per.setdefault(r["Kernel_Name"], []).append(
+                (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    ours = {k: v for k, v in per.items() if "_ZN2sg" in k}
+    hot = max(ours, key=lambda k: sum(d for _, d in ours[k]))
+    seq = [d for _, d in sorted(ours[hot])]
+    window = seq[win["first"]:win["first"] + win["count"]]
+    mean_ns = statistics.mean(window)
+    pm = {}
+    for key in ("fetch", "write", "sq"):
+        rows = _pmc(_glob1(f"{pdir}/**/{w}_{key}_counter_collection.csv"))
+        sel = [c for _, (n, c, _d) in sorted(rows.items()) if n == hot]
+        durs = [d for _, (n, c, d) in sorted(rows.items()) if n == hot and d > 0]
+        agg = {}
+        for c in sel:
+            for kk, v in c.items():
+                agg.setdefault(kk, []).append(v)
+        pm[key] = ({kk: statistics.mean(v) for kk, v in agg.items()},
+                   statistics.mean(durs) if durs else None)
+    fetch_b = pm["fetch"][0]["FETCH_SIZE"] * 1024 * scale["FETCH_SIZE"]
+    write_b = pm["write"][0]["WRITE_SIZE"] * 1024 * scale["WRITE_SIZE"]
+    sq, sq_dur = pm["sq"]
+    flops = 2.0 * M * N * K
+    algo = 2.0 * (M * K + N * K + M * N)
+    roof = roofline_of(M, N, K, mean_ns / 1e6)
+    short = hot.split("Cfg")[1].split("EEE")[0].replace("ILi", "").replace("ELi", "_").replace("E", "")
+    family = hot.split("2sg")[1].split("INS_")[0].lstrip("0123456789")
+    util = sq["SQ_VALU_MFMA_BUSY_CYCLES"] / (4 * sq["SQ_BUSY_CU_CYCLES"])
+    conflict = sq["SQ_LDS_BANK_CONFLICT"] / max(sq["SQ_LDS_IDX_ACTIVE"], 1)
+    ghz = sq["GRBM_GUI_ACTIVE"] / 8 / sq_dur if sq_dur else float("nan")
+    P = f"python bench.py --workload {w} --no-per-config --no-cpu-baseline --steps 5 --warmup 1"
+    trace_cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/trace_{w} -o {w} -- "
+                 f"python bench.py --workload {w} --no-per-config --no-cpu-baseline")
+    lines = [
+        f"# {family}<{short}> on {w} (M={M}, N={N}, K={K})", "",
+        f"Kernel: `{hot}`", "",
+        "## Kernel trace, timed dispatches only", "",
+        f"Command: `{trace_cmd}`", "",
+        f"Summarised with `python bench.py --mode profile_summary --prof-dir <dir> --workload {w}`.", "",
+        "| Dispatches in trace | Timed window | Mean over window (us) | Roofline at that mean | bench.py events (us) | trace / events |",
+        "|---|---|---|---|---|---|",
+        f"| {len(seq)} | {win['first']}..{win['first'] + win['count'] - 1} | {mean_ns / 1e3:.2f} | "
+        f"{roof['achieved']} {roof['unit']}, frac {roof['frac']} | {b['config']['kernel_ms_mean'] * 1e3:.2f} | "
+        f"{mean_ns / 1e3 / (b['config']['kernel_ms_mean'] * 1e3):.4f} |", "",
+        f"Launches: {b['config'].get('launch', 'eager')}; variant {b['config']['variant']}.", "",
+        "## Bytes leaving L2 (two --pmc passes, scaled by a plain copy)", "",
+        f"Commands: `rocprofv3 --pmc FETCH_SIZE --output-format csv -- {P}` and the same with `WRITE_SIZE`; "
+        "calibration: `rocprofv3 --pmc FETCH_SIZE -- python bench.py --mode calibrate_copy --steps 3 --warmup 1` "
+        f"(and `WRITE_SIZE`), a copy of 512 MiB each way: scales {scale['FETCH_SIZE']:.3f} and {scale['WRITE_SIZE']:.3f}.",
+        "The L2's misses may still hit the memory-side Infinity Cache (no counter for its hits is exposed), "
+        "so these bytes bound the HBM bytes from above.", "",
+        "| Per launch | Value |", "|---|---|",
+        f"| FETCH_SIZE (raw) | {pm['fetch'][0]['FETCH_SIZE']:.0f} KiB |",
+        f"| WRITE_SIZE (raw) | {pm['write'][0]['WRITE_SIZE']:.0f} KiB |",
+        f"| fetched (scaled) | {fetch_b / 1e6:.1f} MB |",
+        f"| written (scaled) | {write_b / 1e6:.1f} MB |",
+        f"| leaving L2, total | {(fetch_b + write_b) / 1e6:.1f} MB |",
+        f"| algorithmic 2(MK+NK+MN) | {algo / 1e6:.1f} MB |",
+        f"| leaving L2 / algorithmic | {(fetch_b + write_b) / algo:.2f} |",
+        f"| GB/s at the window mean | {(fetch_b + write_b) / mean_ns:.0f} |", "",
+        "## SQ counters (one --pmc pass)", "",
+        f"Command: `rocprofv3 --pmc {SQ_COUNTERS} --output-format csv -- {P}`", "",
+        "| Counter | Per launch |", "|---|---|"]
+    lines += [f"| {c} | {v:.4g} |" for c, v in sorted(sq.items())]
+    lines += ["", "Derived:",
+              f"- MFMA utilisation: SQ_VALU_MFMA_BUSY_CYCLES / (4 SIMDs x SQ_BUSY_CU_CYCLES) = {100 * util:.1f} %",
+              f"- LDS bank-conflict rate: SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE = {conflict:.4f}"]
+    if sq_dur and sq_dur >= 100e3:
+        lines += [f"- shader clock in the counter pass: GRBM_GUI_ACTIVE / 8 XCDs / duration = {ghz:.2f} GHz "
+                  f"(peak at that clock: {256 * 4096 * ghz / 1e3:.0f} TFLOP/s)"]
+    md = "\n".join(lines) + "\n"
+    fn = os.path.join(PROFILES, f"gemm_tn_{short}_{w}.md")
+    with open(fn, "w") as f:
+        f.write(md)
+    tj = {"workload": w, "kernel": hot, "kernel_source_sha": kernel_source_sha(),
+          "hbm_bytes_per_launch": round(fetch_b + write_b), "fetch_bytes": round(fetch_b),
+          "write_bytes": round(write_b), "fetch_scale": round(scale["FETCH_SIZE"], 4),
+          "write_scale": round(scale["WRITE_SIZE"], 4), "summary": os.path.basename(fn),
+          "kind": "bytes leaving L2 (FETCH_SIZE + WRITE_SIZE, copy-scaled)"}
+    with open(os.path.join(PROFILES, f"traffic_{w}.json"), "w") as f:
+        json.dump(tj, f, indent=1)
+    print(json.dumps({"summary": fn, "window_us": round(mean_ns / 1e3, 2), "mfma_util": round(util, 4),
+                      "lds_conflict_rate": round(conflict, 4),
+                      "l2_egress_mb": round((fetch_b + write_b) / 1e6, 1)}))
+    return 0
+
+
+def mode_ksweep_summary(args) -> int:
+    """profiles/ksweep_m2048_n2048.md from a kernel trace and three counter
+    passes of `python bench.py --mode ksweep` (files in --prof-dir:
+    ks_trace/ and ks_trace.log from `--steps 10 --warmup 3`; ks_fetch,
+    ks_write, ks_sq counter CSVs and ks_pmc.log from `--steps 1 --warmup 0`),
+    plus the CPU baselines of a default bench.py run (--bench-log).  Each
+    sweep line's dispatches are found by order; a split-K call's time runs
+    from its first kernel's start to its reduction's end."""
+    import csv
+    import statistics
+    pdir = args.prof_dir
+    scale = _copy_scales(pdir)
+
+    def lines_of(path):
+        with open(path) as f:
+            return [json.loads(ln) for ln in f if ln.startswith("{") and '"ksweep"' in ln]
+    tl = lines_of(f"{pdir}/ks_trace.log")
+    pl = lines_of(f"{pdir}/ks_pmc.log")
+    rows = []
+    with open(_glob1(f"{pdir}/ks_trace/**/*kernel_trace.csv")) as f:
+        for r in csv.DictReader(f):
+            if "_ZN2sg" in r["Kernel_Name"]:
+                rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    rows.sort()
+    timing, i = [], 0
+    for ln in tl:
+        k, n = ln["kernels_per_call"], ln["launches"]
+        calls = [rows[i + j * k:i + (j + 1) * k] for j in range(n)]
+        i += n * k
+        timed = calls[ln["warmup"]:]
+        timing.append(statistics.mean(c[-1][1] - c[0][0] for c in timed) / 1e3)
+    pmc = {key: sorted(_pmc(_glob1(f"{pdir}/**/ks_{key}_counter_collection.csv")).items())
+           for key in ("fetch", "write", "sq")}
+    cpu = {}
+    if args.bench_log:
+        with open(args.bench_log) as f:
+            bl = json.loads([ln for ln in f if ln.startswith("{")][-1])
+        for K, e in bl["per_config"]["ksweep"]["K"].items():
+            cpu[int(K)] = e.get("cpu_baseline")
+    out = ["# K-sweep at M = N = 2048 (stage-count tuning)", "",
+           "Commands (each run's dispatches are mapped to the sweep lines by order):",
+           "- timing: `rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/ks_trace -o ksweep -- "
+           "python bench.py --mode ksweep --steps 10 --warmup 3` (mean over the 10 timed calls of each line)",
+           f"- counters: `rocprofv3 --pmc {SQ_COUNTERS} --output-format csv -d <dir> -o ks_sq -- "
+           "python bench.py --mode ksweep --steps 1 --warmup 0`, and the same with `FETCH_SIZE` (-o ks_fetch) "
+           "and `WRITE_SIZE` (-o ks_write); copy calibration as in the per-workload summaries "
+           f"(scales {scale['FETCH_SIZE']:.3f} / {scale['WRITE_SIZE']:.3f})",
+           "- summarised with `python bench.py --mode ksweep_summary --prof-dir <dir> --bench-log <bench.py output>`",
+           "",
+           "Inputs: A, B = 2048 x K fp16, uniform[-1,1] (seeds 5/6).  `us` = mean GPU time per call from the trace "
+           "(a split-K call: first kernel's start to the reduction's end); `busy` = SQ_VALU_MFMA_BUSY_CYCLES / "
+           "(4 x SQ_BUSY_CU_CYCLES); `conflict` = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; `L2 out` = "
+           "copy-scaled FETCH_SIZE + WRITE_SIZE per call (bytes leaving L2, an upper bound on HBM bytes) and "
+           "`GB/s` that over `us`; `ring` = stages x (tile_m + tile_n) x tile_k x 2 bytes, `lds` = allocated LDS, "
+           "`wg/cu` = resident workgroups per CU (runtime query), `regs` = registers per lane.  The library line "
+           "is the call bench.py times for this shape.", ""]
+    j = 0
+    for K in sorted({ln["K"] for ln in tl}):
+        c = cpu.get(K)
+        out += [f"## K = {K}", ""]
+        if c:
+            out += [f"Oracle on this host: {c['value']:.4f} TFLOP/s on {c['cores']} threads ({c['sample']}).", ""]
+        out += ["| variant | S | us | TFLOP/s | frac | busy | conflict | L2 out MB | GB/s | ring B | lds B | wg/cu | regs |",
+                "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+        for idx, ln in enumerate(tl):
+            if ln["K"] != K:
+                continue
+            us = timing[idx]
+            k = ln["kernels_per_call"]
+            sq = {}
+            fetch = write = 0.0
+            for q in range(k):
+                for cn, v in pmc["sq"][j + q][1][1].items():
+                    sq[cn] = sq.get(cn, 0.0) + v
+                fetch += pmc["fetch"][j + q][1][1].get("FETCH_SIZE", 0.0)
+                write += pmc["write"][j + q][1][1].get("WRITE_SIZE", 0.0)
+            j += k * pl[idx]["launches"] if idx < len(pl) else k
+            l2 = (fetch * scale["FETCH_SIZE"] + write * scale["WRITE_SIZE"]) * 1024
+            M = N = 2048
+            tf = 2.0 * M * N * K / us / 1e6
+            busy = sq.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) / max(4 * sq.get("SQ_BUSY_CU_CYCLES", 1), 1)
+            conf = sq.get("SQ_LDS_BANK_CONFLICT", 0) / max(sq.get("SQ_LDS_IDX_ACTIVE", 1), 1)
+            info = ln.get("info", {})
+            st = ln["config"][3] if "config" in ln else "-"
+            name = ("**library: " + ln["variant"] + "**") if ln["kind"] == "library" else ln["variant"]
+            out.append(f"| {name} | {st} | {us:.1f} | {tf:.1f} | {tf / PEAK_TFLOPS:.3f} | {100 * busy:.1f} % | "
+                       f"{conf:.3f} | {l2 / 1e6:.1f} | {l2 / us / 1e3:.0f} | {info.get('lds_bytes', '-')} | "
+                       f"{info.get('lds_total_bytes', '-')} | {info.get('wg_per_cu', '-')} | {info.get('regs', '-')} |")
+        out.append("")
+    fn = os.path.join(PROFILES, "ksweep_m2048_n2048.md")
+    with open(fn, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print(json.dumps({"summary": fn, "lines": len(tl)}))
+    return 0
+
+
 def mode_trace_summary(args) -> int:
     """Summarise a rocprofv3 kernel trace (CSV) of a bench.py run, given that
     run's JSON line: per kernel, dispatches and mean duration over all of
@@ -630,9 +884,11 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--mode", default="bench",
                     choices=["bench", "variants", "ksweep", "calibrate_copy", "attention",
-                             "trace_summary", "stage_model"])
+                             "trace_summary", "stage_model", "profile_summary", "ksweep_summary"])
     ap.add_argument("--trace", default=None, help="kernel-trace CSV for --mode trace_summary")
     ap.add_argument("--bench-log", default=None, help="that run's output for --mode trace_summary")
+    ap.add_argument("--prof-dir", default=None,
+                    help="directory of rocprofv3 outputs for --mode profile_summary / ksweep_summary")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=None,
@@ -667,6 +923,10 @@ def main() -> int:
         return mode_trace_summary(args)
     if args.mode == "stage_model":
         return mode_stage_model(args)
+    if args.mode == "profile_summary":
+        return mode_profile_summary(args)
+    if args.mode == "ksweep_summary":
+        return mode_ksweep_summary(args)
     if args.mode == "variants":
         return mode_variants(args)
     if args.mode == "ksweep":
