@@ -191,15 +191,14 @@ struct Cfg {
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
     // Order 8 keeps S - 1 slots of A and S slots of B.
     static constexpr int RING_BYTES = ORDER == 8 ? (S - 1) * A_BYTES + S * B_BYTES : S * STAGE_BYTES;
-    // Epilogue staging: each wave's WTM x WTN fp16 sub-tile, rows padded by
-    // 16 bytes (row stride 9 x 16 B for 128-byte rows) against bank conflicts.
-    static constexpr int EPI_ROW = WTN * 2 + 16;
+    // Epilogue staging: one 32-row block of each wave's sub-tile at a time,
+    // unpadded rows with the slot swizzle of staged_slot.
+    static constexpr int EPI_ROW = WTN * 2;
     static constexpr int EPI_WAVE_BYTES = 32 * EPI_ROW;    // one 32-row block at a time
     static constexpr int EPI_BYTES = NW * EPI_WAVE_BYTES;
     // Persistent and short-K schedules: the ring stays live during the
     // epilogue, so the staging area is separate and holds one 32-row block
-    // of every wave's sub-tile at a time, rows unpadded (an 8-byte XOR
-    // swizzle keeps the accesses conflict-free).
+    // of every wave's sub-tile at a time (same layout).
     static constexpr int EPI_BLOCK_WAVE_BYTES = 32 * WTN * 2;
     static constexpr int EPI_BLOCK_BYTES = NW * EPI_BLOCK_WAVE_BYTES;
     static constexpr bool OWN_STAGING = SCHED == 3 || SCHED == 4;   // staging beside the ring
@@ -280,6 +279,22 @@ __device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, i
     tn = in_group / gm;
 }
 
+// Epilogue staging layout (all kernels).  A wave stages a 32-row block of
+// its sub-tile in unpadded rows of WTN fp16, in 8-byte slots (four
+// consecutive columns, what one lane holds per accumulator piece); slot s of
+// row r is stored at slot s ^ (r & 15).  On gfx950 (measured with the LDS
+// bank-conflict counter on isolated access patterns) a 64-bit LDS write
+// serves 16 consecutive lanes per cycle over 32 four-byte banks, and a
+// 128-bit read 16 lanes per cycle over 64 banks.  A write instruction puts 16
+// consecutive lanes on 16 rows (r & 15 all different) at one logical slot,
+// so the XOR spreads them over 16 slot positions: all 32 banks.  A read
+// lane takes the 16-byte chunk ec (slots 2 ec, 2 ec + 1) of its row, found at
+// chunk ec ^ ((r & 15) >> 1) with its halves swapped when r is odd; 16
+// lanes read two whole 128-byte rows (or one 256-byte row) in a permuted
+// order: all 64 banks.  The earlier layouts (16-byte row padding, or a
+// swizzle by (r >> 1)) put two rows of a write group on the same banks.
+__device__ __forceinline__ int staged_slot(int r, int slot) { return slot ^ (r & 15); }
+
 // alpha * acc as one fused operation with a +0 addend: the product is exact
 // inside the fma and the +0 turns an exactly zero product (alpha < 0 times a
 // zero sum) into +0, the value round-to-nearest gives the real sum 0; no other
@@ -293,10 +308,10 @@ __device__ __forceinline__ float scale_acc(float alpha, float acc)
 // One 32-row block of a wave's sub-tile (its FN 32x32 accumulators, rows
 // row0 .. row0+31 of the workgroup tile) to D = RNE16(alpha * acc), through
 // the wave's unpadded staging area: 128-byte rows of sixteen 8-byte slots,
-// slot c of row r at c ^ ((r >> 1) & 15), so the 32 rows of one write land on
-// 32 distinct bank pairs.  Wait for the LDS writes, read back 16 bytes per
-// lane along rows (a logical 16-byte chunk is an aligned slot pair, halves
-// swapped when the row's swizzle is odd) and store with the streaming policy.
+// slot c of row r at c ^ (r & 15) (staged_slot).  Wait for the LDS writes,
+// read back 16 bytes per lane along rows (a logical 16-byte chunk is an
+// aligned slot pair, halves swapped when the row's swizzle is odd) and store
+// with the streaming policy.
 // Lane holds D[m][n .. n+3] for m = row (lane & 31) of each block and
 // n = 8 * g + 4 * (lane >> 5).  LDS runs one wave's accesses in order, so a
 // later block's writes cannot overtake these reads.
@@ -310,7 +325,7 @@ __device__ __forceinline__ void store_block_staged(const f32x16 (&blk)[C::FN], f
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
     const int half = lane >> 5;
     const int wr = lane & 31;
-    const int wsw = (wr >> 1) & 15;
+    const int wsw = wr & 15;
 #pragma unroll
     for (int j = 0; j < C::FN; ++j)
 #pragma unroll
@@ -331,7 +346,7 @@ __device__ __forceinline__ void store_block_staged(const f32x16 (&blk)[C::FN], f
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
         const int r = it * 8 + (lane >> 3);
-        const int sw = (r >> 1) & 15;
+        const int sw = r & 15;
         u32x4 v = *(const u32x4 *)(epi + r * 128 + ((ec ^ (sw >> 1)) << 4));
         if (sw & 1) v = u32x4{v[2], v[3], v[0], v[1]};
         const uint32_t off = n_ok ? (uint32_t)((row0 + r) * N + n) * 2u : kOutOfRange;
@@ -869,13 +884,15 @@ __device__ __forceinline__ void gemm_tn_body(const _Float16 *__restrict__ A,
     __builtin_amdgcn_sched_barrier(0);
     compiler_fence();
     char *epi = smem + wave * C::EPI_WAVE_BYTES;
+    // four consecutive columns c .. c + 3 (c % 4 == 0) of block row r: one
+    // 8-byte slot, at the swizzled position (staged_slot)
     auto stage4 = [&](int r, int c, float v0, float v1, float v2, float v3) {
         u32x2 packed;
         packed[0] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v0) |
                     ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v1) << 16);
         packed[1] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v2) |
                     ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v3) << 16);
-        *(u32x2 *)(epi + r * C::EPI_ROW + c * 2) = packed;
+        *(u32x2 *)(epi + r * C::EPI_ROW + staged_slot(r, c >> 2) * 8) = packed;
     };
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
     constexpr int CPRW = C::EPI_CHUNKS_PER_ROW;        // 16-byte chunks per sub-tile row
@@ -964,7 +981,8 @@ __device__ __forceinline__ void gemm_tn_body(const _Float16 *__restrict__ A,
 #pragma unroll
         for (int it = 0; it < 32 / RPI; ++it) {
             const int rr = it * RPI + lane / CPRW;     // row within block i
-            const u32x4 v = *(const u32x4 *)(epi + rr * C::EPI_ROW + ec * 16);
+            u32x4 v = *(const u32x4 *)(epi + rr * C::EPI_ROW + ((ec ^ ((rr & 15) >> 1)) << 4));
+            if (rr & 1) v = u32x4{v[2], v[3], v[0], v[1]};
             const int ml = wm * C::WTM + i * 32 + rr;  // row within the workgroup tile
             const uint32_t off = n_ok ? (uint32_t)(ml * N + n_st) * 2u : kOutOfRange;
             __builtin_amdgcn_raw_buffer_store_b128(v, rd, off, 0, kStoreStreaming);
