@@ -25,9 +25,10 @@ Prints ONE JSON line (rank 0):
 
 Other modes: variants, ksweep (every compiled variant), attention (the
 fused forward), calibrate_copy (the copy the traffic counters are scaled
-by), stage_model (T_copy and T_compute of the stage-count formula) and
-trace_summary (a kernel trace of this script averaged over exactly the
-timed dispatches).
+by), stage_model (T_copy and T_compute of the stage-count formula),
+lds_patterns (epilogue staging access patterns, for the LDS counters), and
+host-only summaries of rocprofv3 runs of this script: trace_summary,
+profile_summary, ksweep_summary, lds_summary.
 """
 from __future__ import annotations
 
@@ -226,6 +227,7 @@ def mode_variants(args) -> int:
                           "variant": c.as_tuple(), "ms_mean": round(mean, 4),
                           "tflops": round(t, 1),
                           "pct_peak": round(100 * t / PEAK_TFLOPS, 2),
+                          "launches": args.warmup + args.steps, "warmup": args.warmup,
                           "info": variant_info(c)}), flush=True)
     return 0
 
@@ -831,6 +833,116 @@ def mode_ksweep_summary(args) -> int:
     return 0
 
 
+LDS_PATTERNS = [
+    "padded 144-byte rows, 16x16 pieces: 64-bit write (tiled epilogue before)",
+    "padded 144-byte rows: 128-bit read (tiled epilogue before)",
+    "128-byte rows, slot ^ ((r >> 1) & 15), 32x32 pieces: 64-bit write (persistent/short-K before)",
+    "128-byte rows, slot ^ ((r >> 1) & 15): 128-bit read (persistent/short-K before)",
+    "128-byte rows, slot ^ (r & 15), 32x32 pieces: 64-bit write (all epilogues now)",
+    "128-byte rows, slot ^ (r & 15), 16x16 pieces: 64-bit write (all epilogues now)",
+    "128-byte rows, slot ^ (r & 15): 128-bit read (all epilogues now)",
+    "contiguous 64-bit write",
+    "contiguous 128-bit read",
+]
+
+
+def mode_lds_patterns(args) -> int:
+    """Run each epilogue staging access pattern of the probe library once
+    (256 one-wave workgroups x 1000 repetitions of 8 accesses); meant to run
+    under rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS,
+    whose dispatches --mode lds_summary maps back to the patterns."""
+    import ctypes
+
+    import torch
+    P = ctypes.CDLL(os.path.join(ROOT, "stage_pipelined_mainloop_amd", "libsgprobe.so"))
+    P.sg_probe_lds_pattern.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+    P.sg_probe_lds_pattern.restype = ctypes.c_int
+    sink = torch.empty(256 * 64, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    for i, name in enumerate(LDS_PATTERNS):
+        if P.sg_probe_lds_pattern(i, 256, 1000, sink.data_ptr(), stream) != 0:
+            raise RuntimeError(f"pattern {i} failed to launch")
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "lds_patterns", "pattern": i, "name": name}), flush=True)
+    return 0
+
+
+def mode_lds_summary(args) -> int:
+    """profiles/lds_epilogue_patterns.md from a counter pass of --mode
+    lds_patterns (lds_counter_collection.csv in --prof-dir)."""
+    rows = sorted((d, n, c) for d, (n, c, _) in
+                  _pmc(_glob1(f"{args.prof_dir}/**/lds_counter_collection.csv"), "lds_pattern").items())
+    out = ["# LDS bank conflicts of the epilogue staging patterns (gfx950)", "",
+           "Command: `rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS GRBM_GUI_ACTIVE "
+           "--output-format csv -d <dir> -o lds -- python bench.py --mode lds_patterns`; summarised with "
+           "`python bench.py --mode lds_summary --prof-dir <dir>`.", "",
+           "Each pattern: 256 one-wave workgroups, 1000 repetitions of 8 accesses of one staging block "
+           "(32 rows of 64 fp16).  Cycles and conflict cycles per LDS instruction (the compiler may pair two "
+           "64-bit writes into one instruction: then one instruction is two accesses).", "",
+           "| pattern | LDS instructions | active cycles / instr | conflict cycles / instr |", "|---|---|---|---|"]
+    for i, (d, n, c) in enumerate(rows):
+        ins = max(c.get("SQ_INSTS_LDS", 0.0), 1.0)
+        out.append(f"| {LDS_PATTERNS[i] if i < len(LDS_PATTERNS) else n} | {ins:.0f} | "
+                   f"{c.get('SQ_LDS_IDX_ACTIVE', 0) / ins:.2f} | {c.get('SQ_LDS_BANK_CONFLICT', 0) / ins:.2f} |")
+    fn = os.path.join(PROFILES, "lds_epilogue_patterns.md")
+    with open(fn, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print(json.dumps({"summary": fn, "patterns": len(rows)}))
+    return 0
+
+
+def mode_variants_summary(args) -> int:
+    """profiles/variants_<workload>.md from a kernel trace of `python bench.py
+    --mode variants --workload W` (trace CSV under --prof-dir/var_<W>/, that
+    run's output in --bench-log): every compiled variant's mean GPU time over
+    its timed dispatches, mapped by order."""
+    import csv
+    import statistics
+    w = args.workload
+    with open(args.bench_log) as f:
+        lines = [json.loads(ln) for ln in f if ln.startswith("{") and '"variants"' in ln]
+    rows = []
+    with open(_glob1(f"{args.prof_dir}/var_{w}/**/*kernel_trace.csv")) as f:
+        for r in csv.DictReader(f):
+            if "_ZN2sg" in r["Kernel_Name"]:
+                rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"]),
+                             r["Kernel_Name"]))
+    rows.sort()
+    M, N, K = inputs_shape(w)
+    out = [f"# Every compiled variant on {w} (M={M}, N={N}, K={K})", "",
+           f"Command: `rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/var_{w} -o {w} -- "
+           f"python bench.py --mode variants --workload {w} --steps {lines[0]['launches'] - lines[0]['warmup']} "
+           f"--warmup {lines[0]['warmup']}`; summarised with `python bench.py --mode variants_summary "
+           f"--prof-dir <dir> --bench-log <that run's output> --workload {w}`.", "",
+           "`us` = mean kernel-trace duration over each variant's timed dispatches (mapped by order).  "
+           "Schedules: 0 three-phase, 1 cute order, 2 ping-pong, 3 persistent, 4 short K, 5 cute order on "
+           "16x16x32 MFMAs, 7 ping-pong on 16x16x32, 8 split-load ping-pong.", "",
+           "| variant (tile_m, tile_n, tile_k, stages, waves, schedule) | us | TFLOP/s | frac |", "|---|---|---|---|"]
+    i = 0
+    res = []
+    for ln in lines:
+        n = ln["launches"]
+        seg = rows[i:i + n]
+        i += n
+        us = statistics.mean(d for _, d, _ in seg[ln["warmup"]:]) / 1e3
+        res.append((us, ln["variant"]))
+    for us, v in sorted(res):
+        tf = 2.0 * M * N * K / us / 1e6
+        out.append(f"| {tuple(v)} | {us:.1f} | {tf:.1f} | {tf / PEAK_TFLOPS:.3f} |")
+    fn = os.path.join(PROFILES, f"variants_{w}.md")
+    with open(fn, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print(json.dumps({"summary": fn, "variants": len(res), "fastest": res and min(res)[1]}))
+    return 0
+
+
+def inputs_shape(workload: str):
+    from stage_pipelined_mainloop_amd import inputs
+    M, N, K, _, _ = inputs.WORKLOADS[workload]
+    return M, N, K
+
+
 def mode_trace_summary(args) -> int:
     """Summarise a rocprofv3 kernel trace (CSV) of a bench.py run, given that
     run's JSON line: per kernel, dispatches and mean duration over all of
@@ -884,7 +996,8 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--mode", default="bench",
                     choices=["bench", "variants", "ksweep", "calibrate_copy", "attention",
-                             "trace_summary", "stage_model", "profile_summary", "ksweep_summary"])
+                             "trace_summary", "stage_model", "profile_summary", "ksweep_summary",
+                             "lds_patterns", "lds_summary", "variants_summary"])
     ap.add_argument("--trace", default=None, help="kernel-trace CSV for --mode trace_summary")
     ap.add_argument("--bench-log", default=None, help="that run's output for --mode trace_summary")
     ap.add_argument("--prof-dir", default=None,
@@ -927,6 +1040,12 @@ def main() -> int:
         return mode_profile_summary(args)
     if args.mode == "ksweep_summary":
         return mode_ksweep_summary(args)
+    if args.mode == "lds_patterns":
+        return mode_lds_patterns(args)
+    if args.mode == "lds_summary":
+        return mode_lds_summary(args)
+    if args.mode == "variants_summary":
+        return mode_variants_summary(args)
     if args.mode == "variants":
         return mode_variants(args)
     if args.mode == "ksweep":

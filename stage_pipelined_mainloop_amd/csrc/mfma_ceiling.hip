@@ -188,9 +188,88 @@ stage_timing_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__
     }
 }
 
+// LDS access-pattern probe: one wave per workgroup repeats one pattern of
+// 64-bit writes or 128-bit reads over an epilogue staging block (32 rows of
+// 64 fp16), `iters` times; run under the LDS bank-conflict counters, it
+// shows how many cycles each pattern takes and how many of them are
+// conflicts.  Pattern p, access v (0..7) of lane l, byte address in a
+// 16 KiB block:
+//   0 padded rows (144 B), 16x16 accumulator pieces, 64-bit write
+//   1 padded rows, 16-byte read along rows
+//   2 128-byte rows, slot swizzle by (r >> 1) & 15, 32x32 pieces, write
+//   3 the same layout, read
+//   4 128-byte rows, slot swizzle by r & 15, 32x32 pieces, write
+//   5 the same layout, 16x16 pieces, write
+//   6 the same layout, read
+//   7 contiguous 64-bit write, 8 contiguous 128-bit read (no conflicts)
+__device__ __forceinline__ int lds_pattern_addr(int p, int l, int v)
+{
+    switch (p) {
+    case 0: { const int r = 16 * (v & 1) + (l & 15), c = 16 * ((v >> 1) & 3) + 4 * (l >> 4); return r * 144 + c * 2; }
+    case 1: { const int r = (v & 3) * 8 + l / 8; return r * 144 + (l % 8) * 16; }
+    case 2: { const int r = l & 31, s = (8 * (v & 1) + 2 * ((v >> 1) & 3) + (l >> 5)) ^ ((r >> 1) & 15); return r * 128 + s * 8; }
+    case 3: { const int r = (v & 3) * 8 + (l >> 3); return r * 128 + (((l & 7) ^ (((r >> 1) & 15) >> 1)) << 4); }
+    case 4: { const int r = l & 31, s = (8 * (v & 1) + 2 * ((v >> 1) & 3) + (l >> 5)) ^ (r & 15); return r * 128 + s * 8; }
+    case 5: { const int r = 16 * (v & 1) + (l & 15), s = 4 * ((v >> 1) & 3) + (l >> 4); return r * 128 + (s ^ (r & 15)) * 8; }
+    case 6: { const int r = (v & 3) * 8 + (l >> 3); return r * 128 + (((l & 7) ^ ((r & 15) >> 1)) << 4); }
+    case 7: return l * 8;
+    default: return l * 16;
+    }
+}
+
+template <int P, bool WRITE>
+__global__ void __launch_bounds__(64) lds_pattern_kernel(unsigned *__restrict__ sink, int iters)
+{
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    __shared__ __attribute__((aligned(1024))) char lds[16384];
+    const int l = threadIdx.x;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+            // volatile LDS accesses: every one is issued as written (none
+            // merged or dropped, though nothing reads the written values)
+            typedef __attribute__((address_space(3))) char lds_char;
+            lds_char *at = (lds_char *)lds + lds_pattern_addr(P, l, v);
+            if constexpr (WRITE)
+                *(volatile __attribute__((address_space(3))) u32x2 *)at =
+                    u32x2{(unsigned)(l + it), (unsigned)v};
+            else
+                acc += *(const volatile __attribute__((address_space(3))) u32x4 *)at;
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+    }
+    sink[blockIdx.x * 64 + l] = acc[0] + acc[1] + acc[2] + acc[3];
+}
+
 }  // namespace
 
 extern "C" {
+
+// LDS pattern probe launch: pattern 0..8 (see lds_pattern_addr; 0, 2, 4,
+// 5, 7 write, the others read), `blocks` one-wave workgroups, `iters`
+// repetitions; sink: device buffer of blocks * 64 32-bit words.  Returns a
+// hipError_t value.
+int sg_probe_lds_pattern(int pattern, int blocks, int iters, void *sink, void *stream)
+{
+    if (!sink || blocks <= 0 || iters <= 0 || pattern < 0 || pattern > 8)
+        return (int)hipErrorInvalidValue;
+    static const void *const kernels[9] = {
+        reinterpret_cast<const void *>(&lds_pattern_kernel<0, true>),
+        reinterpret_cast<const void *>(&lds_pattern_kernel<1, false>),
+        reinterpret_cast<const void *>(&lds_pattern_kernel<2, true>),
+        reinterpret_cast<const void *>(&lds_pattern_kernel<3, false>),
+        reinterpret_cast<const void *>(&lds_pattern_kernel<4, true>),
+        reinterpret_cast<const void *>(&lds_pattern_kernel<5, true>),
+        reinterpret_cast<const void *>(&lds_pattern_kernel<6, false>),
+        reinterpret_cast<const void *>(&lds_pattern_kernel<7, true>),
+        reinterpret_cast<const void *>(&lds_pattern_kernel<8, false>)};
+    unsigned *s = static_cast<unsigned *>(sink);
+    void *args[] = {&s, &iters};
+    return (int)hipLaunchKernel(kernels[pattern], dim3(blocks), dim3(64), args, 0,
+                                static_cast<hipStream_t>(stream));
+}
 
 // Stage-model probe launch: `blocks` workgroups (one per CU is the intended
 // use) over an M x K (A) and N x K (B) fp16 pair with M >= 256 * tiles_m and
