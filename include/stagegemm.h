@@ -175,6 +175,27 @@ size_t gemm_fp16_tn_splitk_workspace_bytes(int M, int N, int K, int splits);
  * a failed device query. */
 int gemm_fp16_tn_splitk_splits(int M, int N, int K);
 
+/* The split plan gemm_fp16_tn_splitk makes for a device that keeps
+ * `capacity` workgroups of the split kernel resident (one per compute unit:
+ * 256 on MI355X), computed on the host without any HIP call: 256 x 256
+ * tiles, the tiles computed whole (whole rounds of `capacity`), the tiles cut
+ * along K, the split count after the caller's is lowered to the K tiles and
+ * to 16, the workgroups launched by the first kernel, the workspace bytes,
+ * and the split count the library's time model would choose for this shape
+ * on such a device.  SG_ERR_SHAPE for non-positive or out-of-range sizes,
+ * splits < 1 or capacity < 1; SG_ERR_NULL if out is NULL. */
+typedef struct sg_split_info {
+    int tiles;
+    int whole_tiles;
+    int cut_tiles;
+    int splits;
+    long long workgroups;
+    size_t workspace_bytes;
+    int chosen_splits;
+} sg_split_info;
+
+sg_status sg_split_plan(int M, int N, int K, int splits, int capacity, sg_split_info *out);
+
 /* gemm_fp16_tn_splitk without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP-graph capture, tight serving loops,
  * harnesses that forbid allocation).  The partial tiles live in a fixed

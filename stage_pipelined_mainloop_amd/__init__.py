@@ -18,7 +18,7 @@ from ._lib import (SgConfig, SgConfigInfo, SgError, attention_fp16_fwd, attentio
                    gemm_fp16_tn_splitk_splits, gemm_fp16_tn_splitk_workspace_bytes, sg_get_config,
                    sg_minimum_stages, sg_num_configs,
                    sg_persistent_wait_count, sg_pipeline_wait_count, sg_query_config, sg_select_config,
-                   sg_status_string)
+                   sg_split_plan, sg_status_string, SgSplitInfo)
 
 # Split-K workspaces kept per (device, stream) and reused: calls on one
 # stream never overlap, calls on different streams get different buffers.
@@ -177,7 +177,7 @@ __all__ = [
     "gemm", "attention", "attention_fp16_fwd", "attention_fp16_fwd_split", "attention_fp16_splits",
     "attention_fp16_workspace_bytes", "gemm_fp16_tn", "gemm_fp16_tn_alpha", "gemm_fp16_tn_alpha_beta", "gemm_fp16_tn_cfg",
     "gemm_fp16_tn_splitk", "gemm_fp16_tn_splitk_splits", "gemm_fp16_tn_splitk_workspace_bytes",
-    "split_workspace",
+    "split_workspace", "sg_split_plan", "SgSplitInfo",
     "sg_select_config",
     "sg_num_configs", "sg_get_config", "sg_query_config", "sg_minimum_stages",
     "sg_pipeline_wait_count", "sg_persistent_wait_count", "sg_status_string", "configs", "SgConfig", "SgConfigInfo",

@@ -44,6 +44,15 @@ class SgConfigInfo(ctypes.Structure):
         return {f: getattr(self, f) for f, _ in self._fields_}
 
 
+class SgSplitInfo(ctypes.Structure):
+    _fields_ = [("tiles", ctypes.c_int), ("whole_tiles", ctypes.c_int), ("cut_tiles", ctypes.c_int),
+                ("splits", ctypes.c_int), ("workgroups", ctypes.c_longlong),
+                ("workspace_bytes", ctypes.c_size_t), ("chosen_splits", ctypes.c_int)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
 class SgError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -91,6 +100,8 @@ def lib() -> ctypes.CDLL:
         L.gemm_fp16_tn_splitk_noalloc.restype = i
         L.gemm_fp16_tn_splitk_workspace_bytes.argtypes = [i, i, i, i]
         L.gemm_fp16_tn_splitk_workspace_bytes.restype = ctypes.c_size_t
+        L.sg_split_plan.argtypes = [i, i, i, i, i, ctypes.POINTER(SgSplitInfo)]
+        L.sg_split_plan.restype = i
         L.gemm_fp16_tn_splitk_splits.argtypes = [i, i, i]
         L.gemm_fp16_tn_splitk_splits.restype = i
         L.gemm_fp16_tn_cfg.argtypes = [i, i, i, f, vp, vp, vp, ctypes.POINTER(SgConfig), vp]
@@ -194,6 +205,12 @@ def gemm_fp16_tn_splitk_workspace_bytes(M: int, N: int, K: int, splits: int) -> 
 
 def gemm_fp16_tn_splitk_splits(M: int, N: int, K: int) -> int:
     return int(lib().gemm_fp16_tn_splitk_splits(M, N, K))
+
+
+def sg_split_plan(M: int, N: int, K: int, splits: int, capacity: int) -> SgSplitInfo:
+    info = SgSplitInfo()
+    _check(lib().sg_split_plan(M, N, K, splits, capacity, ctypes.byref(info)), "sg_split_plan")
+    return info
 
 
 def sg_select_config(M: int, N: int, K: int) -> SgConfig:

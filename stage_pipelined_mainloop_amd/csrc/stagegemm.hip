@@ -454,6 +454,23 @@ sg_status gemm_fp16_tn_cfg(int M, int N, int K, float alpha, const void *A, cons
     return run(v, M, N, K, alpha, 0.0f, A, B, nullptr, D, stream);
 }
 
+sg_status sg_split_plan(int M, int N, int K, int splits, int capacity, sg_split_info *out)
+{
+    if (!out) return SG_ERR_NULL;
+    if (M <= 0 || N <= 0 || K <= 0 || splits < 1 || capacity < 1 || M > kMaxM || K > (1 << 21) ||
+        N > (1 << 21))
+        return SG_ERR_SHAPE;
+    const SplitPlan p = plan_split(M, N, K, splits, capacity);
+    out->tiles = p.tiles;
+    out->whole_tiles = p.dp_tiles;
+    out->cut_tiles = p.left;
+    out->splits = p.splits;
+    out->workgroups = p.grid;
+    out->workspace_bytes = p.bytes;
+    out->chosen_splits = choose_splits(M, N, K, capacity);
+    return SG_OK;
+}
+
 int gemm_fp16_tn_splitk_splits(int M, int N, int K)
 {
     if (M <= 0 || N <= 0 || K < 0 || M > kMaxM || K > (1 << 21) || N > (1 << 21)) return -1;

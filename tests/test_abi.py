@@ -17,7 +17,7 @@ S = _lib
 
 def test_every_declared_symbol_is_exported():
     declared = _lib.header_functions()
-    assert len(declared) == 20
+    assert len(declared) == 21
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
@@ -346,3 +346,40 @@ def test_missing_library_fails_loudly(monkeypatch):
     a = torch.zeros((8, 8), dtype=torch.float16)
     with pytest.raises(ValueError, match="device tensors"):
         sg.gemm(a, a)
+
+
+def test_split_plan_on_the_host():
+    # the plan gemm_fp16_tn_splitk launches, for a device of `capacity`
+    # resident workgroups, with no HIP call
+    P = _lib.sg_split_plan
+    tile = 256 * 256 * 4
+    for (M, N, K, s, cap) in [(2048, 2048, 16384, 4, 256), (6144, 6144, 4096, 4, 256),
+                              (4352, 4352, 4096, 7, 256), (300, 264, 520, 12, 256),
+                              (8192, 8192, 8192, 4, 256), (2048, 2048, 8192, 3, 32),
+                              (8000, 7936, 8200, 2, 256), (264, 8, 136, 3, 256)]:
+        p = P(M, N, K, s, cap)
+        tiles = -(-M // 256) * -(-N // 256)
+        ntile = -(-K // 64)
+        left = tiles % cap if tiles >= cap else tiles
+        eff = min(s, ntile, 16)
+        assert p.tiles == tiles
+        if left == 0 or eff <= 1:
+            assert (p.whole_tiles, p.cut_tiles, p.splits, p.workgroups, p.workspace_bytes) == \
+                (tiles, 0, 1, tiles, 0)
+        else:
+            assert (p.whole_tiles, p.cut_tiles, p.splits) == (tiles - left, left, eff)
+            assert p.workgroups == tiles - left + left * eff
+            assert p.workspace_bytes == left * eff * tile
+    # the time model's choices on a 256-CU device, for shapes it was fitted to
+    want = {(2048, 2048, 16384): 4, (2048, 2048, 8192): 4, (6144, 6144, 4096): 4,
+            (4352, 4352, 4096): 6, (2048, 2048, 2048): 1, (2048, 2048, 512): 1,
+            (3072, 3072, 4096): 1, (2560, 2560, 4096): 1, (8192, 8192, 8192): 1,
+            (8000, 7936, 8200): 1, (81920, 256, 256): 1, (4096, 4096, 128): 1}
+    for shape, s in want.items():
+        assert P(*shape, 1, 256).chosen_splits == s, shape
+    with pytest.raises(_lib.SgError):
+        P(0, 8, 8, 2, 256)
+    with pytest.raises(_lib.SgError):
+        P(8, 8, 8, 0, 256)
+    with pytest.raises(_lib.SgError):
+        P(8, 8, 8, 2, 0)
