@@ -50,9 +50,10 @@ HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-# the sources that decide which GEMM kernel runs and what it does (the
-# attention forward and the measurement probe are separate sources)
-GEMM_SOURCES = ("gemm_kernel.hpp", "persistent_kernel.hpp", "shortk_kernel.hpp", "stagegemm.hip")
+# the device code of the GEMM kernels (the attention forward, the launcher's
+# host code and the measurement probe are separate sources; which kernel a
+# workload runs is checked through the variant recorded with the traffic)
+GEMM_SOURCES = ("gemm_kernel.hpp", "persistent_kernel.hpp", "shortk_kernel.hpp")
 
 
 def kernel_source_sha() -> str:
@@ -64,15 +65,18 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str):
-    """HBM bytes per launch from profiles/traffic_<workload>.json when it was
-    measured on the current kernel source; otherwise None."""
+def load_traffic(workload: str, variant: str | None = None):
+    """Bytes leaving L2 per launch from profiles/traffic_<workload>.json when
+    it was measured on the current kernel source and (if given) on the same
+    variant; otherwise None."""
     p = os.path.join(PROFILES, f"traffic_{workload}.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
         t = json.load(f)
     if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    if variant is not None and t.get("variant") != variant:
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -402,12 +406,13 @@ def timed_mean_ms(fn, target_ms: float = 40.0, min_launches: int = 20):
     return time_launches(fn, n, n), "eager"
 
 
-def roofline_of(M: int, N: int, K: int, ms: float, workload: str | None = None) -> dict:
+def roofline_of(M: int, N: int, K: int, ms: float, workload: str | None = None,
+                variant: str | None = None) -> dict:
     """MFMA roofline above the ridge (about 315 flop/B), HBM below it, with
     the algorithmic work 2MNK flop or 2(MK + NK + MN) bytes per launch."""
     flops = 2.0 * M * N * K
     algo_bytes = 2.0 * (M * K + N * K + M * N)
-    traffic = load_traffic(workload) if workload else None
+    traffic = load_traffic(workload, variant) if workload else None
     ridge = PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     if flops / algo_bytes < ridge:
         gbs = algo_bytes / (ms / 1e3) / 1e9
@@ -459,7 +464,7 @@ def per_config(args) -> dict:
         entry = {"M": M, "N": N, "K": K, "dist": dist, "variant": vname, "launch": kind,
                  "kernel_us": round(ms * 1e3, 2),
                  "tflops": round(2.0 * M * N * K / (ms / 1e3) / 1e12, 1),
-                 "roofline": roofline_of(M, N, K, ms, name)}
+                 "roofline": roofline_of(M, N, K, ms, name, vname)}
         if not args.no_cpu_baseline:
             entry["cpu_baseline"] = (cpu_baseline_full(A, B) if M * N * K <= 1 << 26
                                      else cpu_baseline(A, B, cpu_s))
@@ -724,7 +729,8 @@ def mode_profile_summary(args) -> int:
     fn = os.path.join(PROFILES, f"gemm_tn_{short}_{w}.md")
     with open(fn, "w") as f:
         f.write(md)
-    tj = {"workload": w, "kernel": hot, "kernel_source_sha": kernel_source_sha(),
+    tj = {"workload": w, "kernel": hot, "variant": b["config"]["variant"],
+          "kernel_source_sha": kernel_source_sha(),
           "hbm_bytes_per_launch": round(fetch_b + write_b), "fetch_bytes": round(fetch_b),
           "write_bytes": round(write_b), "fetch_scale": round(scale["FETCH_SIZE"], 4),
           "write_scale": round(scale["WRITE_SIZE"], 4), "summary": os.path.basename(fn),
@@ -1141,7 +1147,7 @@ def main() -> int:
     achieved = flops / mean_launch_s / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
-                "traffic": load_traffic(args.workload), "traffic_kind": "l2_egress_bytes"}
+                "traffic": load_traffic(args.workload, vname), "traffic_kind": "l2_egress_bytes"}
     algo_bytes = 2.0 * (M * K + N * K + M * N)
     ridge = PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)          # ~315 flop/B
     if flops / algo_bytes < ridge:
@@ -1149,7 +1155,7 @@ def main() -> int:
         gbs = algo_bytes / mean_launch_s / 1e9
         roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                    "traffic": load_traffic(args.workload), "traffic_kind": "l2_egress_bytes"}
+                    "traffic": load_traffic(args.workload, vname), "traffic_kind": "l2_egress_bytes"}
 
     out = {
         "metric": METRIC,

@@ -209,3 +209,29 @@ def test_library_split_choice():
         assert sg.gemm_fp16_tn_splitk_splits(*shape) == s, shape
     assert sg.gemm_fp16_tn_splitk_splits(4352, 4352, 4096) > 1
     assert sg.gemm_fp16_tn_splitk_splits(1024, 1024, 8192) > 1
+
+
+def test_split_random_shapes_counts_and_alpha():
+    # seeded random cases: any M, N and K tail, any split count 2..16, any
+    # alpha; every element, and the allocation-free entry point's bits equal
+    # to the workspace entry point's
+    g = np.random.Generator(np.random.PCG64(5151))
+    for case in range(30):
+        M = int(g.integers(1, 1300))
+        N = 8 * int(g.integers(1, 170))
+        K = 8 * int(g.integers(1, 260))
+        s = int(g.integers(2, 17))
+        alpha = float(np.float32(g.choice([1.0, 0.5, -1.25, 1.0 / 3.0, 2.0 ** -7])))
+        A = g.uniform(-1, 1, (M, K)).astype(np.float16)
+        B = g.uniform(-1, 1, (N, K)).astype(np.float16)
+        say(f"[case] splitk random {case}: {M}x{N}x{K} splits={s} alpha={alpha}")
+        a, b = to_dev(A), to_dev(B)
+        d, _, need = split_call(a, b, M, N, K, s, alpha=alpha)
+        rep = oracle.check(d.cpu().numpy(), oracle.gemm_tn_f64(A, B, alpha), K)
+        assert rep.ok, (case, M, N, K, s, alpha, str(rep))
+        if need <= 64 << 20:
+            d2 = torch.full((M, N), float("nan"), dtype=torch.float16, device=DEV)
+            sg.gemm_fp16_tn_splitk_noalloc(M, N, K, alpha, a.data_ptr(), b.data_ptr(), d2.data_ptr(),
+                                           s, torch.cuda.current_stream().cuda_stream)
+            torch.cuda.synchronize()
+            assert torch.equal(d2.view(torch.int16), d.view(torch.int16)), case
