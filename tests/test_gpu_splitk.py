@@ -54,6 +54,7 @@ def split_call(a, b, M, N, K, splits, alpha=1.0, ws=None):
     ((300, 264, 520), (2, 5, 9, 12)),         # 9 K tiles: 9 and 12 give runs of one tile
     ((4352, 4352, 1024), (3, 7)),             # 289 tiles: 256 whole, 33 cut
     ((264, 8, 136), (3,)),                    # N = 8, K tail inside the last run
+    ((81920, 256, 256), (2, 4)),              # the tall shape: 320 tiles, 64 cut
 ])
 def test_split_runs_match_the_oracle(shape, splits):
     M, N, K = shape
@@ -235,3 +236,27 @@ def test_split_random_shapes_counts_and_alpha():
                                            s, torch.cuda.current_stream().cuda_stream)
             torch.cuda.synchronize()
             assert torch.equal(d2.view(torch.int16), d.view(torch.int16)), case
+
+
+def test_split_edge_cases():
+    # K at the documented limit 2^21 (minus a tail) cut into 16 runs of 2048
+    # K tiles: per-piece offsets and buffer ranges come closest to 2^31 here
+    M, N, K = 264, 24, (1 << 21) - 8
+    g = np.random.Generator(np.random.PCG64(903))
+    A = g.uniform(-1, 1, (M, K)).astype(np.float16)
+    B = g.uniform(-1, 1, (N, K)).astype(np.float16)
+    say(f"[case] splitk max K {M}x{N}x{K}")
+    d, _, need = split_call(to_dev(A), to_dev(B), M, N, K, 16)
+    assert need == 2 * 16 * 256 * 256 * 4
+    rep = oracle.check(d.cpu().numpy(), oracle.gemm_tn_f64(A, B), K)
+    assert rep.ok, str(rep)
+    # K = 0 through the split entry point: the empty sum, +0 for alpha < 0
+    # too, no workspace needed
+    say("[case] splitk K=0")
+    a = torch.zeros((300, 0), dtype=torch.float16, device=DEV)
+    b = torch.zeros((264, 0), dtype=torch.float16, device=DEV)
+    d = torch.full((300, 264), float("nan"), dtype=torch.float16, device=DEV)
+    sg.gemm_fp16_tn_splitk(300, 264, 0, -2.0, a.data_ptr(), b.data_ptr(), d.data_ptr(), 4, 0, 0,
+                           torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert bool((d.view(torch.int16) == 0).all())
