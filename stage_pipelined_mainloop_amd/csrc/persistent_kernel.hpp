@@ -34,7 +34,7 @@ template <class C>
 __global__ void __launch_bounds__(C::T, C::NW == 4 ? 2 : 1)
 gemm_tn_persistent_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
                           const _Float16 *Cm, _Float16 *D, int M, int N, int K, float alpha,
-                          float beta, int kt_rot)
+                          float beta)
 {
     static_assert(C::SCHED == 3, "persistent schedule");
     (void)Cm;
@@ -55,16 +55,15 @@ gemm_tn_persistent_kernel(const _Float16 *__restrict__ A, const _Float16 *__rest
     const int ntile = (K + C::BK - 1) / C::BK;
     const int total = nu * ntile;                  // K tiles in this workgroup's stream
 
-    // Output tile u of this workgroup: origin, valid rows, K-loop rotation.
-    auto geometry = [&](int u, int &m0, int &n0, int &rows_a, int &rows_b,
-                        int &kt0) __attribute__((always_inline)) {
+    // Output tile u of this workgroup: origin and valid rows.
+    auto geometry = [&](int u, int &m0, int &n0, int &rows_a,
+                        int &rows_b) __attribute__((always_inline)) {
         int tm, tn;
         tile_coords((int)blockIdx.x + u * G, tiles_m, tiles_n, tiles_m * tiles_n, tm, tn);
         m0 = tm * C::BM;
         n0 = tn * C::BN;
         rows_a = (M - m0 < C::BM) ? (M - m0) : C::BM;
         rows_b = (N - n0 < C::BN) ? (N - n0) : C::BN;
-        kt0 = (kt_rot > 1 && ntile > 0) ? (tm % kt_rot) % ntile : 0;
     };
 
     // ---- epilogue of one output tile: D = RNE16(alpha * acc), one rounding,
@@ -92,8 +91,8 @@ gemm_tn_persistent_kernel(const _Float16 *__restrict__ A, const _Float16 *__rest
     zero_acc();
     if (ntile == 0) {                              // K == 0: every output is the empty sum
         for (int u = 0; u < nu; ++u) {
-            int m0, n0, rows_a, rows_b, kt0;
-            geometry(u, m0, n0, rows_a, rows_b, kt0);
+            int m0, n0, rows_a, rows_b;
+            geometry(u, m0, n0, rows_a, rows_b);
             epilogue(m0, n0, rows_a);
         }
         return;
@@ -110,11 +109,11 @@ gemm_tn_persistent_kernel(const _Float16 *__restrict__ A, const _Float16 *__rest
     const uint32_t l_step = (uint32_t)(C::NW * ROWS_PER_LOAD) * (uint32_t)K * 2u;
 
     // Producer cursor: output tile iu, K step ik of the next group to issue.
-    int iu = 0, ik = 0, ikt0 = 0;
+    int iu = 0, ik = 0;
     __amdgpu_buffer_rsrc_t ira, irb;
     auto set_issue_tile = [&](int u) __attribute__((always_inline)) {
         int m0, n0, rows_a, rows_b;
-        geometry(u, m0, n0, rows_a, rows_b, ikt0);
+        geometry(u, m0, n0, rows_a, rows_b);
         ira = make_rsrc(A + (size_t)m0 * K, (uint32_t)rows_a * K * 2u);
         irb = make_rsrc(B + (size_t)n0 * K, (uint32_t)rows_b * K * 2u);
     };
@@ -124,9 +123,7 @@ gemm_tn_persistent_kernel(const _Float16 *__restrict__ A, const _Float16 *__rest
     // into the first 1 KiB of this wave's staging area).  The cursor is
     // advanced separately, outside the scheduling regions of the K steps.
     auto issue = [&](bool real, int slot) __attribute__((always_inline)) {
-        int kt = ik + ikt0;
-        if (kt >= ntile) kt -= ntile;
-        const int kbase = kt * C::BK;
+        const int kbase = ik * C::BK;
         const bool valid = real && l_chunk * 8 < K - kbase;
         const uint32_t v = valid ? l_base + (uint32_t)kbase * 2u : kOutOfRange;
         const uint32_t step = valid ? l_step : 0u;
@@ -261,8 +258,8 @@ gemm_tn_persistent_kernel(const _Float16 *__restrict__ A, const _Float16 *__rest
     };
 
     // Consumer side: output tile u's origin for its epilogue.
-    int cm0, cn0, crows_a, crows_b, ckt0;
-    geometry(0, cm0, cn0, crows_a, crows_b, ckt0);
+    int cm0, cn0, crows_a, crows_b;
+    geometry(0, cm0, cn0, crows_a, crows_b);
     // After the last K tile g of output tile u: the early group g + S (into
     // slot g mod S) if it exists, then the epilogue.  The epilogue writes the
     // staging area, where out-of-range loads of this output tile's first K
@@ -282,7 +279,7 @@ gemm_tn_persistent_kernel(const _Float16 *__restrict__ A, const _Float16 *__rest
         }
         epilogue(cm0, cn0, crows_a);
         zero_acc();
-        if (u + 1 < nu) geometry(u + 1, cm0, cn0, crows_a, crows_b, ckt0);
+        if (u + 1 < nu) geometry(u + 1, cm0, cn0, crows_a, crows_b);
     };
 
     int u = 0, k = 0;                              // output tile and K step of stream tile g

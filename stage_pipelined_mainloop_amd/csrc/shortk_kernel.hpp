@@ -22,12 +22,11 @@ template <class C>
 __global__ void __launch_bounds__(C::T)
 gemm_tn_shortk_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
                       const _Float16 *Cm, _Float16 *D, int M, int N, int K, float alpha,
-                      float beta, int kt_rot)
+                      float beta)
 {
     static_assert(C::SCHED == 4, "short-K schedule");
     (void)Cm;
     (void)beta;                                    // the launcher passes beta == 0 only
-    (void)kt_rot;                                  // one pass over K: nothing to rotate
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
     const int lane = threadIdx.x & 63;

@@ -22,8 +22,7 @@ static __device__ __align__(256) float scratch[256 * 256 * 256];
 namespace {
 
 typedef hipError_t (*launch_fn)(int M, int N, int K, float alpha, float beta, const void *A,
-                                const void *B, const void *Cm, void *D, int kt_rot,
-                                hipStream_t stream);
+                                const void *B, const void *Cm, void *D, hipStream_t stream);
 
 struct Variant {
     sg_config cfg;
@@ -37,7 +36,7 @@ struct Variant {
 
 // The kernel's parameter list; the argument array below must match it.
 typedef void (*gemm_kernel_fn)(const _Float16 *, const _Float16 *, const _Float16 *, _Float16 *,
-                               int, int, int, float, float, int);
+                               int, int, int, float, float);
 
 template <class C>
 constexpr gemm_kernel_fn kernel_of()
@@ -73,7 +72,7 @@ int resident_capacity(const void *k, int threads, std::atomic<int> (&cache)[16])
 
 template <class C>
 hipError_t launch(int M, int N, int K, float alpha, float beta, const void *A, const void *B,
-                  const void *Cm, void *D, int kt_rot, hipStream_t stream)
+                  const void *Cm, void *D, hipStream_t stream)
 {
     const gemm_kernel_fn kernel = kernel_of<C>();  // fails to compile on drift
     const long long tiles = (long long)((M + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
@@ -89,8 +88,8 @@ hipError_t launch(int M, int N, int K, float alpha, float beta, const void *A, c
     const _Float16 *b = static_cast<const _Float16 *>(B);
     const _Float16 *c = static_cast<const _Float16 *>(Cm);
     _Float16 *d = static_cast<_Float16 *>(D);
-    void *args[] = {&a, &b, &c, &d, &M, &N, &K, &alpha, &beta, &kt_rot};
-    static_assert(sizeof(args) / sizeof(args[0]) == 10, "one entry per kernel parameter");
+    void *args[] = {&a, &b, &c, &d, &M, &N, &K, &alpha, &beta};
+    static_assert(sizeof(args) / sizeof(args[0]) == 9, "one entry per kernel parameter");
     return hipLaunchKernel(reinterpret_cast<const void *>(kernel), dim3((unsigned)grid),
                            dim3(C::T), args, 0, stream);
 }
@@ -360,13 +359,8 @@ sg_status run(const Variant *v, int M, int N, int K, float alpha, float beta, co
     if ((v->cfg.schedule == 3 || v->cfg.schedule == 4) && beta != 0.0f) return SG_ERR_UNSUPPORTED;
     if (v->cfg.schedule == 4 && (long long)(K + v->cfg.tile_k - 1) / v->cfg.tile_k > v->cfg.stages)
         return SG_ERR_UNSUPPORTED;
-    // Rotate the K loop over 4 tile rows once the grid is more than one wave
-    // of workgroups on the 256 CUs (measured: +14% at 8192^3, -2% at 4096^3
-    // where all workgroups are resident and the operands fit in the 256 MB
-    // last-level cache).
-    const int kt_rot = (tiles > 256) ? 4 : 1;
     const hipError_t e = v->launch(M, N, K, alpha, beta, A, B, beta == 0.0f ? nullptr : Cm, D,
-                                   kt_rot, static_cast<hipStream_t>(stream));
+                                   static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SG_OK : SG_ERR_HIP;
 }
 
@@ -379,10 +373,7 @@ sg_status launch_split(const SplitPlan &p, int M, int N, int K, float alpha, con
     float *part = static_cast<float *>(workspace);
     int dp = p.dp_tiles, splits = p.splits;
     const hipStream_t st = static_cast<hipStream_t>(stream);
-    // the whole-tile part keeps the tiled kernel's K rotation when it spans
-    // more than one round
-    int kt_rot = dp > 256 ? 4 : 1;
-    void *args[] = {&a, &b, &d, &M, &N, &K, &alpha, &kt_rot, &part, &dp, &splits};
+    void *args[] = {&a, &b, &d, &M, &N, &K, &alpha, &part, &dp, &splits};
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&sg::gemm_tn_split_kernel<SplitCfg>),
                                    dim3((unsigned)p.grid), dim3(SplitCfg::T), args, 0, st);
     if (e != hipSuccess) return SG_ERR_HIP;

@@ -144,12 +144,12 @@ def test_tiny_shape_grid(cfg):
                                        ((4352, 4360, 336), (256, 256, 64, 2, 8, 2)),
                                        ((4352, 4360, 336), (128, 128, 32, 3, 4, 3)),
                                        ((4352, 4360, 200), (128, 128, 64, 2, 4, 3))])
-def test_rotated_k_loop_with_k_tail(shape, cfg):
-    # more than 256 workgroups, so each tile row starts its K loop at a
-    # rotated tile and the K-tail tile lands mid-sequence
+def test_k_tail_on_grids_of_several_rounds(shape, cfg):
+    # more than 256 workgroups (several rounds per CU, M and N tails) with a
+    # ragged last K tile in every workgroup's loop
     M, N, K = shape
     A, B = inputs.operands(M, N, K, 500 + K)
-    full_check(A, B, config=cfg, label=f"rotated {shape}")
+    full_check(A, B, config=cfg, label=f"several rounds {shape}")
 
 
 PERSISTENT = [c for c in VARIANTS if c[5] == 3]
