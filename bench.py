@@ -236,6 +236,56 @@ def mode_variants(args) -> int:
     return 0
 
 
+def mode_vendor_blas(args) -> int:
+    """Reference point, not part of the library: this GEMM against the ROCm
+    BLAS that torch.matmul dispatches to (hipBLASLt) on the same operands and
+    stream, interleaved (7 alternating rounds of --steps launches after
+    --warmup of each).  One JSON line per workload: median microseconds and
+    TFLOP/s of each, their ratio, and the largest |difference| of the two
+    fp16 results (different summation orders)."""
+    import statistics
+
+    import torch
+
+    import stage_pipelined_mainloop_amd as sg
+    from stage_pipelined_mainloop_amd import inputs
+    for w in args.workload.split(","):
+        M, N, K, dist, seed = inputs.WORKLOADS[w]
+        A, B = inputs.workload(w)
+        a = torch.from_numpy(A).cuda()
+        b = torch.from_numpy(B).cuda()
+        bt = b.t()
+        d_sg = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        calls = {"stagegemm": lambda: sg.gemm(a, b, out=d_sg),
+                 "rocm_blas": lambda: torch.matmul(a, bt)}
+        st = torch.cuda.current_stream()
+        for f in calls.values():
+            for _ in range(args.warmup):
+                f()
+        res = {n: [] for n in calls}
+        for rnd in range(7):
+            order = list(calls) if rnd % 2 == 0 else list(calls)[::-1]
+            for n in order:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                e0.record(st)
+                for _ in range(args.steps):
+                    calls[n]()
+                e1.record(st)
+                torch.cuda.synchronize()
+                res[n].append(e0.elapsed_time(e1) * 1e3 / args.steps)
+        us = {n: statistics.median(v) for n, v in res.items()}
+        tf = {n: 2.0 * M * N * K / (u * 1e-6) / 1e12 for n, u in us.items()}
+        diff = float((calls["stagegemm"]().float() - calls["rocm_blas"]().float()).abs().max())
+        print(json.dumps({"mode": "vendor_blas", "workload": w, "shape": [M, N, K],
+                          "us": {n: round(u, 2) for n, u in us.items()},
+                          "tflops": {n: round(t, 1) for n, t in tf.items()},
+                          "stagegemm_over_rocm_blas": round(tf["stagegemm"] / tf["rocm_blas"], 4),
+                          "max_abs_diff": diff, "rounds": 7, "launches_per_round": args.steps}),
+              flush=True)
+    return 0
+
+
 def mode_ksweep(args) -> int:
     """M = N = 2048, K in the sweep list: the library's choice (split-K when
     it picks it), then every compiled stage count of the 128x128 (4 waves)
@@ -680,6 +730,18 @@ def mode_profile_summary(args) -> int:
     flops = 2.0 * M * N * K
     algo = 2.0 * (M * K + N * K + M * N)
     roof = roofline_of(M, N, K, mean_ns / 1e6)
+    # The bench's own timing of this workload: from a default bench.py run
+    # made without the profiler (--bench-log), else from the traced run.
+    # (Under the kernel tracer, events around a replayed HIP graph do not
+    # bracket its kernels, so a graph-launched workload needs the former.)
+    events_us, events_src = b["config"]["kernel_ms_mean"] * 1e3, "the traced run"
+    if args.bench_log:
+        with open(args.bench_log) as f:
+            bl = json.loads([ln for ln in f if ln.startswith("{")][-1])
+        if bl["config"]["workload"] == w:
+            events_us, events_src = bl["config"]["kernel_ms_mean"] * 1e3, "a bench.py run without the profiler"
+        elif w in bl.get("per_config", {}):
+            events_us, events_src = bl["per_config"][w]["kernel_us"], "a bench.py run without the profiler"
     short = hot.split("Cfg")[1].split("EEE")[0].replace("ILi", "").replace("ELi", "_").replace("E", "")
     family = hot.split("2sg")[1].split("INS_")[0].lstrip("0123456789")
     util = sq["SQ_VALU_MFMA_BUSY_CYCLES"] / (4 * sq["SQ_BUSY_CU_CYCLES"])
@@ -697,9 +759,10 @@ def mode_profile_summary(args) -> int:
         "| Dispatches in trace | Timed window | Mean over window (us) | Roofline at that mean | bench.py events (us) | trace / events |",
         "|---|---|---|---|---|---|",
         f"| {len(seq)} | {win['first']}..{win['first'] + win['count'] - 1} | {mean_ns / 1e3:.2f} | "
-        f"{roof['achieved']} {roof['unit']}, frac {roof['frac']} | {b['config']['kernel_ms_mean'] * 1e3:.2f} | "
-        f"{mean_ns / 1e3 / (b['config']['kernel_ms_mean'] * 1e3):.4f} |", "",
-        f"Launches: {b['config'].get('launch', 'eager')}; variant {b['config']['variant']}.", "",
+        f"{roof['achieved']} {roof['unit']}, frac {roof['frac']} | {events_us:.2f} | "
+        f"{mean_ns / 1e3 / events_us:.4f} |", "",
+        f"Launches: {b['config'].get('launch', 'eager')}; variant {b['config']['variant']}. "
+        f"bench.py events: the mean per launch from {events_src}.", "",
         "## Bytes leaving L2 (two --pmc passes, scaled by a plain copy)", "",
         f"Commands: `rocprofv3 --pmc FETCH_SIZE --output-format csv -- {P}` and the same with `WRITE_SIZE`; "
         "calibration: `rocprofv3 --pmc FETCH_SIZE -- python bench.py --mode calibrate_copy --steps 3 --warmup 1` "
@@ -1003,7 +1066,7 @@ def main() -> int:
     ap.add_argument("--mode", default="bench",
                     choices=["bench", "variants", "ksweep", "calibrate_copy", "attention",
                              "trace_summary", "stage_model", "profile_summary", "ksweep_summary",
-                             "lds_patterns", "lds_summary", "variants_summary"])
+                             "lds_patterns", "lds_summary", "variants_summary", "vendor_blas"])
     ap.add_argument("--trace", default=None, help="kernel-trace CSV for --mode trace_summary")
     ap.add_argument("--bench-log", default=None, help="that run's output for --mode trace_summary")
     ap.add_argument("--prof-dir", default=None,
@@ -1054,6 +1117,8 @@ def main() -> int:
         return mode_variants_summary(args)
     if args.mode == "variants":
         return mode_variants(args)
+    if args.mode == "vendor_blas":
+        return mode_vendor_blas(args)
     if args.mode == "ksweep":
         return mode_ksweep(args)
     if args.mode == "calibrate_copy":
