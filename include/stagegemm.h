@@ -91,7 +91,16 @@ typedef enum sg_status {
  *      fragment-read phase.  A keeps stages - 1 ring slots and B keeps
  *      `stages` (stages = 3: 64 + 96 KiB for 256 x 256 x 64 tiles), which
  *      gives the second group's loads two phases to land.  The library's
- *      choice for 256 x 256 tiles. */
+ *      choice for 256 x 256 tiles when rows of A or B straddle 128-byte
+ *      lines (K % 64 != 0, or a base address not 128-byte aligned);
+ *  10  one wave per SIMD ("cute(9) multistage_gemm", section 6, with the
+ *      two-slot ring of "Lesson 6", section 4): 4 waves of 128 x 128 each,
+ *      64-deep K tiles in two 64 KiB slots, one barrier per tile between
+ *      its two 32-deep halves; the second half's fragment reads and the
+ *      LDS-DMA of tile k + 2 into the slot just freed overlap its MFMAs.
+ *      Only 256 x 256 x 64, stages 2, waves 4.  The library's choice for
+ *      256 x 256 tiles when every row of A and B starts on a 128-byte line
+ *      (K % 64 == 0 and 128-byte aligned A and B). */
 typedef struct sg_config {
     int tile_m;
     int tile_n;
@@ -222,7 +231,8 @@ sg_status gemm_fp16_tn_cfg(int M, int N, int K, float alpha, const void *A,
                            void *stream);
 
 /* The variant gemm_fp16_tn (and gemm_fp16_tn_alpha) would run for this
- * shape (no pointers needed).  gemm_fp16_tn_alpha_beta with beta != 0 runs
+ * shape with 128-byte aligned A and B (a less aligned A or B turns
+ * schedule 10 into schedule 8).  gemm_fp16_tn_alpha_beta with beta != 0 runs
  * the same variant unless it is persistent (schedule 3) or short-K
  * (schedule 4), which take no C operand: the choice is then made among the
  * tiled variants only, by the same cost model. */

@@ -664,8 +664,9 @@ def schedule_split_pingpong(ntile: int, loads: int, a_slots: int = 2, b_slots: i
                             a_ahead: int = 1, b_ahead: int = 2, g0_keep: int = 0,
                             g1_keep: int | None = None):
     """The ping-pong with the loads split between the groups: G0 loads A
-    tiles only, G1 B tiles only, `loads` per wave per tile, each after its
-    fragment reads.  A tile j lives in slot j mod a_slots, B tile j in slot
+    tiles only, G1 B tiles only, `loads` per wave per tile, each in its
+    fragment-read phase (the order of issues and reads within a phase does
+    not matter here: no slot is read and refilled in the same phase).  A tile j lives in slot j mod a_slots, B tile j in slot
     j mod b_slots.  Phase 2j: G0 reads tile j, issues A(j + a_ahead); G1
     computes tile j-1.  Phase 2j+1: G0 computes tile j and waits until at
     most g0_keep loads remain; G1 reads tile j, issues B(j + b_ahead) and

@@ -40,27 +40,30 @@ def probe_sources() -> list[str]:
     return [os.path.join(CSRC, "mfma_ceiling.hip")]
 
 
-def check_m0_confined() -> int:
-    """The attention kernels issue their LDS-DMA through inline assembly that
-    writes m0 (the LDS address register of the instruction) and lists it as
-    clobbered.  The compiler does not preserve a reserved register across
-    such a statement, so the DMA is safe only while no compiler-generated code
-    in that translation unit uses m0.  Compile it to assembly and check that
-    every m0 operand lies inside an inline-assembly region; raise otherwise
-    (for instance after a compiler update).  Returns the number of m0
-    operands found, all inside the DMA statements."""
+def _device_asm(source: str) -> str:
+    """Compile one source to gfx950 assembly under build/ and return its path."""
     out_dir = os.path.join(ROOT, "build")
     os.makedirs(out_dir, exist_ok=True)
-    asm = os.path.join(out_dir, "attention.s")
+    asm = os.path.join(out_dir, os.path.splitext(os.path.basename(source))[0] + ".s")
     cmd = [HIPCC, *[f for f in FLAGS if f not in ("-shared", "-fPIC")], "--cuda-device-only",
-           "-S", "-I", INCLUDE, "-I", CSRC, os.path.join(CSRC, "attention.hip"), "-o", asm]
+           "-S", "-I", INCLUDE, "-I", CSRC, source, "-o", asm]
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
         sys.stderr.write(p.stdout + p.stderr)
-        raise RuntimeError("hipcc failed compiling attention.hip to assembly")
-    inside, found, stray = False, 0, []
+        raise RuntimeError(f"hipcc failed compiling {os.path.basename(source)} to assembly")
+    return asm
+
+
+def m0_uses(asm: str, function=None) -> tuple[int, list[str]]:
+    """m0 operands in a compiled assembly file, within the functions whose
+    symbol `function(name)` accepts (every function when None): the count
+    inside inline-assembly regions and the lines outside them."""
+    inside, take, found, stray = False, function is None, 0, []
     with open(asm) as f:
         for n, line in enumerate(f, 1):
+            head = None if inside else re.match(r"^([A-Za-z_.$][\w.$]*):", line)
+            if head and not head.group(1).startswith("."):      # a function's symbol
+                take = function is None or function(head.group(1))
             if ";;#ASMSTART" in line:
                 inside = True
                 continue
@@ -68,18 +71,40 @@ def check_m0_confined() -> int:
                 inside = False
                 continue
             code = line.split(";", 1)[0]
-            if re.search(r"\bm0\b", code):
+            if take and re.search(r"\bm0\b", code):
                 if inside:
                     found += 1
                 else:
                     stray.append(f"{n}: {line.strip()}")
-    if stray:
-        raise RuntimeError("compiler-generated code uses m0 in attention.hip, which the inline "
-                           "LDS-DMA clobbers:\n" + "\n".join(stray[:20]))
-    if found == 0:
-        raise RuntimeError("no m0 operand found in the attention DMA statements: the check "
-                           "no longer sees them")
-    return found
+    return found, stray
+
+
+def check_m0_confined() -> int:
+    """The attention kernels and the schedule-10 GEMM mainloop issue their
+    LDS-DMA through inline assembly that writes m0 (the LDS address register
+    of the instruction) and lists it as clobbered.  The compiler does not
+    preserve a reserved register across such a statement, so the DMA is safe
+    only while no compiler-generated code in those functions uses m0: all of
+    attention.hip, and in stagegemm.hip the kernels instantiated for schedule
+    10 (the other GEMM kernels load through the compiler's own LDS-DMA
+    builtin, which sets m0 itself).  Compile both to assembly and check that
+    every m0 operand there lies inside an inline-assembly region; raise
+    otherwise (for instance after a compiler update).  Returns the number of
+    m0 operands found, all inside the DMA statements."""
+    total = 0
+    checks = [("attention.hip", None),
+              # Cfg<256, 256, 64, 2, 2, 2, 10>: the template's last argument mangles as Li10EE
+              ("stagegemm.hip", lambda name: "Li10EE" in name)]
+    for src, function in checks:
+        found, stray = m0_uses(_device_asm(os.path.join(CSRC, src)), function)
+        if stray:
+            raise RuntimeError(f"compiler-generated code uses m0 in {src}, which the inline "
+                               "LDS-DMA clobbers:\n" + "\n".join(stray[:20]))
+        if found == 0:
+            raise RuntimeError(f"no m0 operand found in the DMA statements of {src}: the check "
+                               "no longer sees them")
+        total += found
+    return total
 
 
 def build(verbose: bool = False) -> str:

@@ -30,7 +30,6 @@
 
 namespace sg {
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <int NWAVES>
@@ -59,14 +58,6 @@ __device__ __forceinline__ int k_chunk(int r, int c) { return c ^ (r & 15); }
 // of 4 apart) and 4 chunks 4 q .. 4 q + 3, which this places in 16 distinct
 // 16-byte bank groups.
 __device__ __forceinline__ int v_chunk(int r, int c) { return c ^ ((r & 3) << 2); }
-
-// Buffer resource words for `bytes` bytes from `base` (stride 0): reads past
-// the range return zero.
-__device__ __forceinline__ u32x4 rsrc_words(const void *base, uint32_t bytes)
-{
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, (uint32_t)kRsrcWord3};
-}
 
 // LDS-DMA of 16 bytes per lane to the wave's 1 KiB at LDS address `lds`
 // (lane l fills bytes 16 l .. 16 l + 15), issued through inline assembly.

@@ -64,6 +64,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // gfx9 buffer resource word 3 (raw 32-bit data format, no swizzle).
 constexpr int kRsrcWord3 = 0x00020000;
@@ -154,7 +155,9 @@ __device__ __forceinline__ int swz(int r)
 // wave groups (one computes while the other reads and refills), 3 =
 // persistent, 4 = short K, 5 = order 1 on 16x16x32 MFMAs, 7 = order 2 on
 // 16x16x32 MFMAs, 8 = order 7 with the LDS-DMA loads split between the two
-// wave groups (A ring of S - 1 slots, B ring of S; "order 8" below).
+// wave groups (A ring of S - 1 slots, B ring of S; "order 8" below), 10 = one
+// wave per SIMD with a 128x128 tile each, its whole mainloop one scheduled
+// inline-assembly statement ("order 10" below).
 //
 // MFMA shape.  Schedules 0-4 use v_mfma_f32_32x32x16_f16 (32x32 blocks, K
 // steps of 16); schedules 5, 7 and 8 use v_mfma_f32_16x16x32_f16 (16x16
@@ -175,7 +178,7 @@ template <int BM_, int BN_, int BK_, int S_, int WM_, int WN_, int SCHED_ = 1>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_, WM = WM_, WN = WN_;
     static constexpr int SCHED = SCHED_;
-    static constexpr bool MF16 = SCHED == 5 || SCHED == 7 || SCHED == 8;   // 16x16x32 MFMAs
+    static constexpr bool MF16 = SCHED == 5 || SCHED == 7 || SCHED == 8 || SCHED == 10;   // 16x16x32 MFMAs
     static constexpr int ORDER = SCHED == 5 ? 1 : SCHED == 7 ? 2 : SCHED;   // mainloop order
     static constexpr int NW = WM * WN;              // wavefronts
     static constexpr int T = 64 * NW;               // threads
@@ -217,7 +220,7 @@ struct Cfg {
     static constexpr int NB = BN * CPR / (64 * NW);
     static constexpr int L = NA + NB;
     static_assert(S >= 2, "a ring needs at least two slots");
-    static_assert(SCHED >= 0 && SCHED <= 8 && SCHED != 6, "mainloop order");
+    static_assert(SCHED >= 0 && SCHED <= 10 && SCHED != 6 && SCHED != 9, "mainloop order");
     static_assert(!MF16 || BK == 64, "16x16x32 order: two K steps of 32 per tile");
     static_assert(SCHED != 3 || S == 2 || S == 3, "persistent ring: two or three slots");
     static_assert(!OWN_STAGING || WTN == 64, "unpadded staging rows are 128 bytes");
@@ -226,6 +229,8 @@ struct Cfg {
     static_assert(ORDER != 8 || (S == 3 && NW % 4 == 0 && (NW / 2) % 2 == 0 && BK == 64 && BM == BN),
                   "split-load ping-pong: A ring of two slots, B ring of three, square tiles");
     static_assert(NKS % 2 == 0, "fragment double buffer alternates per K step");
+    static_assert(ORDER != 10 || (BM == 256 && BN == 256 && BK == 64 && S == 2 && WM == 2 && WN == 2),
+                  "one-wave form: 256x256x64 tiles, two slots, 2x2 waves of 128x128");
     static_assert(BK == 32 || BK == 64, "BK");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile is whole 32x32 blocks");
     static_assert(NA * 64 * NW == BM * CPR && NB * 64 * NW == BN * CPR, "even load split");
@@ -236,10 +241,19 @@ struct Cfg {
     static_assert((WTN * 2) % 16 == 0 && 64 % ((WTN * 2) / 16) == 0, "epilogue row chunks");
 };
 
+// Buffer resource for `bytes` bytes from `base` (stride 0): reads past the
+// range return zero and stores past it are dropped.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
                                              kRsrcWord3);
+}
+
+// The same resource as plain words, for inline assembly (an SGPR quad).
+__device__ __forceinline__ u32x4 rsrc_words(const void *base, uint32_t bytes)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, (uint32_t)kRsrcWord3};
 }
 
 // Compiler-level fence: no memory access moves across it (emits nothing).
@@ -545,7 +559,7 @@ __device__ __forceinline__ void gemm_tn_body(const _Float16 *__restrict__ A,
     };
 
     // ---- prologue: tiles 0 .. S-2 (order 8 has a prologue of its own)
-    if constexpr (C::ORDER != 8) {
+    if constexpr (C::ORDER != 8 && C::ORDER != 10) {
 #pragma unroll
         for (int t = 0; t < C::S - 1; ++t)
             if (t < ntile) issue(t, t);
@@ -657,6 +671,40 @@ __device__ __forceinline__ void gemm_tn_body(const _Float16 *__restrict__ A,
             barrier();
         }
         if (grp == 0) barrier();                   // G0 idles in the last phase
+    } else if constexpr (C::ORDER == 10) {
+        // ---- One wave per SIMD, 128x128 of the tile each, 64-deep K tiles in
+        // two LDS slots, one barrier per K tile between its two 32-deep halves:
+        // the ring protocol of "cute(9) multistage_gemm" (section 6) with the
+        // minimum ring of "Lesson 6" (section 4, S = 2: a tile's copy takes
+        // about as long as its MFMAs).  With a single wave per SIMD nothing else
+        // hides an instruction that is not an MFMA, so the loop is one
+        // inline-assembly statement in which every fragment read, LDS-DMA load
+        // and address update sits between two MFMAs (onewave_mainloop.inc,
+        // written by gen_onewave_mainloop.py, which gives the schedule, the
+        // wait counts and the hazards it covers).  The accumulators stay in
+        // the 256 AGPRs, which leaves the 256 VGPRs to two fragment buffers of
+        // a 32-deep step each.  Tile t's loads use the same lane-to-LDS
+        // mapping and K-tail handling as `issue` above, computed in the loop.
+        static_assert(C::AM == 8 && C::AN == 8 && C::NKS == 2 && C::NA == 8 && C::NB == 8,
+                      "the assembly is written for 8x8 MFMA blocks and 8 + 8 loads per wave");
+        static_assert(C::STAGE_BYTES == 65536 && C::A_BYTES == 32768, "slot layout of the assembly");
+        const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(
+            (__attribute__((address_space(3))) char *)smem);
+        const u32x4 rwa = rsrc_words(A + (size_t)m0 * K, (uint32_t)rows_a * K * 2u);
+        const u32x4 rwb = rsrc_words(B + (size_t)n0 * K, (uint32_t)rows_b * K * 2u);
+        // this lane's first fragment of each slot and K step (fb holds + A_BYTES)
+        const uint32_t rA00 = lds0 + fa[0], rA01 = lds0 + fa[1];
+        const uint32_t rA10 = rA00 + (uint32_t)C::STAGE_BYTES, rA11 = rA01 + (uint32_t)C::STAGE_BYTES;
+        const uint32_t rB00 = lds0 + fb[0], rB01 = lds0 + fb[1];
+        const uint32_t rB10 = rB00 + (uint32_t)C::STAGE_BYTES, rB11 = rB01 + (uint32_t)C::STAGE_BYTES;
+        const uint32_t lbase = l_base, lch8 = (uint32_t)(l_chunk * 8), lstep = l_step;
+        const uint32_t oor = kOutOfRange;
+        const uint32_t wb = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)wave * 1024u);
+        const uint32_t ow_nk = __builtin_amdgcn_readfirstlane(nk);
+        const uint32_t ow_kk = __builtin_amdgcn_readfirstlane(K);
+        f16x8 xa[8], xb[8], ya[8], yb[8];
+        uint32_t o0, o1, o2, o3, o4, o5, o6, o7, vs, sk, st, se;
+#include "onewave_mainloop.inc"
     } else if constexpr (C::ORDER == 8) {
         // ---- Ping-pong with the loads split between the groups.  The phases
         // are those of order 2, but G0 loads only A tiles and G1 only B

@@ -138,6 +138,9 @@ const Variant kVariants[] = {
     // loads split between the groups (schedule 8: A ring of 2, B ring of 3)
     variant<sg::Cfg<256, 256, 64, 2, 2, 4, 7>>(),
     variant<sg::Cfg<256, 256, 64, 3, 2, 4, 8>>(),
+    // one wave per SIMD, 128x128 each, the mainloop as scheduled assembly
+    // (schedule 10: two 64 KiB slots)
+    variant<sg::Cfg<256, 256, 64, 2, 2, 2, 10>>(),
     // whole K extent in the ring, epilogue per row block (schedule 4, K <= S * BK)
     variant<sg::Cfg<128, 128, 64, 2, 2, 2, 4>>(),
     // persistent workgroups, one ring across output tiles (schedule 3)
@@ -166,7 +169,7 @@ const Variant *find_variant(const sg_config *c)
 // the tiled 256x256 kernel; 2048 x 2048 x 128: 4.8 against 5.1 us for
 // 128x128 S3).  Otherwise the cheapest of these, in units of
 // one full round of 256 workgroups of the 256x256 kernel:
-//   256x256x64, schedule 8 (one workgroup per CU)    1.00 per round of 256
+//   256x256x64, schedule 8 or 10 (one per CU)        1.00 per round of 256
 //   128x128x64 S2, schedule 1 (two per CU)           0.66 per round of 512
 //   128x128x64 S3, schedule 1 (one per CU)           0.42 per round of 256
 //   128x128x64 S2 persistent (K <= 1024, no C)       0.9 x the S2 figure
@@ -177,6 +180,20 @@ const Variant *find_variant(const sg_config *c)
 // and at K = 1024 and 512 it is within 2 % of the best choice.  The
 // persistent factor comes from the tall shape 81920 x 256 x 256 (21.3 us
 // against 23.7 tiled and 25.1 for 256x256 tiles).
+// Within the 256x256 family, schedule 10 (one wave per SIMD) when every row
+// of A and B starts on a 128-byte line (K % 64 == 0 and 128-byte aligned
+// operands), else schedule 8.  Schedule 10 was 1-4 % faster at 8192^3,
+// 4096^3, 12288^2 x 4096, 6144^2 x 4096, 5120^2 x 8192, 8000^2 x 8192 and
+// 16384 x 1024 x 4096, and 6-7 % slower when the rows straddle lines
+// (K = 8200): with two ring slots its loads have less time to land, and a
+// row that straddles lines costs two line fetches per 128 bytes.
+
+// Whether A and B start on 128-byte lines (with K % 64 == 0, every row does).
+bool lines_aligned(const void *A, const void *B)
+{
+    return ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & 127) == 0;
+}
+
 double rounds(long long tiles, long long per_round)
 {
     const long long full = tiles / per_round;
@@ -186,7 +203,8 @@ double rounds(long long tiles, long long per_round)
 
 // The library's choice and its cost in rounds of the 256x256 kernel (0 for
 // the short-K schedule, which the split form never competes with).
-const Variant *select_variant(int M, int N, int K, bool with_c, double *cost = nullptr)
+const Variant *select_variant(int M, int N, int K, bool with_c, double *cost = nullptr,
+                              bool lines_aligned = true)
 {
     const long long t256 = (long long)((M + 255) / 256) * ((N + 255) / 256);
     const long long t128 = (long long)((M + 127) / 128) * ((N + 127) / 128);
@@ -200,7 +218,8 @@ const Variant *select_variant(int M, int N, int K, bool with_c, double *cost = n
         const double c3 = 0.42 * rounds(t128, 256);
         const bool persistent = K <= 1024 && !with_c && t128 > 256;
         const double cp = persistent ? 0.9 * c2 : 1e300;
-        c = sg_config{256, 256, 64, 3, 8, 8};
+        c = (lines_aligned && K % 64 == 0) ? sg_config{256, 256, 64, 2, 4, 10}
+                                           : sg_config{256, 256, 64, 3, 8, 8};
         best = c256;
         if (c3 < best) { best = c3; c = sg_config{128, 128, 64, 3, 4, 1}; }
         if (c2 < best) { best = c2; c = sg_config{128, 128, 64, 2, 4, 1}; }
@@ -411,7 +430,7 @@ sg_status gemm_fp16_tn_alpha(int M, int N, int K, float alpha, const void *A, co
 {
     const sg_status st = validate(M, N, K, A, B, D);
     if (st != SG_OK || M == 0 || N == 0) return st;
-    const Variant *v = select_variant(M, N, K, false);
+    const Variant *v = select_variant(M, N, K, false, nullptr, lines_aligned(A, B));
     if (!v) return SG_ERR_UNSUPPORTED;
     return run(v, M, N, K, alpha, 0.0f, A, B, nullptr, D, stream);
 }
@@ -423,7 +442,7 @@ sg_status gemm_fp16_tn_alpha_beta(int M, int N, int K, float alpha, float beta, 
     if (st != SG_OK) return st;
     st = validate_c(M, N, beta, Cm, D);
     if (st != SG_OK || M == 0 || N == 0) return st;
-    const Variant *v = select_variant(M, N, K, beta != 0.0f);
+    const Variant *v = select_variant(M, N, K, beta != 0.0f, nullptr, lines_aligned(A, B));
     if (!v) return SG_ERR_UNSUPPORTED;
     return run(v, M, N, K, alpha, beta, A, B, Cm, D, stream);
 }

@@ -284,15 +284,18 @@ def test_selection_returns_compiled_variants():
                   (8192, 8192, 8192), (8000, 7936, 8200), (1, 8, 8), (81920, 256, 256)]:
         c = _lib.sg_select_config(*shape)
         assert c.as_tuple() in {x.as_tuple() for x in _lib.configs()}
-    # the measured choices: big squares tiled 256x256x64, the skinny tall
+    # the measured choices: big squares tiled 256x256x64 (one wave per SIMD
+    # when K % 64 == 0, else the split-load ping-pong), the skinny tall
     # shape persistent 128x128x64, the one-wave sweep grid 128x128x64 S3
-    assert _lib.sg_select_config(8192, 8192, 8192).as_tuple() == (256, 256, 64, 3, 8, 8)
+    assert _lib.sg_select_config(8192, 8192, 8192).as_tuple() == (256, 256, 64, 2, 4, 10)
+    assert _lib.sg_select_config(8000, 7936, 8200).as_tuple() == (256, 256, 64, 3, 8, 8)
+    assert _lib.sg_select_config(8192, 8192, 8200).as_tuple() == (256, 256, 64, 3, 8, 8)
     assert _lib.sg_select_config(81920, 256, 256).as_tuple() == (128, 128, 64, 2, 4, 3)
     assert _lib.sg_select_config(2048, 2048, 2048).as_tuple() == (128, 128, 64, 3, 4, 1)
-    assert _lib.sg_select_config(81920, 256, 4096).as_tuple() == (256, 256, 64, 3, 8, 8)
+    assert _lib.sg_select_config(81920, 256, 4096).as_tuple() == (256, 256, 64, 2, 4, 10)
     assert _lib.sg_select_config(2560, 2560, 4096).as_tuple() == (128, 128, 64, 2, 4, 1)
-    assert _lib.sg_select_config(3072, 3072, 4096).as_tuple() == (256, 256, 64, 3, 8, 8)
-    assert _lib.sg_select_config(6144, 6144, 4096).as_tuple() == (256, 256, 64, 3, 8, 8)
+    assert _lib.sg_select_config(3072, 3072, 4096).as_tuple() == (256, 256, 64, 2, 4, 10)
+    assert _lib.sg_select_config(6144, 6144, 4096).as_tuple() == (256, 256, 64, 2, 4, 10)
     assert _lib.sg_select_config(4096, 4096, 128).as_tuple() == (128, 128, 64, 2, 4, 4)
     assert _lib.sg_select_config(2048, 2048, 128).as_tuple() == (128, 128, 64, 2, 4, 4)
     assert _lib.sg_select_config(2048, 2048, 512).as_tuple() == (128, 128, 64, 3, 4, 1)

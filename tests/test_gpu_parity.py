@@ -118,7 +118,8 @@ def test_every_variant_on_ragged_shapes(shape):
                                  (128, 128, 64, 3, 4, 1), (256, 256, 64, 2, 8, 2),
                                  (128, 128, 64, 2, 4, 3), (256, 256, 64, 2, 8, 3),
                                  (128, 128, 64, 2, 4, 4), (256, 256, 64, 2, 8, 5),
-                                 (256, 256, 64, 2, 8, 7), (256, 256, 64, 3, 8, 8)])
+                                 (256, 256, 64, 2, 8, 7), (256, 256, 64, 3, 8, 8),
+                                 (256, 256, 64, 2, 4, 10)])
 def test_tiny_shape_grid(cfg):
     # every M, N and K tail against every tile boundary of the variant
     say(f"[case] tiny grid cfg={cfg}")
@@ -139,6 +140,8 @@ def test_tiny_shape_grid(cfg):
                                        ((4352, 4104, 200), (256, 256, 64, 2, 8, 1)),
                                        ((4352, 4104, 200), (256, 256, 64, 2, 8, 7)),
                                        ((4352, 4104, 200), (256, 256, 64, 3, 8, 8)),
+                                       ((4352, 4104, 200), (256, 256, 64, 2, 4, 10)),
+                                       ((4352, 4360, 4104), (256, 256, 64, 2, 4, 10)),
                                        ((2304, 2304, 520), (128, 128, 32, 4, 4, 1)),
                                        ((2304, 2312, 1000), (256, 256, 32, 3, 8, 0)),
                                        ((4352, 4360, 336), (256, 256, 64, 2, 8, 2)),
@@ -150,6 +153,33 @@ def test_k_tail_on_grids_of_several_rounds(shape, cfg):
     M, N, K = shape
     A, B = inputs.operands(M, N, K, 500 + K)
     full_check(A, B, config=cfg, label=f"several rounds {shape}")
+
+
+def test_operand_line_alignment_selects_schedule():
+    # with K % 64 == 0 the library runs the one-wave schedule (10) when A
+    # and B start on 128-byte lines and the split-load ping-pong (8) when A
+    # starts 16 bytes past one; both are compared with the oracle element
+    # by element, and with each other bit for bit (same MFMA, same K order)
+    M, N, K = 4104, 4096, 1088
+    A, B = inputs.operands(M, N, K, 4096 + 11)
+    ref = oracle.gemm_tn_f64(A, B)
+    a, b = to_dev(A), to_dev(B)
+    assert a.data_ptr() % 128 == 0 and b.data_ptr() % 128 == 0
+    flat = torch.empty(M * K + 64, dtype=torch.float16, device=DEV)
+    a16 = flat[8:8 + M * K].view(M, K)
+    a16.copy_(a)
+    assert a16.data_ptr() % 128 == 16
+    outs = []
+    for x, label in ((a, "lines"), (a16, "16 bytes past a line")):
+        say(f"[case] alignment {label} {M}x{N}x{K}")
+        d = torch.full((M, N), float("nan"), dtype=torch.float16, device=DEV)
+        sg.gemm(x, b, out=d)
+        torch.cuda.synchronize()
+        rep = oracle.check(d.cpu().numpy(), ref, K)
+        assert rep.ok, (label, str(rep))
+        outs.append(d)
+    assert torch.equal(outs[0], outs[1])
+    assert sg._lib.sg_select_config(M, N, K).as_tuple() == (256, 256, 64, 2, 4, 10)
 
 
 PERSISTENT = [c for c in VARIANTS if c[5] == 3]
@@ -176,7 +206,8 @@ def test_persistent_workgroups_loop_over_tiles(shape):
 
 @pytest.mark.parametrize("alpha", [None, -1.0, -0.375])
 @pytest.mark.parametrize("cfg", [None] + PERSISTENT[:2] + SHORTK +
-                         [(256, 256, 64, 2, 8, 7), (256, 256, 64, 3, 8, 8)])
+                         [(256, 256, 64, 2, 8, 7), (256, 256, 64, 3, 8, 8),
+                          (256, 256, 64, 2, 4, 10)])
 def test_k_zero_every_schedule(cfg, alpha):
     # the empty sum is +0 (bit pattern 0) for either sign of alpha
     say(f"[case] K=0 {cfg} alpha={alpha}")
@@ -213,7 +244,8 @@ def test_zero_sums_are_plus_zero_every_variant(alpha):
 
 @pytest.mark.parametrize("shape,cfg", [((40, 16, 1 << 21), None), ((8, 1 << 21, 8), None),
                                        ((264, 24, (1 << 21) - 8), None),
-                                       ((264, 24, (1 << 21) - 8), (256, 256, 64, 3, 8, 8))])
+                                       ((264, 24, (1 << 21) - 8), (256, 256, 64, 3, 8, 8)),
+                                       ((264, 24, 1 << 21), (256, 256, 64, 2, 4, 10))])
 def test_maximum_k_and_n(shape, cfg):
     # K and N at the documented limit 2^21: per-workgroup buffer ranges and
     # offsets come closest to 2^31 here (the last case with 256-row A and B
@@ -252,7 +284,8 @@ def test_empty_m_or_n_leaves_output_untouched():
                                        ((128, 128, 64, 2, 4, 4), (4200, 4104, 72)),
                                        ((256, 256, 64, 2, 8, 5), (300, 264, 136)),
                                        ((256, 256, 64, 2, 8, 7), (300, 264, 136)),
-                                       ((256, 256, 64, 3, 8, 8), (300, 264, 136))])
+                                       ((256, 256, 64, 3, 8, 8), (300, 264, 136)),
+                                       ((256, 256, 64, 2, 4, 10), (300, 264, 136))])
 def test_canary_guard_bands(cfg, shape):
     # D sits inside a larger buffer filled with a NaN pattern; nothing outside
     # D may change and every element of D must be written
@@ -277,17 +310,18 @@ def test_alpha_values(alpha):
     A, B = inputs.operands(384, 392, 520, 91)
     a32 = float(np.float32(alpha))
     # the library's choice, and the large-shape kernel on the same operands
-    for cfg in (None, (256, 256, 64, 3, 8, 8)):
+    for cfg in (None, (256, 256, 64, 3, 8, 8), (256, 256, 64, 2, 4, 10)):
         full_check(A, B, alpha=a32, config=cfg, label=f"alpha {alpha} {cfg}")
 
 
 @pytest.mark.parametrize("shape", [(300, 264, 200), (4352, 520, 264), (256, 256, 0),
-                                   (20480, 256, 256), (3848, 3840, 136)])
+                                   (20480, 256, 256), (3848, 3840, 136), (4096, 4104, 256)])
 @pytest.mark.parametrize("alpha,beta", [(1.0, 1.0), (0.5, -0.75), (-1.0, 0.3), (0.0, 2.0)])
 def test_beta_c(shape, alpha, beta):
     # (20480, 256, 256): without C the library picks the persistent schedule;
     # with C it must fall back to a tiled variant.  (3848, 3840, 136) takes
-    # the 256 x 256 tiles, with M and N tails.
+    # the 256 x 256 tiles, with M and N tails; (4096, 4104, 256) the same
+    # tiles on the one-wave schedule (K % 64 == 0), with an N tail.
     M, N, K = shape
     say(f"[case] beta {shape} alpha={alpha} beta={beta}")
     A, B = inputs.operands(M, N, K, 600 + M + K)
