@@ -986,7 +986,7 @@ def mode_variants_summary(args) -> int:
            f"--prof-dir <dir> --bench-log <that run's output> --workload {w}`.", "",
            "`us` = mean kernel-trace duration over each variant's timed dispatches (mapped by order).  "
            "Schedules: 0 three-phase, 1 cute order, 2 ping-pong, 3 persistent, 4 short K, 5 cute order on "
-           "16x16x32 MFMAs, 7 ping-pong on 16x16x32, 8 split-load ping-pong.", "",
+           "16x16x32 MFMAs, 7 ping-pong on 16x16x32, 8 split-load ping-pong, 10 one wave per SIMD.", "",
            "| variant (tile_m, tile_n, tile_k, stages, waves, schedule) | us | TFLOP/s | frac |", "|---|---|---|---|"]
     i = 0
     res = []
