@@ -149,7 +149,9 @@ sg_status gemm_fp16_tn_alpha_beta(int M, int N, int K, float alpha, float beta,
  * (one per compute unit), or a last round that is only partly full
  * ("cute(9) multistage_gemm", section 11.3, names split-K as the remedy for
  * too few output tiles).  Output tiles that fill whole rounds are computed
- * as by the tiled schedule 8; each remaining tile is cut along K into
+ * as by the tiled schedule the library would pick (10 when every row of A
+ * and B starts on a 128-byte line, else 8); each remaining tile is cut
+ * along K into
  * `splits` contiguous runs of 64-deep K tiles (fewer if K has fewer tiles,
  * at most 16), each run computed by its own workgroup through the same
  * stage-pipelined mainloop, which writes the run's fp32 partial tile to the

@@ -373,7 +373,7 @@ __device__ __forceinline__ void store_block_staged(const f32x16 (&blk)[C::FN], f
     compiler_fence();
 }
 
-// Work of a split-K launch (schedule 8 only).  Grid positions below
+// Work of a split-K launch (schedules 8 and 10).  Grid positions below
 // dp_tiles compute whole output tiles, as the tiled kernel does.  The
 // remaining L = tiles - dp_tiles output tiles are each cut into `splits`
 // contiguous runs of K tiles; run p of cut tile t is grid position
@@ -398,7 +398,8 @@ __device__ __forceinline__ void gemm_tn_body(const _Float16 *__restrict__ A,
                                              float beta, const SplitWork &sw)
 {
     static_assert(C::SCHED <= 2 || C::SCHED >= 5, "schedules 3 and 4 have kernels of their own");
-    static_assert(!SPLIT || C::ORDER == 8, "split-K runs the split-load ping-pong");
+    static_assert(!SPLIT || C::ORDER == 8 || C::ORDER == 10,
+                  "split-K runs the split-load ping-pong or the one-wave schedule");
     // Cm and D may be the same buffer (in-place D = alpha A B^T + beta D): each
     // wave reads C only inside its own sub-tile and finishes those reads
     // before it stores, so they are not declared __restrict__.
@@ -697,11 +698,14 @@ __device__ __forceinline__ void gemm_tn_body(const _Float16 *__restrict__ A,
         const uint32_t rA10 = rA00 + (uint32_t)C::STAGE_BYTES, rA11 = rA01 + (uint32_t)C::STAGE_BYTES;
         const uint32_t rB00 = lds0 + fb[0], rB01 = lds0 + fb[1];
         const uint32_t rB10 = rB00 + (uint32_t)C::STAGE_BYTES, rB11 = rB01 + (uint32_t)C::STAGE_BYTES;
-        const uint32_t lbase = l_base, lch8 = (uint32_t)(l_chunk * 8), lstep = l_step;
+        // The statement counts K tiles from 0: a split piece's first tile kt0
+        // enters as a shifted source offset and a shorter K.
+        const uint32_t lbase = l_base + (uint32_t)kt0 * (uint32_t)(C::BK * 2);
+        const uint32_t lch8 = (uint32_t)(l_chunk * 8), lstep = l_step;
         const uint32_t oor = kOutOfRange;
         const uint32_t wb = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)wave * 1024u);
         const uint32_t ow_nk = __builtin_amdgcn_readfirstlane(nk);
-        const uint32_t ow_kk = __builtin_amdgcn_readfirstlane(K);
+        const uint32_t ow_kk = __builtin_amdgcn_readfirstlane(K - kt0 * C::BK);
         f16x8 xa[8], xb[8], ya[8], yb[8];
         uint32_t o0, o1, o2, o3, o4, o5, o6, o7, vs, sk, st, se;
 #include "onewave_mainloop.inc"
@@ -889,7 +893,6 @@ __device__ __forceinline__ void gemm_tn_body(const _Float16 *__restrict__ A,
     // as in the epilogue): 64-byte row pieces of 16 rows per instruction.
     if constexpr (SPLIT) {
         if (partial) {
-            typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
             const __amdgpu_buffer_rsrc_t rw = make_rsrc(
                 sw.part + (size_t)(ltile * sw.splits + krun) * (C::BM * C::BN),
                 (uint32_t)(C::BM * C::BN * 4));
@@ -1040,7 +1043,7 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
     gemm_tn_body<C, false>(A, B, Cm, D, M, N, K, alpha, beta, SplitWork{nullptr, 0, 1});
 }
 
-// Split-K form of schedule 8 (see SplitWork): D = alpha * A * B^T, no C.
+// Split-K form of schedules 8 and 10 (see SplitWork): D = alpha * A * B^T, no C.
 template <class C>
 __global__ void __launch_bounds__(C::T)
 gemm_tn_split_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,

@@ -232,12 +232,21 @@ const Variant *select_variant(int M, int N, int K, bool with_c, double *cost = n
 // Largest M: tile counts (M + tile_m - 1) / tile_m stay within int.
 constexpr int kMaxM = 0x7fffffff - 256;
 
-// ---- split-K form of schedule 8 (gemm_fp16_tn_splitk).  Output tiles that
-// fill whole rounds of resident workgroups run as in the tiled kernel; the
-// rest -- every tile when there are fewer than one round -- are cut along K
-// into `splits` runs computed by separate workgroups, whose fp32 partials a
-// second kernel adds up (sg::SplitWork, sg::split_reduce_kernel).
+// ---- split-K form of schedules 8 and 10 (gemm_fp16_tn_splitk).  Output
+// tiles that fill whole rounds of resident workgroups run as in the tiled
+// kernel; the rest -- every tile when there are fewer than one round -- are
+// cut along K into `splits` runs computed by separate workgroups, whose fp32
+// partials a second kernel adds up (sg::SplitWork, sg::split_reduce_kernel).
+// The mainloop follows the tiled choice: schedule 10 when every row starts
+// on a 128-byte line, else schedule 8.  Both hold one workgroup per CU (LDS),
+// so the plan and the resident count are the same for either.
 using SplitCfg = sg::Cfg<256, 256, 64, 3, 2, 4, 8>;
+using SplitCfg10 = sg::Cfg<256, 256, 64, 2, 2, 2, 10>;
+static_assert(SplitCfg10::BM == SplitCfg::BM && SplitCfg10::BN == SplitCfg::BN &&
+                  SplitCfg10::BK == SplitCfg::BK && SplitCfg10::T <= SplitCfg::T,
+              "one split plan serves both kernels");
+static_assert(2 * SplitCfg10::LDS_BYTES > 160 * 1024 && 2 * SplitCfg::LDS_BYTES > 160 * 1024,
+              "one split workgroup per CU for both kernels");
 constexpr size_t kSplitTileBytes = (size_t)SplitCfg::BM * SplitCfg::BN * 4;
 constexpr int kMaxSplits = 16;
 
@@ -393,8 +402,11 @@ sg_status launch_split(const SplitPlan &p, int M, int N, int K, float alpha, con
     int dp = p.dp_tiles, splits = p.splits;
     const hipStream_t st = static_cast<hipStream_t>(stream);
     void *args[] = {&a, &b, &d, &M, &N, &K, &alpha, &part, &dp, &splits};
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&sg::gemm_tn_split_kernel<SplitCfg>),
-                                   dim3((unsigned)p.grid), dim3(SplitCfg::T), args, 0, st);
+    const bool one_wave = K % 64 == 0 && lines_aligned(A, B);
+    const void *fn = one_wave ? reinterpret_cast<const void *>(&sg::gemm_tn_split_kernel<SplitCfg10>)
+                              : reinterpret_cast<const void *>(&sg::gemm_tn_split_kernel<SplitCfg>);
+    hipError_t e = hipLaunchKernel(fn, dim3((unsigned)p.grid),
+                                   dim3(one_wave ? SplitCfg10::T : SplitCfg::T), args, 0, st);
     if (e != hipSuccess) return SG_ERR_HIP;
     const float *cpart = part;
     void *rargs[] = {&cpart, &d, &M, &N, &alpha, &dp, &splits};

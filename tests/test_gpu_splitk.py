@@ -73,6 +73,31 @@ def test_split_runs_match_the_oracle(shape, splits):
         assert torch.equal(d2.view(torch.int16), d.view(torch.int16)), (shape, s)
 
 
+def test_split_line_alignment_selects_schedule():
+    # K % 64 == 0: with A and B on 128-byte lines the pieces run the one-wave
+    # schedule (10), with A 16 bytes past a line the split-load ping-pong
+    # (8); the same runs in the same order give the same bits, and both
+    # match the oracle in every element (M and N tails, uneven runs)
+    M, N, K = 2056, 1040, 1024
+    A, B = inputs.operands(M, N, K, 2999)
+    ref = oracle.gemm_tn_f64(A, B)
+    a, b = to_dev(A), to_dev(B)
+    flat = torch.empty(M * K + 64, dtype=torch.float16, device=DEV)
+    a16 = flat[8:8 + M * K].view(M, K)
+    a16.copy_(a)
+    assert a.data_ptr() % 128 == 0 and b.data_ptr() % 128 == 0 and a16.data_ptr() % 128 == 16
+    for s in (3, 16):
+        outs = []
+        for x, label in ((a, "lines"), (a16, "16 bytes past a line")):
+            say(f"[case] splitk alignment {label} splits={s}")
+            d, _, need = split_call(x, b, M, N, K, s)
+            assert need > 0
+            rep = oracle.check(d.cpu().numpy(), ref, K)
+            assert rep.ok, (label, s, str(rep))
+            outs.append(d)
+        assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), s
+
+
 def test_split_6144_square_library_choice():
     # 576 tiles: two whole rounds and a quarter round cut along K, the
     # library's own split count, through the Python entry
