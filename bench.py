@@ -414,8 +414,11 @@ def library_call(M: int, N: int, K: int, a, b, d, alpha):
         def fn():
             sg.gemm_fp16_tn_splitk(M, N, K, al, *ptrs, s, ws.data_ptr(), need, stream)
         fn.workspace = ws
-        # the split-K form runs the split-load ping-pong (schedule 8)
-        return fn, variant_name(sg.SgConfig(256, 256, 64, 3, 8, 8), s), s
+        # the split-K pieces run the one-wave schedule (10) when every row
+        # starts on a 128-byte line, else the split-load ping-pong (8)
+        lines = K % 64 == 0 and (a.data_ptr() | b.data_ptr()) % 128 == 0
+        cfg = sg.SgConfig(256, 256, 64, 2, 4, 10) if lines else sg.SgConfig(256, 256, 64, 3, 8, 8)
+        return fn, variant_name(cfg, s), s
 
     def fn():
         sg.gemm_fp16_tn_alpha(M, N, K, al, *ptrs, stream)
