@@ -414,10 +414,10 @@ def library_call(M: int, N: int, K: int, a, b, d, alpha):
         def fn():
             sg.gemm_fp16_tn_splitk(M, N, K, al, *ptrs, s, ws.data_ptr(), need, stream)
         fn.workspace = ws
-        # the split-K pieces run the one-wave schedule (10) when every row
-        # starts on a 128-byte line, else the split-load ping-pong (8)
+        # the split-K pieces run schedule 10 when every row starts on a
+        # 128-byte line, else schedule 12
         lines = K % 64 == 0 and (a.data_ptr() | b.data_ptr()) % 128 == 0
-        cfg = sg.SgConfig(256, 256, 64, 2, 4, 10) if lines else sg.SgConfig(256, 256, 64, 3, 8, 8)
+        cfg = sg.SgConfig(256, 256, 64, 2, 4, 10) if lines else sg.SgConfig(256, 256, 64, 3, 4, 12)
         return fn, variant_name(cfg, s), s
 
     def fn():
@@ -631,7 +631,7 @@ def mode_stage_model(args) -> int:
     stage_bytes = (256 + 256) * 64 * 2
     rings = [{"stages": st, "lds_bytes": st * stage_bytes,
               "wg_per_cu_lds": (160 * 1024) // (st * stage_bytes)} for st in range(2, 6)]
-    _, info = sg.sg_query_config(sg.SgConfig(256, 256, 64, 3, 8, 8))
+    _, info = sg.sg_query_config(sg.SgConfig(256, 256, 64, 3, 4, 12))
     print(json.dumps({
         "mode": "stage_model", "workload": args.workload, "tile": "256x256x64",
         "workgroups": blocks, "k_tiles_timed": ntile, "probe_ms": round(e0.elapsed_time(e1), 3),
@@ -642,9 +642,13 @@ def mode_stage_model(args) -> int:
                           "copy_over_compute": round(t_copy_wg / t_comp_wg, 3), "S_min": s_min_wg,
                           "statistic": "slowest wave of each workgroup, median over workgroups"},
         "rings_of_whole_stages": rings,
-        "kernel_ring": {"A_slots": 2, "B_slots": 3, "lds_bytes": info.lds_bytes,
-                        "wg_per_cu": info.wg_per_cu,
-                        "tiles_in_flight_ahead": {"A": 1, "B": 2}}}), flush=True)
+        "kernel_rings": {
+            "schedule_10": {"A_slots": 2, "B_slots": 2, "lds_bytes": 2 * stage_bytes, "wg_per_cu": 1,
+                            "loads_issued": "A(k+2), B(k+2) in the second half of tile k"},
+            "schedule_12": {"A_slots": 2, "B_slots": 3, "lds_bytes": info.lds_bytes,
+                            "wg_per_cu": info.wg_per_cu,
+                            "loads_issued": "B(k+2) in the first half, A(k+2) in the second half of tile k"}}}),
+          flush=True)
     return 0
 
 

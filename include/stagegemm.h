@@ -90,9 +90,8 @@ typedef enum sg_status {
  *      the first group loads A tiles, the second B tiles, each in its own
  *      fragment-read phase.  A keeps stages - 1 ring slots and B keeps
  *      `stages` (stages = 3: 64 + 96 KiB for 256 x 256 x 64 tiles), which
- *      gives the second group's loads two phases to land.  The library's
- *      choice for 256 x 256 tiles when rows of A or B straddle 128-byte
- *      lines (K % 64 != 0, or a base address not 128-byte aligned);
+ *      gives the second group's loads two phases to land.  Compiled for
+ *      comparison;
  *  10  one wave per SIMD ("cute(9) multistage_gemm", section 6, with the
  *      two-slot ring of "Lesson 6", section 4): 4 waves of 128 x 128 each,
  *      64-deep K tiles in two 64 KiB slots, one barrier per tile between
@@ -100,7 +99,16 @@ typedef enum sg_status {
  *      LDS-DMA of tile k + 2 into the slot just freed overlap its MFMAs.
  *      Only 256 x 256 x 64, stages 2, waves 4.  The library's choice for
  *      256 x 256 tiles when every row of A and B starts on a 128-byte line
- *      (K % 64 == 0 and 128-byte aligned A and B). */
+ *      (K % 64 == 0 and 128-byte aligned A and B);
+ *  11  order 10 with a third B slot (A: 2 slots, B: 3, 160 KiB), B loaded
+ *      three tiles ahead.  Compiled for comparison;
+ *  12  order 11 with the B loads moved to the first half of each tile (B two
+ *      tiles ahead, into the slot the tile before last left), so each half
+ *      tile issues 8 loads per wave instead of 16.  Only 256 x 256 x 64,
+ *      stages 3, waves 4.  The library's choice for 256 x 256 tiles when
+ *      rows of A or B straddle 128-byte lines (K % 64 != 0, or a base
+ *      address not 128-byte aligned), where each load touches two lines
+ *      and holds the issuing wave longer. */
 typedef struct sg_config {
     int tile_m;
     int tile_n;
@@ -150,7 +158,7 @@ sg_status gemm_fp16_tn_alpha_beta(int M, int N, int K, float alpha, float beta,
  * ("cute(9) multistage_gemm", section 11.3, names split-K as the remedy for
  * too few output tiles).  Output tiles that fill whole rounds are computed
  * as by the tiled schedule the library would pick (10 when every row of A
- * and B starts on a 128-byte line, else 8); each remaining tile is cut
+ * and B starts on a 128-byte line, else 12); each remaining tile is cut
  * along K into
  * `splits` contiguous runs of 64-deep K tiles (fewer if K has fewer tiles,
  * at most 16), each run computed by its own workgroup through the same
@@ -234,7 +242,7 @@ sg_status gemm_fp16_tn_cfg(int M, int N, int K, float alpha, const void *A,
 
 /* The variant gemm_fp16_tn (and gemm_fp16_tn_alpha) would run for this
  * shape with 128-byte aligned A and B (a less aligned A or B turns
- * schedule 10 into schedule 8).  gemm_fp16_tn_alpha_beta with beta != 0 runs
+ * schedule 10 into schedule 12).  gemm_fp16_tn_alpha_beta with beta != 0 runs
  * the same variant unless it is persistent (schedule 3) or short-K
  * (schedule 4), which take no C operand: the choice is then made among the
  * tiled variants only, by the same cost model. */

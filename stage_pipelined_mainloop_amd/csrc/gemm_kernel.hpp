@@ -157,7 +157,9 @@ __device__ __forceinline__ int swz(int r)
 // 16x16x32 MFMAs, 8 = order 7 with the LDS-DMA loads split between the two
 // wave groups (A ring of S - 1 slots, B ring of S; "order 8" below), 10 = one
 // wave per SIMD with a 128x128 tile each, its whole mainloop one scheduled
-// inline-assembly statement ("order 10" below).
+// inline-assembly statement ("order 10" below), 11 = order 10 with a third B
+// slot, B loaded three tiles ahead, 12 = order 11 with the B loads moved to
+// the first half of each tile.
 //
 // MFMA shape.  Schedules 0-4 use v_mfma_f32_32x32x16_f16 (32x32 blocks, K
 // steps of 16); schedules 5, 7 and 8 use v_mfma_f32_16x16x32_f16 (16x16
@@ -178,7 +180,7 @@ template <int BM_, int BN_, int BK_, int S_, int WM_, int WN_, int SCHED_ = 1>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_, WM = WM_, WN = WN_;
     static constexpr int SCHED = SCHED_;
-    static constexpr bool MF16 = SCHED == 5 || SCHED == 7 || SCHED == 8 || SCHED == 10;   // 16x16x32 MFMAs
+    static constexpr bool MF16 = SCHED == 5 || SCHED == 7 || SCHED >= 8;   // 16x16x32 MFMAs
     static constexpr int ORDER = SCHED == 5 ? 1 : SCHED == 7 ? 2 : SCHED;   // mainloop order
     static constexpr int NW = WM * WN;              // wavefronts
     static constexpr int T = 64 * NW;               // threads
@@ -196,8 +198,9 @@ struct Cfg {
     static constexpr int A_BYTES = BM * RB;
     static constexpr int B_BYTES = BN * RB;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-    // Order 8 keeps S - 1 slots of A and S slots of B.
-    static constexpr int RING_BYTES = ORDER == 8 ? (S - 1) * A_BYTES + S * B_BYTES : S * STAGE_BYTES;
+    // Orders 8, 11 and 12 keep S - 1 slots of A and S slots of B.
+    static constexpr int RING_BYTES =
+        ORDER == 8 || ORDER >= 11 ? (S - 1) * A_BYTES + S * B_BYTES : S * STAGE_BYTES;
     // Epilogue staging: one 32-row block of each wave's sub-tile at a time,
     // unpadded rows with the slot swizzle of staged_slot.
     static constexpr int EPI_ROW = WTN * 2;
@@ -220,7 +223,7 @@ struct Cfg {
     static constexpr int NB = BN * CPR / (64 * NW);
     static constexpr int L = NA + NB;
     static_assert(S >= 2, "a ring needs at least two slots");
-    static_assert(SCHED >= 0 && SCHED <= 10 && SCHED != 6 && SCHED != 9, "mainloop order");
+    static_assert(SCHED >= 0 && SCHED <= 12 && SCHED != 6 && SCHED != 9, "mainloop order");
     static_assert(!MF16 || BK == 64, "16x16x32 order: two K steps of 32 per tile");
     static_assert(SCHED != 3 || S == 2 || S == 3, "persistent ring: two or three slots");
     static_assert(!OWN_STAGING || WTN == 64, "unpadded staging rows are 128 bytes");
@@ -231,6 +234,9 @@ struct Cfg {
     static_assert(NKS % 2 == 0, "fragment double buffer alternates per K step");
     static_assert(ORDER != 10 || (BM == 256 && BN == 256 && BK == 64 && S == 2 && WM == 2 && WN == 2),
                   "one-wave form: 256x256x64 tiles, two slots, 2x2 waves of 128x128");
+    static_assert((ORDER != 11 && ORDER != 12) ||
+                      (BM == 256 && BN == 256 && BK == 64 && S == 3 && WM == 2 && WN == 2),
+                  "one-wave form, third B slot: 256x256x64 tiles, 2x2 waves of 128x128");
     static_assert(BK == 32 || BK == 64, "BK");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile is whole 32x32 blocks");
     static_assert(NA * 64 * NW == BM * CPR && NB * 64 * NW == BN * CPR, "even load split");
@@ -373,7 +379,7 @@ __device__ __forceinline__ void store_block_staged(const f32x16 (&blk)[C::FN], f
     compiler_fence();
 }
 
-// Work of a split-K launch (schedules 8 and 10).  Grid positions below
+// Work of a split-K launch (the library runs it on schedules 10 and 12).  Grid positions below
 // dp_tiles compute whole output tiles, as the tiled kernel does.  The
 // remaining L = tiles - dp_tiles output tiles are each cut into `splits`
 // contiguous runs of K tiles; run p of cut tile t is grid position
@@ -398,8 +404,8 @@ __device__ __forceinline__ void gemm_tn_body(const _Float16 *__restrict__ A,
                                              float beta, const SplitWork &sw)
 {
     static_assert(C::SCHED <= 2 || C::SCHED >= 5, "schedules 3 and 4 have kernels of their own");
-    static_assert(!SPLIT || C::ORDER == 8 || C::ORDER == 10,
-                  "split-K runs the split-load ping-pong or the one-wave schedule");
+    static_assert(!SPLIT || C::ORDER == 8 || C::ORDER >= 10,
+                  "split-K runs the split-load ping-pong or a one-wave schedule");
     // Cm and D may be the same buffer (in-place D = alpha A B^T + beta D): each
     // wave reads C only inside its own sub-tile and finishes those reads
     // before it stores, so they are not declared __restrict__.
@@ -560,7 +566,7 @@ __device__ __forceinline__ void gemm_tn_body(const _Float16 *__restrict__ A,
     };
 
     // ---- prologue: tiles 0 .. S-2 (order 8 has a prologue of its own)
-    if constexpr (C::ORDER != 8 && C::ORDER != 10) {
+    if constexpr (C::ORDER != 8 && C::ORDER < 10) {
 #pragma unroll
         for (int t = 0; t < C::S - 1; ++t)
             if (t < ntile) issue(t, t);
@@ -672,32 +678,44 @@ __device__ __forceinline__ void gemm_tn_body(const _Float16 *__restrict__ A,
             barrier();
         }
         if (grp == 0) barrier();                   // G0 idles in the last phase
-    } else if constexpr (C::ORDER == 10) {
-        // ---- One wave per SIMD, 128x128 of the tile each, 64-deep K tiles in
-        // two LDS slots, one barrier per K tile between its two 32-deep halves:
-        // the ring protocol of "cute(9) multistage_gemm" (section 6) with the
-        // minimum ring of "Lesson 6" (section 4, S = 2: a tile's copy takes
-        // about as long as its MFMAs).  With a single wave per SIMD nothing else
-        // hides an instruction that is not an MFMA, so the loop is one
-        // inline-assembly statement in which every fragment read, LDS-DMA load
-        // and address update sits between two MFMAs (onewave_mainloop.inc,
-        // written by gen_onewave_mainloop.py, which gives the schedule, the
-        // wait counts and the hazards it covers).  The accumulators stay in
-        // the 256 AGPRs, which leaves the 256 VGPRs to two fragment buffers of
-        // a 32-deep step each.  Tile t's loads use the same lane-to-LDS
-        // mapping and K-tail handling as `issue` above, computed in the loop.
+    } else if constexpr (C::ORDER >= 10) {
+        // ---- One wave per SIMD, 128x128 of the tile each, 64-deep K tiles,
+        // one barrier per K tile between its two 32-deep halves: the ring
+        // protocol of "cute(9) multistage_gemm" (section 6) with the minimum
+        // ring of "Lesson 6" (section 4, S = 2: a tile's copy takes about as
+        // long as its MFMAs).  Order 10 keeps A and B in two slots; order 11
+        // gives B a third slot and loads it three tiles ahead; order 12 loads
+        // B two tiles ahead in the first half of each tile, so each half
+        // issues 8 loads per wave instead of 16.  With a single wave per SIMD
+        // nothing else hides an instruction that is not an MFMA, so the loop
+        // is one inline-assembly statement in which every fragment read,
+        // LDS-DMA load and address update sits between two MFMAs
+        // (onewave_mainloop.inc, onewave_b3_mainloop.inc and
+        // onewave_b3h_mainloop.inc, written by gen_onewave_mainloop.py, which
+        // gives the schedule, the wait counts and the hazards it covers).
+        // The accumulators stay in the 256 AGPRs,
+        // which leaves the VGPRs to two fragment buffers of a 32-deep step
+        // each.  Tile t's loads use the same lane-to-LDS mapping and K-tail
+        // handling as `issue` above, computed in the loop.
         static_assert(C::AM == 8 && C::AN == 8 && C::NKS == 2 && C::NA == 8 && C::NB == 8,
                       "the assembly is written for 8x8 MFMA blocks and 8 + 8 loads per wave");
-        static_assert(C::STAGE_BYTES == 65536 && C::A_BYTES == 32768, "slot layout of the assembly");
+        static_assert(C::A_BYTES == 32768 && C::B_BYTES == 32768, "slot layout of the assembly");
         const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(
             (__attribute__((address_space(3))) char *)smem);
         const u32x4 rwa = rsrc_words(A + (size_t)m0 * K, (uint32_t)rows_a * K * 2u);
         const u32x4 rwb = rsrc_words(B + (size_t)n0 * K, (uint32_t)rows_b * K * 2u);
-        // this lane's first fragment of each slot and K step (fb holds + A_BYTES)
+        // This lane's first fragment of each slot and K step.  fa / fb are
+        // offsets within a stage of A rows then B rows (fb includes A_BYTES).
+        // Order 10: slot s is the stage at s * STAGE_BYTES.  Orders 11 and 12:
+        // two A slots of A_BYTES, then three B slots of B_BYTES.
+        constexpr uint32_t A_SLOT = C::ORDER == 10 ? C::STAGE_BYTES : C::A_BYTES;
+        constexpr uint32_t B_FIRST = C::ORDER == 10 ? 0u : (uint32_t)C::A_BYTES;
+        constexpr uint32_t B_SLOT = C::ORDER == 10 ? C::STAGE_BYTES : C::B_BYTES;
         const uint32_t rA00 = lds0 + fa[0], rA01 = lds0 + fa[1];
-        const uint32_t rA10 = rA00 + (uint32_t)C::STAGE_BYTES, rA11 = rA01 + (uint32_t)C::STAGE_BYTES;
-        const uint32_t rB00 = lds0 + fb[0], rB01 = lds0 + fb[1];
-        const uint32_t rB10 = rB00 + (uint32_t)C::STAGE_BYTES, rB11 = rB01 + (uint32_t)C::STAGE_BYTES;
+        const uint32_t rA10 = rA00 + A_SLOT, rA11 = rA01 + A_SLOT;
+        const uint32_t rB00 = lds0 + fb[0] + B_FIRST, rB01 = lds0 + fb[1] + B_FIRST;
+        const uint32_t rB10 = rB00 + B_SLOT, rB11 = rB01 + B_SLOT;
+        const uint32_t rB20 = rB10 + B_SLOT, rB21 = rB11 + B_SLOT;
         // The statement counts K tiles from 0: a split piece's first tile kt0
         // enters as a shifted source offset and a shorter K.
         const uint32_t lbase = l_base + (uint32_t)kt0 * (uint32_t)(C::BK * 2);
@@ -708,7 +726,17 @@ __device__ __forceinline__ void gemm_tn_body(const _Float16 *__restrict__ A,
         const uint32_t ow_kk = __builtin_amdgcn_readfirstlane(K - kt0 * C::BK);
         f16x8 xa[8], xb[8], ya[8], yb[8];
         uint32_t o0, o1, o2, o3, o4, o5, o6, o7, vs, sk, st, se;
+        if constexpr (C::ORDER == 10) {
+            (void)rB20;
+            (void)rB21;
 #include "onewave_mainloop.inc"
+        } else if constexpr (C::ORDER == 11) {
+            uint32_t p0, p1, p2, p3, p4, p5, p6, p7, ps;
+#include "onewave_b3_mainloop.inc"
+        } else {
+            uint32_t p0, p1, p2, p3, p4, p5, p6, p7, ps;
+#include "onewave_b3h_mainloop.inc"
+        }
     } else if constexpr (C::ORDER == 8) {
         // ---- Ping-pong with the loads split between the groups.  The phases
         // are those of order 2, but G0 loads only A tiles and G1 only B
@@ -1043,7 +1071,7 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
     gemm_tn_body<C, false>(A, B, Cm, D, M, N, K, alpha, beta, SplitWork{nullptr, 0, 1});
 }
 
-// Split-K form of schedules 8 and 10 (see SplitWork): D = alpha * A * B^T, no C.
+// Split-K form of schedules 8, 10, 11 and 12 (see SplitWork): D = alpha * A * B^T, no C.
 template <class C>
 __global__ void __launch_bounds__(C::T)
 gemm_tn_split_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,

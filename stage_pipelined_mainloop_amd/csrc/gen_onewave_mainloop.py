@@ -44,11 +44,35 @@ lstep (this lane's LDS-DMA source offset of tile 0, 8 x its chunk index,
 and the offset step of one load), oor (an offset past every buffer range),
 wb (LDS address of this wave's first 1 KiB), rwa / rwb (buffer resources of
 the workgroup's A and B rows), ow_nk (K tiles), ow_kk (K), all wave-uniform."""
+import math
 import os
 
-SLOT = 65536          # bytes of one ring slot: 256 A rows + 256 B rows of 128 bytes
-B_OFF = 32768         # B rows within a slot
+A_PART = 32768        # bytes of one operand tile: 256 rows of 128 bytes
 FRAG = 2048           # 16 rows of 128 bytes: one MFMA block of fragments
+
+
+class Form:
+    """One mainloop form: B ring depth and how far ahead B is loaded (A
+    always has two slots and is loaded two tiles ahead), and the LDS byte
+    offset of each slot."""
+
+    def __init__(self, b_slots, b_first_half=False):
+        self.b_slots = b_slots
+        # B loads in the first half of tile k (B(k + 2), into the slot B(k - 1)
+        # left) or with the A loads in the second half (B(k + b_slots), into
+        # the slot B(k) leaves)
+        self.b_first = b_first_half
+        self.b_ahead = 2 if b_first_half else b_slots
+        self.unroll = math.lcm(2, b_slots)
+        self.split = b_slots != 2       # A and B use separate offset registers
+
+    def a_off(self, slot):
+        # schedule 10: slot s = A rows then B rows at s * 64 KiB;
+        # schedule 11: two A slots, then three B slots, 32 KiB each
+        return slot * 2 * A_PART if not self.split else slot * A_PART
+
+    def b_off(self, slot):
+        return slot * 2 * A_PART + A_PART if not self.split else 2 * A_PART + slot * A_PART
 
 
 def q(x):
@@ -63,67 +87,111 @@ def mfma(m, buf):
     return q(f'v_mfma_f32_16x16x32_f16 %[c{i}{j}], %[{buf}b{j}], %[{buf}a{i}], %[c{i}{j}]')
 
 
-def offsets(first):
+def offsets(first, reg="o", step="vs"):
     """LDS-DMA source offsets of the tile whose index `first` puts in st:
-    o0 = this lane's offset of load 0 (or oor when the tile is past the last
-    one or this lane's 16-byte chunk lies past K), o1..o7 = o0 + i * step
-    (step 0 for an out-of-range lane)."""
-    return first + [
-        q('s_lshl_b32 %[se], %[st], 6'),                 # first K index of the tile
-        q('s_sub_i32 %[se], %[kk], %[se]'),              # K left from there
-        q('s_cmp_lt_u32 %[st], %[nk]'),
-        q('s_cselect_b32 %[se], %[se], 0x80000000'),     # none left past the last tile
-        q('v_cmp_gt_i32 vcc, %[se], %[lch8]'),           # this lane's chunk in range
-        q('s_lshl_b32 %[se], %[st], 7'),                 # byte offset of the tile
-        q('v_add_u32 %[o0], %[se], %[lbase]'),
-        q('v_cndmask_b32 %[o0], %[oor], %[o0], vcc'),
-        q('v_cndmask_b32 %[vs], 0, %[lstep], vcc'),
-    ] + [q(f'v_add_u32 %[o{i}], %[o{i - 1}], %[vs]') for i in range(1, 8)]
+    reg0 = this lane's offset of load 0 (or oor when the tile is past the
+    last one or this lane's 16-byte chunk lies past K), reg1..reg7 = reg0 +
+    i * step (step 0 for an out-of-range lane).  A list of chunks: the
+    compare and the select that reads its SCC stay together, so nothing that
+    writes SCC (an m0 update) can be placed between them."""
+    return [[x] for x in first] + [
+        [q('s_lshl_b32 %[se], %[st], 6')],               # first K index of the tile
+        [q('s_sub_i32 %[se], %[kk], %[se]')],            # K left from there
+        [q('s_cmp_lt_u32 %[st], %[nk]'),
+         q('s_cselect_b32 %[se], %[se], 0x80000000')],   # none left past the last tile
+        [q('v_cmp_gt_i32 vcc, %[se], %[lch8]')],         # this lane's chunk in range
+        [q('s_lshl_b32 %[se], %[st], 7')],               # byte offset of the tile
+        [q(f'v_add_u32 %[{reg}0], %[se], %[lbase]')],
+        [q(f'v_cndmask_b32 %[{reg}0], %[oor], %[{reg}0], vcc')],
+        [q(f'v_cndmask_b32 %[{step}], 0, %[lstep], vcc')],
+    ] + [[q(f'v_add_u32 %[{reg}{i}], %[{reg}{i - 1}], %[{step}]')] for i in range(1, 8)]
 
 
-def dma(g, slot):
-    """LDS-DMA load g (0..15) of a tile into `slot`: loads 0..7 fill A rows
-    32 i + (8 wave .. 8 wave + 7), loads 8..15 the same B rows."""
-    off = slot * SLOT + (g * 4096 if g < 8 else B_OFF + (g - 8) * 4096)
-    rsrc = 'rwa' if g < 8 else 'rwb'
+def flat(chunks):
+    return [x for c in chunks for x in c]
+
+
+def spread(chunks, g, n=14):
+    """The instructions of `chunks` that go after MFMA group g (2..15):
+    the chunks dealt in order, ceil(len / n) to a group.  In a half without
+    LDS-DMA loads nothing between the chunks writes SCC, so there the
+    instructions are dealt one by one (single-instruction chunks)."""
+    per = -(-len(chunks) // n)
+    return flat(chunks[(g - 2) * per:(g - 1) * per]) if g >= 2 else []
+
+
+def dma(f, g, a_slot, b_slot, b_reg="o"):
+    """LDS-DMA load g (0..15) of a tile: loads 0..7 fill A rows
+    32 i + (8 wave .. 8 wave + 7) of slot a_slot, loads 8..15 the same B rows
+    of slot b_slot."""
+    if g < 8:
+        off, rsrc, reg = f.a_off(a_slot) + g * 4096, "rwa", "o"
+    else:
+        off, rsrc, reg = f.b_off(b_slot) + (g - 8) * 4096, "rwb", b_reg
     return [q(f's_add_u32 m0, %[wb], {off}'), q('s_nop 0'),
-            q(f'buffer_load_dwordx4 %[o{g % 8}], %[{rsrc}], 0 offen lds')]
+            q(f'buffer_load_dwordx4 %[{reg}{g % 8}], %[{rsrc}], 0 offen lds')]
 
 
-def reads(buf, slot, ks):
+def reads(buf, a_slot, b_slot, ks):
     """The 16 fragment reads of one 32-deep step: 8 A blocks then 8 B blocks."""
-    return ([q(f'ds_read_b128 %[{buf}a{g}], %[rA{slot}{ks}] offset:{g * FRAG}') for g in range(8)] +
-            [q(f'ds_read_b128 %[{buf}b{g}], %[rB{slot}{ks}] offset:{g * FRAG}') for g in range(8)])
+    return ([q(f'ds_read_b128 %[{buf}a{g}], %[rA{a_slot}{ks}] offset:{g * FRAG}') for g in range(8)] +
+            [q(f'ds_read_b128 %[{buf}b{g}], %[rB{b_slot}{ks}] offset:{g * FRAG}') for g in range(8)])
 
 
-def mainloop():
+def mainloop(f):
     body = []
-    # prologue: tiles 0 and 1 into slots 0 and 1; tile 0 landed; its first step
+    breg = "p" if f.split else "o"
+    # prologue: A and B tiles 0 and 1, and B tiles up to b_ahead - 1 (or the
+    # offsets of B tile 2 when the first half of tile 0 loads it); tile 0
+    # landed; its first step
     for t in range(2):
-        body += offsets([q(f's_mov_b32 %[st], {t}')])
+        body += flat(offsets([q(f's_mov_b32 %[st], {t}')]))
         for g in range(16):
-            body += dma(g, t)
-    body += [q('s_waitcnt vmcnt(16)'), q('s_barrier')]
-    body += reads('x', 0, 0)
+            body += dma(f, g, t, t)
+    for t in range(2, 3 if f.b_first else f.b_ahead):
+        if f.b_first:
+            body += flat(offsets([q(f's_mov_b32 %[st], {t}')], "p", "ps"))
+        else:
+            body += flat(offsets([q(f's_mov_b32 %[st], {t}')]))
+            for g in range(8, 16):
+                body += dma(f, g, None, t)
+    pro_keep = 0 if f.b_first else 8 * (f.b_ahead - 2)
+    body += [q(f's_waitcnt vmcnt({16 + pro_keep})'), q('s_barrier')]
+    body += reads('x', 0, 0, 0)
     body += [q('s_mov_b32 %[sk], 0'), q('s_cmp_eq_u32 %[nk], 0'), q('s_cbranch_scc1 L_ow_done_%=')]
     body += [q('L_ow_top_%=:')]
-    for s in range(2):                                  # tile k with k % 2 == s
-        load_off = offsets([q('s_add_u32 %[st], %[sk], 2')])   # tile k + 2, loaded this tile
+    for p in range(f.unroll):                           # tile k with k % unroll == p
+        sa, sb = p % 2, p % f.b_slots
+        na, nb = (p + 1) % 2, (p + 1) % f.b_slots
+        # offsets of A(k + 2), loaded in this tile's second half, and of the
+        # B tile loaded with it or, when B loads in first halves, of B(k + 3)
+        # for the next tile's first half
+        a_off = offsets([q('s_add_u32 %[st], %[sk], 2')])
+        b_tile = 3 if f.b_first else f.b_ahead
+        b_off = offsets([q(f's_add_u32 %[st], %[sk], {b_tile}')], "p", "ps") if f.split else []
+        first_off = a_off if f.b_first else [[x] for x in flat(a_off + b_off)]
         body += [q('s_waitcnt lgkmcnt(0)')]
-        rd = reads('y', s, 1)
+        rd = reads('y', sa, sb, 1)
         for g in range(16):
             body += [mfma(4 * g, 'x'), mfma(4 * g + 1, 'x'), rd[g], mfma(4 * g + 2, 'x')]
-            h = g - 2                                   # two groups in: the last loads have issued
-            if 0 <= h < 8:
-                body += load_off[2 * h:2 * h + 2]
-            elif h == 8:
-                body += load_off[16:]
+            if f.b_first and g % 2 == 1:                # B(k + 2) into the slot B(k - 1) left
+                body += dma(f, 8 + g // 2, None, (p + 2) % f.b_slots, breg)
+            # from two groups in (the previous half's last loads have issued)
+            body += spread(first_off, g)
             body.append(mfma(4 * g + 3, 'x'))
-        body += [q('s_waitcnt vmcnt(0) lgkmcnt(0)'), q('s_barrier')]
-        rd = reads('x', 1 - s, 0)
+        # tile k + 1 landed for this wave (the B tile loaded last may stay
+        # in flight), and this wave's reads of slot (sa, sb) are done
+        keep = 8 if f.split else 0
+        body += [q(f's_waitcnt vmcnt({keep}) lgkmcnt(0)'), q('s_barrier')]
+        rd = reads('x', na, nb, 0)
         for g in range(16):
             body += [mfma(4 * g, 'y'), mfma(4 * g + 1, 'y'), rd[g], mfma(4 * g + 2, 'y')]
-            body += dma(g, s)
+            if not f.b_first:
+                body += dma(f, g, sa, sb, breg)
+            elif g % 2 == 0:                            # A(k + 2) into the slot A(k) leaves
+                body += dma(f, g // 2, sa, None)
+            if f.b_first:
+                body += spread(b_off, g)
             body.append(mfma(4 * g + 3, 'y'))
         body += [q('s_add_u32 %[sk], %[sk], 1'), q('s_cmp_ge_u32 %[sk], %[nk]'),
                  q('s_cbranch_scc1 L_ow_done_%=')]
@@ -133,29 +201,42 @@ def mainloop():
     return body
 
 
-def statement():
+def statement(f, name):
     outs = [f'[c{i}{j}] "+a"(acc[{i}][{j}])' for i in range(8) for j in range(8)]
     outs += [f'[{b}{o}{i}] "=&v"({b}{o}[{i}])' for b in 'xy' for o in 'ab' for i in range(8)]
     outs += [f'[o{i}] "=&v"(o{i})' for i in range(8)] + ['[vs] "=&v"(vs)']
+    if f.split:
+        outs += [f'[p{i}] "=&v"(p{i})' for i in range(8)] + ['[ps] "=&v"(ps)']
     outs += [f'[{n}] "=&s"({n})' for n in ('sk', 'st', 'se')]
-    ins = [f'[r{o}{s}{k}] "v"(r{o}{s}{k})' for o in 'AB' for s in range(2) for k in range(2)]
+    ins = [f'[rA{s}{k}] "v"(rA{s}{k})' for s in range(2) for k in range(2)]
+    ins += [f'[rB{s}{k}] "v"(rB{s}{k})' for s in range(f.b_slots) for k in range(2)]
     ins += [f'[{n}] "v"({n})' for n in ('lbase', 'lch8', 'lstep', 'oor')]
     ins += [f'[{n}] "s"({n})' for n in ('wb', 'rwa', 'rwb')] + ['[nk] "s"(ow_nk)', '[kk] "s"(ow_kk)']
-    lines = ["// Generated by gen_onewave_mainloop.py (same directory); do not edit.",
+    lines = [f"// Generated by gen_onewave_mainloop.py (same directory); do not edit.  {name}",
              "asm volatile("]
-    lines += ["    " + ln for ln in mainloop()]
+    lines += ["    " + ln for ln in mainloop(f)]
     lines.append("    : " + ",\n      ".join(outs))
     lines.append("    : " + ",\n      ".join(ins))
     lines.append('    : "memory", "m0", "scc", "vcc");')
     return "\n".join(lines) + "\n"
 
 
-def write(path=None):
-    path = path or os.path.join(os.path.dirname(os.path.abspath(__file__)), "onewave_mainloop.inc")
-    with open(path, "w") as f:
-        f.write(statement())
-    return path
+FORMS = {"onewave_mainloop.inc": (Form(2), "Schedule 10: A and B in two slots."),
+         "onewave_b3_mainloop.inc": (Form(3), "Schedule 11: A in two slots, B in three."),
+         "onewave_b3h_mainloop.inc": (Form(3, True),
+                                      "Schedule 12: A in two slots, B in three, B loaded in first halves.")}
+
+
+def write(directory=None):
+    directory = directory or os.path.dirname(os.path.abspath(__file__))
+    paths = []
+    for fname, (f, name) in FORMS.items():
+        path = os.path.join(directory, fname)
+        with open(path, "w") as fh:
+            fh.write(statement(f, name))
+        paths.append(path)
+    return paths
 
 
 if __name__ == "__main__":
-    print(write())
+    print("\n".join(write()))

@@ -141,6 +141,10 @@ const Variant kVariants[] = {
     // one wave per SIMD, 128x128 each, the mainloop as scheduled assembly
     // (schedule 10: two 64 KiB slots)
     variant<sg::Cfg<256, 256, 64, 2, 2, 2, 10>>(),
+    // (schedule 11: A in two slots, B in three, 160 KiB)
+    variant<sg::Cfg<256, 256, 64, 3, 2, 2, 11>>(),
+    // (schedule 12: as 11, the B loads in the first half of each tile)
+    variant<sg::Cfg<256, 256, 64, 3, 2, 2, 12>>(),
     // whole K extent in the ring, epilogue per row block (schedule 4, K <= S * BK)
     variant<sg::Cfg<128, 128, 64, 2, 2, 2, 4>>(),
     // persistent workgroups, one ring across output tiles (schedule 3)
@@ -169,7 +173,7 @@ const Variant *find_variant(const sg_config *c)
 // the tiled 256x256 kernel; 2048 x 2048 x 128: 4.8 against 5.1 us for
 // 128x128 S3).  Otherwise the cheapest of these, in units of
 // one full round of 256 workgroups of the 256x256 kernel:
-//   256x256x64, schedule 8 or 10 (one per CU)        1.00 per round of 256
+//   256x256x64, schedule 10 or 12 (one per CU)       1.00 per round of 256
 //   128x128x64 S2, schedule 1 (two per CU)           0.66 per round of 512
 //   128x128x64 S3, schedule 1 (one per CU)           0.42 per round of 256
 //   128x128x64 S2 persistent (K <= 1024, no C)       0.9 x the S2 figure
@@ -180,13 +184,16 @@ const Variant *find_variant(const sg_config *c)
 // and at K = 1024 and 512 it is within 2 % of the best choice.  The
 // persistent factor comes from the tall shape 81920 x 256 x 256 (21.3 us
 // against 23.7 tiled and 25.1 for 256x256 tiles).
-// Within the 256x256 family, schedule 10 (one wave per SIMD) when every row
+// Within the 256x256 family, one wave per SIMD: schedule 10 when every row
 // of A and B starts on a 128-byte line (K % 64 == 0 and 128-byte aligned
-// operands), else schedule 8.  Schedule 10 was 1-4 % faster at 8192^3,
-// 4096^3, 12288^2 x 4096, 6144^2 x 4096, 5120^2 x 8192, 8000^2 x 8192 and
-// 16384 x 1024 x 4096, and 6-7 % slower when the rows straddle lines
-// (K = 8200): with two ring slots its loads have less time to land, and a
-// row that straddles lines costs two line fetches per 128 bytes.
+// operands), else schedule 12.  Schedule 10 was 1-4 % faster than the
+// two-group ping-pong (schedule 8) at 8192^3, 4096^3, 12288^2 x 4096,
+// 6144^2 x 4096, 5120^2 x 8192, 8000^2 x 8192 and 16384 x 1024 x 4096, and
+// about 0.5 % faster than schedule 12 there.  Where rows straddle lines
+// (K = 8200, 4104) a 16-byte load of a row slice touches two lines and the
+// LDS-DMA issue holds the wave longer; schedule 12, which issues half as
+// many loads in each half tile, was 2-3 % faster than schedule 8 there and
+// schedule 10 1-4 % slower than schedule 8.
 
 // Whether A and B start on 128-byte lines (with K % 64 == 0, every row does).
 bool lines_aligned(const void *A, const void *B)
@@ -219,7 +226,7 @@ const Variant *select_variant(int M, int N, int K, bool with_c, double *cost = n
         const bool persistent = K <= 1024 && !with_c && t128 > 256;
         const double cp = persistent ? 0.9 * c2 : 1e300;
         c = (lines_aligned && K % 64 == 0) ? sg_config{256, 256, 64, 2, 4, 10}
-                                           : sg_config{256, 256, 64, 3, 8, 8};
+                                           : sg_config{256, 256, 64, 3, 4, 12};
         best = c256;
         if (c3 < best) { best = c3; c = sg_config{128, 128, 64, 3, 4, 1}; }
         if (c2 < best) { best = c2; c = sg_config{128, 128, 64, 2, 4, 1}; }
@@ -238,15 +245,16 @@ constexpr int kMaxM = 0x7fffffff - 256;
 // cut along K into `splits` runs computed by separate workgroups, whose fp32
 // partials a second kernel adds up (sg::SplitWork, sg::split_reduce_kernel).
 // The mainloop follows the tiled choice: schedule 10 when every row starts
-// on a 128-byte line, else schedule 8.  Both hold one workgroup per CU (LDS),
-// so the plan and the resident count are the same for either.
-using SplitCfg = sg::Cfg<256, 256, 64, 3, 2, 4, 8>;
+// on a 128-byte line, else schedule 12.  The plan is made for the schedule-12
+// kernel (SplitCfg, whose resident count the runtime reports: one per CU);
+// the schedule-10 kernel has the same tiles, threads and residency.
+using SplitCfg = sg::Cfg<256, 256, 64, 3, 2, 2, 12>;
 using SplitCfg10 = sg::Cfg<256, 256, 64, 2, 2, 2, 10>;
 static_assert(SplitCfg10::BM == SplitCfg::BM && SplitCfg10::BN == SplitCfg::BN &&
-                  SplitCfg10::BK == SplitCfg::BK && SplitCfg10::T <= SplitCfg::T,
-              "one split plan serves both kernels");
+                  SplitCfg10::BK == SplitCfg::BK && SplitCfg10::T == SplitCfg::T,
+              "one split plan serves both split kernels");
 static_assert(2 * SplitCfg10::LDS_BYTES > 160 * 1024 && 2 * SplitCfg::LDS_BYTES > 160 * 1024,
-              "one split workgroup per CU for both kernels");
+              "one split workgroup per CU for both split kernels");
 constexpr size_t kSplitTileBytes = (size_t)SplitCfg::BM * SplitCfg::BN * 4;
 constexpr int kMaxSplits = 16;
 
@@ -402,11 +410,10 @@ sg_status launch_split(const SplitPlan &p, int M, int N, int K, float alpha, con
     int dp = p.dp_tiles, splits = p.splits;
     const hipStream_t st = static_cast<hipStream_t>(stream);
     void *args[] = {&a, &b, &d, &M, &N, &K, &alpha, &part, &dp, &splits};
-    const bool one_wave = K % 64 == 0 && lines_aligned(A, B);
-    const void *fn = one_wave ? reinterpret_cast<const void *>(&sg::gemm_tn_split_kernel<SplitCfg10>)
-                              : reinterpret_cast<const void *>(&sg::gemm_tn_split_kernel<SplitCfg>);
-    hipError_t e = hipLaunchKernel(fn, dim3((unsigned)p.grid),
-                                   dim3(one_wave ? SplitCfg10::T : SplitCfg::T), args, 0, st);
+    const bool lines = K % 64 == 0 && lines_aligned(A, B);
+    const void *fn = lines ? reinterpret_cast<const void *>(&sg::gemm_tn_split_kernel<SplitCfg10>)
+                           : reinterpret_cast<const void *>(&sg::gemm_tn_split_kernel<SplitCfg>);
+    hipError_t e = hipLaunchKernel(fn, dim3((unsigned)p.grid), dim3(SplitCfg::T), args, 0, st);
     if (e != hipSuccess) return SG_ERR_HIP;
     const float *cpart = part;
     void *rargs[] = {&cpart, &d, &M, &N, &alpha, &dp, &splits};

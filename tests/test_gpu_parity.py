@@ -119,7 +119,8 @@ def test_every_variant_on_ragged_shapes(shape):
                                  (128, 128, 64, 2, 4, 3), (256, 256, 64, 2, 8, 3),
                                  (128, 128, 64, 2, 4, 4), (256, 256, 64, 2, 8, 5),
                                  (256, 256, 64, 2, 8, 7), (256, 256, 64, 3, 8, 8),
-                                 (256, 256, 64, 2, 4, 10)])
+                                 (256, 256, 64, 2, 4, 10), (256, 256, 64, 3, 4, 11),
+                                 (256, 256, 64, 3, 4, 12)])
 def test_tiny_shape_grid(cfg):
     # every M, N and K tail against every tile boundary of the variant
     say(f"[case] tiny grid cfg={cfg}")
@@ -142,6 +143,10 @@ def test_tiny_shape_grid(cfg):
                                        ((4352, 4104, 200), (256, 256, 64, 3, 8, 8)),
                                        ((4352, 4104, 200), (256, 256, 64, 2, 4, 10)),
                                        ((4352, 4360, 4104), (256, 256, 64, 2, 4, 10)),
+                                       ((4352, 4104, 200), (256, 256, 64, 3, 4, 11)),
+                                       ((4352, 4360, 4104), (256, 256, 64, 3, 4, 11)),
+                                       ((4352, 4104, 200), (256, 256, 64, 3, 4, 12)),
+                                       ((4352, 4360, 4104), (256, 256, 64, 3, 4, 12)),
                                        ((2304, 2304, 520), (128, 128, 32, 4, 4, 1)),
                                        ((2304, 2312, 1000), (256, 256, 32, 3, 8, 0)),
                                        ((4352, 4360, 336), (256, 256, 64, 2, 8, 2)),
@@ -156,10 +161,10 @@ def test_k_tail_on_grids_of_several_rounds(shape, cfg):
 
 
 def test_operand_line_alignment_selects_schedule():
-    # with K % 64 == 0 the library runs the one-wave schedule (10) when A
-    # and B start on 128-byte lines and the split-load ping-pong (8) when A
-    # starts 16 bytes past one; both are compared with the oracle element
-    # by element, and with each other bit for bit (same MFMA, same K order)
+    # with K % 64 == 0 the library runs schedule 10 when A and B start on
+    # 128-byte lines and schedule 12 when A starts 16 bytes past one; both
+    # are compared with the oracle element by element, and with each other
+    # bit for bit (same MFMA, same K order)
     M, N, K = 4104, 4096, 1088
     A, B = inputs.operands(M, N, K, 4096 + 11)
     ref = oracle.gemm_tn_f64(A, B)
@@ -207,7 +212,8 @@ def test_persistent_workgroups_loop_over_tiles(shape):
 @pytest.mark.parametrize("alpha", [None, -1.0, -0.375])
 @pytest.mark.parametrize("cfg", [None] + PERSISTENT[:2] + SHORTK +
                          [(256, 256, 64, 2, 8, 7), (256, 256, 64, 3, 8, 8),
-                          (256, 256, 64, 2, 4, 10)])
+                          (256, 256, 64, 2, 4, 10), (256, 256, 64, 3, 4, 11),
+                          (256, 256, 64, 3, 4, 12)])
 def test_k_zero_every_schedule(cfg, alpha):
     # the empty sum is +0 (bit pattern 0) for either sign of alpha
     say(f"[case] K=0 {cfg} alpha={alpha}")
@@ -245,7 +251,9 @@ def test_zero_sums_are_plus_zero_every_variant(alpha):
 @pytest.mark.parametrize("shape,cfg", [((40, 16, 1 << 21), None), ((8, 1 << 21, 8), None),
                                        ((264, 24, (1 << 21) - 8), None),
                                        ((264, 24, (1 << 21) - 8), (256, 256, 64, 3, 8, 8)),
-                                       ((264, 24, 1 << 21), (256, 256, 64, 2, 4, 10))])
+                                       ((264, 24, 1 << 21), (256, 256, 64, 2, 4, 10)),
+                                       ((264, 24, (1 << 21) - 8), (256, 256, 64, 3, 4, 11)),
+                                       ((264, 24, (1 << 21) - 8), (256, 256, 64, 3, 4, 12))])
 def test_maximum_k_and_n(shape, cfg):
     # K and N at the documented limit 2^21: per-workgroup buffer ranges and
     # offsets come closest to 2^31 here (the last case with 256-row A and B
@@ -285,7 +293,9 @@ def test_empty_m_or_n_leaves_output_untouched():
                                        ((256, 256, 64, 2, 8, 5), (300, 264, 136)),
                                        ((256, 256, 64, 2, 8, 7), (300, 264, 136)),
                                        ((256, 256, 64, 3, 8, 8), (300, 264, 136)),
-                                       ((256, 256, 64, 2, 4, 10), (300, 264, 136))])
+                                       ((256, 256, 64, 2, 4, 10), (300, 264, 136)),
+                                       ((256, 256, 64, 3, 4, 11), (300, 264, 136)),
+                                       ((256, 256, 64, 3, 4, 12), (300, 264, 136))])
 def test_canary_guard_bands(cfg, shape):
     # D sits inside a larger buffer filled with a NaN pattern; nothing outside
     # D may change and every element of D must be written
@@ -310,7 +320,8 @@ def test_alpha_values(alpha):
     A, B = inputs.operands(384, 392, 520, 91)
     a32 = float(np.float32(alpha))
     # the library's choice, and the large-shape kernel on the same operands
-    for cfg in (None, (256, 256, 64, 3, 8, 8), (256, 256, 64, 2, 4, 10)):
+    for cfg in (None, (256, 256, 64, 3, 8, 8), (256, 256, 64, 2, 4, 10), (256, 256, 64, 3, 4, 11),
+                (256, 256, 64, 3, 4, 12)):
         full_check(A, B, alpha=a32, config=cfg, label=f"alpha {alpha} {cfg}")
 
 
@@ -526,7 +537,7 @@ def test_calls_from_several_host_threads():
 
 def test_two_streams_concurrently():
     # independent calls on three streams at once (two persistent launches
-    # competing for the same CUs, and the split-load ping-pong, whose
+    # competing for the same CUs, and the one-wave schedule 12, whose
     # workgroups take a whole CU's LDS) each match the oracle
     A1, B1 = inputs.operands(20480, 256, 256, 1601)
     A2, B2 = inputs.operands(2048, 2048, 1024, 1603)
@@ -545,7 +556,7 @@ def test_two_streams_concurrently():
             o3 = sg.gemm(a3, b3)
         outs.append((o1, o2, o3))
     torch.cuda.synchronize()
-    assert sg._lib.sg_select_config(3072, 3080, 520).as_tuple() == (256, 256, 64, 3, 8, 8)
+    assert sg._lib.sg_select_config(3072, 3080, 520).as_tuple() == (256, 256, 64, 3, 4, 12)
     ref1 = oracle.gemm_tn_f64(A1, B1)
     ref2 = oracle.gemm_tn_f64(A2, B2)
     ref3 = oracle.gemm_tn_f64(A3, B3)
@@ -608,12 +619,12 @@ def test_ragged8000():
 @pytest.mark.parametrize("shape", [(3072, 3080, 520), (40960, 256, 2056), (2600, 2560, 1032)])
 def test_selection_refit_shapes(shape):
     # shapes whose tile family the fitted round-cost model decides: mid-size
-    # squares and a tall shape with a long K loop go to the 256x256
-    # split-load ping-pong, 2600 x 2560 to 128x128 tiles; every element
+    # squares and a tall shape with a long K loop go to 256x256 tiles
+    # (schedule 12: K % 64 != 0), 2600 x 2560 to 128x128 tiles; every element
     M, N, K = shape
     A, B = inputs.operands(M, N, K, 1500 + K)
     cfg = sg._lib.sg_select_config(M, N, K).as_tuple()
-    want = (128, 128, 64, 2, 4, 1) if M == 2600 else (256, 256, 64, 3, 8, 8)
+    want = (128, 128, 64, 2, 4, 1) if M == 2600 else (256, 256, 64, 3, 4, 12)
     assert cfg == want, (shape, cfg)
     full_check(A, B, label=f"refit {shape} -> {cfg}")
 

@@ -74,9 +74,9 @@ def test_split_runs_match_the_oracle(shape, splits):
 
 
 def test_split_line_alignment_selects_schedule():
-    # K % 64 == 0: with A and B on 128-byte lines the pieces run the one-wave
-    # schedule (10), with A 16 bytes past a line the split-load ping-pong
-    # (8); the same runs in the same order give the same bits, and both
+    # K % 64 == 0: with A and B on 128-byte lines the pieces run schedule
+    # 10, with A 16 bytes past a line schedule 12; the same runs in the same
+    # order give the same bits, and both
     # match the oracle in every element (M and N tails, uneven runs)
     M, N, K = 2056, 1040, 1024
     A, B = inputs.operands(M, N, K, 2999)

@@ -1,6 +1,7 @@
-"""CPU checks of the schedule-10 mainloop text (onewave_mainloop.inc).
+"""CPU checks of the mainloop texts of schedules 10, 11 and 12
+(onewave_mainloop.inc, onewave_b3_mainloop.inc, onewave_b3h_mainloop.inc).
 
-The mainloop is one inline-assembly statement written by
+Each mainloop is one inline-assembly statement written by
 gen_onewave_mainloop.py, so neither the compiler nor the GPU parity tests see
 its hazards one by one.  This file executes the statement's text
 symbolically, for one wave, for every K-tile count up to a few tiles past the
@@ -33,10 +34,30 @@ import pytest
 
 CSRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                     "stage_pipelined_mainloop_amd", "csrc")
-INC = os.path.join(CSRC, "onewave_mainloop.inc")
-
-SLOT = 65536          # one ring slot: 32 KiB of A rows, then 32 KiB of B rows
+PART = 32768          # one operand tile in LDS: 256 rows of 128 bytes
 LOADS = 8             # 16-byte LDS-DMA loads per lane per operand per tile
+
+
+def slot_sched10(off):
+    """Schedule 10: slot s holds A rows at s * 64 KiB, then B rows."""
+    slot, within = divmod(off, 2 * PART)
+    return ("A" if within < PART else "B"), slot
+
+
+def slot_sched11(off):
+    """Schedule 11: two A slots, then three B slots, 32 KiB each."""
+    return ("A", off // PART) if off < 2 * PART else ("B", (off - 2 * PART) // PART)
+
+
+# text file, its LDS layout, its mid-tile wait, its prologue wait
+FORMS = {
+    "sched10": ("onewave_mainloop.inc", slot_sched10, "s_waitcnt vmcnt(0) lgkmcnt(0)",
+                "s_waitcnt vmcnt(16)"),
+    "sched11": ("onewave_b3_mainloop.inc", slot_sched11, "s_waitcnt vmcnt(8) lgkmcnt(0)",
+                "s_waitcnt vmcnt(24)"),
+    "sched12": ("onewave_b3h_mainloop.inc", slot_sched11, "s_waitcnt vmcnt(8) lgkmcnt(0)",
+                "s_waitcnt vmcnt(16)"),
+}
 SGPR_OPERANDS = {"wb", "rwa", "rwb", "nk", "kk", "sk", "st", "se"}
 
 
@@ -57,7 +78,7 @@ class Hazard(AssertionError):
     pass
 
 
-def run(code: list[str], nk: int):
+def run(code: list[str], nk: int, layout=slot_sched10):
     """Execute `code` for nk K tiles.  Returns the per-accumulator sequences
     of (tile, K step) and the smallest number of MFMAs issued between an MFMA
     reading a fragment register and the next LDS read into it."""
@@ -186,7 +207,7 @@ def run(code: list[str], nk: int):
             d = name(a[0])
             if not v or v[0] != "range":
                 fail("selection without the range compare")
-            if d == "vs":
+            if d in ("vs", "ps"):
                 tag[d] = ("step", v[1])
             else:
                 t = tag.get(d)
@@ -204,9 +225,9 @@ def run(code: list[str], nk: int):
                 fail("source offset not from the offset block")
             tile = t[1]
             operand = {"rwa": "A", "rwb": "B"}[name(a[1])]
-            slot, within = divmod(m0, SLOT)
-            if ("A" if within < SLOT // 2 else "B") != operand or within % 4096:
-                fail("m0 names another operand's part of the slot")
+            named, slot = layout(m0)
+            if named != operand or m0 % 4096:
+                fail("m0 names another operand's part of the ring")
             key = (operand, slot)
             if any(e >= epoch for e in read_done.get(key, [])) or \
                     any(k == key for _, k in lgkm):
@@ -276,21 +297,23 @@ def run(code: list[str], nk: int):
     return acc, min_gap
 
 
-@pytest.fixture(scope="module")
-def code():
-    with open(INC) as f:
+def load(form):
+    with open(os.path.join(CSRC, FORMS[form][0])) as f:
         return instructions(f.read())
 
 
-def test_committed_text_is_the_generator_output(tmp_path):
-    out = _generator().write(str(tmp_path / "mainloop.inc"))
-    with open(out) as f, open(INC) as g:
-        assert f.read() == g.read(), "regenerate onewave_mainloop.inc"
+def test_committed_texts_are_the_generator_output(tmp_path):
+    paths = _generator().write(str(tmp_path))
+    assert sorted(os.path.basename(p) for p in paths) == sorted(v[0] for v in FORMS.values())
+    for path in paths:
+        with open(path) as f, open(os.path.join(CSRC, os.path.basename(path))) as g:
+            assert f.read() == g.read(), "regenerate " + os.path.basename(path)
 
 
-@pytest.mark.parametrize("nk", range(0, 7))
-def test_ring_protocol_and_mfma_operands(code, nk):
-    acc, min_gap = run(code, nk)
+@pytest.mark.parametrize("form", sorted(FORMS))
+@pytest.mark.parametrize("nk", range(0, 8))
+def test_ring_protocol_and_mfma_operands(form, nk):
+    acc, min_gap = run(load(form), nk, FORMS[form][1])
     want = [(t, ks) for t in range(nk) for ks in (0, 1)]
     if nk == 0:
         assert acc == {}
@@ -302,7 +325,9 @@ def test_ring_protocol_and_mfma_operands(code, nk):
         assert min_gap >= 28, min_gap
 
 
-def test_ends_drained_with_accumulator_wait_states(code):
+@pytest.mark.parametrize("form", sorted(FORMS))
+def test_ends_drained_with_accumulator_wait_states(form):
+    code = load(form)
     done = code.index(next(i for i in code if i.startswith("L_ow_done")))
     assert code[done + 1] == "s_waitcnt vmcnt(0) lgkmcnt(0)"
     assert code[done + 2:] == ["s_nop 7"] * 3
@@ -315,27 +340,35 @@ def _mutate(code, old, new, nth=0):
     return out
 
 
-@pytest.mark.parametrize("mutation,expect", [
-    # the wait before the mid-tile barrier no longer retires the next tile
-    (("s_waitcnt vmcnt(0) lgkmcnt(0)", "s_waitcnt lgkmcnt(0)"), "not published"),
-    # the prologue barrier waits for tile 1 as well: still correct
-    (("s_waitcnt vmcnt(16)", "s_waitcnt vmcnt(0)"), None),
-    # the prologue keeps tile 0 in flight
-    (("s_waitcnt vmcnt(16)", "s_waitcnt vmcnt(24)"), "not published"),
-    # a refill right after the first tile's reads, in the same phase
-    (("s_barrier", "s_nop 0", 1), "while reads of it may be in flight"),
-    # x fragments used before their reads complete
-    (("s_waitcnt lgkmcnt(0)", "s_nop 0"), "before its LDS read completed"),
-    # m0 hazard: no s_nop between the m0 write and the DMA
-    (("s_nop 0", "s_nop 1"), "not preceded by its m0 write"),
-])
-def test_checker_catches_planted_mistakes(code, mutation, expect):
+@pytest.mark.parametrize("form", sorted(FORMS))
+@pytest.mark.parametrize("case", ["mid wait", "prologue waits for all", "prologue keeps tile 0",
+                                  "missing barrier", "missing lgkmcnt", "m0 nop", "mid wait one short"])
+def test_checker_catches_planted_mistakes(form, case):
+    fname, layout, mid, pro = FORMS[form]
+    code = load(form)
+    keep = int(re.search(r"vmcnt\((\d+)\)", mid).group(1))
+    mutation, expect = {
+        # the wait before the mid-tile barrier no longer retires the next tile
+        "mid wait": ((mid, "s_waitcnt lgkmcnt(0)"), "not published"),
+        # the prologue barrier waits for every prologue load: still correct
+        "prologue waits for all": ((pro, "s_waitcnt vmcnt(0)"), None),
+        # the prologue keeps part of tile 0 in flight
+        "prologue keeps tile 0": ((pro, "s_waitcnt vmcnt(40)"), "not published"),
+        # a refill right after the first tile's reads, in the same phase
+        "missing barrier": (("s_barrier", "s_nop 0", 1), "while reads of it may be in flight"),
+        # x fragments used before their reads complete
+        "missing lgkmcnt": (("s_waitcnt lgkmcnt(0)", "s_nop 0"), "before its LDS read completed"),
+        # m0 hazard: no s_nop between the m0 write and the DMA
+        "m0 nop": (("s_nop 0", "s_nop 1"), "not preceded by its m0 write"),
+        # one more load left in flight at the mid-tile barrier
+        "mid wait one short": ((mid, f"s_waitcnt vmcnt({keep + 1}) lgkmcnt(0)"), "not published"),
+    }[case]
     old, new = mutation[0], mutation[1]
     nth = mutation[2] if len(mutation) > 2 else 0
     bad = _mutate(code, old, new, nth)
     if expect is None:
-        run(bad, 3)
+        run(bad, 4, layout)
         return
     with pytest.raises(Hazard, match=expect):
-        for nk in range(1, 5):
-            run(bad, nk)
+        for nk in range(1, 6):
+            run(bad, nk, layout)
