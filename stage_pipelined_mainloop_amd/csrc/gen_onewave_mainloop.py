@@ -1,7 +1,8 @@
-"""Write onewave_mainloop.inc, the mainloop of schedule 10 as one inline-assembly
-statement (included by gemm_kernel.hpp; `python gen_onewave_mainloop.py` in
-this directory regenerates it, and a CPU test checks that the committed file
-is this script's output).
+"""Write onewave_mainloop.inc, onewave_b3_mainloop.inc and
+onewave_b3h_mainloop.inc, the mainloops of schedules 10, 11 and 12, each as
+one inline-assembly statement (included by gemm_kernel.hpp; `python
+gen_onewave_mainloop.py` in this directory regenerates them, and a CPU test
+checks that the committed files are this script's output).
 
 Schedule 10: a 256x256 output tile, 4 waves (one per SIMD), 128x128 per wave
 as 8x8 blocks of v_mfma_f32_16x16x32_f16 with the 64 accumulator quads in
@@ -19,6 +20,14 @@ between them:
   second half  MFMAs of (k, K step 1) from y; read (k + 1, K step 0) into x
                from slot (k + 1) % 2; LDS-DMA tile k + 2 into slot k % 2.
 
+Schedules 11 and 12 keep A in two slots of 32 KiB and B in three (160 KiB).
+Schedule 11 loads B(k + 3) with A(k + 2) in the second half of tile k, into
+the slot B(k) leaves.  Schedule 12 moves the B loads to the first half of
+tile k: B(k + 2), into the slot B(k - 1) left at the barrier in the middle of
+tile k - 1, so each half tile issues 8 loads per wave instead of 16.  Both
+wait with vmcnt(8) at the mid-tile barrier: the 8 B loads issued last may
+stay in flight.
+
 One barrier per 2048 MFMA cycles.  Tile k + 2's loads are issued over the
 second half of tile k and first needed at the barrier in the middle of tile
 k + 1: between half a tile and a whole tile of MFMA time to land (the
@@ -32,13 +41,13 @@ Hazards handled in the text: s_nop 0 between each write of m0 and the
 LDS-DMA that uses it; s_waitcnt before every fragment use and before the
 barrier; three s_nop 7 after the last MFMA so the compiler's epilogue can
 read the accumulators; fragment registers are rewritten only after at least
-28 MFMAs have issued since their last reader; SCC-using pairs (s_cmp,
-s_cselect) have no SCC-writing instruction between them; every VOP2/VOPC
-reads at most one SGPR or VCC.
+28 MFMAs have issued since their last reader; no SCC-writing instruction
+(an m0 update is an s_add_u32, which writes SCC) between a compare and the
+select that reads its SCC; every VOP2/VOPC reads at most one SGPR or VCC.
 
 Operands (named in the text): acc[8][8] ("+a"), fragment buffers xa, xb,
-ya, yb[8] and load offsets o0..o7, vs ("=&v"), scalar temporaries sk, st,
-se ("=&s"); inputs rA<slot><kstep>, rB<slot><kstep> (LDS byte address of
+ya, yb[8] and load offsets o0..o7, vs (and, for schedules 11 and 12, the
+B tile's p0..p7, ps) ("=&v"), scalar temporaries sk, st, se ("=&s"); inputs rA<slot><kstep>, rB<slot><kstep> (LDS byte address of
 this lane's first A / B fragment for that slot and K step), lbase / lch8 /
 lstep (this lane's LDS-DMA source offset of tile 0, 8 x its chunk index,
 and the offset step of one load), oor (an offset past every buffer range),
