@@ -54,7 +54,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 # host code and the measurement probe are separate sources; which kernel a
 # workload runs is checked through the variant recorded with the traffic)
 GEMM_SOURCES = ("gemm_kernel.hpp", "persistent_kernel.hpp", "shortk_kernel.hpp", "onewave_mainloop.inc",
-                "onewave_b3_mainloop.inc", "onewave_b3h_mainloop.inc")
+                "onewave_b3_mainloop.inc", "onewave_b3h_mainloop.inc", "onewave128_mainloop.inc")
 
 
 def kernel_source_sha() -> str:

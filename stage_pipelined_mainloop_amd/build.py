@@ -86,15 +86,15 @@ def check_m0_confined() -> int:
     preserve a reserved register across such a statement, so the DMA is safe
     only while no compiler-generated code in those functions uses m0: all of
     attention.hip, and in stagegemm.hip the kernels instantiated for schedules
-    10-12 (the other GEMM kernels load through the compiler's own LDS-DMA
+    10-12 and 14 (the other GEMM kernels load through the compiler's own LDS-DMA
     builtin, which sets m0 itself).  Compile both to assembly and check that
     every m0 operand there lies inside an inline-assembly region; raise
     otherwise (for instance after a compiler update).  Returns the number of
     m0 operands found, all inside the DMA statements."""
     total = 0
     checks = [("attention.hip", None),
-              # Cfg<..., 10 | 11 | 12>: the template's last argument mangles as Li10EE ...
-              ("stagegemm.hip", lambda name: any(f"Li{k}EE" in name for k in (10, 11, 12)))]
+              # Cfg<..., 10 | 11 | 12 | 14>: the template's last argument mangles as Li10EE ...
+              ("stagegemm.hip", lambda name: any(f"Li{k}EE" in name for k in (10, 11, 12, 14)))]
     for src, function in checks:
         found, stray = m0_uses(_device_asm(os.path.join(CSRC, src)), function)
         if stray:

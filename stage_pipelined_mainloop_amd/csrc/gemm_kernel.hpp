@@ -159,7 +159,8 @@ __device__ __forceinline__ int swz(int r)
 // wave per SIMD with a 128x128 tile each, its whole mainloop one scheduled
 // inline-assembly statement ("order 10" below), 11 = order 10 with a third B
 // slot, B loaded three tiles ahead, 12 = order 11 with the B loads moved to
-// the first half of each tile.
+// the first half of each tile, 14 = order 10 on a 128x128 tile (64x64 per
+// wave) with a ring of four slots.
 //
 // MFMA shape.  Schedules 0-4 use v_mfma_f32_32x32x16_f16 (32x32 blocks, K
 // steps of 16); schedules 5, 7 and 8 use v_mfma_f32_16x16x32_f16 (16x16
@@ -200,7 +201,7 @@ struct Cfg {
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
     // Orders 8, 11 and 12 keep S - 1 slots of A and S slots of B.
     static constexpr int RING_BYTES =
-        ORDER == 8 || ORDER >= 11 ? (S - 1) * A_BYTES + S * B_BYTES : S * STAGE_BYTES;
+        ORDER == 8 || ORDER == 11 || ORDER == 12 ? (S - 1) * A_BYTES + S * B_BYTES : S * STAGE_BYTES;
     // Epilogue staging: one 32-row block of each wave's sub-tile at a time,
     // unpadded rows with the slot swizzle of staged_slot.
     static constexpr int EPI_ROW = WTN * 2;
@@ -223,7 +224,7 @@ struct Cfg {
     static constexpr int NB = BN * CPR / (64 * NW);
     static constexpr int L = NA + NB;
     static_assert(S >= 2, "a ring needs at least two slots");
-    static_assert(SCHED >= 0 && SCHED <= 12 && SCHED != 6 && SCHED != 9, "mainloop order");
+    static_assert(SCHED >= 0 && SCHED <= 14 && SCHED != 6 && SCHED != 9 && SCHED != 13, "mainloop order");
     static_assert(!MF16 || BK == 64, "16x16x32 order: two K steps of 32 per tile");
     static_assert(SCHED != 3 || S == 2 || S == 3, "persistent ring: two or three slots");
     static_assert(!OWN_STAGING || WTN == 64, "unpadded staging rows are 128 bytes");
@@ -237,6 +238,8 @@ struct Cfg {
     static_assert((ORDER != 11 && ORDER != 12) ||
                       (BM == 256 && BN == 256 && BK == 64 && S == 3 && WM == 2 && WN == 2),
                   "one-wave form, third B slot: 256x256x64 tiles, 2x2 waves of 128x128");
+    static_assert(ORDER != 14 || (BM == 128 && BN == 128 && BK == 64 && S == 4 && WM == 2 && WN == 2),
+                  "one-wave form, 128x128x64 tiles, four slots, 2x2 waves of 64x64");
     static_assert(BK == 32 || BK == 64, "BK");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile is whole 32x32 blocks");
     static_assert(NA * 64 * NW == BM * CPR && NB * 64 * NW == BN * CPR, "even load split");
@@ -678,6 +681,37 @@ __device__ __forceinline__ void gemm_tn_body(const _Float16 *__restrict__ A,
             barrier();
         }
         if (grp == 0) barrier();                   // G0 idles in the last phase
+    } else if constexpr (C::ORDER == 14) {
+        // ---- Order 10 on a 128x128 tile: four waves of 64x64 (4x4 blocks of
+        // 16x16x32 MFMAs, 16 per 32-deep half tile), 64-deep K tiles in a ring
+        // of four 32 KiB slots, one barrier per tile between its halves.  Tile
+        // k + 3 refills the slot tile k - 1 left, its A loads in the first half
+        // of tile k and its B loads in the second (onewave128_mainloop.inc,
+        // written by gen_onewave_mainloop.py).
+        static_assert(C::AM == 4 && C::AN == 4 && C::NKS == 2 && C::NA == 4 && C::NB == 4,
+                      "the assembly is written for 4x4 MFMA blocks and 4 + 4 loads per wave");
+        static_assert(C::STAGE_BYTES == 32768 && C::A_BYTES == 16384, "slot layout of the assembly");
+        const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(
+            (__attribute__((address_space(3))) char *)smem);
+        const u32x4 rwa = rsrc_words(A + (size_t)m0 * K, (uint32_t)rows_a * K * 2u);
+        const u32x4 rwb = rsrc_words(B + (size_t)n0 * K, (uint32_t)rows_b * K * 2u);
+        // this lane's first fragment of each slot and K step (fb holds + A_BYTES)
+        constexpr uint32_t SB = C::STAGE_BYTES;
+        const uint32_t rA00 = lds0 + fa[0], rA01 = lds0 + fa[1];
+        const uint32_t rA10 = rA00 + SB, rA11 = rA01 + SB, rA20 = rA00 + 2 * SB, rA21 = rA01 + 2 * SB;
+        const uint32_t rA30 = rA00 + 3 * SB, rA31 = rA01 + 3 * SB;
+        const uint32_t rB00 = lds0 + fb[0], rB01 = lds0 + fb[1];
+        const uint32_t rB10 = rB00 + SB, rB11 = rB01 + SB, rB20 = rB00 + 2 * SB, rB21 = rB01 + 2 * SB;
+        const uint32_t rB30 = rB00 + 3 * SB, rB31 = rB01 + 3 * SB;
+        const uint32_t lbase = l_base + (uint32_t)kt0 * (uint32_t)(C::BK * 2);
+        const uint32_t lch8 = (uint32_t)(l_chunk * 8), lstep = l_step;
+        const uint32_t oor = kOutOfRange;
+        const uint32_t wb = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)wave * 1024u);
+        const uint32_t ow_nk = __builtin_amdgcn_readfirstlane(nk);
+        const uint32_t ow_kk = __builtin_amdgcn_readfirstlane(K - kt0 * C::BK);
+        f16x8 xa[4], xb[4], ya[4], yb[4];
+        uint32_t o0, o1, o2, o3, vs, sk, st, se;
+#include "onewave128_mainloop.inc"
     } else if constexpr (C::ORDER >= 10) {
         // ---- One wave per SIMD, 128x128 of the tile each, 64-deep K tiles,
         // one barrier per K tile between its two 32-deep halves: the ring

@@ -210,6 +210,99 @@ def mainloop(f):
     return body
 
 
+def mainloop128():
+    """Schedule 14: a 128x128 tile, 4 waves of 64x64 (4x4 blocks), 64-deep K
+    tiles in a ring of four 32 KiB slots (A rows then B rows), one barrier
+    per tile between its halves.  Tile k + 3 goes into the slot tile k - 1
+    left, its 4 A loads per wave in the first half of tile k and its 4 B
+    loads early in the second; its offsets are computed late in the second
+    half of tile k - 1.  The mid-tile wait keeps the
+    loads of tile k + 2 and the first half's loads of tile k + 3 in flight."""
+    SL, AP = 32768, 16384
+
+    def dma4(g, slot):
+        off = slot * SL + (g * 4096 if g < 4 else AP + (g - 4) * 4096)
+        rsrc = 'rwa' if g < 4 else 'rwb'
+        return [q(f's_add_u32 m0, %[wb], {off}'), q('s_nop 0'),
+                q(f'buffer_load_dwordx4 %[o{g % 4}], %[{rsrc}], 0 offen lds')]
+
+    def offs4(first):
+        return [[x] for x in first] + [
+            [q('s_lshl_b32 %[se], %[st], 6')],
+            [q('s_sub_i32 %[se], %[kk], %[se]')],
+            [q('s_cmp_lt_u32 %[st], %[nk]'), q('s_cselect_b32 %[se], %[se], 0x80000000')],
+            [q('v_cmp_gt_i32 vcc, %[se], %[lch8]')],
+            [q('s_lshl_b32 %[se], %[st], 7')],
+            [q('v_add_u32 %[o0], %[se], %[lbase]')],
+            [q('v_cndmask_b32 %[o0], %[oor], %[o0], vcc')],
+            [q('v_cndmask_b32 %[vs], 0, %[lstep], vcc')],
+        ] + [[q(f'v_add_u32 %[o{i}], %[o{i - 1}], %[vs]')] for i in range(1, 4)]
+
+    def rd4(buf, slot, ks):
+        return ([q(f'ds_read_b128 %[{buf}a{g}], %[rA{slot}{ks}] offset:{g * FRAG}') for g in range(4)] +
+                [q(f'ds_read_b128 %[{buf}b{g}], %[rB{slot}{ks}] offset:{g * FRAG}') for g in range(4)])
+
+    def mf(m, buf):
+        i, j = divmod(m, 4)
+        return q(f'v_mfma_f32_16x16x32_f16 %[c{i}{j}], %[{buf}b{j}], %[{buf}a{i}], %[c{i}{j}]')
+
+    body = []
+    for t in range(3):                                  # prologue: tiles 0..2 into slots 0..2
+        body += flat(offs4([q(f's_mov_b32 %[st], {t}')]))
+        for g in range(8):
+            body += dma4(g, t)
+    body += flat(offs4([q('s_mov_b32 %[st], 3')]))     # offsets of tile 3
+    body += [q('s_waitcnt vmcnt(16)'), q('s_barrier')]
+    body += rd4('x', 0, 0)
+    body += [q('s_mov_b32 %[sk], 0'), q('s_cmp_eq_u32 %[nk], 0'), q('s_cbranch_scc1 L_ow_done_%=')]
+    body += [q('L_ow_top_%=:')]
+    for p in range(4):                                  # tile k with k % 4 == p
+        s, nx, w = p, (p + 1) % 4, (p + 3) % 4          # read slot, next slot, refill slot
+        body += [q('s_waitcnt lgkmcnt(0)')]
+        rd = rd4('y', s, 1)
+        for g in range(8):                              # 16 MFMAs: 8 groups of 2
+            body += [mf(2 * g, 'x'), rd[g]]
+            if g % 2 == 1:                              # A loads 0..3 of tile k + 3
+                body += dma4(g // 2, w)
+            body.append(mf(2 * g + 1, 'x'))
+        body += [q('s_waitcnt vmcnt(12) lgkmcnt(0)'), q('s_barrier')]
+        rd = rd4('x', nx, 0)
+        # B loads of tile k + 3 in the first four groups, then the offsets of
+        # tile k + 4 (loaded in tile k + 1), which overwrite the registers
+        nxt = offs4([q('s_add_u32 %[st], %[sk], 4')])
+        for g in range(8):
+            body += [mf(2 * g, 'y'), rd[g]]
+            if g < 4:
+                body += dma4(4 + g, w)
+            else:
+                body += flat(nxt[(g - 4) * 4:(g - 3) * 4])
+            body.append(mf(2 * g + 1, 'y'))
+        body += flat(nxt[16:])
+        body += [q('s_add_u32 %[sk], %[sk], 1'), q('s_cmp_ge_u32 %[sk], %[nk]'),
+                 q('s_cbranch_scc1 L_ow_done_%=')]
+    body += [q('s_branch L_ow_top_%=')]
+    body += [q('L_ow_done_%=:'), q('s_waitcnt vmcnt(0) lgkmcnt(0)'),
+             q('s_nop 7'), q('s_nop 7'), q('s_nop 7')]
+    return body
+
+
+def statement128(name):
+    outs = [f'[c{i}{j}] "+a"(acc[{i}][{j}])' for i in range(4) for j in range(4)]
+    outs += [f'[{b}{o}{i}] "=&v"({b}{o}[{i}])' for b in 'xy' for o in 'ab' for i in range(4)]
+    outs += [f'[o{i}] "=&v"(o{i})' for i in range(4)] + ['[vs] "=&v"(vs)']
+    outs += [f'[{n}] "=&s"({n})' for n in ('sk', 'st', 'se')]
+    ins = [f'[r{o}{s}{k}] "v"(r{o}{s}{k})' for o in 'AB' for s in range(4) for k in range(2)]
+    ins += [f'[{n}] "v"({n})' for n in ('lbase', 'lch8', 'lstep', 'oor')]
+    ins += [f'[{n}] "s"({n})' for n in ('wb', 'rwa', 'rwb')] + ['[nk] "s"(ow_nk)', '[kk] "s"(ow_kk)']
+    lines = [f"// Generated by gen_onewave_mainloop.py (same directory); do not edit.  {name}",
+             "asm volatile("]
+    lines += ["    " + ln for ln in mainloop128()]
+    lines.append("    : " + ",\n      ".join(outs))
+    lines.append("    : " + ",\n      ".join(ins))
+    lines.append('    : "memory", "m0", "scc", "vcc");')
+    return "\n".join(lines) + "\n"
+
+
 def statement(f, name):
     outs = [f'[c{i}{j}] "+a"(acc[{i}][{j}])' for i in range(8) for j in range(8)]
     outs += [f'[{b}{o}{i}] "=&v"({b}{o}[{i}])' for b in 'xy' for o in 'ab' for i in range(8)]
@@ -239,10 +332,13 @@ FORMS = {"onewave_mainloop.inc": (Form(2), "Schedule 10: A and B in two slots.")
 def write(directory=None):
     directory = directory or os.path.dirname(os.path.abspath(__file__))
     paths = []
-    for fname, (f, name) in FORMS.items():
+    texts = {fname: statement(f, name) for fname, (f, name) in FORMS.items()}
+    texts["onewave128_mainloop.inc"] = statement128(
+        "Schedule 14: a 128x128 tile, four slots, tile k + 3 loaded over both halves of tile k.")
+    for fname, text in texts.items():
         path = os.path.join(directory, fname)
         with open(path, "w") as fh:
-            fh.write(statement(f, name))
+            fh.write(text)
         paths.append(path)
     return paths
 

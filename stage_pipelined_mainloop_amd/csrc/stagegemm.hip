@@ -145,6 +145,8 @@ const Variant kVariants[] = {
     variant<sg::Cfg<256, 256, 64, 3, 2, 2, 11>>(),
     // (schedule 12: as 11, the B loads in the first half of each tile)
     variant<sg::Cfg<256, 256, 64, 3, 2, 2, 12>>(),
+    // (schedule 14: the same on 128x128 tiles, four 32 KiB slots)
+    variant<sg::Cfg<128, 128, 64, 4, 2, 2, 14>>(),
     // whole K extent in the ring, epilogue per row block (schedule 4, K <= S * BK)
     variant<sg::Cfg<128, 128, 64, 2, 2, 2, 4>>(),
     // persistent workgroups, one ring across output tiles (schedule 3)
@@ -175,7 +177,8 @@ const Variant *find_variant(const sg_config *c)
 // one full round of 256 workgroups of the 256x256 kernel:
 //   256x256x64, schedule 10 or 12 (one per CU)       1.00 per round of 256
 //   128x128x64 S2, schedule 1 (two per CU)           0.66 per round of 512
-//   128x128x64 S3, schedule 1 (one per CU)           0.42 per round of 256
+//   128x128x64, one per CU: schedule 14 for a single round with K >= 1024
+//     and rows on 128-byte lines, else S3 schedule 1  0.34 or 0.42 per round of 256
 //   128x128x64 S2 persistent (K <= 1024, no C)       0.9 x the S2 figure
 // A partial round costs 0.75 + 0.25 x its fill: its workgroups still run
 // the whole K loop, only with less contention.  Fitted to interleaved
@@ -222,13 +225,23 @@ const Variant *select_variant(int M, int N, int K, bool with_c, double *cost = n
     } else {
         const double c256 = rounds(t256, 256);
         const double c2 = 0.66 * rounds(t128, 512);
-        const double c3 = 0.42 * rounds(t128, 256);
+        // schedule 14 (one wave per SIMD, four slots) against schedule 1 S3,
+        // interleaved at M = N = 2048: K = 2048 20.1 / 22.2 us, 8192 61.8 /
+        // 75.1, 16384 119.3 / 145.8, 1024 10.7 / 11.9 (S2), but 8.5 / 7.6
+        // at K = 512 (a longer prologue) and slower on rows that straddle
+        // lines.  Over several rounds its tiles lose their L2 reuse: 4352^2
+        // x 4096 189.6 against 159.4 us for 256x256 tiles (schedule 10).
+        const bool c3_one_wave = lines_aligned && K % 64 == 0 && K >= 1024 && t128 <= 256;
+        const double c3 = (c3_one_wave ? 0.34 : 0.42) * rounds(t128, 256);
         const bool persistent = K <= 1024 && !with_c && t128 > 256;
         const double cp = persistent ? 0.9 * c2 : 1e300;
         c = (lines_aligned && K % 64 == 0) ? sg_config{256, 256, 64, 2, 4, 10}
                                            : sg_config{256, 256, 64, 3, 4, 12};
         best = c256;
-        if (c3 < best) { best = c3; c = sg_config{128, 128, 64, 3, 4, 1}; }
+        if (c3 < best) {
+            best = c3;
+            c = c3_one_wave ? sg_config{128, 128, 64, 4, 4, 14} : sg_config{128, 128, 64, 3, 4, 1};
+        }
         if (c2 < best) { best = c2; c = sg_config{128, 128, 64, 2, 4, 1}; }
         if (cp < best) { best = cp; c = sg_config{128, 128, 64, 2, 4, 3}; }
     }

@@ -286,12 +286,14 @@ def test_selection_returns_compiled_variants():
         assert c.as_tuple() in {x.as_tuple() for x in _lib.configs()}
     # the measured choices: big squares tiled 256x256x64 on one wave per
     # SIMD (schedule 10 when K % 64 == 0, else 12), the skinny tall
-    # shape persistent 128x128x64, the one-wave sweep grid 128x128x64 S3
+    # shape persistent 128x128x64, the one-wave sweep grid 128x128x64 on one
+    # wave per SIMD (schedule 14) from K = 1024, S3 schedule 1 below
     assert _lib.sg_select_config(8192, 8192, 8192).as_tuple() == (256, 256, 64, 2, 4, 10)
     assert _lib.sg_select_config(8000, 7936, 8200).as_tuple() == (256, 256, 64, 3, 4, 12)
     assert _lib.sg_select_config(8192, 8192, 8200).as_tuple() == (256, 256, 64, 3, 4, 12)
     assert _lib.sg_select_config(81920, 256, 256).as_tuple() == (128, 128, 64, 2, 4, 3)
-    assert _lib.sg_select_config(2048, 2048, 2048).as_tuple() == (128, 128, 64, 3, 4, 1)
+    assert _lib.sg_select_config(2048, 2048, 2048).as_tuple() == (128, 128, 64, 4, 4, 14)
+    assert _lib.sg_select_config(2048, 2048, 1000).as_tuple() == (128, 128, 64, 3, 4, 1)
     assert _lib.sg_select_config(81920, 256, 4096).as_tuple() == (256, 256, 64, 2, 4, 10)
     assert _lib.sg_select_config(2560, 2560, 4096).as_tuple() == (128, 128, 64, 2, 4, 1)
     assert _lib.sg_select_config(3072, 3072, 4096).as_tuple() == (256, 256, 64, 2, 4, 10)
@@ -374,7 +376,7 @@ def test_split_plan_on_the_host():
             assert p.workgroups == tiles - left + left * eff
             assert p.workspace_bytes == left * eff * tile
     # the time model's choices on a 256-CU device, for shapes it was fitted to
-    want = {(2048, 2048, 16384): 4, (2048, 2048, 8192): 4, (6144, 6144, 4096): 4,
+    want = {(2048, 2048, 16384): 4, (2048, 2048, 8192): 1, (6144, 6144, 4096): 4,
             (4352, 4352, 4096): 6, (2048, 2048, 2048): 1, (2048, 2048, 512): 1,
             (3072, 3072, 4096): 1, (2560, 2560, 4096): 1, (8192, 8192, 8192): 1,
             (8000, 7936, 8200): 1, (81920, 256, 256): 1, (4096, 4096, 128): 1}

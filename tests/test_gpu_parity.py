@@ -120,7 +120,7 @@ def test_every_variant_on_ragged_shapes(shape):
                                  (128, 128, 64, 2, 4, 4), (256, 256, 64, 2, 8, 5),
                                  (256, 256, 64, 2, 8, 7), (256, 256, 64, 3, 8, 8),
                                  (256, 256, 64, 2, 4, 10), (256, 256, 64, 3, 4, 11),
-                                 (256, 256, 64, 3, 4, 12)])
+                                 (256, 256, 64, 3, 4, 12), (128, 128, 64, 4, 4, 14)])
 def test_tiny_shape_grid(cfg):
     # every M, N and K tail against every tile boundary of the variant
     say(f"[case] tiny grid cfg={cfg}")
@@ -147,6 +147,8 @@ def test_tiny_shape_grid(cfg):
                                        ((4352, 4360, 4104), (256, 256, 64, 3, 4, 11)),
                                        ((4352, 4104, 200), (256, 256, 64, 3, 4, 12)),
                                        ((4352, 4360, 4104), (256, 256, 64, 3, 4, 12)),
+                                       ((4352, 4104, 200), (128, 128, 64, 4, 4, 14)),
+                                       ((2056, 2312, 4104), (128, 128, 64, 4, 4, 14)),
                                        ((2304, 2304, 520), (128, 128, 32, 4, 4, 1)),
                                        ((2304, 2312, 1000), (256, 256, 32, 3, 8, 0)),
                                        ((4352, 4360, 336), (256, 256, 64, 2, 8, 2)),
@@ -213,7 +215,7 @@ def test_persistent_workgroups_loop_over_tiles(shape):
 @pytest.mark.parametrize("cfg", [None] + PERSISTENT[:2] + SHORTK +
                          [(256, 256, 64, 2, 8, 7), (256, 256, 64, 3, 8, 8),
                           (256, 256, 64, 2, 4, 10), (256, 256, 64, 3, 4, 11),
-                          (256, 256, 64, 3, 4, 12)])
+                          (256, 256, 64, 3, 4, 12), (128, 128, 64, 4, 4, 14)])
 def test_k_zero_every_schedule(cfg, alpha):
     # the empty sum is +0 (bit pattern 0) for either sign of alpha
     say(f"[case] K=0 {cfg} alpha={alpha}")
@@ -253,7 +255,8 @@ def test_zero_sums_are_plus_zero_every_variant(alpha):
                                        ((264, 24, (1 << 21) - 8), (256, 256, 64, 3, 8, 8)),
                                        ((264, 24, 1 << 21), (256, 256, 64, 2, 4, 10)),
                                        ((264, 24, (1 << 21) - 8), (256, 256, 64, 3, 4, 11)),
-                                       ((264, 24, (1 << 21) - 8), (256, 256, 64, 3, 4, 12))])
+                                       ((264, 24, (1 << 21) - 8), (256, 256, 64, 3, 4, 12)),
+                                       ((136, 24, (1 << 21) - 8), (128, 128, 64, 4, 4, 14))])
 def test_maximum_k_and_n(shape, cfg):
     # K and N at the documented limit 2^21: per-workgroup buffer ranges and
     # offsets come closest to 2^31 here (the last case with 256-row A and B
@@ -295,7 +298,8 @@ def test_empty_m_or_n_leaves_output_untouched():
                                        ((256, 256, 64, 3, 8, 8), (300, 264, 136)),
                                        ((256, 256, 64, 2, 4, 10), (300, 264, 136)),
                                        ((256, 256, 64, 3, 4, 11), (300, 264, 136)),
-                                       ((256, 256, 64, 3, 4, 12), (300, 264, 136))])
+                                       ((256, 256, 64, 3, 4, 12), (300, 264, 136)),
+                                       ((128, 128, 64, 4, 4, 14), (300, 264, 136))])
 def test_canary_guard_bands(cfg, shape):
     # D sits inside a larger buffer filled with a NaN pattern; nothing outside
     # D may change and every element of D must be written

@@ -1,5 +1,6 @@
-"""CPU checks of the mainloop texts of schedules 10, 11 and 12
-(onewave_mainloop.inc, onewave_b3_mainloop.inc, onewave_b3h_mainloop.inc).
+"""CPU checks of the mainloop texts of schedules 10, 11, 12 and 14
+(onewave_mainloop.inc, onewave_b3_mainloop.inc, onewave_b3h_mainloop.inc,
+onewave128_mainloop.inc).
 
 Each mainloop is one inline-assembly statement written by
 gen_onewave_mainloop.py, so neither the compiler nor the GPU parity tests see
@@ -35,7 +36,6 @@ import pytest
 CSRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                     "stage_pipelined_mainloop_amd", "csrc")
 PART = 32768          # one operand tile in LDS: 256 rows of 128 bytes
-LOADS = 8             # 16-byte LDS-DMA loads per lane per operand per tile
 
 
 def slot_sched10(off):
@@ -49,14 +49,26 @@ def slot_sched11(off):
     return ("A", off // PART) if off < 2 * PART else ("B", (off - 2 * PART) // PART)
 
 
-# text file, its LDS layout, its mid-tile wait, its prologue wait
+def slot_sched14(off):
+    """Schedule 14: four 32 KiB slots of 128 A rows, then 128 B rows."""
+    slot, within = divmod(off, PART)
+    return ("A" if within < PART // 2 else "B"), slot
+
+
+# text file, its LDS layout, its mid-tile wait, its prologue wait, loads per
+# lane per operand per tile, MFMA blocks per wave side, and the smallest
+# number of MFMAs allowed between the last reader of a fragment register
+# and the LDS read that overwrites it (an MFMA reads its A and B operands as
+# it issues; the 16-MFMA halves of schedule 14 leave room for 7)
 FORMS = {
     "sched10": ("onewave_mainloop.inc", slot_sched10, "s_waitcnt vmcnt(0) lgkmcnt(0)",
-                "s_waitcnt vmcnt(16)"),
+                "s_waitcnt vmcnt(16)", 8, 8, 28),
     "sched11": ("onewave_b3_mainloop.inc", slot_sched11, "s_waitcnt vmcnt(8) lgkmcnt(0)",
-                "s_waitcnt vmcnt(24)"),
+                "s_waitcnt vmcnt(24)", 8, 8, 28),
     "sched12": ("onewave_b3h_mainloop.inc", slot_sched11, "s_waitcnt vmcnt(8) lgkmcnt(0)",
-                "s_waitcnt vmcnt(16)"),
+                "s_waitcnt vmcnt(16)", 8, 8, 28),
+    "sched14": ("onewave128_mainloop.inc", slot_sched14, "s_waitcnt vmcnt(12) lgkmcnt(0)",
+                "s_waitcnt vmcnt(16)", 4, 4, 6),
 }
 SGPR_OPERANDS = {"wb", "rwa", "rwb", "nk", "kk", "sk", "st", "se"}
 
@@ -78,7 +90,7 @@ class Hazard(AssertionError):
     pass
 
 
-def run(code: list[str], nk: int, layout=slot_sched10):
+def run(code: list[str], nk: int, layout=slot_sched10, loads=8):
     """Execute `code` for nk K tiles.  Returns the per-accumulator sequences
     of (tile, K step) and the smallest number of MFMAs issued between an MFMA
     reading a fragment register and the next LDS read into it."""
@@ -266,7 +278,7 @@ def run(code: list[str], nk: int, layout=slot_sched10):
             key = (operand, slot)
             tile = ring.get(key)
             done = dma_epochs.get((operand, slot, tile), [])
-            ready = (tile is not None and tile < nk and len(done) == LOADS and
+            ready = (tile is not None and tile < nk and len(done) == loads and
                      all(e is not None and e < epoch for e in done) and
                      last_dma_epoch[key] < epoch)
             frag[d] = (operand, tile, ks, off // 2048, ready)
@@ -311,18 +323,19 @@ def test_committed_texts_are_the_generator_output(tmp_path):
 
 
 @pytest.mark.parametrize("form", sorted(FORMS))
-@pytest.mark.parametrize("nk", range(0, 8))
+@pytest.mark.parametrize("nk", range(0, 10))
 def test_ring_protocol_and_mfma_operands(form, nk):
-    acc, min_gap = run(load(form), nk, FORMS[form][1])
+    fname, layout, mid, pro, loads, blocks, gap = FORMS[form]
+    acc, min_gap = run(load(form), nk, layout, loads)
     want = [(t, ks) for t in range(nk) for ks in (0, 1)]
     if nk == 0:
         assert acc == {}
     else:
-        assert sorted(acc) == [(i, j) for i in range(8) for j in range(8)]
+        assert sorted(acc) == [(i, j) for i in range(blocks) for j in range(blocks)]
         for ij, seq in acc.items():
             assert seq == want, ij
         # a fragment register is rewritten only well after its last MFMA reader
-        assert min_gap >= 28, min_gap
+        assert min_gap >= gap, min_gap
 
 
 @pytest.mark.parametrize("form", sorted(FORMS))
@@ -344,7 +357,7 @@ def _mutate(code, old, new, nth=0):
 @pytest.mark.parametrize("case", ["mid wait", "prologue waits for all", "prologue keeps tile 0",
                                   "missing barrier", "missing lgkmcnt", "m0 nop", "mid wait one short"])
 def test_checker_catches_planted_mistakes(form, case):
-    fname, layout, mid, pro = FORMS[form]
+    fname, layout, mid, pro, loads = FORMS[form][:5]
     code = load(form)
     keep = int(re.search(r"vmcnt\((\d+)\)", mid).group(1))
     mutation, expect = {
@@ -354,8 +367,10 @@ def test_checker_catches_planted_mistakes(form, case):
         "prologue waits for all": ((pro, "s_waitcnt vmcnt(0)"), None),
         # the prologue keeps part of tile 0 in flight
         "prologue keeps tile 0": ((pro, "s_waitcnt vmcnt(40)"), "not published"),
-        # a refill right after the first tile's reads, in the same phase
-        "missing barrier": (("s_barrier", "s_nop 0", 1), "while reads of it may be in flight"),
+        # the mid-tile barrier of the first tile gone: a refill in the phase
+        # that reads the slot, or reads of a tile not yet published
+        "missing barrier": (("s_barrier", "s_nop 0", 1),
+                            "while reads of it may be in flight|not published"),
         # x fragments used before their reads complete
         "missing lgkmcnt": (("s_waitcnt lgkmcnt(0)", "s_nop 0"), "before its LDS read completed"),
         # m0 hazard: no s_nop between the m0 write and the DMA
@@ -367,8 +382,8 @@ def test_checker_catches_planted_mistakes(form, case):
     nth = mutation[2] if len(mutation) > 2 else 0
     bad = _mutate(code, old, new, nth)
     if expect is None:
-        run(bad, 4, layout)
+        run(bad, 4, layout, loads)
         return
     with pytest.raises(Hazard, match=expect):
         for nk in range(1, 6):
-            run(bad, nk, layout)
+            run(bad, nk, layout, loads)
