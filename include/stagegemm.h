@@ -108,7 +108,12 @@ typedef enum sg_status {
  *      stages 3, waves 4.  The library's choice for 256 x 256 tiles when
  *      rows of A or B straddle 128-byte lines (K % 64 != 0, or a base
  *      address not 128-byte aligned), where each load touches two lines
- *      and holds the issuing wave longer. */
+ *      and holds the issuing wave longer;
+ *  14  order 10 on 128 x 128 x 64 tiles: 4 waves of 64 x 64, a ring of four
+ *      32 KiB slots, tile k + 3 loaded over the two halves of tile k.  Only
+ *      stages 4, waves 4.  The library's choice for grids of at most one
+ *      round of 128 x 128 tiles (one per compute unit) with K >= 1024 and
+ *      rows on 128-byte lines. */
 typedef struct sg_config {
     int tile_m;
     int tile_n;
