@@ -423,7 +423,11 @@ def library_call(M: int, N: int, K: int, a, b, d, alpha):
 
     def fn():
         sg.gemm_fp16_tn_alpha(M, N, K, al, *ptrs, stream)
-    return fn, variant_name(sg.sg_select_config(M, N, K)), 1
+    name = variant_name(sg.sg_select_config(M, N, K))
+    quarters = sg.gemm_fp16_tn_remainder_quarters(M, N, K)
+    if quarters > 0:
+        name += f" + {quarters} 128x128 quarters on sched14"
+    return fn, name, 1
 
 
 def timed_mean_ms(fn, target_ms: float = 40.0, min_launches: int = 20):

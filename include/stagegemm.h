@@ -135,7 +135,17 @@ typedef struct sg_config_info {
     int wg_per_cu;          /* resident workgroups per CU reported by the runtime, -1 if unknown */
 } sg_config_info;
 
-/* D = A * B^T.  See the rules above.  `stream` is a hipStream_t. */
+/* D = A * B^T.  See the rules above.  `stream` is a hipStream_t.
+ *
+ * The call runs the variant sg_select_config names, except where a grid of
+ * more than one round of 256 x 256 tiles leaves its last round at most a
+ * quarter full (rows on 128-byte lines, K % 64 == 0, K >= 1024): then the
+ * whole rounds run as 256 x 256 tiles (schedule 10) and each remaining tile
+ * as four 128 x 128 quarters (schedule 14), two kernels on `stream`
+ * ("cute(9) multistage_gemm", section 11.3, names adaptive tile sizes beside
+ * split-K).  Every element is computed the same way either way: the same
+ * MFMA in the same K order, so the results are bit for bit the same.  The
+ * same holds for gemm_fp16_tn_alpha and gemm_fp16_tn_alpha_beta. */
 sg_status gemm_fp16_tn(int M, int N, int K, const void *A, const void *B, void *D,
                        void *stream);
 
@@ -244,6 +254,13 @@ sg_status gemm_fp16_tn_splitk_noalloc(int M, int N, int K, float alpha, const vo
 sg_status gemm_fp16_tn_cfg(int M, int N, int K, float alpha, const void *A,
                            const void *B, void *D, const sg_config *cfg,
                            void *stream);
+
+/* The number of 128 x 128 quarter tiles gemm_fp16_tn would run in the
+ * remainder form for this shape with 128-byte aligned A and B on the current
+ * device (0: it runs the variant sg_select_config names alone), or -1 for a
+ * negative or empty shape or when the runtime cannot report the device's
+ * resident workgroup count.  Reads only device attributes. */
+int gemm_fp16_tn_remainder_quarters(int M, int N, int K);
 
 /* The variant gemm_fp16_tn (and gemm_fp16_tn_alpha) would run for this
  * shape with 128-byte aligned A and B (a less aligned A or B turns

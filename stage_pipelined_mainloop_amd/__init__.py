@@ -17,6 +17,7 @@ from ._lib import (SgConfig, SgConfigInfo, SgError, attention_fp16_fwd, attentio
                    gemm_fp16_tn_alpha_beta, gemm_fp16_tn_cfg, gemm_fp16_tn_splitk,
                    gemm_fp16_tn_splitk_noalloc,
                    gemm_fp16_tn_splitk_splits, gemm_fp16_tn_splitk_workspace_bytes, sg_get_config,
+                   gemm_fp16_tn_remainder_quarters,
                    sg_minimum_stages, sg_num_configs,
                    sg_persistent_wait_count, sg_pipeline_wait_count, sg_query_config, sg_select_config,
                    sg_split_plan, sg_status_string, SgSplitInfo)
@@ -178,6 +179,7 @@ __all__ = [
     "gemm", "attention", "attention_fp16_fwd", "attention_fp16_fwd_split", "attention_fp16_splits",
     "attention_fp16_workspace_bytes", "gemm_fp16_tn", "gemm_fp16_tn_alpha", "gemm_fp16_tn_alpha_beta", "gemm_fp16_tn_cfg",
     "gemm_fp16_tn_splitk", "gemm_fp16_tn_splitk_noalloc", "gemm_fp16_tn_splitk_splits",
+    "gemm_fp16_tn_remainder_quarters",
     "gemm_fp16_tn_splitk_workspace_bytes",
     "split_workspace", "sg_split_plan", "SgSplitInfo",
     "sg_select_config",

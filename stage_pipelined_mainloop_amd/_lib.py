@@ -104,6 +104,8 @@ def lib() -> ctypes.CDLL:
         L.sg_split_plan.restype = i
         L.gemm_fp16_tn_splitk_splits.argtypes = [i, i, i]
         L.gemm_fp16_tn_splitk_splits.restype = i
+        L.gemm_fp16_tn_remainder_quarters.argtypes = [i, i, i]
+        L.gemm_fp16_tn_remainder_quarters.restype = i
         L.gemm_fp16_tn_cfg.argtypes = [i, i, i, f, vp, vp, vp, ctypes.POINTER(SgConfig), vp]
         L.gemm_fp16_tn_cfg.restype = i
         L.sg_select_config.argtypes = [i, i, i, ctypes.POINTER(SgConfig)]
@@ -205,6 +207,10 @@ def gemm_fp16_tn_splitk_workspace_bytes(M: int, N: int, K: int, splits: int) -> 
 
 def gemm_fp16_tn_splitk_splits(M: int, N: int, K: int) -> int:
     return int(lib().gemm_fp16_tn_splitk_splits(M, N, K))
+
+
+def gemm_fp16_tn_remainder_quarters(M: int, N: int, K: int) -> int:
+    return int(lib().gemm_fp16_tn_remainder_quarters(M, N, K))
 
 
 def sg_split_plan(M: int, N: int, K: int, splits: int, capacity: int) -> SgSplitInfo:

@@ -399,8 +399,11 @@ struct SplitWork {
 };
 
 // The mainloop and epilogue of one workgroup (or, for a split piece, the
-// mainloop and the write of its partial tile).
-template <class C, bool SPLIT>
+// mainloop and the write of its partial tile).  SUB: the workgroup computes
+// one 128x128 quarter of a 256x256 output tile whose linear id in the
+// grouped walk is sw.dp_tiles or later (the remainder of a grid whose whole
+// rounds ran as 256x256 tiles; see gemm_tn_sub_kernel).
+template <class C, bool SPLIT, bool SUB = false>
 __device__ __forceinline__ void gemm_tn_body(const _Float16 *__restrict__ A,
                                              const _Float16 *__restrict__ B, const _Float16 *Cm,
                                              _Float16 *D, int M, int N, int K, float alpha,
@@ -425,7 +428,9 @@ __device__ __forceinline__ void gemm_tn_body(const _Float16 *__restrict__ A,
     // This workgroup's output tile (linear id in the grouped walk) and its
     // run of K tiles [kfirst, kfirst + nk).
     int tile_id = blockIdx.x;
-    int renumber = tiles_m * tiles_n;
+    // the XCD renumbering spans the whole grid, or (gemm_tn_dp_kernel) the
+    // first sw.dp_tiles tiles that its grid covers
+    int renumber = (!SPLIT && !SUB && sw.dp_tiles > 0) ? sw.dp_tiles : tiles_m * tiles_n;
     int kfirst = 0, nk = ntile;
     bool partial = false;
     int krun = 0, ltile = 0;
@@ -447,8 +452,22 @@ __device__ __forceinline__ void gemm_tn_body(const _Float16 *__restrict__ A,
     }
     int tm, tn;
     tile_coords(tile_id, tiles_m, tiles_n, renumber, tm, tn);
-    const int m0 = tm * C::BM;
-    const int n0 = tn * C::BN;
+    int m0v = tm * C::BM, n0v = tn * C::BN;
+    if constexpr (SUB) {
+        static_assert(!SPLIT && C::BM == 128 && C::BN == 128, "quarters of 256x256 tiles");
+        // quarter q of remainder tile sw.dp_tiles + q / 4; the four quarters
+        // of a tile go to one XCD (contiguous runs per XCD, as in tile_coords)
+        const int G = gridDim.x;
+        int q = blockIdx.x;
+        if ((G & 7) == 0) q = (q & 7) * (G >> 3) + (q >> 3);
+        int pm, pn;
+        tile_coords(sw.dp_tiles + q / 4, (M + 255) / 256, (N + 255) / 256, 0, pm, pn);
+        m0v = pm * 256 + 128 * ((q >> 1) & 1);
+        n0v = pn * 256 + 128 * (q & 1);
+        if (m0v >= M || n0v >= N) return;          // a quarter past the edge: nothing to do
+    }
+    const int m0 = m0v;
+    const int n0 = n0v;
     const int rows_a = (M - m0 < C::BM) ? (M - m0) : C::BM;
     const int rows_b = (N - n0 < C::BN) ? (N - n0) : C::BN;
 
@@ -1103,6 +1122,33 @@ gemm_tn_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
                const _Float16 *Cm, _Float16 *D, int M, int N, int K, float alpha, float beta)
 {
     gemm_tn_body<C, false>(A, B, Cm, D, M, N, K, alpha, beta, SplitWork{nullptr, 0, 1});
+}
+
+// The remainder of a grid of 256x256 output tiles whose first dp_tiles (in
+// the grouped walk) ran as whole rounds elsewhere: each of the remaining
+// tiles as four 128x128 quarters, one workgroup each, so a part-full last
+// round fills four times as many CUs ("cute(9) multistage_gemm", section
+// 11.3, names adaptive tile sizes beside split-K).  Grid: 4 x the remaining
+// tiles; quarters outside M x N end at once.
+template <class C>
+__global__ void __launch_bounds__(C::T)
+gemm_tn_sub_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
+                   const _Float16 *Cm, _Float16 *D, int M, int N, int K, float alpha, float beta,
+                   int dp_tiles)
+{
+    gemm_tn_body<C, false, true>(A, B, Cm, D, M, N, K, alpha, beta, SplitWork{nullptr, dp_tiles, 1});
+}
+
+// The first dp_tiles output tiles (in the grouped walk) of a grid, as the
+// tiled kernel computes them: the whole rounds of a call whose remainder
+// runs in gemm_tn_sub_kernel.  Grid: dp_tiles.
+template <class C>
+__global__ void __launch_bounds__(C::T)
+gemm_tn_dp_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
+                  const _Float16 *Cm, _Float16 *D, int M, int N, int K, float alpha, float beta,
+                  int dp_tiles)
+{
+    gemm_tn_body<C, false>(A, B, Cm, D, M, N, K, alpha, beta, SplitWork{nullptr, dp_tiles, 1});
 }
 
 // Split-K form of schedules 8, 10, 11 and 12 (see SplitWork): D = alpha * A * B^T, no C.

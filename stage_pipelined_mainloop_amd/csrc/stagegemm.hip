@@ -249,6 +249,52 @@ const Variant *select_variant(int M, int N, int K, bool with_c, double *cost = n
     return find_variant(&c);
 }
 
+// ---- remainder form of a plain call (adaptive tile size).  A grid of more
+// than one round of 256x256 tiles whose last round is at most a quarter
+// full runs its whole rounds as 256x256 tiles (schedule 10,
+// gemm_tn_dp_kernel) and each remaining tile as four 128x128 quarters
+// (schedule 14, gemm_tn_sub_kernel): one round of at most `capacity`
+// quarters instead of a round of few 256x256 workgroups.  Only where
+// schedule 14 runs well: rows on 128-byte lines and K >= 1024.  Estimated
+// like a single-round schedule-14 grid (0.34 of a 256x256 round); measured
+// in the comments of plain_rounds below.
+using SubCfg = sg::Cfg<128, 128, 64, 4, 2, 2, 14>;
+using DpCfg = sg::Cfg<256, 256, 64, 2, 2, 2, 10>;
+
+struct SubPlan {
+    int dp = 0;          // 256x256 tiles in whole rounds
+    int quarters = 0;    // 128x128 quarters of the rest (0: no remainder form)
+};
+
+SubPlan plan_sub(int M, int N, int K, bool lines_aligned, int capacity)
+{
+    SubPlan p;
+    const long long t256 = (long long)((M + 255) / 256) * ((N + 255) / 256);
+    if (!lines_aligned || K % 64 != 0 || K < 1024 || capacity <= 0 || t256 <= capacity) return p;
+    const long long left = t256 % capacity;
+    if (left == 0 || 4 * left > capacity) return p;
+    p.dp = (int)(t256 - left);
+    p.quarters = (int)(4 * left);
+    return p;
+}
+
+// Cost of the plain call in rounds of the 256x256 kernel, with the
+// remainder form where it applies and the 256x256 family is chosen.
+double plain_rounds(int M, int N, int K, bool with_c, bool lines_aligned, int capacity,
+                    const Variant **chosen = nullptr, SubPlan *sub = nullptr)
+{
+    double cost = 0.0;
+    const Variant *v = select_variant(M, N, K, with_c, &cost, lines_aligned);
+    if (chosen) *chosen = v;
+    if (!v || v->cfg.tile_m != 256) return cost;
+    const SubPlan p = plan_sub(M, N, K, lines_aligned, capacity);
+    if (p.quarters == 0) return cost;
+    const double sub_cost = (double)p.dp / capacity + 0.34 * rounds(p.quarters, 256);
+    if (sub_cost >= cost) return cost;
+    if (sub) *sub = p;
+    return sub_cost;
+}
+
 // Largest M: tile counts (M + tile_m - 1) / tile_m stay within int.
 constexpr int kMaxM = 0x7fffffff - 256;
 
@@ -333,10 +379,11 @@ int choose_splits(int M, int N, int K, int capacity)
     if (left == 0 || ntile < 2 || capacity <= 0) return 1;
     const double k_tile_us = 1.55, round_us = 3.0, reduce_us = 2.0, partial_mb_per_us = 4.6;
     const double full_round = ntile * k_tile_us + round_us;
-    double plain_rounds = 0.0;
-    select_variant(M, N, K, false, &plain_rounds);
-    if (plain_rounds <= 0.0) return 1;                 // short K: never split
-    const double plain = plain_rounds * full_round;
+    // the plain call as the library would run it (remainder form included),
+    // for 128-byte aligned operands
+    const double plain_cost = plain_rounds(M, N, K, false, true, capacity);
+    if (plain_cost <= 0.0) return 1;                   // short K: never split
+    const double plain = plain_cost * full_round;
     const double dp = (double)(whole.tiles / capacity) * full_round;   // whole-tile rounds
     int best_s = 1;
     double best = plain;
@@ -413,6 +460,52 @@ sg_status run(const Variant *v, int M, int N, int K, float alpha, float beta, co
     return e == hipSuccess ? SG_OK : SG_ERR_HIP;
 }
 
+// Resident 256x256 workgroups of the remainder form's first kernel on the
+// current device (one per CU), cached per device; 0 if the runtime cannot
+// tell.
+int sub_capacity()
+{
+    static std::atomic<int> cache[16];
+    return resident_capacity(reinterpret_cast<const void *>(&sg::gemm_tn_dp_kernel<DpCfg>),
+                             DpCfg::T, cache);
+}
+
+// The remainder form: the whole rounds, then the quarters of the rest.
+sg_status launch_sub(const SubPlan &p, int M, int N, int K, float alpha, float beta,
+                     const void *A, const void *B, const void *Cm, void *D, void *stream)
+{
+    const _Float16 *a = static_cast<const _Float16 *>(A);
+    const _Float16 *b = static_cast<const _Float16 *>(B);
+    const _Float16 *c = beta == 0.0f ? nullptr : static_cast<const _Float16 *>(Cm);
+    _Float16 *d = static_cast<_Float16 *>(D);
+    int dp = p.dp;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    void *args[] = {&a, &b, &c, &d, &M, &N, &K, &alpha, &beta, &dp};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&sg::gemm_tn_dp_kernel<DpCfg>),
+                                   dim3((unsigned)p.dp), dim3(DpCfg::T), args, 0, st);
+    if (e != hipSuccess) return SG_ERR_HIP;
+    e = hipLaunchKernel(reinterpret_cast<const void *>(&sg::gemm_tn_sub_kernel<SubCfg>),
+                        dim3((unsigned)p.quarters), dim3(SubCfg::T), args, 0, st);
+    return e == hipSuccess ? SG_OK : SG_ERR_HIP;
+}
+
+// The plain call: the chosen variant, or the remainder form where the plan
+// takes it (the plan needs the device's resident count; without it, the
+// chosen variant).
+sg_status run_plain(int M, int N, int K, float alpha, float beta, const void *A, const void *B,
+                    const void *Cm, void *D, void *stream)
+{
+    const bool lines = lines_aligned(A, B);
+    const Variant *v = nullptr;
+    SubPlan sub;
+    const long long t256 = (long long)((M + 255) / 256) * ((N + 255) / 256);
+    const int cap = t256 > 256 && lines && K % 64 == 0 && K >= 1024 ? sub_capacity() : 0;
+    plain_rounds(M, N, K, beta != 0.0f, lines, cap, &v, &sub);
+    if (!v) return SG_ERR_UNSUPPORTED;
+    if (sub.quarters > 0) return launch_sub(sub, M, N, K, alpha, beta, A, B, Cm, D, stream);
+    return run(v, M, N, K, alpha, beta, A, B, Cm, D, stream);
+}
+
 sg_status launch_split(const SplitPlan &p, int M, int N, int K, float alpha, const void *A,
                        const void *B, void *D, void *workspace, void *stream)
 {
@@ -462,9 +555,7 @@ sg_status gemm_fp16_tn_alpha(int M, int N, int K, float alpha, const void *A, co
 {
     const sg_status st = validate(M, N, K, A, B, D);
     if (st != SG_OK || M == 0 || N == 0) return st;
-    const Variant *v = select_variant(M, N, K, false, nullptr, lines_aligned(A, B));
-    if (!v) return SG_ERR_UNSUPPORTED;
-    return run(v, M, N, K, alpha, 0.0f, A, B, nullptr, D, stream);
+    return run_plain(M, N, K, alpha, 0.0f, A, B, nullptr, D, stream);
 }
 
 sg_status gemm_fp16_tn_alpha_beta(int M, int N, int K, float alpha, float beta, const void *A,
@@ -474,9 +565,7 @@ sg_status gemm_fp16_tn_alpha_beta(int M, int N, int K, float alpha, float beta, 
     if (st != SG_OK) return st;
     st = validate_c(M, N, beta, Cm, D);
     if (st != SG_OK || M == 0 || N == 0) return st;
-    const Variant *v = select_variant(M, N, K, beta != 0.0f, nullptr, lines_aligned(A, B));
-    if (!v) return SG_ERR_UNSUPPORTED;
-    return run(v, M, N, K, alpha, beta, A, B, Cm, D, stream);
+    return run_plain(M, N, K, alpha, beta, A, B, Cm, D, stream);
 }
 
 sg_status gemm_fp16_tn(int M, int N, int K, const void *A, const void *B, void *D, void *stream)
@@ -574,6 +663,16 @@ sg_status gemm_fp16_tn_splitk_noalloc(int M, int N, int K, float alpha, const vo
     void *ws = scratch_address();
     if (!ws) return SG_ERR_HIP;
     return launch_split(p, M, N, K, alpha, A, B, D, ws, stream);
+}
+
+int gemm_fp16_tn_remainder_quarters(int M, int N, int K)
+{
+    if (M <= 0 || N <= 0 || K < 0 || M > kMaxM) return -1;
+    const int cap = sub_capacity();
+    if (cap <= 0) return -1;
+    SubPlan sub;
+    plain_rounds(M, N, K, false, true, cap, nullptr, &sub);
+    return sub.quarters;
 }
 
 sg_status sg_select_config(int M, int N, int K, sg_config *out)

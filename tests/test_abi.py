@@ -17,7 +17,7 @@ S = _lib
 
 def test_every_declared_symbol_is_exported():
     declared = _lib.header_functions()
-    assert len(declared) == 21
+    assert len(declared) == 22
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
@@ -376,8 +376,8 @@ def test_split_plan_on_the_host():
             assert p.workgroups == tiles - left + left * eff
             assert p.workspace_bytes == left * eff * tile
     # the time model's choices on a 256-CU device, for shapes it was fitted to
-    want = {(2048, 2048, 16384): 4, (2048, 2048, 8192): 1, (6144, 6144, 4096): 4,
-            (4352, 4352, 4096): 6, (2048, 2048, 2048): 1, (2048, 2048, 512): 1,
+    want = {(2048, 2048, 16384): 4, (2048, 2048, 8192): 1, (6144, 6144, 4096): 1,
+            (4352, 4352, 4096): 1, (2048, 2048, 2048): 1, (2048, 2048, 512): 1,
             (3072, 3072, 4096): 1, (2560, 2560, 4096): 1, (8192, 8192, 8192): 1,
             (8000, 7936, 8200): 1, (81920, 256, 256): 1, (4096, 4096, 128): 1}
     for shape, s in want.items():

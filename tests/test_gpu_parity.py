@@ -189,6 +189,32 @@ def test_operand_line_alignment_selects_schedule():
     assert sg._lib.sg_select_config(M, N, K).as_tuple() == (256, 256, 64, 2, 4, 10)
 
 
+@pytest.mark.parametrize("shape", [(4352, 4104, 1088), (4360, 4352, 1088), (81920, 256, 1088)])
+def test_remainder_form(shape):
+    # grids of more than one round of 256x256 tiles with a last round at
+    # most a quarter full: the library's call runs the whole rounds as
+    # 256x256 tiles and each remaining tile as four 128x128 quarters
+    # (quarters past N or M end at once).  Every element against the
+    # oracle, and bit for bit against the 256x256 tiled kernel alone (same
+    # MFMA, same K order); with alpha, and with beta and C
+    M, N, K = shape
+    q = sg.gemm_fp16_tn_remainder_quarters(M, N, K)
+    assert q > 0, (shape, q)
+    A, B = inputs.operands(M, N, K, 2700 + K)
+    a32 = float(np.float32(0.375))
+    say(f"[case] remainder form {shape} quarters={q}")
+    d = full_check(A, B, alpha=a32, label=f"remainder {shape}")
+    tiled = run_gemm(A, B, alpha=a32, config=(256, 256, 64, 2, 4, 10)).cpu().numpy()
+    assert np.array_equal(d.view(np.uint16), tiled.view(np.uint16))
+    Cm = inputs.matrix(M, N, 2800 + N, "normal")
+    b32 = float(np.float32(-0.5))
+    dd = torch.full((M, N), float("nan"), dtype=torch.float16, device=DEV)
+    sg.gemm(to_dev(A), to_dev(B), out=dd, alpha=a32, beta=b32, C=to_dev(Cm))
+    torch.cuda.synchronize()
+    rep = oracle.check(dd.cpu().numpy(), oracle.gemm_tn_f64_beta(A, B, Cm, a32, b32), K)
+    assert rep.ok, str(rep)
+
+
 PERSISTENT = [c for c in VARIANTS if c[5] == 3]
 
 

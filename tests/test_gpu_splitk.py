@@ -98,20 +98,29 @@ def test_split_line_alignment_selects_schedule():
         assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), s
 
 
-def test_split_6144_square_library_choice():
-    # 576 tiles: two whole rounds and a quarter round cut along K, the
-    # library's own split count, through the Python entry
+def test_6144_square_remainder_form_and_split():
+    # 576 tiles: two whole rounds and a quarter round.  The library's call
+    # runs the whole rounds as 256x256 tiles and the quarter round as 256
+    # quarters of 128x128 (no split); the split call with 4 runs cuts the
+    # quarter round along K instead.  Both against the oracle in every
+    # element, through the Python entry and the C-ABI
     M = N = 6144
     K = 4096
     A, B = inputs.operands(M, N, K, 2201)
     a, b = to_dev(A), to_dev(B)
-    s = sg.gemm_fp16_tn_splitk_splits(M, N, K)
-    say(f"[case] splitk 6144^2 x 4096 library splits={s}")
-    assert s > 1
+    assert sg.gemm_fp16_tn_splitk_splits(M, N, K) == 1
+    assert sg.gemm_fp16_tn_remainder_quarters(M, N, K) == 256
+    ref = oracle.gemm_tn_f64(A, B)
+    say("[case] 6144^2 x 4096 library call (remainder form)")
     d = torch.full((M, N), float("nan"), dtype=torch.float16, device=DEV)
     sg.gemm(a, b, out=d)
     torch.cuda.synchronize()
-    rep = oracle.check(d.cpu().numpy(), oracle.gemm_tn_f64(A, B), K)
+    rep = oracle.check(d.cpu().numpy(), ref, K)
+    assert rep.ok, str(rep)
+    say("[case] 6144^2 x 4096 split x4")
+    d2, _, need = split_call(a, b, M, N, K, 4)
+    assert need > 0
+    rep = oracle.check(d2.cpu().numpy(), ref, K)
     assert rep.ok, str(rep)
 
 
@@ -227,13 +236,14 @@ def test_split_graph_replays_and_streams():
 def test_library_split_choice():
     # the split counts the cost model picks for shapes whose timings it was
     # fitted to (1: the plain call); every compiled choice must run
-    expect = {(2048, 2048, 16384): 4, (2048, 2048, 8192): 1, (6144, 6144, 4096): 4,
+    expect = {(2048, 2048, 16384): 4, (2048, 2048, 8192): 1, (6144, 6144, 4096): 1,
               (2048, 2048, 2048): 1, (2048, 2048, 512): 1, (3072, 3072, 4096): 1,
               (8192, 8192, 8192): 1, (8000, 7936, 8200): 1, (81920, 256, 256): 1,
               (4096, 4096, 128): 1}
     for shape, s in expect.items():
         assert sg.gemm_fp16_tn_splitk_splits(*shape) == s, shape
-    assert sg.gemm_fp16_tn_splitk_splits(4352, 4352, 4096) > 1
+    assert sg.gemm_fp16_tn_splitk_splits(4352, 4352, 4096) == 1       # the remainder form instead
+    assert sg.gemm_fp16_tn_remainder_quarters(4352, 4352, 4096) == 132
     assert sg.gemm_fp16_tn_splitk_splits(1024, 1024, 8192) > 1
 
 
