@@ -287,6 +287,121 @@ def mode_vendor_blas(args) -> int:
     return 0
 
 
+FORMS_SHAPES = [(6144, 6144, 4096), (4352, 4352, 4096), (81920, 256, 4096), (4352, 4104, 1088),
+                (2048, 2048, 8192), (2048, 2048, 16384), (8192, 8192, 8200)]
+
+
+def mode_forms(args) -> int:
+    """The call forms the library chooses between, interleaved on the same
+    uniform [-1, 1] operands (7 alternating rounds of --steps launches after
+    --warmup of each): the library's plain call (the remainder form where it
+    applies), the split-K call with the split count given in each line
+    (the library's own when it splits, else 4), the 256x256 tiled kernel
+    alone (schedule 10, or 12 when K % 64 != 0), and torch.matmul (hipBLASLt)
+    as a reference point.  One JSON line per shape: median microseconds,
+    TFLOP/s, the plan (splits, remainder quarters), and whether the plain
+    call and the tiled kernel agree bit for bit."""
+    import statistics
+
+    import torch
+
+    import stage_pipelined_mainloop_amd as sg
+    for M, N, K in FORMS_SHAPES:
+        g = torch.Generator(device="cuda")
+        g.manual_seed(M + N + K)
+        a = (torch.rand((M, K), generator=g, device="cuda") * 2 - 1).half()
+        b = (torch.rand((N, K), generator=g, device="cuda") * 2 - 1).half()
+        bt = b.t()
+        lib_splits = sg.gemm_fp16_tn_splitk_splits(M, N, K)
+        splits = lib_splits if lib_splits > 1 else 4
+        need = sg.gemm_fp16_tn_splitk_workspace_bytes(M, N, K, splits)
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+        outs = {n: torch.empty((M, N), dtype=torch.float16, device="cuda")
+                for n in ("plain", "split", "tiled256")}
+        stream = torch.cuda.current_stream().cuda_stream
+        tiled = (256, 256, 64, 2, 4, 10) if K % 64 == 0 else (256, 256, 64, 3, 4, 12)
+        calls = {
+            "plain": lambda: sg.gemm_fp16_tn_alpha(M, N, K, 1.0, a.data_ptr(), b.data_ptr(),
+                                                   outs["plain"].data_ptr(), stream),
+            "split": lambda: sg.gemm_fp16_tn_splitk(M, N, K, 1.0, a.data_ptr(), b.data_ptr(),
+                                                    outs["split"].data_ptr(), splits, ws.data_ptr(),
+                                                    ws.numel(), stream),
+            "tiled256": lambda: sg.gemm_fp16_tn_cfg(M, N, K, 1.0, a.data_ptr(), b.data_ptr(),
+                                                    outs["tiled256"].data_ptr(), tiled, stream),
+            "rocm_blas": lambda: torch.matmul(a, bt),
+        }
+        st = torch.cuda.current_stream()
+        for f in calls.values():
+            for _ in range(args.warmup):
+                f()
+        res = {n: [] for n in calls}
+        for rnd in range(7):
+            order = list(calls) if rnd % 2 == 0 else list(calls)[::-1]
+            for n in order:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                e0.record(st)
+                for _ in range(args.steps):
+                    calls[n]()
+                e1.record(st)
+                torch.cuda.synchronize()
+                res[n].append(e0.elapsed_time(e1) * 1e3 / args.steps)
+        us = {n: statistics.median(v) for n, v in res.items()}
+        print(json.dumps({
+            "mode": "forms", "shape": [M, N, K],
+            "plan": {"library_splits": lib_splits, "split_run": splits,
+                     "remainder_quarters": sg.gemm_fp16_tn_remainder_quarters(M, N, K),
+                     "plain_variant": variant_name(sg.sg_select_config(M, N, K)),
+                     "tiled256": list(tiled)},
+            "us": {n: round(u, 2) for n, u in us.items()},
+            "tflops": {n: round(2.0 * M * N * K / (u * 1e-6) / 1e12, 1) for n, u in us.items()},
+            "plain_equals_tiled256": bool(torch.equal(outs["plain"].view(torch.int16),
+                                                      outs["tiled256"].view(torch.int16))),
+            "rounds": 7, "launches_per_round": args.steps}), flush=True)
+    return 0
+
+
+def mode_forms_summary(args) -> int:
+    """profiles/call_forms.md from `python bench.py --mode forms` (its output
+    in --bench-log) and a kernel trace of the same command (stats CSV under
+    --prof-dir/forms/).  Host-only."""
+    import csv
+    with open(args.bench_log) as f:
+        lines = [json.loads(ln) for ln in f if ln.startswith("{") and '"forms"' in ln]
+    names = ["plain", "split", "tiled256", "rocm_blas"]
+    out = ["# Call forms: remainder form, split-K, 256x256 tiles alone, hipBLASLt", "",
+           f"Command: `python bench.py --mode forms --steps {lines[0]['launches_per_round']} "
+           f"--warmup {args.warmup}` (7 interleaved rounds, median per launch from HIP events); "
+           "kernel statistics from `rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/forms "
+           "-o forms -- python bench.py --mode forms` with the same arguments; summarised with "
+           "`python bench.py --mode forms_summary --prof-dir <dir> --bench-log <that run's output>`.", "",
+           "`plain` is the library's call (gemm_fp16_tn_alpha: the remainder form where the plan takes "
+           "it), `split` gemm_fp16_tn_splitk with the count in the plan column, `tiled256` the "
+           "256x256 kernel alone (gemm_fp16_tn_cfg), `rocm_blas` torch.matmul on the same operands.", "",
+           "| shape | plan | plain us | split us | tiled256 us | rocm_blas us | plain TFLOP/s | plain = tiled256 bitwise |",
+           "|---|---|---|---|---|---|---|---|"]
+    for ln in lines:
+        p = ln["plan"]
+        plan = (f"splits {p['library_splits']} (split run x{p['split_run']}), "
+                f"quarters {p['remainder_quarters']}, {p['plain_variant']}")
+        out.append(f"| {ln['shape'][0]}x{ln['shape'][1]}x{ln['shape'][2]} | {plan} | " +
+                   " | ".join(f"{ln['us'][n]:.2f}" for n in names) +
+                   f" | {ln['tflops']['plain']:.1f} | {ln['plain_equals_tiled256']} |")
+    stats = _glob1(f"{args.prof_dir}/forms/**/*kernel_stats.csv")
+    if stats:
+        out += ["", "## Kernel statistics of the traced run", "",
+                "| kernel | calls | average us |", "|---|---|---|"]
+        with open(stats) as f:
+            rows = sorted(csv.DictReader(f), key=lambda r: -float(r["TotalDurationNs"]))
+        for r in rows[:16]:
+            out.append(f"| `{r['Name'][:110]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} |")
+    fn = os.path.join(PROFILES, "call_forms.md")
+    with open(fn, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print(json.dumps({"summary": fn, "shapes": len(lines)}))
+    return 0
+
+
 def mode_ksweep(args) -> int:
     """M = N = 2048, K in the sweep list: the library's choice (split-K when
     it picks it), then every compiled stage count of the 128x128 (4 waves)
@@ -1078,7 +1193,8 @@ def main() -> int:
     ap.add_argument("--mode", default="bench",
                     choices=["bench", "variants", "ksweep", "calibrate_copy", "attention",
                              "trace_summary", "stage_model", "profile_summary", "ksweep_summary",
-                             "lds_patterns", "lds_summary", "variants_summary", "vendor_blas"])
+                             "lds_patterns", "lds_summary", "variants_summary", "vendor_blas",
+                             "forms", "forms_summary"])
     ap.add_argument("--trace", default=None, help="kernel-trace CSV for --mode trace_summary")
     ap.add_argument("--bench-log", default=None, help="that run's output for --mode trace_summary")
     ap.add_argument("--prof-dir", default=None,
@@ -1131,6 +1247,10 @@ def main() -> int:
         return mode_variants(args)
     if args.mode == "vendor_blas":
         return mode_vendor_blas(args)
+    if args.mode == "forms":
+        return mode_forms(args)
+    if args.mode == "forms_summary":
+        return mode_forms_summary(args)
     if args.mode == "ksweep":
         return mode_ksweep(args)
     if args.mode == "calibrate_copy":
