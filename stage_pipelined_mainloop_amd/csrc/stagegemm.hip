@@ -211,29 +211,46 @@ double rounds(long long tiles, long long per_round)
     return (double)full + (rest ? 0.75 + 0.25 * (double)rest / (double)per_round : 0.0);
 }
 
+// Compute units of the current device, cached per device; 256 (MI355X)
+// when the runtime cannot tell, so host-only queries keep one answer.
+int device_cus()
+{
+    static std::atomic<int> cache[16];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return 256;
+    int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+        return 256;
+    cache[dev].store(c, std::memory_order_relaxed);
+    return c;
+}
+
 // The library's choice and its cost in rounds of the 256x256 kernel (0 for
-// the short-K schedule, which the split form never competes with).
+// the short-K schedule, which the split form never competes with).  A round
+// is `cus` workgroups of the one-per-CU families and 2 x cus of the
+// two-per-CU one; the costs per round were measured on MI355X (256 CUs).
 const Variant *select_variant(int M, int N, int K, bool with_c, double *cost = nullptr,
-                              bool lines_aligned = true)
+                              bool lines_aligned = true, int cus = 256)
 {
     const long long t256 = (long long)((M + 255) / 256) * ((N + 255) / 256);
     const long long t128 = (long long)((M + 127) / 128) * ((N + 127) / 128);
     sg_config c;
     double best = 0.0;
-    if (K <= 128 && t128 >= 256 && !with_c) {
+    if (K <= 128 && t128 >= cus && !with_c) {
         c = sg_config{128, 128, 64, 2, 4, 4};
     } else {
-        const double c256 = rounds(t256, 256);
-        const double c2 = 0.66 * rounds(t128, 512);
+        const double c256 = rounds(t256, cus);
+        const double c2 = 0.66 * rounds(t128, 2 * cus);
         // schedule 14 (one wave per SIMD, four slots) against schedule 1 S3,
         // interleaved at M = N = 2048: K = 2048 20.1 / 22.2 us, 8192 61.8 /
         // 75.1, 16384 119.3 / 145.8, 1024 10.7 / 11.9 (S2), but 8.5 / 7.6
         // at K = 512 (a longer prologue) and slower on rows that straddle
         // lines.  Over several rounds its tiles lose their L2 reuse: 4352^2
         // x 4096 189.6 against 159.4 us for 256x256 tiles (schedule 10).
-        const bool c3_one_wave = lines_aligned && K % 64 == 0 && K >= 1024 && t128 <= 256;
-        const double c3 = (c3_one_wave ? 0.34 : 0.42) * rounds(t128, 256);
-        const bool persistent = K <= 1024 && !with_c && t128 > 256;
+        const bool c3_one_wave = lines_aligned && K % 64 == 0 && K >= 1024 && t128 <= cus;
+        const double c3 = (c3_one_wave ? 0.34 : 0.42) * rounds(t128, cus);
+        const bool persistent = K <= 1024 && !with_c && t128 > cus;
         const double cp = persistent ? 0.9 * c2 : 1e300;
         c = (lines_aligned && K % 64 == 0) ? sg_config{256, 256, 64, 2, 4, 10}
                                            : sg_config{256, 256, 64, 3, 4, 12};
@@ -284,12 +301,13 @@ double plain_rounds(int M, int N, int K, bool with_c, bool lines_aligned, int ca
                     const Variant **chosen = nullptr, SubPlan *sub = nullptr)
 {
     double cost = 0.0;
-    const Variant *v = select_variant(M, N, K, with_c, &cost, lines_aligned);
+    const Variant *v = select_variant(M, N, K, with_c, &cost, lines_aligned,
+                                      capacity > 0 ? capacity : 256);
     if (chosen) *chosen = v;
     if (!v || v->cfg.tile_m != 256) return cost;
     const SubPlan p = plan_sub(M, N, K, lines_aligned, capacity);
     if (p.quarters == 0) return cost;
-    const double sub_cost = (double)p.dp / capacity + 0.34 * rounds(p.quarters, 256);
+    const double sub_cost = (double)p.dp / capacity + 0.34 * rounds(p.quarters, capacity);
     if (sub_cost >= cost) return cost;
     if (sub) *sub = p;
     return sub_cost;
@@ -498,9 +516,10 @@ sg_status run_plain(int M, int N, int K, float alpha, float beta, const void *A,
     const bool lines = lines_aligned(A, B);
     const Variant *v = nullptr;
     SubPlan sub;
-    const long long t256 = (long long)((M + 255) / 256) * ((N + 255) / 256);
-    const int cap = t256 > 256 && lines && K % 64 == 0 && K >= 1024 ? sub_capacity() : 0;
-    plain_rounds(M, N, K, beta != 0.0f, lines, cap, &v, &sub);
+    // rounds of the device's CUs; the remainder form's resident count is a
+    // cached runtime query, made only where that form can apply
+    const int cap = lines && K % 64 == 0 && K >= 1024 && (M > 256 || N > 256) ? sub_capacity() : 0;
+    plain_rounds(M, N, K, beta != 0.0f, lines, cap > 0 ? cap : device_cus(), &v, &sub);
     if (!v) return SG_ERR_UNSUPPORTED;
     if (sub.quarters > 0) return launch_sub(sub, M, N, K, alpha, beta, A, B, Cm, D, stream);
     return run(v, M, N, K, alpha, beta, A, B, Cm, D, stream);
@@ -679,7 +698,7 @@ sg_status sg_select_config(int M, int N, int K, sg_config *out)
 {
     if (!out) return SG_ERR_NULL;
     if (M < 0 || N < 0 || K < 0) return SG_ERR_SHAPE;
-    const Variant *v = select_variant(M, N, K, false);
+    const Variant *v = select_variant(M, N, K, false, nullptr, true, device_cus());
     if (!v) return SG_ERR_UNSUPPORTED;
     *out = v->cfg;
     return SG_OK;
