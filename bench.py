@@ -287,8 +287,8 @@ def mode_vendor_blas(args) -> int:
     return 0
 
 
-FORMS_SHAPES = [(6144, 6144, 4096), (4352, 4352, 4096), (81920, 256, 4096), (4352, 4104, 1088),
-                (2048, 2048, 8192), (2048, 2048, 16384), (8192, 8192, 8200)]
+FORMS_SHAPES = [(6144, 6144, 4096), (4352, 4352, 4096), (81920, 256, 4096), (65536, 256, 2048),
+                (4352, 4104, 1088), (2048, 2048, 8192), (2048, 2048, 16384), (8192, 8192, 8200)]
 
 
 def mode_forms(args) -> int:
@@ -297,7 +297,8 @@ def mode_forms(args) -> int:
     --warmup of each): the library's plain call (the remainder form where it
     applies), the split-K call with the split count given in each line
     (the library's own when it splits, else 4), the 256x256 tiled kernel
-    alone (schedule 10, or 12 when K % 64 != 0), and torch.matmul (hipBLASLt)
+    alone (schedule 10, or 12 when K % 64 != 0 or the grid has at most two
+    tile rows or columns), and torch.matmul (hipBLASLt)
     as a reference point.  One JSON line per shape: median microseconds,
     TFLOP/s, the plan (splits, remainder quarters), and whether the plain
     call and the tiled kernel agree bit for bit."""
@@ -319,7 +320,8 @@ def mode_forms(args) -> int:
         outs = {n: torch.empty((M, N), dtype=torch.float16, device="cuda")
                 for n in ("plain", "split", "tiled256")}
         stream = torch.cuda.current_stream().cuda_stream
-        tiled = (256, 256, 64, 2, 4, 10) if K % 64 == 0 else (256, 256, 64, 3, 4, 12)
+        streaming = min((M + 255) // 256, (N + 255) // 256) <= 2
+        tiled = (256, 256, 64, 2, 4, 10) if K % 64 == 0 and not streaming else (256, 256, 64, 3, 4, 12)
         calls = {
             "plain": lambda: sg.gemm_fp16_tn_alpha(M, N, K, 1.0, a.data_ptr(), b.data_ptr(),
                                                    outs["plain"].data_ptr(), stream),

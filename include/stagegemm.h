@@ -108,7 +108,8 @@ typedef enum sg_status {
  *      stages 3, waves 4.  The library's choice for 256 x 256 tiles when
  *      rows of A or B straddle 128-byte lines (K % 64 != 0, or a base
  *      address not 128-byte aligned), where each load touches two lines
- *      and holds the issuing wave longer;
+ *      and holds the issuing wave longer, and for grids of at most two
+ *      tile rows or columns, whose operands stream from HBM;
  *  14  order 10 on 128 x 128 x 64 tiles: 4 waves of 64 x 64, a ring of four
  *      32 KiB slots, tile k + 3 loaded over the two halves of tile k.  Only
  *      stages 4, waves 4.  The library's choice for grids of at most one
@@ -140,7 +141,8 @@ typedef struct sg_config_info {
  * The call runs the variant sg_select_config names, except where a grid of
  * more than one round of 256 x 256 tiles leaves its last round at most a
  * quarter full (rows on 128-byte lines, K % 64 == 0, K >= 1024): then the
- * whole rounds run as 256 x 256 tiles (schedule 10) and each remaining tile
+ * whole rounds run as 256 x 256 tiles (schedule 10, or 12 for a grid of at
+ * most two tile rows or columns) and each remaining tile
  * as four 128 x 128 quarters (schedule 14), two kernels on `stream`
  * ("cute(9) multistage_gemm", section 11.3, names adaptive tile sizes beside
  * split-K).  Every element is computed the same way either way: the same
@@ -173,7 +175,8 @@ sg_status gemm_fp16_tn_alpha_beta(int M, int N, int K, float alpha, float beta,
  * ("cute(9) multistage_gemm", section 11.3, names split-K as the remedy for
  * too few output tiles).  Output tiles that fill whole rounds are computed
  * as by the tiled schedule the library would pick (10 when every row of A
- * and B starts on a 128-byte line, else 12); each remaining tile is cut
+ * and B starts on a 128-byte line, else 12, and 12 for grids of at most two
+ * tile rows or columns); each remaining tile is cut
  * along K into
  * `splits` contiguous runs of 64-deep K tiles (fewer if K has fewer tiles,
  * at most 16), each run computed by its own workgroup through the same

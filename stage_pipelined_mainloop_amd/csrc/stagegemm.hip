@@ -204,6 +204,19 @@ bool lines_aligned(const void *A, const void *B)
     return ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & 127) == 0;
 }
 
+// Whether the 256x256 grid reuses its panels so little that the operands
+// stream from HBM: at most two tile rows or two tile columns, so each panel
+// of the other operand is read by at most two tiles.  There schedule 12,
+// which issues half as many loads in each half tile, beat schedule 10:
+// 81920 x 256 x 4096 200.3 against 236.0 us, 65536 x 256 x 2048 56.6
+// against 61.1, 32768 x 512 x 8192 215.2 against 221.6 (20480 x 512 x 4096
+// equal).  A mirrored form with A in the third slot measured the same as
+// schedule 12: the spread of the loads is what counts.
+bool streams_from_hbm(int M, int N)
+{
+    return (M + 255) / 256 <= 2 || (N + 255) / 256 <= 2;
+}
+
 double rounds(long long tiles, long long per_round)
 {
     const long long full = tiles / per_round;
@@ -252,8 +265,8 @@ const Variant *select_variant(int M, int N, int K, bool with_c, double *cost = n
         const double c3 = (c3_one_wave ? 0.34 : 0.42) * rounds(t128, cus);
         const bool persistent = K <= 1024 && !with_c && t128 > cus;
         const double cp = persistent ? 0.9 * c2 : 1e300;
-        c = (lines_aligned && K % 64 == 0) ? sg_config{256, 256, 64, 2, 4, 10}
-                                           : sg_config{256, 256, 64, 3, 4, 12};
+        c = (lines_aligned && K % 64 == 0 && !streams_from_hbm(M, N)) ? sg_config{256, 256, 64, 2, 4, 10}
+                                                                       : sg_config{256, 256, 64, 3, 4, 12};
         best = c256;
         if (c3 < best) {
             best = c3;
@@ -277,6 +290,7 @@ const Variant *select_variant(int M, int N, int K, bool with_c, double *cost = n
 // in the comments of plain_rounds below.
 using SubCfg = sg::Cfg<128, 128, 64, 4, 2, 2, 14>;
 using DpCfg = sg::Cfg<256, 256, 64, 2, 2, 2, 10>;
+using DpCfg12 = sg::Cfg<256, 256, 64, 3, 2, 2, 12>;   // the whole rounds of a streaming grid
 
 struct SubPlan {
     int dp = 0;          // 256x256 tiles in whole rounds
@@ -499,8 +513,11 @@ sg_status launch_sub(const SubPlan &p, int M, int N, int K, float alpha, float b
     int dp = p.dp;
     const hipStream_t st = static_cast<hipStream_t>(stream);
     void *args[] = {&a, &b, &c, &d, &M, &N, &K, &alpha, &beta, &dp};
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&sg::gemm_tn_dp_kernel<DpCfg>),
-                                   dim3((unsigned)p.dp), dim3(DpCfg::T), args, 0, st);
+    static_assert(DpCfg12::T == DpCfg::T, "one block size for the whole rounds");
+    const void *dpk = streams_from_hbm(M, N)
+                          ? reinterpret_cast<const void *>(&sg::gemm_tn_dp_kernel<DpCfg12>)
+                          : reinterpret_cast<const void *>(&sg::gemm_tn_dp_kernel<DpCfg>);
+    hipError_t e = hipLaunchKernel(dpk, dim3((unsigned)p.dp), dim3(DpCfg::T), args, 0, st);
     if (e != hipSuccess) return SG_ERR_HIP;
     e = hipLaunchKernel(reinterpret_cast<const void *>(&sg::gemm_tn_sub_kernel<SubCfg>),
                         dim3((unsigned)p.quarters), dim3(SubCfg::T), args, 0, st);
@@ -535,7 +552,7 @@ sg_status launch_split(const SplitPlan &p, int M, int N, int K, float alpha, con
     int dp = p.dp_tiles, splits = p.splits;
     const hipStream_t st = static_cast<hipStream_t>(stream);
     void *args[] = {&a, &b, &d, &M, &N, &K, &alpha, &part, &dp, &splits};
-    const bool lines = K % 64 == 0 && lines_aligned(A, B);
+    const bool lines = K % 64 == 0 && lines_aligned(A, B) && !streams_from_hbm(M, N);
     const void *fn = lines ? reinterpret_cast<const void *>(&sg::gemm_tn_split_kernel<SplitCfg10>)
                            : reinterpret_cast<const void *>(&sg::gemm_tn_split_kernel<SplitCfg>);
     hipError_t e = hipLaunchKernel(fn, dim3((unsigned)p.grid), dim3(SplitCfg::T), args, 0, st);

@@ -294,7 +294,7 @@ def test_selection_returns_compiled_variants():
     assert _lib.sg_select_config(81920, 256, 256).as_tuple() == (128, 128, 64, 2, 4, 3)
     assert _lib.sg_select_config(2048, 2048, 2048).as_tuple() == (128, 128, 64, 4, 4, 14)
     assert _lib.sg_select_config(2048, 2048, 1000).as_tuple() == (128, 128, 64, 3, 4, 1)
-    assert _lib.sg_select_config(81920, 256, 4096).as_tuple() == (256, 256, 64, 2, 4, 10)
+    assert _lib.sg_select_config(81920, 256, 4096).as_tuple() == (256, 256, 64, 3, 4, 12)   # streams from HBM
     assert _lib.sg_select_config(2560, 2560, 4096).as_tuple() == (128, 128, 64, 2, 4, 1)
     assert _lib.sg_select_config(3072, 3072, 4096).as_tuple() == (256, 256, 64, 2, 4, 10)
     assert _lib.sg_select_config(6144, 6144, 4096).as_tuple() == (256, 256, 64, 2, 4, 10)
