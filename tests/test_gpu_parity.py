@@ -491,10 +491,10 @@ def test_graph_replays_match_eager():
     # the launch path makes no allocation, memset or host synchronisation, so
     # it can be captured into a HIP graph: replays, with eager work between
     # them, must reproduce the eager result bit for bit (tiled, persistent
-    # and short-K kernels, and the 256^3 call that bench.py replays from a
-    # graph)
+    # and short-K kernels, the remainder form's two kernels, schedule 14, and
+    # the 256^3 call that bench.py replays from a graph)
     for (M, N, K) in [(4096, 4096, 512), (2048, 1024, 512), (20480, 256, 256), (4096, 2048, 128),
-                      (256, 256, 256)]:
+                      (256, 256, 256), (4352, 4104, 1088), (2048, 2048, 1024)]:
         say(f"[case] graph {M}x{N}x{K}")
         A, B = inputs.operands(M, N, K, 1500 + K)
         a, b = to_dev(A), to_dev(B)
