@@ -446,8 +446,10 @@ def mode_ksweep(args) -> int:
 def mode_attention(args) -> int:
     """The fused attention forward O = softmax(alpha Q K^T) V on H heads of
     the attention-score shape (M = N = 4096, d = 128, N(0,1) inputs), next to
-    the unfused route on the same GPU: this library's GEMM for the scores,
-    then torch's softmax and batched product (one JSON line per head count)."""
+    the unfused route on the same GPU (this library's GEMM for the scores,
+    then torch's softmax and batched product) and, as a reference point,
+    torch's scaled_dot_product_attention on the same tensors (one JSON line
+    per head count)."""
     import numpy as np
     import torch
 
@@ -482,6 +484,9 @@ def mode_attention(args) -> int:
             p = torch.softmax(s.float(), dim=-1).half()
             return torch.bmm(p, v)
         ref_ms = time_launches(unfused, max(3, args.steps // 5), 2)
+        q4, k4, v4 = q.unsqueeze(0), k.unsqueeze(0), v.unsqueeze(0)
+        sdpa_ms = time_launches(lambda: torch.nn.functional.scaled_dot_product_attention(q4, k4, v4),
+                                args.steps, warm)
         flops = 4.0 * H * M * N * d
         tf = flops / (fused / 1e3) / 1e12
         print(json.dumps({"mode": "attention", "metric": "fused attention forward TFLOP/s (4 H M N d)",
@@ -491,7 +496,8 @@ def mode_attention(args) -> int:
                           "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_TFLOPS,
                                        "unit": "TFLOP/s", "frac": round(tf / PEAK_TFLOPS, 4)},
                           "unfused_ms": round(ref_ms, 4),
-                          "unfused": "library GEMM for S, torch softmax (fp32) and bmm"}), flush=True)
+                          "unfused": "library GEMM for S, torch softmax (fp32) and bmm",
+                          "torch_sdpa_ms": round(sdpa_ms, 4)}), flush=True)
     return 0
 
 
