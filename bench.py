@@ -288,13 +288,17 @@ def mode_vendor_blas(args) -> int:
 
 
 FORMS_SHAPES = [(6144, 6144, 4096), (4352, 4352, 4096), (81920, 256, 4096), (65536, 256, 2048),
-                (4352, 4104, 1088), (2048, 2048, 8192), (2048, 2048, 16384), (8192, 8192, 8200)]
+                (4352, 4104, 1088), (2048, 2048, 8192), (2048, 2048, 16384), (8192, 8192, 8200),
+                (4096, 4096, 128), (2048, 2048, 2048), (2048, 2048, 512), (2048, 2048, 128),
+                (81920, 256, 256), (256, 256, 256)]
 
 
 def mode_forms(args) -> int:
     """The call forms the library chooses between, interleaved on the same
-    uniform [-1, 1] operands (7 alternating rounds of --steps launches after
-    --warmup of each): the library's plain call (the remainder form where it
+    uniform [-1, 1] operands: each form's --steps launches captured in one
+    HIP graph (so host launch costs do not count, for the library and the
+    vendor alike), --warmup eager launches first, then 7 alternating rounds
+    of one replay each: the library's plain call (the remainder form where it
     applies), the split-K call with the split count given in each line
     (the library's own when it splits, else 4), the 256x256 tiled kernel
     alone (schedule 10, or 12 when K % 64 != 0 or the grid has at most two
@@ -319,33 +323,40 @@ def mode_forms(args) -> int:
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
         outs = {n: torch.empty((M, N), dtype=torch.float16, device="cuda")
                 for n in ("plain", "split", "tiled256")}
-        stream = torch.cuda.current_stream().cuda_stream
+        def stream():
+            # the stream current at each call: inside graph capture, the capture stream
+            return torch.cuda.current_stream().cuda_stream
         streaming = min((M + 255) // 256, (N + 255) // 256) <= 2
         tiled = (256, 256, 64, 2, 4, 10) if K % 64 == 0 and not streaming else (256, 256, 64, 3, 4, 12)
         calls = {
             "plain": lambda: sg.gemm_fp16_tn_alpha(M, N, K, 1.0, a.data_ptr(), b.data_ptr(),
-                                                   outs["plain"].data_ptr(), stream),
+                                                   outs["plain"].data_ptr(), stream()),
             "split": lambda: sg.gemm_fp16_tn_splitk(M, N, K, 1.0, a.data_ptr(), b.data_ptr(),
                                                     outs["split"].data_ptr(), splits, ws.data_ptr(),
-                                                    ws.numel(), stream),
+                                                    ws.numel(), stream()),
             "tiled256": lambda: sg.gemm_fp16_tn_cfg(M, N, K, 1.0, a.data_ptr(), b.data_ptr(),
-                                                    outs["tiled256"].data_ptr(), tiled, stream),
+                                                    outs["tiled256"].data_ptr(), tiled, stream()),
             "rocm_blas": lambda: torch.matmul(a, bt),
         }
-        st = torch.cuda.current_stream()
-        for f in calls.values():
+        graphs = {}
+        for n, f in calls.items():
             for _ in range(args.warmup):
                 f()
+            torch.cuda.synchronize()
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                for _ in range(args.steps):
+                    f()
+            graphs[n] = gr
         res = {n: [] for n in calls}
         for rnd in range(7):
             order = list(calls) if rnd % 2 == 0 else list(calls)[::-1]
             for n in order:
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 torch.cuda.synchronize()
-                e0.record(st)
-                for _ in range(args.steps):
-                    calls[n]()
-                e1.record(st)
+                e0.record()
+                graphs[n].replay()
+                e1.record()
                 torch.cuda.synchronize()
                 res[n].append(e0.elapsed_time(e1) * 1e3 / args.steps)
         us = {n: statistics.median(v) for n, v in res.items()}
@@ -373,7 +384,8 @@ def mode_forms_summary(args) -> int:
     names = ["plain", "split", "tiled256", "rocm_blas"]
     out = ["# Call forms: remainder form, split-K, 256x256 tiles alone, hipBLASLt", "",
            f"Command: `python bench.py --mode forms --steps {lines[0]['launches_per_round']} "
-           f"--warmup {args.warmup}` (7 interleaved rounds, median per launch from HIP events); "
+           f"--warmup {args.warmup}` (each form's launches captured in one HIP graph, 7 interleaved "
+           "replays, median per launch from HIP events); "
            "kernel statistics from `rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/forms "
            "-o forms -- python bench.py --mode forms` with the same arguments; summarised with "
            "`python bench.py --mode forms_summary --prof-dir <dir> --bench-log <that run's output>`.", "",
