@@ -59,26 +59,6 @@ __device__ __forceinline__ int k_chunk(int r, int c) { return c ^ (r & 15); }
 // 16-byte bank groups.
 __device__ __forceinline__ int v_chunk(int r, int c) { return c ^ ((r & 3) << 2); }
 
-// LDS-DMA of 16 bytes per lane to the wave's 1 KiB at LDS address `lds`
-// (lane l fills bytes 16 l .. 16 l + 15), issued through inline assembly.
-// The compiler cannot tell the transposing LDS reads apart from any pending
-// DMA target and would wait for every DMA in flight before each of them;
-// here it does not see these loads at all, and the kernel's own vmcnt(0)
-// before each barrier is what orders them.  (Loads the compiler does track
-// are waited for with counts that ignore these: at worst it waits longer.)
-// m0 is written and consumed inside the same statement.  The compiler warns
-// that a reserved register in a clobber list may not be preserved; nothing
-// else in this translation unit uses m0, so no value of its own lives across
-// the statement.  Every build checks that in the generated assembly (every m0
-// operand must sit inside an inline-assembly region) and fails otherwise.
-__device__ __forceinline__ void dma16(const u32x4 &rsrc, uint32_t voff, uint32_t lds)
-{
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :
-                 : "s"(lds), "v"(voff), "s"(rsrc)
-                 : "memory", "m0");
-}
-
 // NEG: alpha < 0, so the largest scaled score comes from the smallest score.
 //
 // With splits > 1 the keys are divided too: workgroup (head, row block,

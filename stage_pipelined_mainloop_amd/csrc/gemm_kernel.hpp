@@ -265,6 +265,28 @@ __device__ __forceinline__ u32x4 rsrc_words(const void *base, uint32_t bytes)
     return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, (uint32_t)kRsrcWord3};
 }
 
+// LDS-DMA of 16 bytes per lane to the wave's 1 KiB at LDS address `lds`
+// (lane l fills bytes 16 l .. 16 l + 15), issued through inline assembly.
+// The compiler cannot tell later LDS reads apart from a pending DMA target
+// and, for its own LDS-DMA builtin, waits for every VMEM operation in flight
+// (the DMA and any earlier stores) before each of them; these loads it does
+// not see at all, and the kernel's own vmcnt waits before its barriers order
+// them.  (Loads the compiler does track are waited for with counts that
+// ignore these: at worst it waits longer.)  m0 is written and consumed inside
+// the statement, with the one wait state gfx9 needs between an SALU write of
+// m0 and an LDS-DMA that reads it.  The compiler warns that a reserved
+// register in a clobber list may not be preserved: no compiler-generated code
+// in a kernel that calls this may use m0, which every build checks in the
+// generated assembly (every m0 operand must sit inside an inline-assembly
+// region).
+__device__ __forceinline__ void dma16(const u32x4 &rsrc, uint32_t voff, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(rsrc)
+                 : "memory", "m0");
+}
+
 // Compiler-level fence: no memory access moves across it (emits nothing).
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 

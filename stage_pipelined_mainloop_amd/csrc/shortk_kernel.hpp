@@ -18,6 +18,71 @@
 
 namespace sg {
 
+// Grid position -> output tile for the short-K schedule: plain row-major
+// order, no XCD renumbering and no grouping.  With K <= 128 the operands are
+// a few MiB that every L2 holds after first touch, and the time goes to
+// writing D; workgroups that run at the same time then write whole stretches
+// of the same rows of D.  At 4096 x 4096 x 128 (HIP-graph replays) this
+// kernel took 11.2 us in the order of tile_coords (XCD renumbering, groups
+// of four tile rows, which serve the panel reuse of long K loops) and
+// 9.9 us in row-major order.
+__device__ __forceinline__ void row_major_coords(int pid, int tiles_n, int &tm, int &tn)
+{
+    tm = pid / tiles_n;
+    tn = pid - tm * tiles_n;
+}
+
+// One output tile of the short-K schedule from a filled ring region `ring`
+// (K tile t at ring + t * STAGE_BYTES, NT tiles): each wave reads its B
+// fragments for the whole K extent once, then walks its sub-tile one 32-row
+// block at a time -- all K steps of that block's MFMAs, then the block's
+// staged store -- with the A fragments of the next block read ahead.  `rd`
+// covers the tile's rows of D from its first row; n is this lane's first
+// column of D and n_ok whether its 16-byte chunk lies inside N.
+template <class C, int NT>
+__device__ __forceinline__ void shortk_tile(const char *ring, char *epi, int lane, int wm, int wn,
+                                            __amdgpu_buffer_rsrc_t rd, int n, bool n_ok, int N,
+                                            float alpha)
+{
+    const int half = lane >> 5;
+    constexpr int NQ = NT * C::NKS;                 // q = t * NKS + ks: every K step
+    const int ra_row = wm * C::WTM + (lane & 31);
+    const int rb_row = wn * C::WTN + (lane & 31);
+    auto frag = [&](int t, int part, int row, int ks) {
+        const int c = 2 * ks + half;
+        return *(const f16x8 *)(ring + t * C::STAGE_BYTES + part + row * C::RB +
+                                ((c ^ swz<C::CPR>(row)) << 4));
+    };
+    f16x8 fb[NQ][C::FN];                           // this wave's B columns, whole K
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+            fb[q][j] = frag(q / C::NKS, C::A_BYTES, rb_row + j * 32, q % C::NKS);
+    f16x8 fa[2][NQ];                               // A rows of blocks i and i + 1
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) fa[0][q] = frag(q / C::NKS, 0, ra_row, q % C::NKS);
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+        if (i + 1 < C::FM) {
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+                fa[(i + 1) & 1][q] = frag(q / C::NKS, 0, ra_row + (i + 1) * 32, q % C::NKS);
+        }
+        f32x16 acc[C::FN];
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[j][e] = 0.0f;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[q][j], fa[i & 1][q], acc[j], 0, 0, 0);
+        store_block_staged<C>(acc, alpha, epi, lane, rd, wm * C::WTM + i * 32, n, n_ok, N);
+    }
+}
+
 template <class C>
 __global__ void __launch_bounds__(C::T)
 gemm_tn_shortk_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B,
@@ -33,12 +98,10 @@ gemm_tn_shortk_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / C::WN;
     const int wn = wave % C::WN;
-    const int half = lane >> 5;
 
-    const int tiles_m = (M + C::BM - 1) / C::BM;
     const int tiles_n = (N + C::BN - 1) / C::BN;
     int tm, tn;
-    tile_coords(blockIdx.x, tiles_m, tiles_n, tiles_m * tiles_n, tm, tn);
+    row_major_coords(blockIdx.x, tiles_n, tm, tn);
     const int m0 = tm * C::BM;
     const int n0 = tn * C::BN;
     const int rows_a = (M - m0 < C::BM) ? (M - m0) : C::BM;
@@ -87,49 +150,11 @@ gemm_tn_shortk_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict
     __builtin_amdgcn_sched_barrier(0);
     compiler_fence();
 
-    // ---- fragments: q = t * NKS + ks runs over every K step of the ring
-    constexpr int NQ = C::S * C::NKS;
-    const int ra_row = wm * C::WTM + (lane & 31);
-    const int rb_row = wn * C::WTN + (lane & 31);
-    auto frag = [&](int t, int part, int row, int ks) {
-        const int c = 2 * ks + half;
-        return *(const f16x8 *)(smem + t * C::STAGE_BYTES + part + row * C::RB +
-                                ((c ^ swz<C::CPR>(row)) << 4));
-    };
-    f16x8 fb[NQ][C::FN];                           // this wave's B columns, whole K
-#pragma unroll
-    for (int q = 0; q < NQ; ++q)
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j)
-            fb[q][j] = frag(q / C::NKS, C::A_BYTES, rb_row + j * 32, q % C::NKS);
-    f16x8 fa[2][NQ];                               // A rows of blocks i and i + 1
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) fa[0][q] = frag(q / C::NKS, 0, ra_row, q % C::NKS);
-
-    // ---- per row block: all K steps, then the block's epilogue
+    // ---- fragments, MFMAs and the row-block epilogue of the one tile
     char *epi = smem + C::RING_BYTES + wave * C::EPI_BLOCK_WAVE_BYTES;
     const __amdgpu_buffer_rsrc_t rd = make_rsrc(D + (size_t)m0 * N, (uint32_t)rows_a * N * 2u);
     const int n = n0 + wn * C::WTN + (lane & 7) * 8;
-    const bool n_ok = n < N;                       // N % 8 == 0: a chunk is all in or out
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i) {
-        if (i + 1 < C::FM) {
-#pragma unroll
-            for (int q = 0; q < NQ; ++q)
-                fa[(i + 1) & 1][q] = frag(q / C::NKS, 0, ra_row + (i + 1) * 32, q % C::NKS);
-        }
-        f32x16 acc[C::FN];
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[j][e] = 0.0f;
-#pragma unroll
-        for (int q = 0; q < NQ; ++q)
-#pragma unroll
-            for (int j = 0; j < C::FN; ++j)
-                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[q][j], fa[i & 1][q], acc[j], 0, 0, 0);
-        store_block_staged<C>(acc, alpha, epi, lane, rd, wm * C::WTM + i * 32, n, n_ok, N);
-    }
+    shortk_tile<C, C::S>(smem, epi, lane, wm, wn, rd, n, n < N, N, alpha);
 }
 
 }  // namespace sg
