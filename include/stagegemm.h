@@ -79,7 +79,10 @@ typedef enum sg_status {
  *   4  short K: the whole K extent (K <= stages * tile_k) loaded into the
  *      ring at once, then each wave's row blocks computed and stored in
  *      turn; D = alpha * A * B^T only (SG_ERR_UNSUPPORTED for a longer K or
- *      with a C operand);
+ *      with a C operand).  Schedules 3 and 4 take output tiles in row-major
+ *      order where A and B together fit in one XCD's L2 (4 MiB), else with
+ *      each XCD given a contiguous run of them; the library runs schedule 4
+ *      for K <= 128 where they fit and schedule 3 where they do not;
  *   5  order 1 on 16x16x32 MFMAs instead of 32x32x16 (tile_k 64): the same
  *      LDS traffic per flop, a different balance between clock and MFMA
  *      occupancy under the power limit.  Compiled for comparison; the

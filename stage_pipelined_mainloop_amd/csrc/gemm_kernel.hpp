@@ -328,6 +328,32 @@ __device__ __forceinline__ void tile_coords(int pid, int tiles_m, int tiles_n, i
     tn = in_group / gm;
 }
 
+// Grid position -> output tile for the kernels whose K loop is short (the
+// short-K and persistent schedules), where writing D takes much of the time
+// and the panels are read by few K steps.  When A and B together fit in one
+// XCD's L2 (4 MiB), every XCD holds all of them after first touch and tiles
+// go in plain row-major order: the workgroups resident together then write
+// whole stretches of the same rows of D.  Otherwise the XCD renumbering of
+// tile_coords comes first (each XCD a contiguous run of tiles, so both
+// column tiles of a tall grid's row band share one L2), then row-major.  No
+// groups of tile rows: they serve the panel reuse of long K loops and cost
+// the write of D here.  Short-K kernel, HIP-graph replays: 4096 x 4096 x 128
+// 11.2 us in tile_coords' order, 9.5-9.9 us row-major, 9.7 us renumbered;
+// 81920 x 256 x 128 19.7 us row-major, 13.3 us renumbered.  Persistent
+// kernel: 8192 x 8192 x 128 40.4 / 36.5 / 39.4 us (tile_coords, row-major,
+// renumbered), 16384 x 4096 x 64 32.0 / 28.4 / 29.9, 81920 x 256 x 256
+// 21.7 / 21.2 / 20.6, 40960 x 512 x 256 17.8 / 20.8 / 17.6.
+__device__ __forceinline__ void short_k_coords(int pid, int tiles_m, int tiles_n, int M, int N,
+                                               int K, int &tm, int &tn)
+{
+    const long long operand_bytes = ((long long)M + N) * K * 2;
+    const int tiles = tiles_m * tiles_n;
+    if (operand_bytes > (4ll << 20) && (tiles & 7) == 0 && pid < tiles)
+        pid = (pid & 7) * (tiles >> 3) + (pid >> 3);
+    tm = pid / tiles_n;
+    tn = pid - tm * tiles_n;
+}
+
 // Epilogue staging layout (all kernels).  A wave stages a 32-row block of
 // its sub-tile in unpadded rows of WTN fp16, in 8-byte slots (four
 // consecutive columns, what one lane holds per accumulator piece); slot s of

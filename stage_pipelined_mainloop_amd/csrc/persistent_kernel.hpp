@@ -59,7 +59,7 @@ gemm_tn_persistent_kernel(const _Float16 *__restrict__ A, const _Float16 *__rest
     auto geometry = [&](int u, int &m0, int &n0, int &rows_a,
                         int &rows_b) __attribute__((always_inline)) {
         int tm, tn;
-        tile_coords((int)blockIdx.x + u * G, tiles_m, tiles_n, tiles_m * tiles_n, tm, tn);
+        short_k_coords((int)blockIdx.x + u * G, tiles_m, tiles_n, M, N, K, tm, tn);
         m0 = tm * C::BM;
         n0 = tn * C::BN;
         rows_a = (M - m0 < C::BM) ? (M - m0) : C::BM;

@@ -11,26 +11,13 @@
 // loads, the MFMAs and the write of D then run one after another on each CU.
 // A wave's B fragments for the whole K extent are read once and stay in
 // registers; the A fragments of block i + 1 are read while block i's MFMAs
-// and stores run.  Only D = alpha * A * B^T (no C operand).
+// and stores run.  Tiles go in the order of short_k_coords (row-major where
+// the operands fit in an L2).  Only D = alpha * A * B^T (no C operand).
 #pragma once
 
 #include "gemm_kernel.hpp"
 
 namespace sg {
-
-// Grid position -> output tile for the short-K schedule: plain row-major
-// order, no XCD renumbering and no grouping.  With K <= 128 the operands are
-// a few MiB that every L2 holds after first touch, and the time goes to
-// writing D; workgroups that run at the same time then write whole stretches
-// of the same rows of D.  At 4096 x 4096 x 128 (HIP-graph replays) this
-// kernel took 11.2 us in the order of tile_coords (XCD renumbering, groups
-// of four tile rows, which serve the panel reuse of long K loops) and
-// 9.9 us in row-major order.
-__device__ __forceinline__ void row_major_coords(int pid, int tiles_n, int &tm, int &tn)
-{
-    tm = pid / tiles_n;
-    tn = pid - tm * tiles_n;
-}
 
 // One output tile of the short-K schedule from a filled ring region `ring`
 // (K tile t at ring + t * STAGE_BYTES, NT tiles): each wave reads its B
@@ -99,9 +86,10 @@ gemm_tn_shortk_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict
     const int wm = wave / C::WN;
     const int wn = wave % C::WN;
 
+    const int tiles_m = (M + C::BM - 1) / C::BM;
     const int tiles_n = (N + C::BN - 1) / C::BN;
     int tm, tn;
-    row_major_coords(blockIdx.x, tiles_n, tm, tn);
+    short_k_coords(blockIdx.x, tiles_m, tiles_n, M, N, K, tm, tn);
     const int m0 = tm * C::BM;
     const int n0 = tn * C::BN;
     const int rows_a = (M - m0 < C::BM) ? (M - m0) : C::BM;
@@ -119,11 +107,14 @@ gemm_tn_shortk_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict
     const int l_chunk = (lane % C::CPR) ^ swz<C::CPR>(l_row0);
     const uint32_t l_base = (uint32_t)(l_row0 * K + l_chunk * 8) * 2u;
     const uint32_t l_step = (uint32_t)(C::NW * ROWS_PER_LOAD) * (uint32_t)K * 2u;
-    // Slots past the last K tile are filled with zeros by the same loads (their
-    // offsets lie past the buffer range), so every block runs all S * NKS
-    // K steps without a branch.
+    // A one-K-tile extent (K <= BK, K = 0 included) fills slot 0 only and
+    // runs one slot's K steps; otherwise slots past the last K tile are
+    // filled with zeros by the same loads (their offsets lie past the buffer
+    // range), so every block runs all S * NKS K steps without a branch.
+    const bool one_tile = ntile <= 1;
 #pragma unroll
     for (int t = 0; t < C::S; ++t) {
+        if (t > 0 && one_tile) break;
         const int kbase = t * C::BK;
         const bool valid = l_chunk * 8 < K - kbase;
         const uint32_t v = valid ? l_base + (uint32_t)kbase * 2u : kOutOfRange;
@@ -141,7 +132,6 @@ gemm_tn_shortk_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict
                 rb, (__attribute__((address_space(3))) void *)(sb + (i * C::NW + wave) * 1024),
                 16, v + (uint32_t)i * step, 0, 0, 0);
     }
-    (void)ntile;
     // every K tile complete and visible (RAW); nothing is refilled (no WAR)
     compiler_fence();
     __builtin_amdgcn_sched_barrier(0);
@@ -154,7 +144,10 @@ gemm_tn_shortk_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict
     char *epi = smem + C::RING_BYTES + wave * C::EPI_BLOCK_WAVE_BYTES;
     const __amdgpu_buffer_rsrc_t rd = make_rsrc(D + (size_t)m0 * N, (uint32_t)rows_a * N * 2u);
     const int n = n0 + wn * C::WTN + (lane & 7) * 8;
-    shortk_tile<C, C::S>(smem, epi, lane, wm, wn, rd, n, n < N, N, alpha);
+    if (one_tile)
+        shortk_tile<C, 1>(smem, epi, lane, wm, wn, rd, n, n < N, N, alpha);
+    else
+        shortk_tile<C, C::S>(smem, epi, lane, wm, wn, rd, n, n < N, N, alpha);
 }
 
 }  // namespace sg

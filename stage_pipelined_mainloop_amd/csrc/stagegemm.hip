@@ -170,10 +170,14 @@ const Variant *find_variant(const sg_config *c)
 
 // Choice from the measured sweeps (MI355X, fp16 uniform[-1,1] inputs).
 // First, K <= 128 with at least one wave of 128x128 workgroups and no C
-// operand takes the short-K schedule, whose row-block epilogue overlaps the
-// write of D with the MFMAs (4096 x 4096 x 128: 10.4 us against 11.0 for
-// the tiled 256x256 kernel; 2048 x 2048 x 128: 4.8 against 5.1 us for
-// 128x128 S3).  Otherwise the cheapest of these, in units of
+// operand: where A and B fit in one XCD's L2 (4 MiB), the short-K schedule,
+// whose row-block epilogue overlaps the write of D with the MFMAs; else the
+// persistent 128x128 schedule, which streams a workgroup's tiles through
+// one ring.  HIP-graph replays, short-K / persistent: 4096 x 4096 x 128 9.4
+// / 9.8 us, x 64 8.0 / 9.1, 8192 x 4096 x 128 17.3 / 18.5, 2048 x 2048 x 128
+// 3.9 / 4.5; 81920 x 256 x 128 12.6 / 11.6, 40960 x 512 x 128 12.5 / 11.7,
+// 20480 x 1024 x 128 12.4 / 11.9 (8192 x 8192 x 64 and 16384 x 4096 x 64
+// within 1.5 %).  Otherwise the cheapest of these, in units of
 // one full round of 256 workgroups of the 256x256 kernel:
 //   256x256x64, schedule 10 or 12 (one per CU)       1.00 per round of 256
 //   128x128x64 S2, schedule 1 (two per CU)           0.66 per round of 512
@@ -251,7 +255,9 @@ const Variant *select_variant(int M, int N, int K, bool with_c, double *cost = n
     sg_config c;
     double best = 0.0;
     if (K <= 128 && t128 >= cus && !with_c) {
-        c = sg_config{128, 128, 64, 2, 4, 4};
+        // short-K where A and B fit in one XCD's L2, else persistent
+        const bool fits = ((long long)M + N) * K * 2 <= (4ll << 20);
+        c = fits ? sg_config{128, 128, 64, 2, 4, 4} : sg_config{128, 128, 64, 2, 4, 3};
     } else {
         const double c256 = rounds(t256, cus);
         const double c2 = 0.66 * rounds(t128, 2 * cus);

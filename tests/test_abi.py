@@ -301,6 +301,11 @@ def test_selection_returns_compiled_variants():
     assert _lib.sg_select_config(4096, 4096, 128).as_tuple() == (128, 128, 64, 2, 4, 4)
     assert _lib.sg_select_config(2048, 2048, 128).as_tuple() == (128, 128, 64, 2, 4, 4)
     assert _lib.sg_select_config(2048, 2048, 512).as_tuple() == (128, 128, 64, 3, 4, 1)
+    # K <= 128: short-K while A and B fit in one XCD's L2 (4 MiB), else persistent
+    assert _lib.sg_select_config(8192, 8192, 128).as_tuple() == (128, 128, 64, 2, 4, 4)
+    assert _lib.sg_select_config(8192, 8200, 128).as_tuple() == (128, 128, 64, 2, 4, 3)
+    assert _lib.sg_select_config(81920, 256, 128).as_tuple() == (128, 128, 64, 2, 4, 3)
+    assert _lib.sg_select_config(16384, 4096, 64).as_tuple() == (128, 128, 64, 2, 4, 4)
 
 
 def _gpu_visible() -> bool:

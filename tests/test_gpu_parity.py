@@ -625,6 +625,24 @@ def test_short_k_schedule(shape):
         assert rep.ok, (cfg, str(rep))
 
 
+@pytest.mark.parametrize("shape", [(2048, 2048, 128), (4104, 4096, 64), (8192, 8200, 128),
+                                   (81920, 256, 128), (81928, 256, 64)])
+def test_short_loop_tile_orders(shape):
+    # the short-K and persistent kernels walk their tiles row-major where A
+    # and B fit in one XCD's L2 (4 MiB) and XCD-renumbered where they do
+    # not (8192 x 8200 x 128 is just past it; 81928 rows give a tile count
+    # that is not a multiple of 8, which the renumbering leaves alone); the
+    # library's own choice among them too, every element
+    M, N, K = shape
+    A, B = inputs.operands(M, N, K, 2100 + K, "uniform")
+    ref = oracle.gemm_tn_f64(A, B)
+    for cfg in [None, (128, 128, 64, 2, 4, 3), (128, 128, 64, 2, 4, 4)]:
+        say(f"[case] short-loop order {shape} {cfg}")
+        d = run_gemm(A, B, config=cfg).cpu().numpy()
+        rep = oracle.check(d, ref, K)
+        assert rep.ok, (cfg, str(rep))
+
+
 def test_attention_scores_persistent():
     A, B = inputs.workload("attn_scores")
     alpha = float(np.float32(1.0 / math.sqrt(128.0)))
