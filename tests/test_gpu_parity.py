@@ -521,6 +521,34 @@ def test_graph_replays_match_eager():
             assert torch.equal(tmp.view(torch.int16), eager.view(torch.int16))
 
 
+@pytest.mark.parametrize("shape", [(4096, 4096, 128), (2048, 2048, 16384), (4352, 4104, 1088)])
+def test_bench_launch_function_replays_from_a_graph(shape):
+    # bench.py times launch-bound calls by replaying a captured graph of the
+    # library call it builds (short-K, split-K with its workspace, the
+    # remainder form): the graph must hold the kernels, so a replay rewrites
+    # D with the eager result
+    import os
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+    M, N, K = shape
+    say(f"[case] bench launch function in a graph {shape}")
+    A, B = inputs.operands(M, N, K, 2300 + K)
+    a, b = to_dev(A), to_dev(B)
+    d = torch.empty((M, N), dtype=torch.float16, device=DEV)
+    fn, _, _ = bench.library_call(M, N, K, a, b, d, None)
+    fn()
+    torch.cuda.synchronize()
+    eager = d.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    for _ in range(2):
+        d.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(d.view(torch.int16), eager.view(torch.int16)), shape
+
+
 def test_calls_from_several_host_threads():
     # host threads, each on its own stream, call the tiled (split-load
     # ping-pong), persistent, short-K and attention entry points at once; the
