@@ -383,6 +383,111 @@ def mode_vendor_summary(args) -> int:
     return 0
 
 
+ATTN_C1 = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_ANY "
+           "SQ_WAVE_CYCLES SQ_BUSY_CU_CYCLES SQ_WAIT_INST_ANY SQ_WAIT_ANY GRBM_GUI_ACTIVE")
+ATTN_C2 = ("SQ_WAIT_INST_LDS SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_ACTIVE_INST_LDS SQ_INSTS_VALU "
+           "SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_VALU_TRANS_F32")
+
+
+def mode_attention_summary(args) -> int:
+    """profiles/attention_fwd_4096x4096x128.md from a kernel trace of `python
+    bench.py --mode attention --heads 16 --steps 20 --warmup 30` (--prof-dir
+    /attn, its output in --bench-log) and four counter passes of the same
+    program with --steps 5 --warmup 2 (attn_c1, attn_c2, attn_fetch,
+    attn_write in --prof-dir, beside the copy calibration).  Host-only."""
+    import csv
+    import statistics
+    pdir = args.prof_dir
+    scale = _copy_scales(pdir)
+    with open(args.bench_log) as f:
+        lines = [json.loads(ln) for ln in f if ln.startswith("{") and '"attention"' in ln]
+    trace = _glob1(f"{pdir}/attn/**/*kernel_trace.csv")
+    groups = {}
+    with open(trace) as f:
+        for r in csv.DictReader(f):
+            n = r["Kernel_Name"]
+            kind = "forward" if "attention_fwd_kernel" in n else "merge" if "attention_combine" in n else None
+            if kind is None:
+                continue
+            wgs = int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"])
+            groups.setdefault((kind, wgs, int(r["Workgroup_Size_X"])), []).append(
+                int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    run = "python bench.py --mode attention --heads 16"
+    out = ["# attention_fwd_kernel on 4096 x 4096 x 128 (d = 128), fp16, N(0,1) inputs", "",
+           "Fused O = softmax(alpha Q K^T) V, alpha = fp32(1/sqrt(128)); `bench.py --mode attention` "
+           "(one head with the library's split count, then 16 heads).", "",
+           "## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
+           f"Command: `rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/attn -o attn -- {run} "
+           "--steps 20 --warmup 30`; summarised with `python bench.py --mode attention_summary --prof-dir <dir> "
+           "--bench-log <that run's output>`.", "",
+           "| Kernel | Workgroups x threads | Calls | Average (us) | Median (us) | Min (us) |",
+           "|---|---|---|---|---|---|"]
+    for (kind, wgs, thr), d in sorted(groups.items()):
+        out.append(f"| {kind} | {wgs} x {thr} | {len(d)} | {statistics.mean(d) / 1e3:.1f} | "
+                   f"{statistics.median(d) / 1e3:.1f} | {min(d) / 1e3:.1f} |")
+    out += ["", "The trace includes the warm-up launches. The bench lines printed under the tracer: " +
+            "; ".join(f"{ln['heads']} head(s), {ln['splits']} split(s): {ln['ms'] * 1e3:.1f} us"
+                      for ln in lines) + ".", ""]
+    # counter passes: the 16-head forward launches (the largest grid)
+    fwd, fwd_thr = max(((wgs, thr) for (kind, wgs, thr) in groups if kind == "forward"),
+                       key=lambda x: x[0] * x[1])
+    vals, durs = {}, []
+    for key in ("attn_c1", "attn_c2", "attn_fetch", "attn_write"):
+        per = {}
+        with open(_glob1(f"{pdir}/**/{key}_counter_collection.csv")) as f:
+            for r in csv.DictReader(f):
+                if "attention_fwd_kernel" not in r["Kernel_Name"]:
+                    continue
+                if (int(r["Grid_Size"]) // int(r["Workgroup_Size"]), int(r["Workgroup_Size"])) != (fwd, fwd_thr):
+                    continue
+                wave_per_wg = int(r["Workgroup_Size"]) // 64
+                d = per.setdefault(int(r["Dispatch_Id"]), [{}, 0])
+                d[0][r["Counter_Name"]] = d[0].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+                if r.get("End_Timestamp"):
+                    d[1] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        for c_, dur in per.values():
+            for k, v in c_.items():
+                vals.setdefault(k, []).append(v)
+            if key == "attn_c1" and dur > 0:
+                durs.append(dur)
+    c = {k: statistics.median(v) for k, v in vals.items()}
+    P = f"{run} --steps 5 --warmup 2"
+    out += ["## Counters, 16 heads (one --pmc pass each; median over the 16-head forward launches)", "",
+            f"Commands: `rocprofv3 --pmc {ATTN_C1} --output-format csv -d <dir> -o attn_c1 -- {P}`, "
+            f"`rocprofv3 --pmc {ATTN_C2} --output-format csv -d <dir> -o attn_c2 -- (same)`, then "
+            "`--pmc FETCH_SIZE` (-o attn_fetch) and `--pmc WRITE_SIZE` (-o attn_write), and both on "
+            "`python bench.py --mode calibrate_copy --steps 3 --warmup 1`.", "",
+            "| Counter | Per launch |", "|---|---|"]
+    for k in sorted(c):
+        out.append(f"| {k} | {c[k]:.4g} |")
+    H, M, N, d = 16, 4096, 4096, 128
+    waves = fwd * wave_per_wg
+    tiles = waves * (N // 64)                       # 64-key tiles, every wave all of them
+    dur = statistics.median(durs) if durs else float("nan")
+    fetched = c["FETCH_SIZE"] * 1024 * scale["FETCH_SIZE"]
+    written = c["WRITE_SIZE"] * 1024 * scale["WRITE_SIZE"]
+    comp = 2.0 * H * (2 * M + 2 * N) * d
+    out += ["", "Derived:",
+            f"- shader clock: GRBM_GUI_ACTIVE / 8 XCDs / median duration in the same pass ({dur / 1e3:.1f} us) = "
+            f"{c['GRBM_GUI_ACTIVE'] / 8 / dur:.2f} GHz",
+            f"- MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs over SQ_BUSY_CU_CYCLES / 256 CUs = "
+            f"{100 * (c['SQ_VALU_MFMA_BUSY_CYCLES'] / 1024) / (c['SQ_BUSY_CU_CYCLES'] / 256):.1f} %",
+            f"- VALU co-issued with MFMA: SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES = "
+            f"{100 * c['SQ_VALU_MFMA_COEXEC_CYCLES'] / c['SQ_VALU_MFMA_BUSY_CYCLES']:.1f} %",
+            f"- LDS bank conflicts: {c['SQ_LDS_BANK_CONFLICT']:.0f}",
+            f"- per wave and 64-key tile: {c['SQ_INSTS_MFMA'] / tiles:.0f} MFMA, {c['SQ_INSTS_LDS'] / tiles:.0f} LDS, "
+            f"{c['SQ_INSTS_VALU_TRANS_F32'] / tiles:.1f} transcendental, {c['SQ_INSTS_VALU'] / tiles:.0f} VALU "
+            "instructions (MFMA included)",
+            f"- bytes leaving L2 (copy-scaled, FETCH x{scale['FETCH_SIZE']:.3f}, WRITE x{scale['WRITE_SIZE']:.3f}): "
+            f"fetched {fetched / 1e6:.1f} MB + written {written / 1e6:.1f} MB = {(fetched + written) / 1e6:.1f} MB; "
+            f"compulsory 2 H (2M + 2N) d = {comp / 1e6:.1f} MB, ratio {(fetched + written) / comp:.2f}"]
+    fn = os.path.join(PROFILES, "attention_fwd_4096x4096x128.md")
+    with open(fn, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print(json.dumps({"summary": fn, "forward_wgs": fwd, "dispatches": len(durs)}))
+    return 0
+
+
 def mode_forms(args) -> int:
     """The call forms the library chooses between, interleaved on the same
     uniform [-1, 1] operands: each form's --steps launches captured in one
@@ -1319,7 +1424,8 @@ def main() -> int:
                     choices=["bench", "variants", "ksweep", "calibrate_copy", "attention",
                              "trace_summary", "stage_model", "profile_summary", "ksweep_summary",
                              "lds_patterns", "lds_summary", "variants_summary", "vendor_blas",
-                             "forms", "forms_summary", "vendor_summary"])
+                             "forms", "forms_summary", "vendor_summary",
+                             "attention_summary"])
     ap.add_argument("--trace", default=None, help="kernel-trace CSV for --mode trace_summary")
     ap.add_argument("--bench-log", default=None, help="that run's output for --mode trace_summary")
     ap.add_argument("--prof-dir", default=None,
@@ -1378,6 +1484,8 @@ def main() -> int:
         return mode_forms_summary(args)
     if args.mode == "vendor_summary":
         return mode_vendor_summary(args)
+    if args.mode == "attention_summary":
+        return mode_attention_summary(args)
     if args.mode == "ksweep":
         return mode_ksweep(args)
     if args.mode == "calibrate_copy":
