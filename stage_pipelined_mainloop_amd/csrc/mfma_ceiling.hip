@@ -188,6 +188,71 @@ stage_timing_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__
     }
 }
 
+// LDS-DMA rate probe: the bytes per shader cycle one CU moves from global
+// memory into LDS through the 16-byte-per-lane LDS-DMA loads of the tiled
+// kernels, with every CU streaming at once and nothing else running -- the
+// copy side of the stage-count model of "Lesson 6" (section 4) as a rate
+// rather than a latency.  Workgroup w (4 waves, one per CU) streams the K
+// tiles (64 deep: ROWS rows of 128 bytes per operand) of the A rows of tile
+// row w % tiles_m and the B rows of tile column (w / tiles_m) % tiles_n of an
+// M x K and N x K pair, in order, into a 128 KiB ring, keeping the loads of
+// DEPTH tiles in flight; nothing reads the LDS, so no barrier is needed.
+// out[w * 4 + wave] receives {cycles from the first issue to the last
+// completion (s_memtime), K tiles, bytes per workgroup and K tile, 0}.
+constexpr int vm_wait(int vm) { return (vm & 15) | (7 << 4) | (((vm >> 4) & 3) << 14); }
+
+template <int ROWS, int DEPTH>
+__global__ void __launch_bounds__(256, 1)
+dma_rate_kernel(const _Float16 *__restrict__ A, const _Float16 *__restrict__ B, int K, int tiles_m,
+                int tiles_n, int ntile, unsigned long long *__restrict__ out)
+{
+    constexpr int TILE = 2 * ROWS * 128;           // bytes of one K tile, A and B
+    constexpr int SLOTS = 131072 / TILE;
+    constexpr int NL = ROWS * 128 / (4 * 1024);    // loads per wave per operand and tile
+    static_assert(2 * NL * (DEPTH - 1) <= 63, "vmcnt is a 6-bit counter");
+    __shared__ __attribute__((aligned(1024))) char lds[131072];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tm = blockIdx.x % tiles_m;
+    const int tn = (blockIdx.x / tiles_m) % tiles_n;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<_Float16 *>(A + (size_t)tm * ROWS * K), (short)0, ROWS * K * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<_Float16 *>(B + (size_t)tn * ROWS * K), (short)0, ROWS * K * 2, 0x00020000);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    const unsigned long long c0 = __builtin_amdgcn_s_memtime();
+    __builtin_amdgcn_sched_barrier(0);
+    for (int t = 0; t < ntile; ++t) {
+        char *slot = lds + (t % SLOTS) * TILE;
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            // load j of this wave: 1 KiB = 8 rows of the K tile's 128 bytes
+            const int q = (j * 4 + wave) * 64 + lane;
+            const uint32_t off = (uint32_t)(((q >> 3) * K + t * 64 + (q & 7) * 8) * 2);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ra, (__attribute__((address_space(3))) void *)(slot + (j * 4 + wave) * 1024), 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rb, (__attribute__((address_space(3))) void *)(slot + ROWS * 128 + (j * 4 + wave) * 1024), 16,
+                off, 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(vm_wait(2 * NL * (DEPTH - 1)));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_waitcnt(vm_wait(0));
+    __builtin_amdgcn_sched_barrier(0);
+    const unsigned long long c1 = __builtin_amdgcn_s_memtime();
+    __builtin_amdgcn_sched_barrier(0);
+    if (lane == 0) {
+        unsigned long long *o = out + ((size_t)blockIdx.x * 4 + wave) * 4;
+        o[0] = c1 - c0;
+        o[1] = (unsigned long long)ntile;
+        o[2] = (unsigned long long)TILE;
+        o[3] = 0;
+    }
+}
+
 // LDS access-pattern probe: one wave per workgroup repeats one pattern of
 // 64-bit writes or 128-bit reads over an epilogue staging block (32 rows of
 // 64 fp16), `iters` times; run under the LDS bank-conflict counters, it
@@ -294,6 +359,40 @@ int sg_probe_stage_timing(const void *A, long long M, const void *B, long long N
                                 dim3(512), args, 0, static_cast<hipStream_t>(stream));
 }
 
+// LDS-DMA rate probe launch: rows 128 or 256 per operand tile, depth 1..4
+// tiles in flight, `blocks` workgroups (one per CU is the intended use) over
+// an M x K (A) and N x K (B) fp16 pair with M >= rows * tiles_m and N >=
+// rows * tiles_n (tiles_m, tiles_n >= 1); K a positive multiple of 64 below
+// 2^21; 1 <= ntile <= K / 64; out: device buffer of blocks * 16 64-bit words.
+// Returns a hipError_t value (hipErrorInvalidValue for arguments outside
+// these bounds, checked here before the launch).
+int sg_probe_dma_rate(const void *A, long long M, const void *B, long long N, int K, int rows,
+                      int depth, int tiles_m, int tiles_n, int blocks, int ntile, void *out,
+                      void *stream)
+{
+    if (!A || !B || !out || K <= 0 || (K & 63) || K > (1 << 21) || tiles_m <= 0 || tiles_n <= 0 ||
+        blocks <= 0 || ntile <= 0 || ntile > K / 64 || (rows != 128 && rows != 256) || depth < 1 ||
+        depth > 4)
+        return (int)hipErrorInvalidValue;
+    if (M < (long long)rows * tiles_m || N < (long long)rows * tiles_n ||
+        (long long)rows * K * 2 >= (1LL << 31))
+        return (int)hipErrorInvalidValue;
+    static const void *const kernels[2][4] = {
+        {reinterpret_cast<const void *>(&dma_rate_kernel<128, 1>),
+         reinterpret_cast<const void *>(&dma_rate_kernel<128, 2>),
+         reinterpret_cast<const void *>(&dma_rate_kernel<128, 3>),
+         reinterpret_cast<const void *>(&dma_rate_kernel<128, 4>)},
+        {reinterpret_cast<const void *>(&dma_rate_kernel<256, 1>),
+         reinterpret_cast<const void *>(&dma_rate_kernel<256, 2>),
+         reinterpret_cast<const void *>(&dma_rate_kernel<256, 3>),
+         reinterpret_cast<const void *>(&dma_rate_kernel<256, 4>)}};
+    const _Float16 *a = static_cast<const _Float16 *>(A);
+    const _Float16 *b = static_cast<const _Float16 *>(B);
+    unsigned long long *o = static_cast<unsigned long long *>(out);
+    void *args[] = {&a, &b, &K, &tiles_m, &tiles_n, &ntile, &o};
+    return (int)hipLaunchKernel(kernels[rows == 256][depth - 1], dim3(blocks), dim3(256), args, 0,
+                                static_cast<hipStream_t>(stream));
+}
 
 // Flops one launch performs: blocks x 4 waves x iters x 16 x 8 MFMAs of
 // 2 * 32 * 32 * 16 flop.
