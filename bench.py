@@ -1427,7 +1427,10 @@ def mode_dma_rate(args) -> int:
     and nothing else running (the probe library's sg_probe_dma_rate).  Tiles
     of 128 rows per operand run on the M = N = 2048, K = 8192 sweep operands
     (a 16 x 16 grid, as the 128x128 kernels see it), tiles of 256 rows on the
-    8192^3 operands.  Each line also gives the MFMA-busy fraction that rate
+    8192^3 operands, and again on the 8000 x 7936 x 8200 operands, whose rows
+    start 16 bytes apart from one 128-byte line to the next, so that each
+    row's 128 bytes of a K tile straddle two lines (K tiles past K / 64 are
+    not streamed).  Each line also gives the MFMA-busy fraction that rate
     could feed at 4096 fp16 flop per CU and cycle (the dense peak per CU):
     2 x 128 x 128 x 64 flop per 32 KiB tile (64 flop per byte), 2 x 256 x 256
     x 64 per 64 KiB (128 flop per byte)."""
@@ -1445,7 +1448,8 @@ def mode_dma_rate(args) -> int:
     P.sg_probe_dma_rate.restype = ctypes.c_int
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     stream = torch.cuda.current_stream()
-    for rows, (A, B) in ((128, inputs.ksweep(8192)), (256, inputs.workload("square8192"))):
+    for rows, (A, B) in ((128, inputs.ksweep(8192)), (256, inputs.workload("square8192")),
+                         (256, inputs.workload("ragged8000"))):
         M, K = A.shape
         N = B.shape[0]
         a, b = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()

@@ -362,15 +362,17 @@ int sg_probe_stage_timing(const void *A, long long M, const void *B, long long N
 // LDS-DMA rate probe launch: rows 128 or 256 per operand tile, depth 1..4
 // tiles in flight, `blocks` workgroups (one per CU is the intended use) over
 // an M x K (A) and N x K (B) fp16 pair with M >= rows * tiles_m and N >=
-// rows * tiles_n (tiles_m, tiles_n >= 1); K a positive multiple of 64 below
-// 2^21; 1 <= ntile <= K / 64; out: device buffer of blocks * 16 64-bit words.
+// rows * tiles_n (tiles_m, tiles_n >= 1); K a positive multiple of 8 below
+// 2^21 (rows start on 16-byte boundaries; with K % 64 != 0 they straddle
+// 128-byte lines, as in the GEMM); 1 <= ntile <= K / 64; out: device buffer
+// of blocks * 16 64-bit words.
 // Returns a hipError_t value (hipErrorInvalidValue for arguments outside
 // these bounds, checked here before the launch).
 int sg_probe_dma_rate(const void *A, long long M, const void *B, long long N, int K, int rows,
                       int depth, int tiles_m, int tiles_n, int blocks, int ntile, void *out,
                       void *stream)
 {
-    if (!A || !B || !out || K <= 0 || (K & 63) || K > (1 << 21) || tiles_m <= 0 || tiles_n <= 0 ||
+    if (!A || !B || !out || K <= 0 || (K & 7) || K > (1 << 21) || tiles_m <= 0 || tiles_n <= 0 ||
         blocks <= 0 || ntile <= 0 || ntile > K / 64 || (rows != 128 && rows != 256) || depth < 1 ||
         depth > 4)
         return (int)hipErrorInvalidValue;
