@@ -185,7 +185,12 @@ const Variant *find_variant(const sg_config *c)
 //     and rows on 128-byte lines, else S3 schedule 1  0.34 or 0.42 per round of 256
 //   128x128x64 S2 persistent (K <= 1024, no C)       0.9 x the S2 figure
 // A partial round costs 0.75 + 0.25 x its fill: its workgroups still run
-// the whole K loop, only with less contention.  Fitted to interleaved
+// the whole K loop, only with less contention.  Each per-round figure is the
+// family's flops per round relative to a 256x256 round over its MFMA busy
+// relative to the 256x256 kernel's (about 0.90): 0.34 = 0.25 x 0.90 / 0.66,
+// 0.66 being schedule 14's busy at M = N = 2048, K = 8192, where the
+// LDS-DMA rate of about 45 bytes per cycle per CU caps a 128x128x64 tile at
+// 0.71 (64 bytes per cycle needed at the full MFMA rate).  Fitted to interleaved
 // timings at K = 4096 (2560^2 ... 6144^2, 16384 x 1024, 81920 x 256) and
 // 8192 (2048^2, 2560^2); it picks the faster family at every one of them,
 // and at K = 1024 and 512 it is within 2 % of the best choice.  The
